@@ -1,0 +1,187 @@
+"""Pins for the CPU oracle's exact top-k (no GPU).
+
+Each test checks the oracle against something other than itself: the O(n^2)
+rank-by-counting definition, closed forms, numpy's own sorts on the float
+values, the counting bisection, or invariants that fix the answer.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check_rank_order(x, k, dtype=None):
+    """Oracle output must equal the elements of rank 0..k-1 in rank order."""
+    x = np.asarray(x)
+    ranks = oracle.rank_by_counting(x, dtype)
+    assert sorted(ranks.tolist()) == list(range(x.size)), "ranks must be a permutation"
+    expect_idx = np.argsort(ranks)[:k]
+    ov, oi = oracle.topk(x, k, dtype)
+    assert oi[0].tolist() == expect_idx.tolist()
+    assert ov[0].view(np.uint8).tobytes() == x[expect_idx].view(np.uint8).tobytes()
+
+
+# ------------------------------------------------------------------ keys
+def test_key_order_special_floats():
+    vals = np.array([np.nan, np.inf, 1.0, 1e-45, 0.0, -0.0, -1e-45, -1.0, -np.inf],
+                    dtype=np.float32)
+    k = oracle.keys(vals)
+    assert k[0] == 0xFFFFFFFF                       # NaN above everything
+    assert k[1] > k[2] > k[3] > k[4]
+    assert k[4] == k[5] == 0x80000000               # -0.0 is +0.0
+    assert k[5] > k[6] > k[7] > k[8]
+    neg_nan = np.array([0xFFC00001], dtype=np.uint32).view(np.float32)
+    assert oracle.keys(neg_nan)[0] == 0xFFFFFFFF
+
+
+def test_keys_numpy_and_c_agree():
+    g = workloads.rng(7)
+    f = g.standard_normal(20000).astype(np.float32)
+    f[:6] = [np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0]
+    raw = g.integers(0, 2 ** 32, 5000, dtype=np.uint64).astype(np.uint32)
+    for arr, dt in [(f, None), (raw.view(np.float32), None),
+                    (g.integers(-2 ** 31, 2 ** 31, 20000, dtype=np.int64).astype(np.int32), None),
+                    (raw.astype(np.uint16), "bf16")]:
+        assert np.array_equal(oracle.keys(arr, dt), oracle.keys_c(arr, dt))
+
+
+def test_key_order_matches_numpy_sort_f32_i32_bf16():
+    g = workloads.rng(11)
+    f = (g.standard_normal(5000) * 100).astype(np.float32)
+    o = np.argsort(oracle.keys(f), kind="stable")
+    assert np.all(np.diff(f[o].astype(np.float64)) >= 0)
+    i = g.integers(-2 ** 31, 2 ** 31, 5000, dtype=np.int64).astype(np.int32)
+    i[:2] = [-2 ** 31, 2 ** 31 - 1]
+    o = np.argsort(oracle.keys(i), kind="stable")
+    assert np.all(np.diff(i[o].astype(np.int64)) >= 0)
+    b = workloads.f32_to_bf16_bits(f)
+    as_f = (b.astype(np.uint32) << 16).view(np.float32)
+    o = np.argsort(oracle.keys(b, "bf16"), kind="stable")
+    assert np.all(np.diff(as_f[o].astype(np.float64)) >= 0)
+
+
+# ------------------------------------------------------------------ rank definition
+def test_rank_figure_fixture():
+    fx = json.load(open(os.path.join(GOLD, "rank_figure.json")))
+    x = np.array(fx["scores"], dtype=np.int32)
+    r = oracle.rank_by_counting(x)
+    assert r[fx["highlighted"]] == fx["rank"]
+    assert r[np.argmax(x)] == 0
+    assert sorted(r.tolist()) == list(range(len(x)))
+
+
+def test_topk_equals_rank_order_config1_full():
+    x, dt, ks, _ = workloads.config("c1")
+    row = x[0]
+    for k in ks + [1, 100, 4096]:
+        _check_rank_order(row, k)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_equals_rank_order_random_ties(seed):
+    g = workloads.rng(100 + seed)
+    n = int(g.integers(1, 700))
+    k = int(g.integers(1, n + 1))
+    _check_rank_order(g.integers(-3, 4, n).astype(np.int32), k)
+    f = g.integers(-4, 5, n).astype(np.float32) * np.float32(0.5)
+    f[g.random(n) < 0.1] = -0.0
+    f[g.random(n) < 0.05] = np.nan
+    _check_rank_order(f, k)
+    b = workloads.f32_to_bf16_bits(g.standard_normal(n).astype(np.float32) * 4)
+    _check_rank_order(b, k, "bf16")
+
+
+# ------------------------------------------------------------------ closed forms
+def test_closed_forms():
+    n = 1000
+    eq = np.full(n, 7, dtype=np.int32)
+    assert oracle.topk(eq, 37)[1][0].tolist() == list(range(37))
+    asc = np.arange(n, dtype=np.float32) - 500
+    assert oracle.topk(asc, 5)[1][0].tolist() == [n - 1, n - 2, n - 3, n - 4, n - 5]
+    desc = asc[::-1].copy()
+    assert oracle.topk(desc, 5)[1][0].tolist() == [0, 1, 2, 3, 4]
+    g = workloads.rng(3)
+    x = g.integers(0, 20, n).astype(np.float32)
+    # k = n: a full stable sort, value descending, lower index first on ties
+    full = np.lexsort((np.arange(n), -x.astype(np.float64)))
+    assert oracle.topk(x, n)[1][0].tolist() == full.tolist()
+    # k = 1: the lowest-index maximum
+    assert oracle.topk(x, 1)[1][0, 0] == int(np.argmax(x))
+
+
+def test_planted_rows_closed_form():
+    x = workloads.planted(4, 5000, 64, 99)
+    ov, oi = oracle.topk(x, 64)
+    for r in range(4):
+        assert np.all(ov[r] == 1.0)
+        assert oi[r].tolist() == sorted(np.flatnonzero(x[r] == 1.0).tolist())
+
+
+def test_nan_and_signed_zero_bits_are_returned():
+    x = np.array([0.0, -0.0, np.nan, 1.0, -np.nan, -0.0], dtype=np.float32)
+    x[4] = np.array([0xFFC00001], dtype=np.uint32).view(np.float32)[0]
+    ov, oi = oracle.topk(x, 6)
+    assert oi[0].tolist() == [2, 4, 3, 0, 1, 5]
+    assert ov[0].view(np.uint32).tolist() == x[[2, 4, 3, 0, 1, 5]].view(np.uint32).tolist()
+
+
+def test_int32_extremes():
+    x = np.array([5, -2 ** 31, 2 ** 31 - 1, 0, -1, 2 ** 31 - 1], dtype=np.int32)
+    ov, oi = oracle.topk(x, 6)
+    assert oi[0].tolist() == [2, 5, 0, 3, 4, 1]
+
+
+def test_rejects_bad_arguments():
+    x = np.zeros(10, dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle.topk(x, 11)
+    with pytest.raises(ValueError):
+        oracle.topk(x, 0)
+
+
+# ------------------------------------------------------------------ invariants
+def _invariant(row, ov, oi, dtype=None):
+    rk = oracle.keys(row, dtype)
+    k = oi.size
+    for r in range(k):
+        assert oracle.outranking(rk, int(rk[oi[r]]), int(oi[r])) == r
+
+
+def test_invariant_exactly_r_outrank_output_r():
+    g = workloads.rng(5)
+    row = workloads.pareto_signed(1, 50000, 5)[0]
+    ov, oi = oracle.topk(row, 50)
+    _invariant(row, ov[0], oi[0])
+    ir = g.integers(0, 300, 20000).astype(np.int32)
+    ov, oi = oracle.topk(ir, 64)
+    _invariant(ir, ov[0], oi[0])
+
+
+# ------------------------------------------------------------------ config 2 and the bisection
+def test_config2_bisection_cutoff():
+    x, dt, ks, meta = workloads.config("c2")
+    row = x[0]
+    k = ks[0]
+    ov, oi = oracle.topk(row, k)
+    cutoff, count, steps = oracle.bisection_cutoff(row, k)
+    assert count == k                          # exactly k scores clear it
+    assert cutoff == int(ov[0, k - 1]) - 1     # integer scores: one below the k-th
+    assert 15 <= steps <= 30
+    # with equal k-th and (k+1)-th scores no cutoff separates them
+    tied = np.array([9, 9, 8, 5, 5, 5, 1], dtype=np.int32)
+    c, cnt, _ = oracle.bisection_cutoff(tied, 4)
+    assert cnt != 4
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = workloads.rng(2).standard_normal(100000).astype(np.float32) * 3
+    ours = workloads.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
