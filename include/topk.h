@@ -1,0 +1,152 @@
+/*
+ * topk.h - C ABI of the MI355X exact top-k selection library (libtopk_mi355x).
+ *
+ * What it computes: for each of `rows` contiguous rows of `n` elements, the k
+ * largest entries together with their indices (Prof-K paper, section 3
+ * "Problem Setup"; a batch applies the selection to each row).  The output is
+ * in rank order: value descending, and on equal values the lower index first
+ * (GPU.js Learn "Rank by Counting": an element is outranked by every larger
+ * value and by every equal value at a lower index).  Values are compared as
+ * follows (readings where the pages are silent): -0.0 equals +0.0; every NaN
+ * ranks above +inf; NaNs tie with each other and are ordered by index.
+ *
+ * How: Prof-K one-pass filtering (section 3 "The Prof-K Algorithm" and
+ * Algorithm 1): a device-side sample gives a threshold tau, one streaming
+ * pass keeps every element >= tau in a bounded candidate buffer, and an exact
+ * radix select plus sort of that buffer yields the answer.  If fewer than k
+ * candidates survive or the buffer overflows, an exact radix select over the
+ * full row runs instead, so the result is always the exact top-k.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are plain device addresses (memory from hipMalloc or a
+ *     framework allocator); the caller owns all memory, the library allocates
+ *     no device memory.
+ *   - `values`: [rows, n] contiguous, element-aligned (4 bytes for int32 and
+ *     float32, 2 bytes for bf16); 1 <= n < 2^32, rows >= 1, 1 <= k <= n.
+ *   - `out_values`: [rows, k] of the input dtype; each output is the exact bit
+ *     pattern of the selected input element.  `out_indices`: [rows, k] int64,
+ *     row-local indices.
+ *   - `workspace`: device memory of at least topk_workspace_size() bytes.  It
+ *     must be zero-filled before its first use (topk_workspace_init does
+ *     that); afterwards every completed call leaves it ready for the next one,
+ *     whatever the shape.  One workspace must not be used by two calls that
+ *     may run at the same time.
+ *   - `stream`: a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; no host synchronisation happens
+ *     inside topk/topk_ex.
+ *   - Errors: argument problems return a negative status before anything is
+ *     enqueued; a HIP launch failure returns TOPK_EHIP.  No exception crosses
+ *     the ABI.  After TOPK_EHIP the workspace contents are undefined: call
+ *     topk_workspace_init again.
+ */
+#ifndef TOPK_MI355X_H
+#define TOPK_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TOPK_I32 = 0, TOPK_F32 = 1, TOPK_BF16 = 2 } topk_dtype;
+
+typedef enum {
+  TOPK_OK = 0,
+  TOPK_EINVAL = -1,     /* bad shape, k, pointer or alignment */
+  TOPK_EDTYPE = -2,     /* unknown dtype */
+  TOPK_EWORKSPACE = -3, /* workspace too small */
+  TOPK_EHIP = -4,       /* a HIP call failed */
+  TOPK_ENOTIMPL = -5
+} topk_status;
+
+/* Parameter policy for (S, t, M).
+ *  TOPK_POLICY_EXACT_TAIL (default): S from Algorithm 1; t and M the least
+ *    values meeting the two conditions of Theorem 3 (recall failure R < k and
+ *    overflow R > M each at most eps/2), evaluated with the exact
+ *    hypergeometric law that Lemma 1 gives for the threshold rank.
+ *  TOPK_POLICY_ALG1: Algorithm 1 verbatim (normal approximation of Lemma 2,
+ *    t = 1 when alpha*S < -ln(eps/2)). */
+typedef enum { TOPK_POLICY_EXACT_TAIL = 0, TOPK_POLICY_ALG1 = 1 } topk_policy;
+
+/* Route.  AUTO: the sampled filter when n >= 8*S and the buffer M is below
+ * n/2, else the exact radix select.  FILTER / EXACT force one route (FILTER
+ * still falls back to the exact select when the sample fails). */
+typedef enum { TOPK_PATH_AUTO = 0, TOPK_PATH_FILTER = 1, TOPK_PATH_EXACT = 2 } topk_path;
+
+typedef struct {
+  double eps;         /* failure budget, Algorithm 1 input (default 1e-3) */
+  int64_t s_min;      /* sample size bounds (default 32768 and 131072) */
+  int64_t s_max;
+  double cost_ratio;  /* tau_B / tau_A of Eq. 13 (default 1) */
+  int32_t policy;     /* topk_policy */
+  int32_t force_path; /* topk_path */
+  uint64_t seed;      /* sampler seed when use_seed != 0 */
+  int32_t use_seed;   /* 0: a fresh seed per call (a process-wide counter) */
+  int32_t reserved;
+  int64_t S;          /* > 0: override the sample size */
+  int64_t t;          /* > 0: override the threshold rank */
+  int64_t M;          /* > 0: override the buffer capacity */
+} topk_params;
+
+/* Resolved plan of one call shape (host arithmetic only; no GPU needed). */
+typedef struct {
+  int32_t path;       /* 0 sampled filter, 1 exact multi-workgroup, 2 exact one workgroup per row */
+  int32_t small_k;    /* 1: k winners sorted in one workgroup; 0: multi-workgroup sort */
+  int64_t S, t, M;    /* sample size, threshold rank, buffer capacity (sampled route) */
+  int64_t cap;        /* candidate buffer capacity per row */
+  int32_t index_bits; /* B: bits of the index field of the composite */
+  int32_t key_bits;   /* 32 (int32, float32) or 16 (bf16) */
+  double p_recall;    /* P(R < k) for distinct values (Lemma 1), sampled route */
+  double p_overflow;  /* P(R > M) for distinct values (Lemma 1), sampled route */
+  size_t workspace_bytes;
+} topk_plan_info;
+
+/* Per-row record of the last call on a workspace (topk_read_stats). */
+typedef struct {
+  uint32_t tau_key;   /* sampled threshold as an order-preserving key */
+  uint32_t r_sampled; /* survivors of the sampled filter pass (R) */
+  uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only */
+  uint32_t passes;    /* histogram passes of the exact select */
+} topk_row_stats;
+
+/* Fill *p with the defaults above.  Returns TOPK_OK, or TOPK_EINVAL for NULL. */
+int topk_default_params(topk_params* p);
+
+/* Plan of a call shape under `params` (NULL = defaults): Algorithm 1 and the
+ * chosen policy, the route, the buffer capacity and the workspace size.
+ * Host arithmetic only.  Errors: TOPK_EINVAL, TOPK_EDTYPE. */
+int topk_plan(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
+              topk_plan_info* out);
+
+/* Workspace bytes one call of this shape needs (params NULL = defaults). */
+int topk_workspace_size(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
+                        size_t* bytes);
+
+/* Zero-fill `bytes` of workspace on `stream` with a fill kernel (no memset
+ * node, so it can sit inside a captured graph). */
+int topk_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Exact top-k with default parameters.  See the conventions above. */
+int topk(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+         int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream);
+
+/* topk with explicit parameters (NULL = defaults).  The result is the exact
+ * top-k whatever the parameters; they only move work between the sampled
+ * route and the exact fallback. */
+int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+            int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
+            const topk_params* params);
+
+/* Copy the per-row records of the last call on `workspace` into out[0..rows)
+ * (host memory).  Synchronises `stream`.  Errors: TOPK_EINVAL, TOPK_EHIP. */
+int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, void* stream);
+
+/* Short English text for a status code (static storage). */
+const char* topk_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_MI355X_H */

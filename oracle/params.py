@@ -43,6 +43,7 @@ def alg1(N: int, k: int, eps: float = EPS_DEFAULT, s_min: int = S_MIN_DEFAULT,
     log2k = math.log2(k)
     s_star = (z * ratio * log2k / 2) ** (2.0 / 3.0) * (k * (N - k)) ** (1.0 / 3.0)
     S = min(s_max, max(s_min, int(math.floor(s_star + 0.5))))
+    S = min(S, N)          # stage 1 draws S of the N items without replacement
     f = 1 - S / N
     t = max(1, math.ceil(S * alpha + (z / 2) * math.sqrt(S * alpha * (1 - alpha) * f)))
     M = math.ceil(k + z * math.sqrt(k * (N - k) / S * f))
@@ -107,14 +108,38 @@ def hyper_sf(N: int, K: int, S: int, t: int) -> float:
     j, lp = walk[-1]
     mode = (K + 1) * (S + 1) // (N + 2)
     terms = []
+    running = 0.0
     while True:
         p = math.exp(lp)
         terms.append(p)
-        if j >= hi or (j > mode and p < math.fsum(terms) * 1e-18):
+        running += p
+        if j >= hi or (j > mode and p < running * 1e-18):
             break
         lp += math.log((K - j) * (S - j)) - math.log((j + 1) * (N - K - S + j + 1))
         j += 1
     return math.fsum(terms)
+
+
+def _upper_tails(N: int, K: int, S: int):
+    """(j0, sf) with sf[i] = P(H >= j0 + i), from one walk of the pmf."""
+    hi = min(K, S)
+    mode = (K + 1) * (S + 1) // (N + 2)
+    walk = _log_pmf_walk(N, K, S, min(hi, mode))
+    j, lp = walk[-1]
+    pm = [math.exp(v) for _, v in walk]
+    running = math.fsum(pm)
+    while j < hi:
+        lp += math.log((K - j) * (S - j)) - math.log((j + 1) * (N - K - S + j + 1))
+        j += 1
+        p = math.exp(lp)
+        pm.append(p)
+        running += p
+        if j > mode and p < running * 1e-18:
+            break
+    sf = [0.0] * (len(pm) + 1)
+    for i in range(len(pm) - 1, -1, -1):
+        sf[i] = sf[i + 1] + pm[i]
+    return walk[0][0], sf
 
 
 def exact_tail(N: int, k: int, eps: float = EPS_DEFAULT, s_min: int = S_MIN_DEFAULT,
@@ -124,8 +149,16 @@ def exact_tail(N: int, k: int, eps: float = EPS_DEFAULT, s_min: int = S_MIN_DEFA
     S = alg1(N, k, eps, s_min, s_max, ratio)["S"]
     half = eps / 2
     t = 1
-    while t < S and hyper_sf(N, k - 1, S, t) > half:
-        t += 1
+    if k > 1:
+        j0, sf = _upper_tails(N, k - 1, S)
+
+        def tail(tt):
+            if tt <= j0:
+                return 1.0
+            i = tt - j0
+            return sf[i] if i < len(sf) else 0.0
+        while t < S and tail(t) > half:
+            t += 1
     lo, hi = k, N
     if hyper_cdf(N, hi, S, t - 1) > half:
         M = N

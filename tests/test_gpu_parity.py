@@ -1,0 +1,264 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element
+(indices and value bits, tolerance 0), through the C ABI.
+
+Sizes here finish on the oracle in seconds and still span many workgroup
+tiles and ragged tails; the full headline shapes are in test_gpu_full.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import assert_same, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _tss():
+    import top_selection_sample_amd as tss
+    return tss
+
+
+def _seeded(seed, **kw):
+    return _tss().default_params(seed=seed, use_seed=1, **kw)
+
+
+# ------------------------------------------------------------ small configs
+def test_config1_heavy_ties():
+    x, dt, ks, _ = workloads.config("c1")
+    say("config 1: int32 [1, 4096] k=10")
+    gv, gi = run_gpu(x, 10, dt)
+    assert_same(gv, gi, x, 10, dt, "c1")
+    ranks = oracle.rank_by_counting(x[0])
+    assert gi[0].tolist() == np.argsort(ranks)[:10].tolist()
+
+
+def test_config2_and_bisection():
+    x, dt, ks, meta = workloads.config("c2")
+    say(f"config 2: int32 [1, 65536] k=10 seed {meta['seed']}")
+    gv, gi = run_gpu(x, 10, dt)
+    assert_same(gv, gi, x, 10, dt, "c2")
+    cutoff, count, _ = oracle.bisection_cutoff(x[0], 10)
+    assert count == 10 and cutoff == int(gv[0, 9]) - 1
+
+
+# ------------------------------------------------------------ edge cases
+def _edge_rows(dt, n, kind, seed):
+    g = workloads.rng(seed)
+    if kind == "equal":
+        base = np.full(n, 3.0)
+    elif kind == "asc":
+        base = np.arange(n, dtype=np.float64) - n / 2
+    elif kind == "desc":
+        base = -(np.arange(n, dtype=np.float64) - n / 2)
+    elif kind == "ties":
+        base = g.integers(-5, 6, n).astype(np.float64)
+    else:
+        base = g.standard_normal(n) * 100
+    if dt == "int32":
+        x = base.astype(np.int32)
+        if kind == "special":
+            x[: min(n, 4)] = np.array([2 ** 31 - 1, -2 ** 31, 0, -1], dtype=np.int32)[: min(n, 4)]
+        return x[None, :]
+    f = base.astype(np.float32)
+    if kind == "special":
+        sp = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 1e-45, -1e-45], dtype=np.float32)
+        f[g.choice(n, min(n, 40), replace=False)] = sp[g.integers(0, len(sp), min(n, 40))]
+        if n > 3:
+            f[1] = np.array([0xFFC00001], dtype=np.uint32).view(np.float32)[0]   # negative NaN
+    if dt == "bf16":
+        b = f.view(np.uint32)
+        nan = (b & 0x7FFFFFFF) > 0x7F800000
+        out = workloads.f32_to_bf16_bits(np.where(nan, 0, f).astype(np.float32))
+        out[nan] = (b[nan] >> 16).astype(np.uint16) | 0x0040
+        return out[None, :]
+    return f[None, :]
+
+
+@pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])
+@pytest.mark.parametrize("kind", ["equal", "asc", "desc", "ties", "special", "normal"])
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (7, 7), (1000, 1), (1000, 1000), (4099, 64),
+                                 (70001, 4096), (70001, 4097), (300007, 33)])
+def test_edge_shapes(dt, kind, n, k):
+    x = _edge_rows(dt, n, kind, n + k)
+    say(f"edge {dt} {kind} n={n} k={k}")
+    gv, gi = run_gpu(x, k, dt)
+    assert_same(gv, gi, x, k, dt, f"{dt}/{kind}/{n}/{k}")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3, 5])
+def test_offset_pointer(offset):
+    # a view that starts at an element offset: rows are not 16-byte aligned
+    full = workloads.normal_f32(1, 400_000 + offset, 31)[0]
+    x = full[offset:][None, :]
+    say(f"offset pointer {offset}")
+    xt = to_dev(full, "float32")[offset:]
+    gv, gi = run_gpu(x, 100, "float32", xt=xt.reshape(1, -1))
+    assert_same(gv, gi, x, 100, "float32", "offset")
+    xb = workloads.relu_bf16(1, 400_000 + offset, 32)[0]
+    xbt = to_dev(xb, "bf16")[offset:]
+    gv, gi = run_gpu(xb[offset:][None, :], 100, "bf16", xt=xbt.reshape(1, -1))
+    assert_same(gv, gi, xb[offset:][None, :], 100, "bf16", "offset bf16")
+
+
+# ------------------------------------------------------------ sampled route
+@pytest.mark.parametrize("k", [1, 16, 64, 2048, 4096])
+def test_sampled_route_fp32(k):
+    n = 3 * 2 ** 20 + 77
+    x = workloads.normal_f32(1, n, 100 + k)
+    say(f"sampled fp32 n={n} k={k}")
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", f"sampled k={k}")
+    st = _tss().read_stats(1)
+    assert st[0]["path"] in (0, 1)
+
+
+@pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])
+def test_tau_and_R_match_sampler_spec(dt):
+    """The device's threshold key and survivor count equal the oracle's
+    sampler for the same seed (Prof-K stages 1-3)."""
+    n = 2 ** 21 + 13
+    if dt == "int32":
+        x = workloads.scores_int(1, n, -10 ** 6, 10 ** 6, 41)
+    elif dt == "bf16":
+        x = workloads.relu_bf16(1, n, 42)
+    else:
+        x = workloads.pareto_signed(1, n, 43)
+    k = 64
+    tss = _tss()
+    pl = tss.plan(n, 1, k, dt)
+    for seed in (1, 2, 3):
+        p = _seeded(seed)
+        say(f"tau/R {dt} seed {seed}")
+        gv, gi = run_gpu(x, k, dt, params=p)
+        assert_same(gv, gi, x, k, dt, f"tau {dt}")
+        st = tss.read_stats(1)[0]
+        tk, R = oracle.tau(x[0], seed, 0, pl["S"], pl["t"], dt)
+        assert st["tau_key"] == tk
+        assert st["r_sampled"] == R
+        exp_path = 0 if (k <= R <= pl["cap"]) else 1
+        assert st["path"] == exp_path
+
+
+def test_forced_overflow_fallback():
+    n = 2 ** 21 + 5
+    x = workloads.normal_f32(1, n, 51)
+    p = _seeded(7, M=100, force_path=1)
+    say("forced overflow")
+    gv, gi = run_gpu(x, 64, "float32", params=p)
+    assert_same(gv, gi, x, 64, "float32", "overflow")
+    st = _tss().read_stats(1)[0]
+    assert st["path"] == 1 and st["r_sampled"] > 100
+
+
+def test_forced_recall_failure_fallback():
+    n = 2 ** 21 + 5
+    x = workloads.normal_f32(1, n, 52)
+    p = _seeded(8, t=1, force_path=1)       # tau = sample maximum: R is small
+    say("forced recall failure")
+    gv, gi = run_gpu(x, 1000, "float32", params=p)
+    assert_same(gv, gi, x, 1000, "float32", "recall")
+    st = _tss().read_stats(1)[0]
+    assert st["path"] == 1 and st["r_sampled"] < 1000
+
+
+@pytest.mark.parametrize("dt", ["float32", "bf16"])
+def test_forced_exact_large_row(dt):
+    n = 2 ** 22 + 3
+    x = workloads.normal_f32(1, n, 53) if dt == "float32" else workloads.relu_bf16(1, n, 53)
+    p = _tss().default_params(force_path=2)
+    say(f"forced exact {dt}")
+    for k in (10, 5000):
+        gv, gi = run_gpu(x, k, dt, params=p)
+        assert_same(gv, gi, x, k, dt, f"exact {dt} k={k}")
+        assert _tss().read_stats(1)[0]["path"] == 2
+
+
+def test_exact_route_all_equal_large_row():
+    # ties far beyond the buffer capacity: the index digits decide
+    n = 2 ** 21
+    x = np.full((1, n), 2.5, dtype=np.float32)
+    p = _tss().default_params(force_path=2)
+    gv, gi = run_gpu(x, 300, "float32", params=p)
+    assert_same(gv, gi, x, 300, "float32", "all-equal exact")
+    gv, gi = run_gpu(x, 300, "float32")
+    assert_same(gv, gi, x, 300, "float32", "all-equal auto")
+
+
+# ------------------------------------------------------------ batched rows
+@pytest.mark.parametrize("variant", ["c4v1", "c4v2", "c4v3"])
+def test_batched_rows_reduced(variant):
+    rows, n, k = 12, 2 ** 20, 64
+    if variant == "c4v3":
+        x = workloads.planted(rows, n, 64, 61)
+    else:
+        x = workloads.pareto_signed(rows, n, 61)
+        if variant == "c4v2":
+            x = workloads.sorted_rows(x)
+    say(f"batched {variant} rows={rows}")
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", variant)
+
+
+def test_batched_small_rows_exact():
+    x = workloads.scores_int(300, 5000, 0, 50, 62)
+    gv, gi = run_gpu(x, 17, "int32")
+    assert_same(gv, gi, x, 17, "int32", "small rows")
+
+
+# ------------------------------------------------------------ large k
+def test_large_k_bf16_sampled():
+    x = workloads.relu_bf16(1, 2 ** 23, 71)
+    k = 8192
+    say("large k bf16 sampled")
+    gv, gi = run_gpu(x, k, "bf16")
+    assert_same(gv, gi, x, k, "bf16", "large k")
+
+
+def test_large_k_batched_fp32():
+    x = workloads.normal_f32(3, 2 ** 20 + 3, 72)
+    k = 20000
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", "large k rows")
+
+
+def test_large_k_exact_small_rows():
+    x = workloads.scores_int(2, 100_000, 0, 300, 73)
+    gv, gi = run_gpu(x, 60_000, "int32")
+    assert_same(gv, gi, x, 60_000, "int32", "large k exact")
+
+
+def test_full_sort_k_equals_n():
+    x = workloads.normal_f32(1, 50_000, 74)
+    gv, gi = run_gpu(x, 50_000, "float32")
+    assert_same(gv, gi, x, 50_000, "float32", "k = n")
+
+
+# ------------------------------------------------------------ determinism
+def test_repeat_with_fresh_seeds_is_identical():
+    x = workloads.relu_bf16(1, 2 ** 22, 81)
+    xt = to_dev(x, "bf16")
+    first = run_gpu(x, 4096, "bf16", xt=xt)
+    for _ in range(20):
+        again = run_gpu(x, 4096, "bf16", xt=xt)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+    assert_same(first[0], first[1], x, 4096, "bf16", "repeat")
+
+
+def test_argument_errors():
+    tss = _tss()
+    x = torch.zeros(1, 100, device="cuda")
+    with pytest.raises(tss.TopkError):
+        tss.topk(x, 101)
+    with pytest.raises(tss.TopkError):
+        tss.topk(x, 0)
+    with pytest.raises(TypeError):
+        tss.topk(x.double(), 5)

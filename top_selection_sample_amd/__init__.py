@@ -1,0 +1,135 @@
+"""Exact top-k selection on one AMD MI355X (gfx950), Prof-K one-pass filtering.
+
+    import torch, top_selection_sample_amd as tss
+    values, indices = tss.topk(x, k)          # x: [rows, n] or [n] on the GPU
+
+``x`` may be int32, float32 or bfloat16.  The result is the exact top-k of
+each row in rank order (value descending, equal values by lower index), as
+the input's own bits and int64 row-local indices.  PyTorch only supplies
+device memory and the stream; the selection runs in libtopk_mi355x.so.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, Params,
+                   TopkError, default_params)
+
+__all__ = ["topk", "plan", "workspace_size", "read_stats", "Workspace", "Params",
+           "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
+           "POLICY_EXACT_TAIL", "POLICY_ALG1", "dtype_code"]
+
+_TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}
+_NAME_CODES = _lib.DTYPE_CODES
+
+
+def dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        return _NAME_CODES[dtype]
+    if dtype not in _TORCH_CODES:
+        raise TypeError(f"unsupported dtype {dtype}; use int32, float32 or bfloat16")
+    return _TORCH_CODES[dtype]
+
+
+def _pp(params):
+    return ctypes.byref(params) if params is not None else None
+
+
+def plan(n: int, rows: int, k: int, dtype, params: Params | None = None) -> dict:
+    """Host-side plan of a call shape (no GPU needed)."""
+    info = _lib.PlanInfo()
+    _lib.check(_lib.lib.topk_plan(n, rows, k, dtype_code(dtype), _pp(params), ctypes.byref(info)),
+               "topk_plan")
+    return {f: getattr(info, f) for f, _ in _lib.PlanInfo._fields_}
+
+
+def workspace_size(n: int, rows: int, k: int, dtype, params: Params | None = None) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.lib.topk_workspace_size(n, rows, k, dtype_code(dtype), _pp(params),
+                                            ctypes.byref(out)), "topk_workspace_size")
+    return out.value
+
+
+class Workspace:
+    """Device scratch for topk calls on one device; grows on demand.  A
+    workspace serves one stream at a time."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf = None
+
+    def get(self, nbytes: int, stream) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            _lib.check(_lib.lib.topk_workspace_init(self.buf.data_ptr(), self.buf.numel(), stream),
+                       "topk_workspace_init")
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _norm_device(device) -> torch.device:
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    return dev
+
+
+def _workspace_for(device) -> Workspace:
+    device = _norm_device(device)
+    key = (device.type, device.index)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Workspace | None = None,
+         out: tuple | None = None):
+    """Exact top-k of each row of ``x`` ([rows, n] or [n], contiguous rows).
+
+    Returns (values, indices) shaped [rows, k] (or [k] for 1-D input)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    squeeze = x.dim() == 1
+    x2 = x.reshape(1, -1) if squeeze else x
+    if x2.dim() != 2 or not x2.is_contiguous():
+        raise ValueError("x must be a contiguous [rows, n] or [n] tensor")
+    rows, n = x2.shape
+    code = dtype_code(x2.dtype)
+    dev = x2.device
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        ws = workspace if workspace is not None else _workspace_for(dev)
+        need = workspace_size(n, rows, k, code, params)
+        buf = ws.get(need, stream)
+        if out is None:
+            vals = torch.empty((rows, k), dtype=x2.dtype, device=dev)
+            idx = torch.empty((rows, k), dtype=torch.int64, device=dev)
+        else:
+            vals, idx = out
+        st = _lib.lib.topk_ex(x2.data_ptr(), n, rows, k, code, vals.data_ptr(), idx.data_ptr(),
+                              buf.data_ptr(), buf.numel(), stream, _pp(params))
+        _lib.check(st, "topk")
+    if squeeze:
+        return vals[0], idx[0]
+    return vals, idx
+
+
+def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> list:
+    """Per-row records of the last call on a workspace (synchronises)."""
+    dev = _norm_device(device)
+    ws = workspace if workspace is not None else _workspace_for(dev)
+    if ws.buf is None:
+        raise RuntimeError("no call has used this workspace yet")
+    arr = (_lib.RowStats * rows)()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
+    return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes}
+            for a in arr]

@@ -1,0 +1,201 @@
+// C ABI entry points of the exact top-k library: argument checks, the plan
+// of the call shape, workspace carving and the launch of the pipeline.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/topk.h"
+#include "topk_device.hpp"
+#include "topk_launch.hpp"
+#include "topk_plan.hpp"
+
+namespace {
+
+std::atomic<uint64_t> g_calls{0};
+
+tk::ParamIn to_in(const topk_params* p) {
+  tk::ParamIn in;
+  if (!p) return in;
+  in.eps = p->eps;
+  in.s_min = p->s_min;
+  in.s_max = p->s_max;
+  in.cost_ratio = p->cost_ratio;
+  in.policy = p->policy;
+  in.force_path = p->force_path;
+  in.S = p->S;
+  in.t = p->t;
+  in.M = p->M;
+  return in;
+}
+
+int check_params(const topk_params* p) {
+  if (!p) return TOPK_OK;
+  if (!(p->eps > 0.0 && p->eps < 1.0)) return TOPK_EINVAL;
+  if (p->s_min < 1 || p->s_max < p->s_min) return TOPK_EINVAL;
+  if (!(p->cost_ratio > 0.0)) return TOPK_EINVAL;
+  if (p->policy < 0 || p->policy > 1) return TOPK_EINVAL;
+  if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
+  if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
+  return TOPK_OK;
+}
+
+int check_shape(int64_t n, int64_t rows, int64_t k, int dtype) {
+  if (dtype < 0 || dtype > 2) return TOPK_EDTYPE;
+  if (n < 1 || rows < 1 || k < 1 || k > n) return TOPK_EINVAL;
+  if (n > (int64_t)0xFFFFFFFEll) return TOPK_EINVAL;   // indices stay below 2^32 - 1
+  if (rows > 65535) return TOPK_EINVAL;                 // rows ride on grid dimension y
+  return TOPK_OK;
+}
+
+int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
+            tk::Plan* plan) {
+  int rc = check_shape(n, rows, k, dtype);
+  if (rc) return rc;
+  rc = check_params(params);
+  if (rc) return rc;
+  tk::ParamIn in = to_in(params);
+  if (in.force_path == 1 && n < 2) return TOPK_EINVAL;
+  tk::make_plan(n, rows, k, dtype, in, plan);
+  if (plan->path == tk::PLAN_SAMPLED && (plan->S < 1 || plan->S > n || plan->t < 1 || plan->t > plan->S))
+    return TOPK_EINVAL;
+  return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_default_params(topk_params* p) {
+  if (!p) return TOPK_EINVAL;
+  std::memset(p, 0, sizeof(*p));
+  p->eps = 1e-3;
+  p->s_min = 32768;
+  p->s_max = 131072;
+  p->cost_ratio = 1.0;
+  p->policy = TOPK_POLICY_EXACT_TAIL;
+  p->force_path = TOPK_PATH_AUTO;
+  return TOPK_OK;
+}
+
+int topk_plan(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
+              topk_plan_info* out) {
+  if (!out) return TOPK_EINVAL;
+  try {
+    tk::Plan p;
+    int rc = plan_of(n, rows, k, dtype, params, &p);
+    if (rc) return rc;
+    out->path = p.path;
+    out->small_k = p.small_k ? 1 : 0;
+    out->S = p.S;
+    out->t = p.t;
+    out->M = p.M;
+    out->cap = p.cap;
+    out->index_bits = (int32_t)p.B;
+    out->key_bits = (int32_t)p.KB;
+    out->p_recall = p.p_recall;
+    out->p_overflow = p.p_overflow;
+    out->workspace_bytes = p.total;
+    return TOPK_OK;
+  } catch (...) {
+    return TOPK_EINVAL;
+  }
+}
+
+int topk_workspace_size(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
+                        size_t* bytes) {
+  if (!bytes) return TOPK_EINVAL;
+  topk_plan_info info;
+  int rc = topk_plan(n, rows, k, dtype, params, &info);
+  if (rc) return rc;
+  *bytes = info.workspace_bytes;
+  return TOPK_OK;
+}
+
+int topk_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace && bytes) return TOPK_EINVAL;
+  if (!bytes) return TOPK_OK;
+  hipError_t e = tk::launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
+}
+
+int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+            int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
+            const topk_params* params) {
+  if (!values || !out_values || !out_indices || !workspace) return TOPK_EINVAL;
+  try {
+    tk::Plan p;
+    int rc = plan_of(n, rows, k, dtype, params, &p);
+    if (rc) return rc;
+    const uintptr_t es = (dtype == TOPK_BF16) ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(values) % es || reinterpret_cast<uintptr_t>(out_values) % es ||
+        reinterpret_cast<uintptr_t>(out_indices) % 8 || reinterpret_cast<uintptr_t>(workspace) % 256)
+      return TOPK_EINVAL;
+    if (workspace_bytes < p.total) return TOPK_EWORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    tk::LaunchArgs a;
+    a.plan = p;
+    a.values = values;
+    a.out_values = out_values;
+    a.out_idx = out_indices;
+    a.states = reinterpret_cast<tk::RowState*>(ws + p.off_states);
+    a.ghist = reinterpret_cast<uint32_t*>(ws + p.off_ghist);
+    a.skeys = reinterpret_cast<uint32_t*>(ws + p.off_skeys);
+    a.cbuf = reinterpret_cast<uint64_t*>(ws + p.off_cbuf);
+    a.aux = reinterpret_cast<uint64_t*>(ws + p.off_aux);
+    const uint64_t ctr = g_calls.fetch_add(1, std::memory_order_relaxed);
+    a.seed = (params && params->use_seed) ? params->seed
+                                          : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = tk::launch_pipeline(a);
+    return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
+  } catch (const std::bad_alloc&) {
+    return TOPK_EINVAL;
+  } catch (...) {
+    return TOPK_EINVAL;
+  }
+}
+
+int topk(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+         int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_ex(values, n, rows, k, dtype, out_values, out_indices, workspace, workspace_bytes,
+                 stream, nullptr);
+}
+
+int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, void* stream) {
+  if (!workspace || !out || rows < 1 || rows > 65535) return TOPK_EINVAL;
+  try {
+    std::vector<tk::RowState> st((size_t)rows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(st.data(), workspace, sizeof(tk::RowState) * (size_t)rows,
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+      return TOPK_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TOPK_EHIP;
+    for (int64_t r = 0; r < rows; ++r) {
+      out[r].tau_key = st[(size_t)r].tau_key;
+      out[r].r_sampled = st[(size_t)r].r_sampled;
+      out[r].path = st[(size_t)r].path;
+      out[r].passes = st[(size_t)r].passes;
+    }
+    return TOPK_OK;
+  } catch (...) {
+    return TOPK_EINVAL;
+  }
+}
+
+const char* topk_status_string(int status) {
+  switch (status) {
+    case TOPK_OK: return "ok";
+    case TOPK_EINVAL: return "invalid argument";
+    case TOPK_EDTYPE: return "unknown dtype";
+    case TOPK_EWORKSPACE: return "workspace too small";
+    case TOPK_EHIP: return "HIP error";
+    case TOPK_ENOTIMPL: return "not implemented";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

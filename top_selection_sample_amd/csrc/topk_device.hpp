@@ -1,0 +1,165 @@
+// Device-side building blocks of the exact top-k engine (gfx950, wave64).
+//
+// Order used everywhere: an element outranks another when its value is
+// larger, or when the values are equal and its index is lower (GPU.js Learn,
+// "Rank by Counting", Goal).  Values are compared through order-preserving
+// unsigned keys; an element is then identified by its composite
+//
+//     comp = key << B | (2^B - 1 - index)          (B = index bits, mult. of 8)
+//
+// which is unique per element and orders exactly as the rank does, so "the k
+// largest composites" is the answer, ties included.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tk {
+
+enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
+
+// Per-row phase of the pipeline.
+enum : uint32_t {
+  ST_IDLE = 0,
+  ST_FILTER = 1,       // sampled threshold set; sampled filter pass pending/done
+  ST_EXACT = 2,        // exact radix select over the whole row in progress
+  ST_EXACT_READY = 3,  // exact threshold known; exact filter pass pending/done
+  ST_SORT = 4,         // candidates ready for the multi-workgroup sort
+  ST_DONE = 5,
+};
+
+// Which route produced a row's answer (reported through the stats call).
+enum : uint32_t { PATH_SAMPLED = 0, PATH_FALLBACK = 1, PATH_EXACT = 2 };
+
+struct alignas(64) RowState {
+  uint32_t status;
+  uint32_t tau_key;     // sampled threshold key (t-th largest sampled key)
+  uint32_t count;       // survivors counted by the current filter pass
+  uint32_t ticket;      // last-workgroup ticket of the current multi-WG pass
+  uint32_t r_sampled;   // survivors of the sampled pass
+  uint32_t path;        // PATH_*
+  uint32_t need;        // exact select: rank wanted inside the prefix bucket
+  uint32_t above;       // exact select: elements above the prefix bucket
+  uint64_t prefix;      // exact select: resolved top bits of the composite
+  uint32_t nbits;       // exact select: number of resolved bits
+  uint32_t thr_key;     // exact threshold: key >= thr_key, and on key ==
+  uint32_t thr_bound;   //   thr_key only indices <= thr_bound
+  uint32_t passes;      // exact select: histogram passes used
+  uint32_t pad[2];
+};
+static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");
+
+// ---------------------------------------------------------------- keys
+// int32: flip the sign bit.  float (32 or 16 bit): a negative value flips all
+// bits, a positive one sets the sign bit; -0 maps to +0's key and every NaN to
+// the top key, so NaN ranks above +inf and ties with other NaNs by index.
+__device__ __forceinline__ uint32_t key_i32(uint32_t b) { return b ^ 0x80000000u; }
+
+__device__ __forceinline__ uint32_t key_f32(uint32_t b) {
+  uint32_t flip = (uint32_t)((int32_t)b >> 31) | 0x80000000u;
+  uint32_t k = b ^ flip;
+  uint32_t mag = b & 0x7FFFFFFFu;
+  k = (mag == 0u) ? 0x80000000u : k;
+  k = (mag > 0x7F800000u) ? 0xFFFFFFFFu : k;
+  return k;
+}
+
+__device__ __forceinline__ uint32_t key_bf16(uint32_t h) {  // h: 16 bits
+  uint32_t flip = ((h & 0x8000u) ? 0xFFFFu : 0x8000u);
+  uint32_t k = h ^ flip;
+  uint32_t mag = h & 0x7FFFu;
+  k = (mag == 0u) ? 0x8000u : k;
+  k = (mag > 0x7F80u) ? 0xFFFFu : k;
+  return k;
+}
+
+template <int DT> struct Dt;
+template <> struct Dt<DT_I32> {
+  using raw = uint32_t;
+  static constexpr int KB = 32;      // key bits
+  static constexpr int ES = 4;       // element bytes
+  static constexpr int VEC = 4;      // elements per 16-byte load
+  __device__ static uint32_t key(uint32_t r) { return key_i32(r); }
+};
+template <> struct Dt<DT_F32> {
+  using raw = uint32_t;
+  static constexpr int KB = 32, ES = 4, VEC = 4;
+  __device__ static uint32_t key(uint32_t r) { return key_f32(r); }
+};
+template <> struct Dt<DT_BF16> {
+  using raw = uint16_t;
+  static constexpr int KB = 16, ES = 2, VEC = 8;
+  __device__ static uint32_t key(uint32_t r) { return key_bf16(r & 0xFFFFu); }
+};
+
+// Raw bits of element i of a row.
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw(const void* row, uint32_t i) {
+  if constexpr (DT == DT_BF16) {
+    return static_cast<const uint16_t*>(row)[i];
+  } else {
+    return static_cast<const uint32_t*>(row)[i];
+  }
+}
+
+__device__ __forceinline__ uint64_t make_comp(uint32_t key, uint32_t idx, uint32_t B) {
+  uint64_t maskB = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+  return ((uint64_t)key << B) | (maskB - (uint64_t)idx);
+}
+
+__device__ __forceinline__ uint32_t comp_index(uint64_t c, uint32_t B) {
+  uint64_t maskB = (1ull << B) - 1ull;
+  return (uint32_t)(maskB - (c & maskB));
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ uint32_t rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Orders this wave's earlier LDS accesses before its later ones, as seen by
+// the other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- buckets
+// Find, over a 256-bin histogram ordered from bin 255 (largest digit) down,
+// the bin b holding the element of rank `need` (1-based from the top), and
+// `acc` = number of elements in bins above b.  Run by the 64 lanes of one
+// wave; the result lands in out[0] = b, out[1] = acc, out[2] = hist[b].
+__device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, uint32_t need,
+                                                 uint32_t* out) {
+  const uint32_t l = lane_id();
+  const uint32_t b3 = 255u - 4u * l;
+  uint32_t c3 = hist[b3], c2 = hist[b3 - 1], c1 = hist[b3 - 2], c0 = hist[b3 - 3];
+  uint32_t s = c3 + c2 + c1 + c0;
+  uint32_t incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t v = __shfl_up(incl, d, 64);
+    if (l >= (uint32_t)d) incl += v;
+  }
+  uint64_t m = ballot(incl >= need);
+  uint32_t first = m ? (uint32_t)__builtin_ctzll(m) : 63u;
+  if (l == first) {
+    uint32_t acc = incl - s, b, hb;
+    if (acc + c3 >= need) { b = b3; hb = c3; }
+    else if (acc + c3 + c2 >= need) { acc += c3; b = b3 - 1; hb = c2; }
+    else if (acc + c3 + c2 + c1 >= need) { acc += c3 + c2; b = b3 - 2; hb = c1; }
+    else { acc += c3 + c2 + c1; b = b3 - 3; hb = c0; }
+    out[0] = b;
+    out[1] = acc;
+    out[2] = hb;
+  }
+}
+
+}  // namespace tk

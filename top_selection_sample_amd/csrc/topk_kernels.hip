@@ -1,0 +1,819 @@
+// HIP kernels of the exact top-k engine for gfx950 (MI355X), and their
+// launchers.  The pipeline follows the four stages of the Prof-K paper
+// (section 3, "The Prof-K Algorithm"): sampling, threshold estimation,
+// filtering into a bounded candidate buffer, exact refinement; with the
+// fallback to an exact selection over the full row when fewer than k
+// candidates survive or the buffer overflows.
+//
+// Kernels (one row = one independent selection; grids are (tiles, rows)):
+//   k_sample       S sample keys per row through a keyed permutation
+//   k_tau          workgroup radix select of the t-th largest sample key
+//   k_filter       the streaming pass: keep composites with key >= tau
+//   k_check        large-k: accept the candidate count or start the fallback
+//   k_setup_exact  rows that start on the exact path
+//   k_hist         exact path: one 8-bit digit histogram pass over a row
+//   k_refine       small k: select, sort and write the k winners
+//   k_exact_small  small rows: the whole exact selection in one workgroup
+//   k_tile_sort / k_merge / k_output   large k: sort all candidates
+#include "topk_device.hpp"
+#include "topk_launch.hpp"
+#include "topk_select.hpp"
+
+namespace tk {
+
+// ======================================================================
+// Sampler: S indices drawn without replacement (Prof-K, section 3, stage 1).
+// The first S images of a keyed permutation of [0, n): a balanced 4-round
+// Feistel network over 2h bits whose round function is the SplitMix64 output
+// mixer (Steele, Lea & Flood 2014), walked back into [0, n) ("cycle walking",
+// Black & Rogaway 2002).  Round keys for (seed, row) are outputs 4*row..4*row+3
+// of the SplitMix64 stream seeded with `seed`.
+// ======================================================================
+__device__ __forceinline__ uint64_t sm64_finalize(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z;
+}
+
+struct Feistel {
+  uint64_t rk[4];
+  uint64_t mask;
+  uint32_t h;
+  __device__ Feistel(uint64_t seed, uint64_t row, uint32_t half_bits) {
+    h = half_bits;
+    mask = (1ull << h) - 1ull;
+    const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rk[r] = sm64_finalize(seed + (4ull * row + (uint64_t)r + 1ull) * gamma);
+  }
+  __device__ uint64_t apply(uint64_t x) const {
+    uint64_t L = x >> h, R = x & mask;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t t = L ^ (sm64_finalize(R ^ rk[r]) & mask);
+      L = R;
+      R = t;
+    }
+    return (L << h) | R;
+  }
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_sample(const void* __restrict__ values, uint32_t n,
+                                                uint32_t S, uint64_t seed, uint32_t half_bits,
+                                                uint32_t* __restrict__ skeys) {
+  const uint32_t row = blockIdx.y;
+  const uint32_t j = blockIdx.x * 256u + threadIdx.x;
+  if (j >= S) return;
+  const Feistel f(seed, row, half_bits);
+  uint64_t x = f.apply(j);
+  while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  skeys[(size_t)row * S + j] = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+}
+
+// ======================================================================
+// Threshold (Prof-K section 3, stage 2): tau = the t-th largest sampled key,
+// found by a workgroup radix select instead of a sort.  Also starts the row.
+// ======================================================================
+struct KeySrc {
+  const uint32_t* p;
+  __device__ uint64_t operator()(uint32_t i) const { return p[i]; }
+};
+
+constexpr uint32_t SEL_THREADS = 1024;
+constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
+
+__global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
+                                                     uint32_t t, uint32_t KB,
+                                                     RowState* __restrict__ states) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  const uint32_t row = blockIdx.x;
+  KeySrc src{skeys + (size_t)row * S};
+  SelectOut r = block_select(src, S, KB, t, 0u, s_hist, s_misc, s_cand, CAND_CAP);
+  if (threadIdx.x == 0) {
+    RowState* st = states + row;
+    st->status = ST_FILTER;
+    st->tau_key = (uint32_t)r.thr;
+    st->count = 0;
+    st->r_sampled = 0;
+    st->path = PATH_SAMPLED;
+    st->passes = 0;
+  }
+}
+
+// ======================================================================
+// Filter (Prof-K section 3, stage 3; Appendix D "Efficient GPU
+// Implementation"): one streaming pass over the row that keeps every element
+// whose key is >= the threshold, appending its composite to the row's
+// candidate buffer.  The counter keeps counting past the capacity, so the
+// exact number of survivors R is known after the pass.
+//
+// Survivor slots come from a wave ballot and the count of set lanes below
+// each lane (the stable split's "how many earlier elements share my flag",
+// GPU.js Learn "One Bit at a Time"); they are staged per wave in LDS and each
+// workgroup appends its survivors with one atomic at the end.
+// ======================================================================
+constexpr uint32_t FILTER_THREADS = 256;
+constexpr uint32_t FILTER_WAVES = FILTER_THREADS / 64;
+constexpr uint32_t STAGE_SLOTS = 256;
+constexpr uint32_t FILTER_UNROLL = 4;
+
+struct Stager {
+  uint64_t* stage;   // this wave's LDS slots
+  uint32_t fill;     // wave-uniform
+  RowState* st;
+  uint64_t* buf;     // row's candidate buffer
+  uint32_t cap;
+
+  __device__ void flush() {
+    wave_lds_sync();
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(&st->count, fill);
+    base = __shfl(base, 0, 64);
+    for (uint32_t i = lane_id(); i < fill; i += 64) {
+      const uint32_t pos = base + i;
+      if (pos < cap) buf[pos] = stage[i];
+    }
+    wave_lds_sync();
+    fill = 0;
+  }
+  // All lanes call together.
+  __device__ void push(bool p, uint64_t comp) {
+    const uint64_t m = ballot(p);
+    if (!m) return;
+    const uint32_t c = (uint32_t)__builtin_popcountll(m);
+    if (fill + c > STAGE_SLOTS) flush();
+    if (p) stage[fill + rank_below(m)] = comp;
+    fill += c;
+  }
+};
+
+// Native-domain threshold for the fast compare.  kind 0: compare in the value
+// domain; kind 1: compare keys (thresholds above +inf, or a tie cut on index).
+struct Thr {
+  float f;
+  int32_t i;
+  uint32_t key;
+  uint32_t bound;
+  int kind;
+};
+
+template <int DT>
+__device__ __forceinline__ Thr make_thr(uint32_t key, uint32_t bound) {
+  Thr t;
+  t.key = key;
+  t.bound = bound;
+  t.kind = (bound != 0xFFFFFFFFu) ? 1 : 0;
+  t.i = (int32_t)(key ^ 0x80000000u);
+  t.f = 0.f;
+  if constexpr (DT == DT_F32) {
+    if (key > 0xFF800000u) t.kind = 1;                       // only NaN passes
+    else if (key <= 0x007FFFFFu) t.f = -__builtin_huge_valf();  // everything passes
+    else t.f = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+  } else if constexpr (DT == DT_BF16) {
+    if (key > 0xFF80u) t.kind = 1;
+    else if (key <= 0x007Fu) t.f = -__builtin_huge_valf();
+    else {
+      const uint32_t b16 = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+      t.f = __uint_as_float(b16 << 16);
+    }
+  }
+  return t;
+}
+
+// key >= thr, with the index cut on the threshold key.
+__device__ __forceinline__ bool key_pass(uint32_t key, uint32_t idx, const Thr& t) {
+  return key > t.key || (key == t.key && idx <= t.bound);
+}
+
+template <int DT>
+__device__ __forceinline__ bool native_pass(uint32_t raw, const Thr& t) {
+  if constexpr (DT == DT_I32) return (int32_t)raw >= t.i;
+  else if constexpr (DT == DT_F32) return !(__uint_as_float(raw) < t.f);
+  else return !(__uint_as_float(raw << 16) < t.f);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__global__ __launch_bounds__(FILTER_THREADS) void k_filter(
+    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t B, uint32_t want) {
+  using D = Dt<DT>;
+  const uint32_t row = blockIdx.y;
+  RowState* st = states + row;
+  if (st->status != want) return;
+  const bool sampled = (want == ST_FILTER);
+  const Thr thr = make_thr<DT>(sampled ? st->tau_key : st->thr_key,
+                               sampled ? 0xFFFFFFFFu : st->thr_bound);
+
+  __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
+  __shared__ uint32_t s_fill[FILTER_WAVES];
+  __shared__ uint32_t s_base;
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  Stager sg{s_stage[w], 0u, st, cbuf + (size_t)row * cap, cap};
+
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
+  const uint64_t maskB = (1ull << B) - 1ull;
+  auto comp_of = [&](uint32_t raw, uint32_t idx) -> uint64_t {
+    return ((uint64_t)D::key(raw) << B) | (maskB - idx);
+  };
+  auto pass_of = [&](uint32_t raw, uint32_t idx) -> bool {
+    if (thr.kind == 0) return native_pass<DT>(raw, thr);
+    return key_pass(D::key(raw), idx, thr);
+  };
+
+  // Split the row into an unaligned head, 16-byte vectors, and a tail.
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(rowp);
+  uint32_t head = (uint32_t)(((16u - (addr & 15u)) & 15u) / D::ES);
+  if (head > n) head = n;
+  const uint32_t nvec = (n - head) / D::VEC;
+  const uint32_t tail0 = head + nvec * D::VEC;
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)head * D::ES);
+
+  // One 16-byte vector: its elements' predicates, then (rarely) survivors.
+  auto handle_vec = [&](const u32x4& v, uint32_t vi, bool valid) {
+    bool p[D::VEC];
+    bool any = false;
+    const uint32_t e0 = head + vi * D::VEC;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (DT == DT_BF16) {
+        const uint32_t lo = v[q] & 0xFFFFu, hi = v[q] >> 16;
+        p[2 * q] = valid && pass_of(lo, e0 + 2 * q);
+        p[2 * q + 1] = valid && pass_of(hi, e0 + 2 * q + 1);
+        any = any || p[2 * q] || p[2 * q + 1];
+      } else {
+        p[q] = valid && pass_of(v[q], e0 + q);
+        any = any || p[q];
+      }
+    }
+    if (ballot(any) == 0) return;
+#pragma unroll
+    for (int e = 0; e < D::VEC; ++e) {
+      uint32_t raw;
+      if constexpr (DT == DT_BF16) raw = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
+      else raw = v[e];
+      sg.push(p[e], p[e] ? comp_of(raw, e0 + e) : 0ull);
+    }
+  };
+
+  const uint32_t bpr = gridDim.x;
+  const size_t stride = (size_t)bpr * FILTER_THREADS;
+  size_t vi = (size_t)blockIdx.x * FILTER_THREADS + tid;
+  // Main loop: FILTER_UNROLL independent 16-byte nontemporal loads per lane.
+  // The bound is tested on the wave's last lane, so every lane of a wave runs
+  // the same trip count (the ballots and the staging counter need that).
+  // With a plain threshold the loop only ORs native compares and skips the
+  // vectors of a wave that has no survivor.
+  if (thr.kind == 0) {
+    for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < nvec; vi += FILTER_UNROLL * stride) {
+      u32x4 v[FILTER_UNROLL];
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+        v[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+      uint32_t any = 0;
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (DT == DT_BF16) {
+            any |= (uint32_t)native_pass<DT>(v[u][q] & 0xFFFFu, thr);
+            any |= (uint32_t)native_pass<DT>(v[u][q] >> 16, thr);
+          } else {
+            any |= (uint32_t)native_pass<DT>(v[u][q], thr);
+          }
+        }
+      }
+      if (ballot(any != 0u) == 0) continue;
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) handle_vec(v[u], (uint32_t)(vi + u * stride), true);
+    }
+  } else {
+    for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < nvec; vi += FILTER_UNROLL * stride) {
+      u32x4 v[FILTER_UNROLL];
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) handle_vec(v[u], (uint32_t)(vi + u * stride), true);
+    }
+  }
+  // Remainder: the loop bound differs between lanes, so iterate on the wave's
+  // first lane index to keep ballots wave-uniform.
+  for (;;) {
+    const size_t wave_first = vi - lane;
+    if (wave_first >= nvec) break;
+    const bool valid = vi < nvec;
+    u32x4 v = valid ? vp[vi] : u32x4{0u, 0u, 0u, 0u};
+    handle_vec(v, (uint32_t)vi, valid);
+    vi += stride;
+  }
+  // Head and tail elements: the first wave of workgroup 0.
+  if (blockIdx.x == 0 && w == 0) {
+    const uint32_t nt = n - tail0;
+    for (uint32_t base = 0; base < head + nt; base += 64) {
+      const uint32_t j = base + lane;
+      bool ok = j < head + nt;
+      uint32_t idx = 0, raw = 0;
+      if (ok) {
+        idx = (j < head) ? j : tail0 + (j - head);
+        raw = load_raw<DT>(rowp, idx);
+      }
+      const bool p = ok && pass_of(raw, idx);
+      sg.push(p, p ? comp_of(raw, idx) : 0ull);
+    }
+  }
+
+  // Workgroup flush: one atomic for the whole workgroup.
+  if (lane == 0) s_fill[w] = sg.fill;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t total = 0;
+    for (uint32_t i = 0; i < FILTER_WAVES; ++i) total += s_fill[i];
+    s_base = total ? atomicAdd(&st->count, total) : 0u;
+  }
+  __syncthreads();
+  uint32_t off = s_base;
+  for (uint32_t i = 0; i < w; ++i) off += s_fill[i];
+  for (uint32_t i = lane; i < sg.fill; i += 64) {
+    const uint32_t pos = off + i;
+    if (pos < cap) sg.buf[pos] = sg.stage[i];
+  }
+}
+
+// ======================================================================
+// Detection (Prof-K section 3, stage 4): R < k is a recall failure, R > M an
+// overflow; either sends the row to the exact path.
+// ======================================================================
+__device__ __forceinline__ void start_exact(RowState* st, uint32_t k, uint32_t path) {
+  st->status = ST_EXACT;
+  st->path = path;
+  st->count = 0;
+  st->need = k;
+  st->above = 0;
+  st->prefix = 0;
+  st->nbits = 0;
+  st->passes = 0;
+}
+
+__global__ void k_check(RowState* __restrict__ states, uint32_t rows, uint32_t k, uint32_t cap,
+                        uint32_t want) {
+  const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  RowState* st = states + row;
+  if (st->status != want) return;
+  const uint32_t R = st->count;
+  if (want == ST_FILTER) {
+    st->r_sampled = R;
+    if (R < k || R > cap) {
+      start_exact(st, k, PATH_FALLBACK);
+      return;
+    }
+  }
+  st->status = ST_SORT;
+}
+
+__global__ void k_setup_exact(RowState* __restrict__ states, uint32_t rows, uint32_t k) {
+  const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  RowState* st = states + row;
+  start_exact(st, k, PATH_EXACT);
+  st->r_sampled = 0;
+  st->tau_key = 0;
+}
+
+// ======================================================================
+// Exact path (Prof-K section 3, stage 4 fallback: exact top-k on the full
+// input), done as a radix select: each pass counts one 8-bit digit of the
+// composite over the elements that match the resolved prefix; the last
+// workgroup to finish resolves the boundary bucket.  It stops as soon as the
+// elements at or above the bucket fit the candidate buffer, so the scratch
+// memory stays O(capacity), never O(n).
+// ======================================================================
+constexpr uint32_t HIST_THREADS = 256;
+constexpr uint32_t HIST_UNROLL = 4;
+
+template <int DT>
+__global__ __launch_bounds__(HIST_THREADS) void k_hist(const void* __restrict__ values, uint32_t n,
+                                                       RowState* __restrict__ states,
+                                                       uint32_t* __restrict__ ghist, uint32_t cap,
+                                                       uint32_t B, uint32_t W) {
+  using D = Dt<DT>;
+  const uint32_t row = blockIdx.y;
+  RowState* st = states + row;
+  if (st->status != ST_EXACT) return;
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_last;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t nb = st->nbits;
+  const uint64_t prefix = st->prefix;
+  const uint32_t shift = W - nb - 8;
+  const uint32_t pshift = W - nb;
+  const uint64_t ptop = nb ? (prefix >> pshift) : 0ull;
+  const uint64_t maskB = (1ull << B) - 1ull;
+  s_hist[tid] = 0;
+  __syncthreads();
+
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
+  const uint32_t bpr = gridDim.x;
+  const size_t stride = (size_t)bpr * HIST_THREADS;
+  // Iterate per wave so that every lane of a wave runs the same trip count.
+  const uint32_t lane = tid & 63u;
+  for (size_t i0 = (size_t)blockIdx.x * HIST_THREADS + (tid - lane); i0 < n;
+       i0 += HIST_UNROLL * stride) {
+    uint32_t raw[HIST_UNROLL];
+    bool ok[HIST_UNROLL];
+#pragma unroll
+    for (uint32_t u = 0; u < HIST_UNROLL; ++u) {
+      const size_t i = i0 + u * stride + lane;
+      ok[u] = i < n;
+      raw[u] = ok[u] ? load_raw<DT>(rowp, (uint32_t)i) : 0u;
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < HIST_UNROLL; ++u) {
+      const uint32_t i = (uint32_t)(i0 + u * stride + lane);
+      const uint64_t c = ((uint64_t)D::key(raw[u]) << B) | (maskB - i);
+      const bool act = ok[u] && ((nb == 0) || ((c >> pshift) == ptop));
+      hist_add(s_hist, (uint32_t)(c >> shift) & 255u, act);
+    }
+  }
+  __syncthreads();
+  if (s_hist[tid]) atomicAdd(&ghist[(size_t)row * 256 + tid], s_hist[tid]);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&st->ticket, 1u) == bpr - 1u) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last workgroup of this row: resolve the pass.
+  __threadfence();
+  s_hist[tid] = __hip_atomic_load(&ghist[(size_t)row * 256 + tid], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t need = st->need;
+  if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
+  __syncthreads();
+  ghist[(size_t)row * 256 + tid] = 0u;
+  if (tid == 0) {
+    const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+    const uint32_t above = st->above + acc;
+    const uint64_t np = prefix | ((uint64_t)b << shift);
+    const uint32_t nnb = nb + 8;
+    st->above = above;
+    st->need = need - acc;
+    st->prefix = np;
+    st->nbits = nnb;
+    st->passes = st->passes + 1;
+    st->ticket = 0;
+    if (above + hb <= cap || nnb >= W) {
+      st->thr_key = (uint32_t)(np >> B);
+      st->thr_bound = (uint32_t)(maskB - (np & maskB));
+      st->count = 0;
+      st->status = ST_EXACT_READY;
+    }
+  }
+}
+
+// ======================================================================
+// Refinement (Prof-K section 3, stage 4): exact top-k of the candidate
+// buffer, one workgroup per row: radix select of the k-th composite, gather
+// of the k winners, bitonic sort into rank order, and the output write
+// (values are re-read from the input so they keep their own bits).
+// ======================================================================
+struct CompSrc {
+  const uint64_t* p;
+  __device__ uint64_t operator()(uint32_t i) const { return p[i]; }
+};
+
+template <int DT>
+struct RowSrc {
+  const char* rowp;
+  uint32_t B;
+  uint64_t maskB;
+  __device__ uint64_t operator()(uint32_t i) const {
+    return ((uint64_t)Dt<DT>::key(load_raw<DT>(rowp, i)) << B) | (maskB - i);
+  }
+};
+
+template <int DT>
+__device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t B, const char* rowp,
+                              uint32_t n, void* out_values, int64_t* out_idx, uint32_t row) {
+  const uint64_t maskB = (1ull << B) - 1ull;
+  for (uint32_t i = threadIdx.x; i < k; i += blockDim.x) {
+    const uint64_t c = s_w[i];
+    uint32_t idx = (uint32_t)(maskB - (c & maskB));
+    if (idx >= n) idx = n - 1;   // only a padding entry could decode out of range
+    const uint32_t raw = load_raw<DT>(rowp, idx);
+    const size_t o = (size_t)row * k + i;
+    if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = (uint16_t)raw;
+    else static_cast<uint32_t*>(out_values)[o] = raw;
+    out_idx[o] = idx;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(SEL_THREADS) void k_refine(
+    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    const uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
+    uint32_t want, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  const uint32_t row = blockIdx.x;
+  RowState* st = states + row;
+  if (st->status != want) return;
+  uint32_t R = st->count;
+  if (want == ST_FILTER) {
+    if (R < k || R > cap) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        st->r_sampled = R;
+        start_exact(st, k, PATH_FALLBACK);
+      }
+      return;
+    }
+  }
+  if (R > cap) R = cap;   // the exact route never exceeds the capacity
+  CompSrc src{cbuf + (size_t)row * cap};
+  SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
+  const uint32_t got = block_collect(src, R, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
+  const uint32_t P = next_pow2(got);
+  for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
+  __syncthreads();
+  block_bitonic_desc(s_cand, P);
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (want == ST_FILTER) st->r_sampled = R;
+    st->status = ST_DONE;
+    st->count = 0;
+  }
+}
+
+// Whole exact selection of a small row in one workgroup.  Small k: writes the
+// answer.  Large k: leaves exactly k winners in the candidate buffer for the
+// multi-workgroup sort.
+template <int DT>
+__global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
+    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
+    uint32_t small_k, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  const uint32_t row = blockIdx.x;
+  RowState* st = states + row;
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  RowSrc<DT> src{rowp, B, (1ull << B) - 1ull};
+  SelectOut sel = block_select(src, n, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
+  if (small_k) {
+    const uint32_t got = block_collect(src, n, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
+    const uint32_t P = next_pow2(got);
+    for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
+    __syncthreads();
+    block_bitonic_desc(s_cand, P);
+    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      st->status = ST_DONE;
+      st->path = PATH_EXACT;
+      st->count = 0;
+      st->r_sampled = 0;
+      st->tau_key = 0;
+    }
+    return;
+  }
+  // large k: scatter the k winners to global memory
+  uint64_t* out = cbuf + (size_t)row * cap;
+  if (threadIdx.x == 0) s_misc[4] = 0;
+  __syncthreads();
+  for (uint32_t i0 = 0; i0 < n; i0 += blockDim.x) {
+    const uint32_t i = i0 + threadIdx.x;
+    uint64_t c = 0;
+    bool keep = false;
+    if (i < n) {
+      c = src(i);
+      keep = c >= sel.thr;
+    }
+    const uint64_t m = ballot(keep);
+    if (m) {
+      const uint32_t first = (uint32_t)__builtin_ctzll(m);
+      uint32_t base = 0;
+      if (lane_id() == first) base = atomicAdd(&s_misc[4], (uint32_t)__builtin_popcountll(m));
+      base = __shfl(base, first, 64);
+      const uint32_t slot = base + rank_below(m);
+      if (keep && slot < cap) out[slot] = c;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st->count = s_misc[4] < cap ? s_misc[4] : cap;
+    st->status = ST_SORT;
+    st->path = PATH_EXACT;
+    st->r_sampled = 0;
+    st->tau_key = 0;
+  }
+}
+
+// ======================================================================
+// Large k: sort all candidates by composite (descending) and keep the first
+// k.  Tiles of SORT_TILE are bitonic-sorted in LDS, then runs are merged
+// pairwise; each element finds its place in the merged run from its own
+// position plus a binary search for the number of larger elements in the
+// partner run (the lower-bound search of GPU.js Learn "Find It in log n";
+// composites are unique, so there are no ties to break).
+// ======================================================================
+constexpr uint32_t SORT_TILE = 4096;
+
+__global__ __launch_bounds__(SEL_THREADS) void k_tile_sort(RowState* __restrict__ states,
+                                                           uint64_t* __restrict__ cbuf,
+                                                           uint32_t cap) {
+  __shared__ uint64_t s[SORT_TILE];
+  const uint32_t row = blockIdx.y;
+  const uint32_t R = min(states[row].count, cap);
+  const uint32_t start = blockIdx.x * SORT_TILE;
+  if (start >= R) return;
+  const uint32_t len = min(SORT_TILE, R - start);
+  uint64_t* p = cbuf + (size_t)row * cap + start;
+  for (uint32_t i = threadIdx.x; i < SORT_TILE; i += blockDim.x) s[i] = (i < len) ? p[i] : 0ull;
+  __syncthreads();
+  block_bitonic_desc(s, SORT_TILE);
+  for (uint32_t i = threadIdx.x; i < len; i += blockDim.x) p[i] = s[i];
+}
+
+__global__ __launch_bounds__(256) void k_merge(RowState* __restrict__ states,
+                                               const uint64_t* __restrict__ src,
+                                               uint64_t* __restrict__ dst, uint32_t cap,
+                                               uint32_t run) {
+  const uint32_t row = blockIdx.y;
+  const uint32_t R = min(states[row].count, cap);
+  const uint32_t p = blockIdx.x * 256u + threadIdx.x;
+  if (p >= R) return;
+  const uint64_t* a = src + (size_t)row * cap;
+  uint64_t* d = dst + (size_t)row * cap;
+  const uint32_t r = p / run;
+  const uint32_t pair_lo = (r & ~1u) * run;
+  const uint32_t mid = min(pair_lo + run, R);
+  const uint32_t end = min(pair_lo + 2 * run, R);
+  const uint64_t x = a[p];
+  uint32_t o, lo, hi;
+  if ((r & 1u) == 0) {  // left run: count larger elements of the right run
+    o = p - pair_lo;
+    lo = mid;
+    hi = end;
+  } else {
+    o = p - mid;
+    lo = pair_lo;
+    hi = mid;
+  }
+  const uint32_t base = lo;
+  while (lo < hi) {
+    const uint32_t m = (lo + hi) >> 1;
+    if (a[m] > x) lo = m + 1;
+    else hi = m;
+  }
+  d[pair_lo + o + (lo - base)] = x;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_output(const void* __restrict__ values, uint32_t n,
+                                                RowState* __restrict__ states,
+                                                const uint64_t* __restrict__ sorted, uint32_t cap,
+                                                uint32_t k, uint32_t B, void* __restrict__ out_values,
+                                                int64_t* __restrict__ out_idx) {
+  const uint32_t row = blockIdx.y;
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= k) return;
+  const uint64_t maskB = (1ull << B) - 1ull;
+  const uint64_t c = sorted[(size_t)row * cap + i];
+  uint32_t idx = (uint32_t)(maskB - (c & maskB));
+  if (idx >= n) idx = n - 1;   // only a padding entry could decode out of range
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  const uint32_t raw = load_raw<DT>(rowp, idx);
+  const size_t o = (size_t)row * k + i;
+  if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = (uint16_t)raw;
+  else static_cast<uint32_t*>(out_values)[o] = raw;
+  out_idx[o] = idx;
+  if (i == 0) states[row].status = ST_DONE;
+}
+
+// ======================================================================
+// Launchers
+// ======================================================================
+#define TK_DISPATCH(dt, KERNEL, ...)                                          \
+  switch (dt) {                                                               \
+    case DT_I32: hipLaunchKernelGGL(KERNEL<DT_I32>, __VA_ARGS__); break;      \
+    case DT_F32: hipLaunchKernelGGL(KERNEL<DT_F32>, __VA_ARGS__); break;      \
+    default: hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__); break;         \
+  }
+
+hipError_t launch_pipeline(const LaunchArgs& a) {
+  const Plan& p = a.plan;
+  const uint32_t rows = (uint32_t)p.rows, n = (uint32_t)p.n, k = (uint32_t)p.k;
+  const uint32_t cap = (uint32_t)p.cap, B = p.B, W = p.W;
+  hipStream_t s = a.stream;
+  const int dt = p.dtype;
+  const dim3 row_grid(rows);
+  const dim3 tiny((rows + 63) / 64);
+
+  if (p.path == PLAN_EXACT_SMALL) {
+    TK_DISPATCH(dt, k_exact_small, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
+                a.cbuf, cap, k, B, W, (uint32_t)(p.small_k ? 1 : 0), a.out_values, a.out_idx);
+  } else {
+    if (p.path == PLAN_SAMPLED) {
+      const dim3 sg((uint32_t)((p.S + 255) / 256), rows);
+      TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, a.seed,
+                  p.half_bits, a.skeys);
+      hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
+                         (uint32_t)p.t, (uint32_t)p.KB, a.states);
+      const dim3 fg(p.filter_bpr, rows);
+      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
+                  cap, B, (uint32_t)ST_FILTER);
+      if (p.small_k) {
+        TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
+                    a.cbuf, cap, k, B, W, (uint32_t)ST_FILTER, a.out_values, a.out_idx);
+      } else {
+        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
+                           (uint32_t)ST_FILTER);
+      }
+    } else {
+      hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, rows, k);
+    }
+    // Exact path / fallback: histogram passes, each a no-op for rows that
+    // are not (or no longer) selecting.
+    const dim3 hg(p.hist_bpr, rows);
+    for (uint32_t pass = 0; pass < W / 8; ++pass) {
+      TK_DISPATCH(dt, k_hist, hg, dim3(HIST_THREADS), 0, s, a.values, n, a.states, a.ghist, cap,
+                  B, W);
+    }
+    const dim3 fg(p.filter_bpr, rows);
+    TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf, cap,
+                B, (uint32_t)ST_EXACT_READY);
+    if (p.small_k) {
+      TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states, a.cbuf,
+                  cap, k, B, W, (uint32_t)ST_EXACT_READY, a.out_values, a.out_idx);
+    } else {
+      hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
+                         (uint32_t)ST_EXACT_READY);
+    }
+  }
+  if (!p.small_k) {
+    // every row now holds R in [k, cap] candidates: sort them, keep k
+    const dim3 tg((cap + SORT_TILE - 1) / SORT_TILE, rows);
+    hipLaunchKernelGGL(k_tile_sort, tg, dim3(SEL_THREADS), 0, s, a.states, a.cbuf, cap);
+    const dim3 mg((cap + 255) / 256, rows);
+    uint64_t* src = a.cbuf;
+    uint64_t* dst = a.aux;
+    for (uint32_t run = SORT_TILE; run < cap; run <<= 1) {
+      hipLaunchKernelGGL(k_merge, mg, dim3(256), 0, s, a.states, src, dst, cap, run);
+      uint64_t* t = src;
+      src = dst;
+      dst = t;
+    }
+    const dim3 og((k + 255) / 256, rows);
+    TK_DISPATCH(dt, k_output, og, dim3(256), 0, s, a.values, n, a.states, src, cap, k, B,
+                a.out_values, a.out_idx);
+  }
+  return hipGetLastError();
+}
+
+__global__ void k_zero_words(uint32_t* __restrict__ p, size_t nwords) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = 0u;
+}
+
+__global__ void k_zero_bytes(unsigned char* __restrict__ p, size_t nbytes) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nbytes) p[i] = 0;
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  // the workspace is 256-byte aligned, so whole words first, then the bytes
+  const size_t nwords = bytes / 4;
+  if (nwords) {
+    size_t blocks = (nwords + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_zero_words, dim3((uint32_t)blocks), dim3(256), 0, s,
+                       static_cast<uint32_t*>(p), nwords);
+  }
+  const size_t rest = bytes - nwords * 4;
+  if (rest) {
+    hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(64), 0, s,
+                       static_cast<unsigned char*>(p) + nwords * 4, rest);
+  }
+  return hipGetLastError();
+}
+
+uint32_t filter_threads() { return FILTER_THREADS; }
+uint32_t filter_unroll() { return FILTER_UNROLL; }
+uint32_t sort_tile() { return SORT_TILE; }
+
+}  // namespace tk

@@ -1,0 +1,50 @@
+// Internal interface between the host dispatcher and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tk {
+
+struct RowState;
+
+enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
+
+constexpr int64_t KSMALL = 4096;            // largest k sorted inside one workgroup
+constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workgroup
+
+struct Plan {
+  int64_t n = 0, rows = 0, k = 0;
+  int dtype = 0;
+  int path = PLAN_SAMPLED;
+  bool small_k = true;
+  int64_t S = 0, t = 0, M = 0, cap = 0;
+  uint32_t B = 8, W = 40, KB = 32, half_bits = 1;
+  uint32_t filter_bpr = 1, hist_bpr = 1;
+  double p_recall = 0, p_overflow = 0;
+  // workspace layout (byte offsets)
+  size_t off_states = 0, off_ghist = 0, off_skeys = 0, off_cbuf = 0, off_aux = 0, total = 0;
+};
+
+struct LaunchArgs {
+  Plan plan;
+  const void* values;
+  void* out_values;
+  int64_t* out_idx;
+  RowState* states;
+  uint32_t* ghist;
+  uint32_t* skeys;
+  uint64_t* cbuf;
+  uint64_t* aux;
+  uint64_t seed;
+  hipStream_t stream;
+};
+
+hipError_t launch_pipeline(const LaunchArgs& a);
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+uint32_t filter_threads();
+uint32_t filter_unroll();
+uint32_t sort_tile();
+
+}  // namespace tk

@@ -1,0 +1,37 @@
+// Host-side parameter arithmetic (Prof-K Algorithm 1, Lemma 1, Theorem 3).
+#pragma once
+
+#include <stdint.h>
+
+#include "topk_launch.hpp"
+
+namespace tk {
+
+struct Alg1 {
+  double z = 0, s_star = 0;
+  int64_t S = 0, t = 0, M = 0;
+};
+
+struct TailParams {
+  int64_t t = 0, M = 0;
+};
+
+struct ParamIn {
+  double eps = 1e-3;
+  int64_t s_min = 32768, s_max = 131072;
+  double cost_ratio = 1.0;
+  int policy = 0;      // 0 exact tail, 1 Algorithm 1
+  int force_path = 0;  // 0 auto, 1 filter, 2 exact
+  int64_t S = 0, t = 0, M = 0;
+};
+
+double normal_quantile(double p);
+Alg1 algorithm1(int64_t N, int64_t k, double eps, int64_t s_min, int64_t s_max, double ratio);
+double hyper_cdf(int64_t N, int64_t K, int64_t S, int64_t t, bool fast);
+double hyper_sf(int64_t N, int64_t K, int64_t S, int64_t t);
+TailParams exact_tail(int64_t N, int64_t k, int64_t S, double eps);
+void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t* t, int64_t* M,
+                   double* p_recall, double* p_overflow);
+int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, Plan* out);
+
+}  // namespace tk

@@ -1,0 +1,170 @@
+// Workgroup-level radix select on composites (one workgroup per row).
+//
+// Radix selection counts elements into digit buckets and recurses into the
+// bucket that holds the boundary (GPU.js Learn "Find the Cutoff Instead",
+// section "Same idea elsewhere").  Here the digits are 8 bits of the
+// composite, taken from the top, the histograms live in LDS, and once the
+// boundary bucket is small enough its elements are copied into LDS so the
+// remaining passes never touch global memory.
+#pragma once
+
+#include "topk_device.hpp"
+
+namespace tk {
+
+// Add one element (digit `d`, if `active`) to an LDS histogram.  All 64 lanes
+// of the wave must call it together.  When every active lane has the same
+// digit, one lane adds the whole count (skewed data hits one bin).
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t d, bool active) {
+  uint64_t act = ballot(active);
+  if (!act) return;
+  const uint32_t first = (uint32_t)__builtin_ctzll(act);
+  const uint32_t d0 = __shfl(d, first, 64);
+  const uint64_t same = ballot(active && d == d0);
+  if (same == act) {
+    if (lane_id() == first) atomicAdd(&h[d0], (uint32_t)__builtin_popcountll(act));
+  } else if (active) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
+// Append `c` (if `keep`) to an LDS array through a shared counter; all lanes
+// of the wave call it together.
+// Slots at or beyond `cap` are counted but not written.
+__device__ __forceinline__ void lds_append(uint64_t* arr, uint32_t* counter, uint32_t cap,
+                                           uint64_t c, bool keep) {
+  uint64_t m = ballot(keep);
+  if (!m) return;
+  uint32_t base = 0;
+  const uint32_t first = (uint32_t)__builtin_ctzll(m);
+  if (lane_id() == first) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(m));
+  base = __shfl(base, first, 64);
+  const uint32_t slot = base + rank_below(m);
+  if (keep && slot < cap) arr[slot] = c;
+}
+
+struct SelectOut {
+  uint64_t thr;       // threshold composite: resolved top bits, zeros below
+  uint32_t count_ge;  // elements with composite >= thr
+};
+
+// Select over `n` composites produced by `src(i)` (W significant bits, W a
+// multiple of 8): the composite of rank `rank` (1-based, from the top).
+// Passes stop as soon as the elements >= the bucket's lower edge number at
+// most `stop` (pass stop = 0 to resolve every bit).
+//
+// LDS: s_hist[256], s_misc[8], s_cand[cand_cap].  Every thread of the
+// workgroup must call it.
+template <class Src>
+__device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32_t rank,
+                                  uint32_t stop, uint32_t* s_hist, uint32_t* s_misc,
+                                  uint64_t* s_cand, uint32_t cand_cap) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  uint64_t prefix = 0;
+  uint32_t nb = 0, need = rank, above = 0, m = 0;
+  bool in_lds = false;
+  for (;;) {
+    const uint32_t shift = W - nb - 8;
+    const uint32_t pshift = W - nb;            // bits below the resolved prefix
+    const uint64_t ptop = nb ? (prefix >> pshift) : 0;
+    for (uint32_t i = tid; i < 256; i += nt) s_hist[i] = 0;
+    __syncthreads();
+    const uint32_t total = in_lds ? m : n;
+    for (uint32_t i0 = 0; i0 < total; i0 += nt) {
+      const uint32_t i = i0 + tid;
+      bool act = i < total;
+      uint64_t c = 0;
+      if (act) {
+        c = in_lds ? s_cand[i] : src(i);
+        act = (nb == 0) || ((c >> pshift) == ptop);
+      }
+      hist_add(s_hist, (uint32_t)(c >> shift) & 255u, act);
+    }
+    __syncthreads();
+    if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
+    __syncthreads();
+    const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+    above += acc;
+    need -= acc;
+    prefix |= (uint64_t)b << shift;
+    nb += 8;
+    const uint32_t count_ge = above + hb;
+    if (count_ge <= stop || nb >= W) {
+      __syncthreads();
+      return SelectOut{prefix, count_ge};
+    }
+    if (!in_lds && hb <= cand_cap) {
+      // copy the boundary bucket into LDS
+      const uint32_t npshift = W - nb;
+      const uint64_t ntop = prefix >> npshift;
+      if (tid == 0) s_misc[3] = 0;
+      __syncthreads();
+      for (uint32_t i0 = 0; i0 < n; i0 += nt) {
+        const uint32_t i = i0 + tid;
+        bool keep = false;
+        uint64_t c = 0;
+        if (i < n) {
+          c = src(i);
+          keep = (c >> npshift) == ntop;
+        }
+        lds_append(s_cand, &s_misc[3], cand_cap, c, keep);
+      }
+      __syncthreads();
+      m = s_misc[3] < cand_cap ? s_misc[3] : cand_cap;
+      in_lds = true;
+    }
+    __syncthreads();
+  }
+}
+
+// Gather every composite >= thr from `src` into s_out (LDS) in any order;
+// returns how many.  Every thread must call it.
+template <class Src>
+__device__ uint32_t block_collect(const Src& src, uint32_t n, uint64_t thr, uint64_t* s_out,
+                                  uint32_t out_cap, uint32_t* s_counter) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  if (tid == 0) *s_counter = 0;
+  __syncthreads();
+  for (uint32_t i0 = 0; i0 < n; i0 += nt) {
+    const uint32_t i = i0 + tid;
+    uint64_t c = 0;
+    bool keep = false;
+    if (i < n) {
+      c = src(i);
+      keep = c >= thr;
+    }
+    lds_append(s_out, s_counter, out_cap, c, keep);
+  }
+  __syncthreads();
+  const uint32_t cnt = *s_counter;
+  __syncthreads();
+  return cnt < out_cap ? cnt : out_cap;
+}
+
+// Bitonic sort of s[0..P) into descending order, P a power of two.
+__device__ __forceinline__ void block_bitonic_desc(uint64_t* s, uint32_t P) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  for (uint32_t size = 2; size <= P; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (uint32_t i = tid; i < (P >> 1); i += nt) {
+        const uint32_t lo = (i / stride) * (stride << 1) + (i % stride);
+        const uint32_t hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = s[lo], c = s[hi];
+        if (desc ? (a < c) : (a > c)) {
+          s[lo] = c;
+          s[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__host__ __device__ __forceinline__ uint32_t next_pow2(uint32_t v) {
+  uint32_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+}  // namespace tk
