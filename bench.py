@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact top-k engine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3k64]
+
+A step is one exact top-k call (the whole pipeline: sample, threshold,
+filter, refine, fallback checks, output) over one synthetic input already
+resident in HBM.  Three input buffers rotate so that no call finds its input
+in the 256 MB last-level cache.  Prints one JSON line.
+
+Extra modes (measurement plumbing, not part of the timed line):
+    --pmc-run                 a short run for rocprofv3 --pmc: a plain copy of
+                              a known size, then a few steps
+    --pmc-summary A B         read the rocprofv3 counter CSVs of the FETCH_SIZE
+                              run (A) and the WRITE_SIZE run (B) and print the
+                              traffic summary that belongs in profiles/
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "top-k Gelem/s and HBM GB/s (% of peak), N=2^28 fp32 k=64, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc", "topk_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_k_filter_c3_k64.txt")
+COPY_BYTES = 1 << 30
+
+WORKLOADS = {
+    # name: (config, k, description)
+    "c3k64": ("c3", 64, "1 row x 2^28 fp32 standard normal, k=64"),
+    "c3k16": ("c3", 16, "1 row x 2^28 fp32 standard normal, k=16"),
+    "c3k2048": ("c3", 2048, "1 row x 2^28 fp32 standard normal, k=2048"),
+    "c4v1": ("c4v1", 64, "128 rows x 2^20 fp32 Pareto(1.5) with random signs, k=64 per row"),
+    "c4v2": ("c4v2", 64, "128 rows x 2^20 fp32 Pareto(1.5) rows sorted ascending, k=64 per row"),
+    "c4v3": ("c4v3", 64, "128 rows x 2^20 fp32 zeros with 64 ones per row, k=64 per row"),
+    "c5": ("c5", 131072, "BatchTopK 4096 x 65536 bf16 ReLU(N(0,1)) flattened, k=131072"),
+    "c1": ("c1", 10, "1 row x 4096 int32 uniform [0,1000), k=10"),
+    "c2": ("c2", 10, "1 row x 65536 int32 uniform [0,2^24), k=10"),
+}
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_inputs(name: str):
+    import numpy as np
+    import workloads
+    cfg, k, desc = WORKLOADS[name]
+    x, dt, _, meta = workloads.config(cfg)
+    if cfg == "c5":
+        x = x.reshape(1, -1)
+    return x, dt, k, desc, meta
+
+
+def to_device(x, dt):
+    import numpy as np
+    import torch
+    if dt == "bf16":
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def algorithmic_bytes(rows, n, k, es, plan, R_mean):
+    """Bytes the method must move per call: one read of the input, the
+    sampled elements and their keys, the candidates written and read back,
+    and the output."""
+    b = rows * n * es
+    if plan["path"] == 0:
+        b += rows * plan["S"] * (es + 4 + 4)
+        b += R_mean * 8 * 2
+    b += rows * k * (es + 8)
+    return b
+
+
+def read_traffic(launch_bytes_alg):
+    """Traffic measured by rocprofv3 counters for the filter kernel, if the
+    committed summary was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            kk, vv = line.split(":", 1)
+            fields[kk.strip()] = vv.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, dt, k, budget_s=12.0, max_calls=5):
+    import oracle
+    oracle.lib()
+    times = []
+    t_start = time.time()
+    while len(times) < max_calls and (time.time() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        oracle.topk(x, k, dt)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return med, len(times)
+
+
+def fallback_rate(tss, bufs, k, rows, calls, policy):
+    p = tss.default_params(policy=policy)
+    fb = 0
+    r_sum = 0
+    nrow = 0
+    for i in range(calls):
+        tss.topk(bufs[i % len(bufs)], k, params=p)
+        st = tss.read_stats(rows)
+        for r in st:
+            fb += 1 if r["path"] == 1 else 0
+            r_sum += r["r_sampled"]
+            nrow += 1
+    return {"calls": calls, "row_selections": nrow, "fallbacks": fb,
+            "rate": fb / max(nrow, 1), "mean_R": r_sum / max(nrow, 1)}
+
+
+def run_bench(args):
+    import numpy as np
+    import torch
+    import top_selection_sample_amd as tss
+
+    x, dt, k, desc, meta = load_inputs(args.workload)
+    rows, n = x.shape
+    es = 2 if dt == "bf16" else 4
+    x0 = to_device(x, dt)
+    bufs = [x0]
+    for shift in (n // 3 + 1, (2 * n) // 3 + 7):
+        bufs.append(torch.roll(x0, shifts=shift, dims=1).contiguous())
+    torch.cuda.synchronize()
+    ov = torch.empty((rows, k), dtype=x0.dtype, device="cuda")
+    oi = torch.empty((rows, k), dtype=torch.int64, device="cuda")
+    plan = tss.plan(n, rows, k, dt)
+
+    for i in range(args.warmup):
+        tss.topk(bufs[i % 3], k, out=(ov, oi))
+    torch.cuda.synchronize()
+
+    # timed region: K whole calls
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        tss.topk(bufs[i % 3], k, out=(ov, oi))
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    # stage timing: HIP events on the launch stream around each stage
+    tss.profile_enable(True)
+    tss.profile_read()
+    ev0.record()
+    for i in range(args.steps):
+        tss.topk(bufs[i % 3], k, out=(ov, oi))
+    ev1.record()
+    torch.cuda.synchronize()
+    stages = tss.profile_read()
+    tss.profile_enable(False)
+    ms_step_profiled = ev0.elapsed_time(ev1) / args.steps
+
+    # fallback rate and mean survivors, both parameter policies
+    fb_calls = args.fallback_calls
+    fb = {"exact_tail": fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_EXACT_TAIL)}
+    if plan["path"] == 0:
+        fb["alg1"] = fallback_rate(tss, bufs, k, rows, max(fb_calls // 2, 1), tss.POLICY_ALG1)
+    R_mean = fb["exact_tail"]["mean_R"] * rows
+
+    elems = rows * n
+    gelem_s = elems / (ms_step * 1e-3) / 1e9
+    alg_bytes = algorithmic_bytes(rows, n, k, es, plan, R_mean)
+    e2e_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+
+    roof = None
+    if plan["path"] == 0 and stages["filter"]["count"]:
+        t_filter = stages["filter"]["ms"] / stages["filter"]["count"] * 1e-3
+        filt_bytes = elems * es + R_mean * 8
+        achieved = filt_bytes / t_filter / 1e9
+        traffic = read_traffic(filt_bytes)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "k_filter",
+                "avg_launch_us": round(t_filter * 1e6, 2),
+                "algorithmic_bytes_per_launch": int(filt_bytes)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        med, calls = cpu_baseline(x, dt, k)
+        cpu = {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the full workload ({desc}); {calls} oracle calls, median "
+                         f"{med:.2f} s each, single-threaded partial sort"}
+
+    stage_ms = {name: round(v["ms"] / v["count"], 4) if v["count"] else None
+                for name, v in stages.items()}
+    line = {
+        "metric": METRIC, "value": round(gelem_s, 3), "unit": "Gelem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else ("i32" if dt == "int32" else "f32"),
+        "data": "synthetic",
+        "config": {"workload": desc, "rows": rows, "n": n, "k": k, "input_dtype": dt,
+                   "seed": meta["seed"], "policy": "exact_tail", "S": plan["S"],
+                   "t": plan["t"], "M": plan["M"], "route": ["sampled", "exact", "exact_small"][plan["path"]]},
+        "hbm_gbs": round(e2e_gbs, 1), "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(alg_bytes),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "fallback": fb,
+        "stage_ms": stage_ms,
+        "ms_per_step_with_stage_events": round(ms_step_profiled, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def pmc_run(args):
+    """Short program for rocprofv3 --pmc: one plain copy of COPY_BYTES (the
+    calibration kernel) then a few steps of the workload."""
+    import torch
+    import top_selection_sample_amd as tss
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    x, dt, k, desc, meta = load_inputs(args.workload)
+    xd = to_device(x, dt)
+    for _ in range(max(args.steps, 1)):
+        tss.topk(xd, k)
+    torch.cuda.synchronize()
+    print("pmc run done", flush=True)
+
+
+def _rows_of(path_glob, counter):
+    out = []
+    for f in glob.glob(path_glob, recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter:
+                    out.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+    return out
+
+
+def pmc_summary(args):
+    fetch_dir, write_dir = args.pmc_summary
+    fe = _rows_of(os.path.join(fetch_dir, "**", "*counter_collection.csv"), "FETCH_SIZE")
+    wr = _rows_of(os.path.join(write_dir, "**", "*counter_collection.csv"), "WRITE_SIZE")
+
+    def pick(rows, key):
+        return [v for name, v in rows if key in name]
+    copy_f = [v for name, v in fe if "copy" in name.lower() or "elementwise" in name.lower()]
+    copy_w = [v for name, v in wr if "copy" in name.lower() or "elementwise" in name.lower()]
+    filt_f = pick(fe, "k_filter")
+    filt_w = pick(wr, "k_filter")
+    kib = 1024.0
+    # FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; the copy kernel moved
+    # COPY_BYTES each way, which calibrates both counters.
+    scale_f = COPY_BYTES / (max(copy_f) * kib) if copy_f else None
+    scale_w = COPY_BYTES / (max(copy_w) * kib) if copy_w else None
+    # the sampled pass is the first k_filter launch of each call; the exact
+    # pass is a no-op launch, so keep the largest per call
+    ff = sorted(filt_f)[-1] * kib if filt_f else None
+    fw = sorted(filt_w)[-1] * kib if filt_w else None
+    lines = [
+        "rocprofv3 counter summary: k_filter on workload c3k64 (2^28 fp32, k=64)",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"fetch_kib_copy_kernel: {max(copy_f) if copy_f else 'n/a'}",
+        f"write_kib_copy_kernel: {max(copy_w) if copy_w else 'n/a'}",
+        f"copy_bytes_known: {COPY_BYTES}",
+        f"scale_fetch: {scale_f}",
+        f"scale_write: {scale_w}",
+        f"fetch_bytes_raw_per_launch: {ff}",
+        f"write_bytes_raw_per_launch: {fw}",
+    ]
+    if ff is not None and fw is not None and scale_f and scale_w:
+        lines.append(f"hbm_bytes_per_launch: {ff * scale_f + fw * scale_w:.0f}")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3k64", choices=sorted(WORKLOADS))
+    ap.add_argument("--fallback-calls", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.gpus != 1:
+        print("bench.py: this engine runs on one GPU; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") not in ("1", ""):
+        print("bench.py: multi-rank launch is not supported (one GPU only)", file=sys.stderr)
+        sys.exit(2)
+    if args.pmc_run:
+        pmc_run(args)
+        return
+    run_bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -142,6 +142,19 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
  * (host memory).  Synchronises `stream`.  Errors: TOPK_EINVAL, TOPK_EHIP. */
 int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, void* stream);
 
+/* Stage timing (measurement aid).  While enabled, each call records HIP
+ * events on its stream around its stages; topk_profile_read waits for them
+ * and returns the summed milliseconds and bracket counts per stage, then
+ * forgets them.  Stage order: sample, tau, filter, refine, exact/fallback,
+ * sort.  The events add a few microseconds per call. */
+typedef struct {
+  double ms[8];
+  int64_t count[8];
+} topk_stage_times;
+
+int topk_profile_enable(int on);
+int topk_profile_read(topk_stage_times* out);
+
 /* Short English text for a status code (static storage). */
 const char* topk_status_string(int status);
 

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, Params,
                    TopkError, default_params)
 
-__all__ = ["topk", "plan", "workspace_size", "read_stats", "Workspace", "Params",
+__all__ = ["topk", "plan", "profile_enable", "profile_read", "workspace_size", "read_stats", "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "dtype_code"]
 
@@ -133,3 +133,16 @@ def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> li
         _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
     return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes}
             for a in arr]
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record HIP events around each pipeline stage of later calls."""
+    _lib.check(_lib.lib.topk_profile_enable(1 if on else 0), "topk_profile_enable")
+
+
+def profile_read() -> dict:
+    """Summed milliseconds and bracket counts per stage since the last read
+    (waits for the recorded events)."""
+    t = _lib.StageTimes()
+    _lib.check(_lib.lib.topk_profile_read(ctypes.byref(t)), "topk_profile_read")
+    return {name: {"ms": t.ms[i], "count": t.count[i]} for i, name in enumerate(_lib.STAGES)}

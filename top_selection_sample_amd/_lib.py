@@ -19,7 +19,9 @@ PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
 
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
-           "topk", "topk_ex", "topk_read_stats", "topk_status_string")
+           "topk", "topk_ex", "topk_read_stats", "topk_profile_enable", "topk_profile_read",
+           "topk_status_string")
+STAGES = ("sample", "tau", "filter", "refine", "exact", "sort")
 
 
 class Params(ctypes.Structure):
@@ -36,6 +38,10 @@ class PlanInfo(ctypes.Structure):
                 ("index_bits", ctypes.c_int32), ("key_bits", ctypes.c_int32),
                 ("p_recall", ctypes.c_double), ("p_overflow", ctypes.c_double),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class StageTimes(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 8), ("count", ctypes.c_int64 * 8)]
 
 
 class RowStats(ctypes.Structure):
@@ -58,6 +64,8 @@ def _load():
     L.topk.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]
     L.topk_ex.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp, P(Params)]
     L.topk_read_stats.argtypes = [vp, i64, P(RowStats), vp]
+    L.topk_profile_enable.argtypes = [i32]
+    L.topk_profile_read.argtypes = [P(StageTimes)]
     L.topk_status_string.argtypes = [i32]
     L.topk_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -16,6 +17,47 @@
 namespace {
 
 std::atomic<uint64_t> g_calls{0};
+
+// ---- stage timing
+std::atomic<int> g_prof{0};
+std::mutex g_prof_mu;
+struct Bracket {
+  hipEvent_t a, b;
+  int stage;
+};
+std::vector<Bracket> g_done;                  // closed brackets
+hipEvent_t g_open[tk::STAGE_COUNT] = {};       // begin events awaiting their end
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void mark_stage(void*, int stage, int begin, hipStream_t s) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  hipEvent_t e = take_event();
+  if (!e) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    g_pool.push_back(e);
+    return;
+  }
+  if (begin) {
+    if (g_open[stage]) g_pool.push_back(g_open[stage]);
+    g_open[stage] = e;
+  } else if (g_open[stage]) {
+    g_done.push_back(Bracket{g_open[stage], e, stage});
+    g_open[stage] = nullptr;
+  } else {
+    g_pool.push_back(e);
+  }
+}
 
 tk::ParamIn to_in(const topk_params* p) {
   tk::ParamIn in;
@@ -150,6 +192,7 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     a.seed = (params && params->use_seed) ? params->seed
                                           : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));
     a.stream = static_cast<hipStream_t>(stream);
+    if (g_prof.load(std::memory_order_relaxed)) a.mark = mark_stage;
     hipError_t e = tk::launch_pipeline(a);
     return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
   } catch (const std::bad_alloc&) {
@@ -184,6 +227,29 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
   } catch (...) {
     return TOPK_EINVAL;
   }
+}
+
+int topk_profile_enable(int on) {
+  g_prof.store(on ? 1 : 0);
+  return TOPK_OK;
+}
+
+int topk_profile_read(topk_stage_times* out) {
+  if (!out) return TOPK_EINVAL;
+  std::memset(out, 0, sizeof(*out));
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  int rc = TOPK_OK;
+  for (const Bracket& br : g_done) {
+    float ms = 0.f;
+    if (hipEventSynchronize(br.b) != hipSuccess || hipEventElapsedTime(&ms, br.a, br.b) != hipSuccess)
+      rc = TOPK_EHIP;
+    out->ms[br.stage] += ms;
+    out->count[br.stage] += 1;
+    g_pool.push_back(br.a);
+    g_pool.push_back(br.b);
+  }
+  g_done.clear();
+  return rc;
 }
 
 const char* topk_status_string(int status) {

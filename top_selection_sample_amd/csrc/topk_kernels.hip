@@ -723,20 +723,32 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
   const int dt = p.dtype;
   const dim3 row_grid(rows);
   const dim3 tiny((rows + 63) / 64);
+  auto mark = [&](int stage, int begin) {
+    if (a.mark) a.mark(a.mark_ctx, stage, begin, s);
+  };
 
   if (p.path == PLAN_EXACT_SMALL) {
+    mark(STAGE_EXACT, 1);
     TK_DISPATCH(dt, k_exact_small, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
                 a.cbuf, cap, k, B, W, (uint32_t)(p.small_k ? 1 : 0), a.out_values, a.out_idx);
+    mark(STAGE_EXACT, 0);
   } else {
     if (p.path == PLAN_SAMPLED) {
       const dim3 sg((uint32_t)((p.S + 255) / 256), rows);
+      mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, a.seed,
                   p.half_bits, a.skeys);
+      mark(STAGE_SAMPLE, 0);
+      mark(STAGE_TAU, 1);
       hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
                          (uint32_t)p.t, (uint32_t)p.KB, a.states);
+      mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
+      mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
                   cap, B, (uint32_t)ST_FILTER);
+      mark(STAGE_FILTER, 0);
+      mark(STAGE_REFINE, 1);
       if (p.small_k) {
         TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
                     a.cbuf, cap, k, B, W, (uint32_t)ST_FILTER, a.out_values, a.out_idx);
@@ -744,11 +756,13 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
         hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
                            (uint32_t)ST_FILTER);
       }
+      mark(STAGE_REFINE, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, rows, k);
     }
     // Exact path / fallback: histogram passes, each a no-op for rows that
     // are not (or no longer) selecting.
+    mark(STAGE_EXACT, 1);
     const dim3 hg(p.hist_bpr, rows);
     for (uint32_t pass = 0; pass < W / 8; ++pass) {
       TK_DISPATCH(dt, k_hist, hg, dim3(HIST_THREADS), 0, s, a.values, n, a.states, a.ghist, cap,
@@ -764,9 +778,11 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
                          (uint32_t)ST_EXACT_READY);
     }
+    mark(STAGE_EXACT, 0);
   }
   if (!p.small_k) {
     // every row now holds R in [k, cap] candidates: sort them, keep k
+    mark(STAGE_SORT, 1);
     const dim3 tg((cap + SORT_TILE - 1) / SORT_TILE, rows);
     hipLaunchKernelGGL(k_tile_sort, tg, dim3(SEL_THREADS), 0, s, a.states, a.cbuf, cap);
     const dim3 mg((cap + 255) / 256, rows);
@@ -781,6 +797,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     const dim3 og((k + 255) / 256, rows);
     TK_DISPATCH(dt, k_output, og, dim3(256), 0, s, a.values, n, a.states, src, cap, k, B,
                 a.out_values, a.out_idx);
+    mark(STAGE_SORT, 0);
   }
   return hipGetLastError();
 }

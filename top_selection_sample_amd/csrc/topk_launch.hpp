@@ -27,7 +27,16 @@ struct Plan {
   size_t off_states = 0, off_ghist = 0, off_skeys = 0, off_cbuf = 0, off_aux = 0, total = 0;
 };
 
+// Pipeline stages that can be bracketed by timing events.
+enum : int { STAGE_SAMPLE = 0, STAGE_TAU = 1, STAGE_FILTER = 2, STAGE_REFINE = 3,
+             STAGE_EXACT = 4, STAGE_SORT = 5, STAGE_COUNT = 6 };
+
+// Called before (begin = 1) and after (begin = 0) a stage's launches.
+typedef void (*StageMark)(void* ctx, int stage, int begin, hipStream_t s);
+
 struct LaunchArgs {
+  StageMark mark = nullptr;
+  void* mark_ctx = nullptr;
   Plan plan;
   const void* values;
   void* out_values;
