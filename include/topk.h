@@ -26,11 +26,14 @@
  *   - `out_values`: [rows, k] of the input dtype; each output is the exact bit
  *     pattern of the selected input element.  `out_indices`: [rows, k] int64,
  *     row-local indices.
- *   - `workspace`: device memory of at least topk_workspace_size() bytes.  It
- *     must be zero-filled before its first use (topk_workspace_init does
- *     that); afterwards every completed call leaves it ready for the next one,
- *     whatever the shape.  One workspace must not be used by two calls that
- *     may run at the same time.
+ *   - `workspace`: device memory of at least topk_workspace_size() bytes,
+ *     256-byte aligned.  The library remembers (host side) the layout of the
+ *     last call on each workspace address: a call with the same layout reuses
+ *     the workspace as the previous call left it (clean), and any other call,
+ *     or the first call on an address not prepared by topk_workspace_init,
+ *     zero-fills it first.  One workspace must not be used by two calls that
+ *     may run at the same time, and its contents must not be modified
+ *     between calls except through topk_workspace_init.
  *   - `stream`: a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; no host synchronisation happens
  *     inside topk/topk_ex.
@@ -108,6 +111,9 @@ typedef struct {
   uint32_t r_sampled; /* survivors of the sampled filter pass (R) */
   uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only */
   uint32_t passes;    /* histogram passes of the exact select */
+  uint32_t flags;     /* bit 0: an exact-route grid barrier gave up waiting (the
+                         result of that call is not trustworthy; never seen in
+                         normal operation) */
 } topk_row_stats;
 
 /* Fill *p with the defaults above.  Returns TOPK_OK, or TOPK_EINVAL for NULL. */

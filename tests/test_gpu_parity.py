@@ -156,7 +156,7 @@ def test_forced_overflow_fallback():
     gv, gi = run_gpu(x, 64, "float32", params=p)
     assert_same(gv, gi, x, 64, "float32", "overflow")
     st = _tss().read_stats(1)[0]
-    assert st["path"] == 1 and st["r_sampled"] > 100
+    assert st["path"] == 1 and st["r_sampled"] > 100 and st["flags"] == 0
 
 
 def test_forced_recall_failure_fallback():
@@ -167,7 +167,7 @@ def test_forced_recall_failure_fallback():
     gv, gi = run_gpu(x, 1000, "float32", params=p)
     assert_same(gv, gi, x, 1000, "float32", "recall")
     st = _tss().read_stats(1)[0]
-    assert st["path"] == 1 and st["r_sampled"] < 1000
+    assert st["path"] == 1 and st["r_sampled"] < 1000 and st["flags"] == 0
 
 
 @pytest.mark.parametrize("dt", ["float32", "bf16"])

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -57,6 +58,26 @@ void mark_stage(void*, int stage, int begin, hipStream_t s) {
   } else {
     g_pool.push_back(e);
   }
+}
+
+// ---- workspace layouts
+// Regions that must start at zero (sample histogram, exact-route histogram,
+// call record) sit at offsets that depend on the call shape.  Every completed
+// call leaves its own layout's zero regions clean, so a workspace can be
+// reused as is while the layout stays the same; when it changes, the
+// workspace is zero-filled again first.  The layout last used on each
+// workspace address is kept here (0 = freshly zero-filled).
+std::mutex g_ws_mu;
+std::map<uintptr_t, uint64_t> g_ws_layout;
+
+uint64_t layout_signature(const tk::Plan& p) {
+  uint64_t h = 0x9E3779B97F4A7C15ull;
+  const uint64_t parts[] = {p.total, p.off_states, p.off_call, p.off_flag, p.off_ghist,
+                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux, (uint64_t)p.rows};
+  for (uint64_t v : parts) {
+    h ^= v + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+  }
+  return h | 1ull;   // never 0
 }
 
 tk::ParamIn to_in(const topk_params* p) {
@@ -161,7 +182,10 @@ int topk_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace && bytes) return TOPK_EINVAL;
   if (!bytes) return TOPK_OK;
   hipError_t e = tk::launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
+  if (e != hipSuccess) return TOPK_EHIP;
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  g_ws_layout[reinterpret_cast<uintptr_t>(workspace)] = 0;
+  return TOPK_OK;
 }
 
 int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
@@ -184,14 +208,27 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     a.out_values = out_values;
     a.out_idx = out_indices;
     a.states = reinterpret_cast<tk::RowState*>(ws + p.off_states);
+    a.call = reinterpret_cast<tk::CallState*>(ws + p.off_call);
+    a.flagged = reinterpret_cast<uint32_t*>(ws + p.off_flag);
     a.ghist = reinterpret_cast<uint32_t*>(ws + p.off_ghist);
     a.skeys = reinterpret_cast<uint32_t*>(ws + p.off_skeys);
+    a.shist = reinterpret_cast<uint32_t*>(ws + p.off_shist);
     a.cbuf = reinterpret_cast<uint64_t*>(ws + p.off_cbuf);
     a.aux = reinterpret_cast<uint64_t*>(ws + p.off_aux);
     const uint64_t ctr = g_calls.fetch_add(1, std::memory_order_relaxed);
     a.seed = (params && params->use_seed) ? params->seed
                                           : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));
     a.stream = static_cast<hipStream_t>(stream);
+    {
+      const uint64_t sig = layout_signature(p);
+      std::lock_guard<std::mutex> g(g_ws_mu);
+      auto it = g_ws_layout.find(reinterpret_cast<uintptr_t>(workspace));
+      const bool fresh = (it != g_ws_layout.end()) && (it->second == 0 || it->second == sig);
+      if (!fresh) {
+        if (tk::launch_zero_fill(workspace, p.total, a.stream) != hipSuccess) return TOPK_EHIP;
+      }
+      g_ws_layout[reinterpret_cast<uintptr_t>(workspace)] = sig;
+    }
     if (g_prof.load(std::memory_order_relaxed)) a.mark = mark_stage;
     hipError_t e = tk::launch_pipeline(a);
     return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
@@ -216,8 +253,14 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
     if (hipMemcpyAsync(st.data(), workspace, sizeof(tk::RowState) * (size_t)rows,
                        hipMemcpyDeviceToHost, s) != hipSuccess)
       return TOPK_EHIP;
+    tk::CallState cs;
+    const size_t off_call = ((size_t)rows * sizeof(tk::RowState) + 255) & ~(size_t)255;
+    if (hipMemcpyAsync(&cs, static_cast<const char*>(workspace) + off_call, sizeof(cs),
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+      return TOPK_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return TOPK_EHIP;
     for (int64_t r = 0; r < rows; ++r) {
+      out[r].flags = cs.error;
       out[r].tau_key = st[(size_t)r].tau_key;
       out[r].r_sampled = st[(size_t)r].r_sampled;
       out[r].path = st[(size_t)r].path;

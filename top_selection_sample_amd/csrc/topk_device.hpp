@@ -49,6 +49,18 @@ struct alignas(64) RowState {
 };
 static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");
 
+// Per-call record shared by all rows: the rows sent to the exact route.
+// Zero between calls (the exact-route kernel clears it when it is done).
+struct alignas(64) CallState {
+  uint32_t nflag;      // rows listed for the exact route
+  uint32_t nactive;    // listed rows whose exact threshold is not resolved yet
+  uint32_t bar_count;  // grid barrier: arrivals in the current round (0 at rest)
+  uint32_t bar_gen;    // grid barrier: round number
+  uint32_t error;      // sticky: bit 0 = a grid barrier gave up waiting
+  uint32_t pad[11];
+};
+static_assert(sizeof(CallState) == 64, "CallState is one 64-byte line");
+
 // ---------------------------------------------------------------- keys
 // int32: flip the sign bit.  float (32 or 16 bit): a negative value flips all
 // bits, a positive one sets the sign bit; -0 maps to +0's key and every NaN to

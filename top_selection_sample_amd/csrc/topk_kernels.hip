@@ -61,18 +61,35 @@ struct Feistel {
   }
 };
 
+// Sample keys also land in an 11-bit histogram of their top bits (LDS per
+// workgroup, merged into the row's global histogram), the first level of the
+// threshold's radix select.
+constexpr uint32_t SH_BITS = 11;
+constexpr uint32_t SH_BINS = 1u << SH_BITS;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_sample(const void* __restrict__ values, uint32_t n,
                                                 uint32_t S, uint64_t seed, uint32_t half_bits,
-                                                uint32_t* __restrict__ skeys) {
-  const uint32_t row = blockIdx.y;
-  const uint32_t j = blockIdx.x * 256u + threadIdx.x;
-  if (j >= S) return;
-  const Feistel f(seed, row, half_bits);
-  uint64_t x = f.apply(j);
-  while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
-  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-  skeys[(size_t)row * S + j] = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+                                                uint32_t* __restrict__ skeys,
+                                                uint32_t* __restrict__ shist) {
+  __shared__ uint32_t h[SH_BINS];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  for (uint32_t i = tid; i < SH_BINS; i += 256) h[i] = 0;
+  __syncthreads();
+  const uint32_t j = blockIdx.x * 256u + tid;
+  if (j < S) {
+    const Feistel f(seed, row, half_bits);
+    uint64_t x = f.apply(j);
+    while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
+    const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+    const uint32_t key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+    skeys[(size_t)row * S + j] = key;
+    atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = shist + (size_t)row * SH_BINS;
+  for (uint32_t i = tid; i < SH_BINS; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
 // ======================================================================
@@ -89,14 +106,45 @@ constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
 
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
                                                      uint32_t t, uint32_t KB,
+                                                     uint32_t* __restrict__ shist,
                                                      RowState* __restrict__ states) {
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[SH_BINS];
   __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tmp[16];
   __shared__ uint64_t s_cand[CAND_CAP];
-  const uint32_t row = blockIdx.x;
+  const uint32_t row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  uint32_t* gh = shist + (size_t)row * SH_BINS;
+  for (uint32_t i = tid; i < SH_BINS; i += nt) {
+    s_hist[i] = gh[i];
+    gh[i] = 0;                      // ready for the next call
+  }
+  __syncthreads();
+  block_find_bucket(s_hist, SH_BINS, t, s_misc, s_tmp);
+  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+  const uint32_t sh = KB - SH_BITS;
   KeySrc src{skeys + (size_t)row * S};
-  SelectOut r = block_select(src, S, KB, t, 0u, s_hist, s_misc, s_cand, CAND_CAP);
-  if (threadIdx.x == 0) {
+  SelectStart st0;
+  st0.prefix = (uint64_t)b << sh;
+  st0.nb = SH_BITS;
+  st0.need = t - acc;
+  st0.above = acc;
+  __syncthreads();
+  if (hb <= CAND_CAP) {
+    // the boundary bucket's keys into LDS; the rest of the select stays there
+    if (tid == 0) s_misc[3] = 0;
+    __syncthreads();
+    for_batched<16, uint32_t>(
+        S, [&](uint32_t i) { return src.p[i]; },
+        [&](uint32_t key, bool ok) {
+          lds_append(s_cand, &s_misc[3], CAND_CAP, key, ok && (key >> sh) == b);
+        });
+    __syncthreads();
+    st0.m = s_misc[3] < CAND_CAP ? s_misc[3] : CAND_CAP;
+    st0.in_lds = true;
+    __syncthreads();
+  }
+  SelectOut r = block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP);
+  if (tid == 0) {
     RowState* st = states + row;
     st->status = ST_FILTER;
     st->tau_key = (uint32_t)r.thr;
@@ -362,122 +410,41 @@ __device__ __forceinline__ void start_exact(RowState* st, uint32_t k, uint32_t p
   st->passes = 0;
 }
 
-__global__ void k_check(RowState* __restrict__ states, uint32_t rows, uint32_t k, uint32_t cap,
-                        uint32_t want) {
+// Rows sent to the exact route are listed for the exact-route kernel.
+__device__ __forceinline__ void flag_row(CallState* cs, uint32_t* flagged, uint32_t row) {
+  const uint32_t slot = atomicAdd(&cs->nflag, 1u);
+  atomicAdd(&cs->nactive, 1u);
+  flagged[slot] = row;
+}
+
+__global__ void k_check(RowState* __restrict__ states, CallState* __restrict__ cs,
+                        uint32_t* __restrict__ flagged, uint32_t rows, uint32_t k, uint32_t cap) {
   const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   RowState* st = states + row;
-  if (st->status != want) return;
+  if (st->status != ST_FILTER) return;
   const uint32_t R = st->count;
-  if (want == ST_FILTER) {
-    st->r_sampled = R;
-    if (R < k || R > cap) {
-      start_exact(st, k, PATH_FALLBACK);
-      return;
-    }
+  st->r_sampled = R;
+  if (R < k || R > cap) {
+    start_exact(st, k, PATH_FALLBACK);
+    flag_row(cs, flagged, row);
+    return;
   }
   st->status = ST_SORT;
 }
 
-__global__ void k_setup_exact(RowState* __restrict__ states, uint32_t rows, uint32_t k) {
+__global__ void k_setup_exact(RowState* __restrict__ states, CallState* __restrict__ cs,
+                              uint32_t* __restrict__ flagged, uint32_t rows, uint32_t k) {
   const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   RowState* st = states + row;
   start_exact(st, k, PATH_EXACT);
   st->r_sampled = 0;
   st->tau_key = 0;
-}
-
-// ======================================================================
-// Exact path (Prof-K section 3, stage 4 fallback: exact top-k on the full
-// input), done as a radix select: each pass counts one 8-bit digit of the
-// composite over the elements that match the resolved prefix; the last
-// workgroup to finish resolves the boundary bucket.  It stops as soon as the
-// elements at or above the bucket fit the candidate buffer, so the scratch
-// memory stays O(capacity), never O(n).
-// ======================================================================
-constexpr uint32_t HIST_THREADS = 256;
-constexpr uint32_t HIST_UNROLL = 4;
-
-template <int DT>
-__global__ __launch_bounds__(HIST_THREADS) void k_hist(const void* __restrict__ values, uint32_t n,
-                                                       RowState* __restrict__ states,
-                                                       uint32_t* __restrict__ ghist, uint32_t cap,
-                                                       uint32_t B, uint32_t W) {
-  using D = Dt<DT>;
-  const uint32_t row = blockIdx.y;
-  RowState* st = states + row;
-  if (st->status != ST_EXACT) return;
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_misc[8];
-  __shared__ uint32_t s_last;
-  const uint32_t tid = threadIdx.x;
-  const uint32_t nb = st->nbits;
-  const uint64_t prefix = st->prefix;
-  const uint32_t shift = W - nb - 8;
-  const uint32_t pshift = W - nb;
-  const uint64_t ptop = nb ? (prefix >> pshift) : 0ull;
-  const uint64_t maskB = (1ull << B) - 1ull;
-  s_hist[tid] = 0;
-  __syncthreads();
-
-  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
-  const uint32_t bpr = gridDim.x;
-  const size_t stride = (size_t)bpr * HIST_THREADS;
-  // Iterate per wave so that every lane of a wave runs the same trip count.
-  const uint32_t lane = tid & 63u;
-  for (size_t i0 = (size_t)blockIdx.x * HIST_THREADS + (tid - lane); i0 < n;
-       i0 += HIST_UNROLL * stride) {
-    uint32_t raw[HIST_UNROLL];
-    bool ok[HIST_UNROLL];
-#pragma unroll
-    for (uint32_t u = 0; u < HIST_UNROLL; ++u) {
-      const size_t i = i0 + u * stride + lane;
-      ok[u] = i < n;
-      raw[u] = ok[u] ? load_raw<DT>(rowp, (uint32_t)i) : 0u;
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < HIST_UNROLL; ++u) {
-      const uint32_t i = (uint32_t)(i0 + u * stride + lane);
-      const uint64_t c = ((uint64_t)D::key(raw[u]) << B) | (maskB - i);
-      const bool act = ok[u] && ((nb == 0) || ((c >> pshift) == ptop));
-      hist_add(s_hist, (uint32_t)(c >> shift) & 255u, act);
-    }
-  }
-  __syncthreads();
-  if (s_hist[tid]) atomicAdd(&ghist[(size_t)row * 256 + tid], s_hist[tid]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&st->ticket, 1u) == bpr - 1u) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-
-  // Last workgroup of this row: resolve the pass.
-  __threadfence();
-  s_hist[tid] = __hip_atomic_load(&ghist[(size_t)row * 256 + tid], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t need = st->need;
-  if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
-  __syncthreads();
-  ghist[(size_t)row * 256 + tid] = 0u;
-  if (tid == 0) {
-    const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
-    const uint32_t above = st->above + acc;
-    const uint64_t np = prefix | ((uint64_t)b << shift);
-    const uint32_t nnb = nb + 8;
-    st->above = above;
-    st->need = need - acc;
-    st->prefix = np;
-    st->nbits = nnb;
-    st->passes = st->passes + 1;
-    st->ticket = 0;
-    if (above + hb <= cap || nnb >= W) {
-      st->thr_key = (uint32_t)(np >> B);
-      st->thr_bound = (uint32_t)(maskB - (np & maskB));
-      st->count = 0;
-      st->status = ST_EXACT_READY;
-    }
+  flagged[row] = row;
+  if (row == 0) {
+    cs->nflag = rows;
+    cs->nactive = rows;
   }
 }
 
@@ -518,44 +485,132 @@ __device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t B, const
   }
 }
 
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* s_tmp) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t o = __shfl_xor(v, d, 64);
+    v = o > v ? o : v;
+  }
+  if ((threadIdx.x & 63u) == 0) s_tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t m = 0;
+  for (uint32_t j = 0; j < (blockDim.x >> 6); ++j) m = s_tmp[j] > m ? s_tmp[j] : m;
+  __syncthreads();
+  return m;
+}
+
+constexpr uint32_t RF_BITS = 11;
+constexpr uint32_t RF_BINS = 1u << RF_BITS;
+constexpr uint32_t RF_SORT_CAP = 4096;
+
+// Sort s[0..cnt) descending in LDS (cnt <= CAND_CAP), zero-padded to a power
+// of two; composites are never zero, so padding sorts last.
+__device__ __forceinline__ void lds_sort_desc(uint64_t* s, uint32_t cnt) {
+  const uint32_t P = next_pow2(cnt);
+  for (uint32_t i = cnt + threadIdx.x; i < P; i += blockDim.x) s[i] = 0ull;
+  __syncthreads();
+  block_bitonic_desc(s, P);
+}
+
+// One row, one workgroup (1024 threads).  want = ST_FILTER: the sampled
+// candidates (a failed check sends the row to the exact route instead);
+// want = ST_EXACT_READY: the exact route's candidates.
 template <int DT>
-__global__ __launch_bounds__(SEL_THREADS) void k_refine(
-    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
-    const uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
-    uint32_t want, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_misc[8];
-  __shared__ uint64_t s_cand[CAND_CAP];
-  const uint32_t row = blockIdx.x;
+__device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+                           CallState* cs, uint32_t* flagged, const uint64_t* __restrict__ cbuf,
+                           uint32_t cap, uint32_t k, uint32_t B, uint32_t W, uint32_t want,
+                           void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+                           uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
+                           uint64_t* s_cand) {
+  // LDS: s_hist[RF_BINS], s_misc[8], s_tmp[16], s_cand[CAND_CAP]
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
   RowState* st = states + row;
   if (st->status != want) return;
   uint32_t R = st->count;
   if (want == ST_FILTER) {
     if (R < k || R > cap) {
       __syncthreads();
-      if (threadIdx.x == 0) {
+      if (tid == 0) {
         st->r_sampled = R;
         start_exact(st, k, PATH_FALLBACK);
+        flag_row(cs, flagged, row);
       }
       return;
     }
   }
   if (R > cap) R = cap;   // the exact route never exceeds the capacity
+  const uint32_t KB = W - B;
+  const uint32_t lo_key = (want == ST_FILTER) ? st->tau_key : st->thr_key;
   CompSrc src{cbuf + (size_t)row * cap};
-  SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
-  const uint32_t got = block_collect(src, R, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
-  const uint32_t P = next_pow2(got);
-  for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
+
+  // pass 1: the largest candidate key
+  uint32_t mx = 0;
+  for_batched<LOADS_IN_FLIGHT, uint64_t>(
+      R, [&](uint32_t i) { return src.p[i]; },
+      [&](uint64_t c, bool ok) {
+        const uint32_t key = ok ? (uint32_t)(c >> B) : 0u;
+        mx = key > mx ? key : mx;
+      });
+  const uint32_t kmax = block_max_u32(mx, s_tmp);
+  // every candidate key lies in [lo_key, kmax]: histogram the 11 key bits
+  // just below their common prefix
+  const uint32_t diff = (lo_key ^ kmax) & (KB == 32 ? 0xFFFFFFFFu : 0xFFFFu);
+  const uint32_t top = diff ? 31u - (uint32_t)__builtin_clz(diff) : 0u;
+  const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
+  for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist[i] = 0;
   __syncthreads();
-  block_bitonic_desc(s_cand, P);
+  for_batched<LOADS_IN_FLIGHT, uint64_t>(
+      R, [&](uint32_t i) { return src.p[i]; },
+      [&](uint64_t c, bool ok) {
+        hist_add(s_hist, ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1), ok);
+      });
+  __syncthreads();
+  block_find_bucket(s_hist, RF_BINS, k, s_misc, s_tmp);
+  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+  __syncthreads();
+  uint32_t got;
+  if (acc + hb <= RF_SORT_CAP) {
+    // pass 2: everything at or above the boundary bucket, then sort in LDS
+    if (tid == 0) s_misc[4] = 0;
+    __syncthreads();
+    for_batched<LOADS_IN_FLIGHT, uint64_t>(
+        R, [&](uint32_t i) { return src.p[i]; },
+        [&](uint64_t c, bool ok) {
+          const bool keep = ok && (((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1)) >= b;
+          lds_append(s_cand, &s_misc[4], CAND_CAP, c, keep);
+        });
+    __syncthreads();
+    got = s_misc[4] < RF_SORT_CAP ? s_misc[4] : RF_SORT_CAP;
+    __syncthreads();
+  } else {
+    // heavy ties or a wide boundary bucket: radix select on the composite
+    SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
+    got = block_collect(src, R, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
+  }
+  lds_sort_desc(s_cand, got);
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
   write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     if (want == ST_FILTER) st->r_sampled = R;
     st->status = ST_DONE;
     st->count = 0;
   }
+  __syncthreads();
+}
+
+template <int DT>
+__global__ __launch_bounds__(SEL_THREADS) void k_refine(
+    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    CallState* __restrict__ cs, uint32_t* __restrict__ flagged, const uint64_t* __restrict__ cbuf,
+    uint32_t cap, uint32_t k, uint32_t B, uint32_t W, void* __restrict__ out_values,
+    int64_t* __restrict__ out_idx) {
+  __shared__ uint32_t s_hist[RF_BINS];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
+                 out_idx, blockIdx.x, s_hist, s_misc, s_tmp, s_cand);
 }
 
 // Whole exact selection of a small row in one workgroup.  Small k: writes the
@@ -620,6 +675,250 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
     st->path = PATH_EXACT;
     st->r_sampled = 0;
     st->tau_key = 0;
+  }
+}
+
+// ======================================================================
+// Exact route (Prof-K section 3, stage 4: exact top-k on the full input when
+// the sampled filter fails), done as a radix select over each listed row:
+// every pass counts one 8-bit digit of the composite over the elements that
+// match the resolved prefix; a workgroup per row then resolves the boundary
+// bucket.  Passes stop as soon as the elements at or above the bucket fit the
+// candidate buffer, so the scratch memory stays O(capacity), never O(n).
+// Then one filter pass with the exact threshold fills the buffer, and the
+// rows are refined (small k) or handed to the sort (large k).
+//
+// One launch does it all, the phases separated by grid-wide barriers.  The
+// grid is one workgroup per compute unit (each CU has room for two), so all
+// workgroups are resident together; every barrier wait is bounded, and a
+// wait that gives up sets CallState::error instead of hanging.  When no row
+// is listed every workgroup returns at once, so the route costs a single
+// empty launch on the common path.
+// ======================================================================
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
+
+__device__ void grid_barrier(CallState* cs, uint32_t G) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t gen = __hip_atomic_load(&cs->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(&cs->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    if (arrived == G) {
+      __hip_atomic_store(&cs->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&cs->bar_gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(&cs->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > SPIN_LIMIT) {
+          __hip_atomic_fetch_or(&cs->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
+
+constexpr uint32_t EX_THREADS = 1024;
+constexpr uint32_t EX_VPT = 4;                            // vectors per thread per item
+constexpr uint32_t EX_ITEM_VEC = EX_THREADS * EX_VPT;     // vectors per item
+
+// (match, digit) of one element for the pass that resolves bits
+// [W - nb - 8, W - nb) of the composite key << B | (2^B - 1 - idx).
+template <int KBITS>
+__device__ __forceinline__ bool digit_of(uint32_t key, uint32_t idx, uint32_t nb, uint64_t prefix,
+                                         uint32_t B, uint32_t* d) {
+  if (nb < (uint32_t)KBITS) {                 // a key digit
+    const uint32_t pkey = (uint32_t)(prefix >> B);
+    const bool m = (nb == 0) || ((key >> (KBITS - nb)) == (pkey >> (KBITS - nb)));
+    *d = (key >> (KBITS - nb - 8)) & 255u;
+    return m;
+  }
+  const uint32_t ib = nb - KBITS;             // resolved index bits
+  const uint32_t low = (uint32_t)(((1ull << B) - 1ull) - idx);
+  const uint32_t plow = (uint32_t)(prefix & ((1ull << B) - 1ull));
+  const bool m = (key == (uint32_t)(prefix >> B)) && (ib == 0 || (low >> (B - ib)) == (plow >> (B - ib)));
+  *d = (low >> (B - ib - 8)) & 255u;
+  return m;
+}
+
+struct RowGeom {
+  const char* rowp;
+  uint32_t head, nvec, tail0;
+  const u32x4* vp;
+};
+
+template <int DT>
+__device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint32_t row) {
+  using D = Dt<DT>;
+  RowGeom g;
+  g.rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(g.rowp);
+  g.head = (uint32_t)(((16u - (addr & 15u)) & 15u) / D::ES);
+  if (g.head > n) g.head = n;
+  g.nvec = (n - g.head) / D::VEC;
+  g.tail0 = g.head + g.nvec * D::VEC;
+  g.vp = reinterpret_cast<const u32x4*>(g.rowp + (size_t)g.head * D::ES);
+  return g;
+}
+
+// Calls f(raw, idx, valid) for every element of item c of a row, with every
+// lane of every wave taking part in each call (valid marks real elements).
+template <int DT, class F>
+__device__ __forceinline__ void for_item(const RowGeom& g, uint32_t n, uint32_t c, F&& f) {
+  using D = Dt<DT>;
+  const uint32_t tid = threadIdx.x;
+#pragma unroll
+  for (uint32_t j = 0; j < EX_VPT; ++j) {
+    const uint32_t v = c * EX_ITEM_VEC + j * EX_THREADS + tid;
+    const bool ok = v < g.nvec;
+    const u32x4 x = ok ? __builtin_nontemporal_load(g.vp + v) : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t e0 = g.head + v * D::VEC;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (DT == DT_BF16) {
+        f(x[q] & 0xFFFFu, e0 + 2 * q, ok);
+        f(x[q] >> 16, e0 + 2 * q + 1, ok);
+      } else {
+        f(x[q], e0 + q, ok);
+      }
+    }
+  }
+  if (c == 0 && tid < 64) {   // head and tail elements, first wave
+    const uint32_t nt = n - g.tail0;
+    const uint32_t j = tid;
+    const bool ok = j < g.head + nt;
+    uint32_t idx = 0, raw = 0;
+    if (ok) {
+      idx = (j < g.head) ? j : g.tail0 + (j - g.head);
+      raw = load_raw<DT>(g.rowp, idx);
+    }
+    f(raw, idx, ok);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
+    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
+    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
+    uint32_t small_k, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+  using D = Dt<DT>;
+  __shared__ uint32_t s_hist[RF_BINS];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  const uint32_t nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (nf == 0) return;                        // the common case: nothing to do
+  const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
+  uint32_t ipr = (n / D::VEC + EX_ITEM_VEC - 1) / EX_ITEM_VEC;   // items per row
+  if (ipr == 0) ipr = 1;
+  const uint64_t total = (uint64_t)nf * ipr;
+  auto sync_all = [&]() { grid_barrier(cs, G); };
+
+  // ---- histogram passes
+  for (uint32_t pass = 0; pass < W / 8; ++pass) {
+    if (__hip_atomic_load(&cs->nactive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
+    for (uint64_t it = blockIdx.x; it < total; it += G) {
+      const uint32_t f = (uint32_t)(it / ipr), c = (uint32_t)(it % ipr);
+      const uint32_t row = flagged[f];
+      RowState* st = states + row;
+      if (st->status != ST_EXACT) continue;
+      const uint32_t nb = st->nbits;
+      const uint64_t prefix = st->prefix;
+      if (tid < 256) s_hist[tid] = 0;
+      __syncthreads();
+      const RowGeom g = row_geom<DT>(values, n, row);
+      for_item<DT>(g, n, c, [&](uint32_t raw, uint32_t idx, bool ok) {
+        uint32_t d;
+        const bool m = digit_of<D::KB>(D::key(raw), idx, nb, prefix, B, &d);
+        hist_add(s_hist, d, ok && m);
+      });
+      __syncthreads();
+      if (tid < 256 && s_hist[tid]) atomicAdd(&ghist[(size_t)f * 256 + tid], s_hist[tid]);
+      __syncthreads();
+    }
+    sync_all();
+    // resolve: one workgroup per listed row
+    for (uint32_t f = blockIdx.x; f < nf; f += G) {
+      const uint32_t row = flagged[f];
+      RowState* st = states + row;
+      if (st->status != ST_EXACT) continue;
+      uint32_t* gh = ghist + (size_t)f * 256;
+      if (tid < 256) {
+        s_hist[tid] = gh[tid];
+        gh[tid] = 0;
+      }
+      __syncthreads();
+      const uint32_t need = st->need;
+      if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t nb = st->nbits;
+        const uint32_t shift = W - nb - 8;
+        const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+        const uint32_t above = st->above + acc;
+        const uint64_t np = st->prefix | ((uint64_t)b << shift);
+        const uint32_t nnb = nb + 8;
+        const uint64_t maskB = (1ull << B) - 1ull;
+        st->above = above;
+        st->need = need - acc;
+        st->prefix = np;
+        st->nbits = nnb;
+        st->passes = st->passes + 1;
+        if (above + hb <= cap || nnb >= W) {
+          st->thr_key = (uint32_t)(np >> B);
+          st->thr_bound = (uint32_t)(maskB - (np & maskB));
+          st->count = 0;
+          st->status = ST_EXACT_READY;
+          atomicSub(&cs->nactive, 1u);
+        }
+      }
+      __syncthreads();
+    }
+    sync_all();
+  }
+
+  // ---- exact filter: every element >= the exact threshold into the buffer
+  {
+    Stager sg{s_cand + (size_t)w * STAGE_SLOTS, 0u, nullptr, nullptr, cap};
+    for (uint64_t it = blockIdx.x; it < total; it += G) {
+      const uint32_t f = (uint32_t)(it / ipr), c = (uint32_t)(it % ipr);
+      const uint32_t row = flagged[f];
+      RowState* st = states + row;
+      if (st->status != ST_EXACT_READY) continue;
+      const Thr thr = make_thr<DT>(st->thr_key, st->thr_bound);
+      const uint64_t maskB = (1ull << B) - 1ull;
+      sg.st = st;
+      sg.buf = cbuf + (size_t)row * cap;
+      const RowGeom g = row_geom<DT>(values, n, row);
+      for_item<DT>(g, n, c, [&](uint32_t raw, uint32_t idx, bool ok) {
+        const uint32_t key = D::key(raw);
+        const bool p = ok && key_pass(key, idx, thr);
+        sg.push(p, p ? (((uint64_t)key << B) | (maskB - idx)) : 0ull);
+      });
+      if (sg.fill) sg.flush();
+    }
+  }
+  sync_all();
+
+  // ---- refine (small k) or hand over to the sort (large k)
+  for (uint32_t f = blockIdx.x; f < nf; f += G) {
+    const uint32_t row = flagged[f];
+    if (small_k) {
+      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_EXACT_READY,
+                     out_values, out_idx, row, s_hist, s_misc, s_tmp, s_cand);
+    } else if (tid == 0) {
+      states[row].status = ST_SORT;
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    // every workgroup read nflag before the first grid barrier
+    cs->nflag = 0;
+    cs->nactive = 0;
   }
 }
 
@@ -715,6 +1014,27 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
     default: hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__); break;         \
   }
 
+template <int DT>
+static hipError_t launch_exact_coop(const LaunchArgs& a, uint32_t small_k) {
+  // one workgroup per compute unit (cached per device)
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cached[dev] = cus > 0 ? cus : 1;
+  }
+  const Plan& p = a.plan;
+  hipLaunchKernelGGL(k_exact_coop<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
+                     a.values, (uint32_t)p.n, a.states, a.call, a.flagged, a.ghist, a.cbuf,
+                     (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, a.out_values, a.out_idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_pipeline(const LaunchArgs& a) {
   const Plan& p = a.plan;
   const uint32_t rows = (uint32_t)p.rows, n = (uint32_t)p.n, k = (uint32_t)p.k;
@@ -737,11 +1057,11 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       const dim3 sg((uint32_t)((p.S + 255) / 256), rows);
       mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, a.seed,
-                  p.half_bits, a.skeys);
+                  p.half_bits, a.skeys, a.shist);
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
       hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
-                         (uint32_t)p.t, (uint32_t)p.KB, a.states);
+                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states);
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
@@ -751,33 +1071,27 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_REFINE, 1);
       if (p.small_k) {
         TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
-                    a.cbuf, cap, k, B, W, (uint32_t)ST_FILTER, a.out_values, a.out_idx);
+                    a.call, a.flagged, a.cbuf, cap, k, B, W, a.out_values, a.out_idx);
       } else {
-        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
-                           (uint32_t)ST_FILTER);
+        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows, k,
+                           cap);
       }
       mark(STAGE_REFINE, 0);
     } else {
-      hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, rows, k);
+      hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
+                         k);
     }
-    // Exact path / fallback: histogram passes, each a no-op for rows that
-    // are not (or no longer) selecting.
+    // Exact route for every listed row (a single no-op launch when none is).
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     mark(STAGE_EXACT, 1);
-    const dim3 hg(p.hist_bpr, rows);
-    for (uint32_t pass = 0; pass < W / 8; ++pass) {
-      TK_DISPATCH(dt, k_hist, hg, dim3(HIST_THREADS), 0, s, a.values, n, a.states, a.ghist, cap,
-                  B, W);
+    const uint32_t sk = p.small_k ? 1u : 0u;
+    switch (dt) {
+      case DT_I32: e = launch_exact_coop<DT_I32>(a, sk); break;
+      case DT_F32: e = launch_exact_coop<DT_F32>(a, sk); break;
+      default: e = launch_exact_coop<DT_BF16>(a, sk); break;
     }
-    const dim3 fg(p.filter_bpr, rows);
-    TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf, cap,
-                B, (uint32_t)ST_EXACT_READY);
-    if (p.small_k) {
-      TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states, a.cbuf,
-                  cap, k, B, W, (uint32_t)ST_EXACT_READY, a.out_values, a.out_idx);
-    } else {
-      hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, rows, k, cap,
-                         (uint32_t)ST_EXACT_READY);
-    }
+    if (e != hipSuccess) return e;
     mark(STAGE_EXACT, 0);
   }
   if (!p.small_k) {

@@ -299,10 +299,16 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   size_t off = 0;
   p.off_states = off;
   off = align256(off + (size_t)rows * 64);
+  p.off_call = off;
+  off = align256(off + 64);
+  p.off_flag = off;
+  off = align256(off + (size_t)rows * 4);
   p.off_ghist = off;
   if (p.path != PLAN_EXACT_SMALL) off = align256(off + (size_t)rows * 256 * 4);
   p.off_skeys = off;
   if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.S * 4);
+  p.off_shist = off;
+  if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 2048 * 4);
   p.off_cbuf = off;
   off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.off_aux = off;

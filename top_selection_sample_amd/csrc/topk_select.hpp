@@ -43,42 +43,78 @@ __device__ __forceinline__ void lds_append(uint64_t* arr, uint32_t* counter, uin
   if (keep && slot < cap) arr[slot] = c;
 }
 
+// Loop over i in [0, total) with U loads in flight per thread: `load(i)` for
+// every valid i first, then `proc(value, valid)` in order.  Every thread of
+// the workgroup runs the same trip count, so proc may use wave operations.
+template <int U, class T, class Load, class Proc>
+__device__ __forceinline__ void for_batched(uint32_t total, Load&& load, Proc&& proc) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  for (uint32_t i0 = 0; i0 < total; i0 += nt * U) {
+    T v[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + (uint32_t)u * nt + tid;
+      ok[u] = i < total;
+      v[u] = ok[u] ? load(i) : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) proc(v[u], ok[u]);
+  }
+}
+
+constexpr int LOADS_IN_FLIGHT = 8;
+
 struct SelectOut {
   uint64_t thr;       // threshold composite: resolved top bits, zeros below
   uint32_t count_ge;  // elements with composite >= thr
 };
 
-// Select over `n` composites produced by `src(i)` (W significant bits, W a
-// multiple of 8): the composite of rank `rank` (1-based, from the top).
+// Where a select starts: `nb` top bits already resolved to `prefix` (bits
+// below zero), `above` elements known to lie above that prefix, and the rank
+// `need` still wanted inside it.  With in_lds, the `m` elements matching the
+// prefix already sit in s_cand.
+struct SelectStart {
+  uint64_t prefix = 0;
+  uint32_t nb = 0, need = 1, above = 0, m = 0;
+  bool in_lds = false;
+};
+
+// Select over `n` composites produced by `src(i)` (W significant bits): the
+// composite of rank `need` (1-based, from the top) among those matching the
+// start prefix.  Digits are 8 bits from the top (the last may be narrower).
 // Passes stop as soon as the elements >= the bucket's lower edge number at
 // most `stop` (pass stop = 0 to resolve every bit).
 //
 // LDS: s_hist[256], s_misc[8], s_cand[cand_cap].  Every thread of the
 // workgroup must call it.
 template <class Src>
-__device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32_t rank,
-                                  uint32_t stop, uint32_t* s_hist, uint32_t* s_misc,
-                                  uint64_t* s_cand, uint32_t cand_cap) {
+__device__ SelectOut block_select_from(const Src& src, uint32_t n, uint32_t W, SelectStart st0,
+                                       uint32_t stop, uint32_t* s_hist, uint32_t* s_misc,
+                                       uint64_t* s_cand, uint32_t cand_cap) {
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  uint64_t prefix = 0;
-  uint32_t nb = 0, need = rank, above = 0, m = 0;
-  bool in_lds = false;
+  uint64_t prefix = st0.prefix;
+  uint32_t nb = st0.nb, need = st0.need, above = st0.above, m = st0.m;
+  bool in_lds = st0.in_lds;
   for (;;) {
-    const uint32_t shift = W - nb - 8;
+    const uint32_t width = (W - nb) < 8u ? (W - nb) : 8u;
+    const uint32_t shift = W - nb - width;
     const uint32_t pshift = W - nb;            // bits below the resolved prefix
     const uint64_t ptop = nb ? (prefix >> pshift) : 0;
+    const uint32_t dmask = (1u << width) - 1u;
     for (uint32_t i = tid; i < 256; i += nt) s_hist[i] = 0;
     __syncthreads();
-    const uint32_t total = in_lds ? m : n;
-    for (uint32_t i0 = 0; i0 < total; i0 += nt) {
-      const uint32_t i = i0 + tid;
-      bool act = i < total;
-      uint64_t c = 0;
-      if (act) {
-        c = in_lds ? s_cand[i] : src(i);
-        act = (nb == 0) || ((c >> pshift) == ptop);
+    auto count = [&](uint64_t c, bool ok) {
+      const bool act = ok && ((nb == 0) || ((c >> pshift) == ptop));
+      hist_add(s_hist, (uint32_t)(c >> shift) & dmask, act);
+    };
+    if (in_lds) {
+      for (uint32_t i0 = 0; i0 < m; i0 += nt) {
+        const uint32_t i = i0 + tid;
+        count(i < m ? s_cand[i] : 0ull, i < m);
       }
-      hist_add(s_hist, (uint32_t)(c >> shift) & 255u, act);
+    } else {
+      for_batched<LOADS_IN_FLIGHT, uint64_t>(n, [&](uint32_t i) { return src(i); }, count);
     }
     __syncthreads();
     if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
@@ -87,7 +123,7 @@ __device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32
     above += acc;
     need -= acc;
     prefix |= (uint64_t)b << shift;
-    nb += 8;
+    nb += width;
     const uint32_t count_ge = above + hb;
     if (count_ge <= stop || nb >= W) {
       __syncthreads();
@@ -99,16 +135,11 @@ __device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32
       const uint64_t ntop = prefix >> npshift;
       if (tid == 0) s_misc[3] = 0;
       __syncthreads();
-      for (uint32_t i0 = 0; i0 < n; i0 += nt) {
-        const uint32_t i = i0 + tid;
-        bool keep = false;
-        uint64_t c = 0;
-        if (i < n) {
-          c = src(i);
-          keep = (c >> npshift) == ntop;
-        }
-        lds_append(s_cand, &s_misc[3], cand_cap, c, keep);
-      }
+      for_batched<LOADS_IN_FLIGHT, uint64_t>(
+          n, [&](uint32_t i) { return src(i); },
+          [&](uint64_t c, bool ok) {
+            lds_append(s_cand, &s_misc[3], cand_cap, c, ok && (c >> npshift) == ntop);
+          });
       __syncthreads();
       m = s_misc[3] < cand_cap ? s_misc[3] : cand_cap;
       in_lds = true;
@@ -117,24 +148,69 @@ __device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32
   }
 }
 
+template <class Src>
+__device__ SelectOut block_select(const Src& src, uint32_t n, uint32_t W, uint32_t rank,
+                                  uint32_t stop, uint32_t* s_hist, uint32_t* s_misc,
+                                  uint64_t* s_cand, uint32_t cand_cap) {
+  SelectStart st;
+  st.need = rank;
+  return block_select_from(src, n, W, st, stop, s_hist, s_misc, s_cand, cand_cap);
+}
+
+// Over an LDS histogram of `nbins` bins (a power of two, at most 4096) taken
+// from the top, find the bin b holding rank `need` (1-based): out[0] = b,
+// out[1] = elements in bins above b, out[2] = hist[b].  Needs need <= total.
+// Every thread of the workgroup calls it; s_tmp holds 16 words.
+__device__ __forceinline__ void block_find_bucket(const uint32_t* hist, uint32_t nbins,
+                                                  uint32_t need, uint32_t* out, uint32_t* s_tmp) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t per = nbins > nt ? nbins / nt : 1u;   // bins per thread
+  const uint32_t used = nbins / per;                   // threads holding bins
+  const uint32_t lane = tid & 63u, w = tid >> 6;
+  uint32_t s = 0;
+  if (tid < used) {
+    for (uint32_t j = 0; j < per; ++j) s += hist[nbins - 1 - (tid * per + j)];
+  }
+  uint32_t incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t v = __shfl_up(incl, d, 64);
+    if (lane >= (uint32_t)d) incl += v;
+  }
+  if (lane == 63) s_tmp[w] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (uint32_t j = 0; j < w; ++j) base += s_tmp[j];
+  incl += base;
+  const uint32_t excl = incl - s;
+  if (tid < used && excl < need && need <= incl) {
+    uint32_t acc = excl;
+    for (uint32_t j = 0; j < per; ++j) {
+      const uint32_t b = nbins - 1 - (tid * per + j);
+      const uint32_t h = hist[b];
+      if (acc + h >= need) {
+        out[0] = b;
+        out[1] = acc;
+        out[2] = h;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
 // Gather every composite >= thr from `src` into s_out (LDS) in any order;
 // returns how many.  Every thread must call it.
 template <class Src>
 __device__ uint32_t block_collect(const Src& src, uint32_t n, uint64_t thr, uint64_t* s_out,
                                   uint32_t out_cap, uint32_t* s_counter) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t tid = threadIdx.x;
   if (tid == 0) *s_counter = 0;
   __syncthreads();
-  for (uint32_t i0 = 0; i0 < n; i0 += nt) {
-    const uint32_t i = i0 + tid;
-    uint64_t c = 0;
-    bool keep = false;
-    if (i < n) {
-      c = src(i);
-      keep = c >= thr;
-    }
-    lds_append(s_out, s_counter, out_cap, c, keep);
-  }
+  for_batched<LOADS_IN_FLIGHT, uint64_t>(
+      n, [&](uint32_t i) { return src(i); },
+      [&](uint64_t c, bool ok) { lds_append(s_out, s_counter, out_cap, c, ok && c >= thr); });
   __syncthreads();
   const uint32_t cnt = *s_counter;
   __syncthreads();
