@@ -114,13 +114,30 @@ int check_shape(int64_t n, int64_t rows, int64_t k, int dtype) {
   return TOPK_OK;
 }
 
+// Compute units of the current device (cached per device; 256 when no
+// device is present, e.g. for a plan query on a host without a GPU).
+int64_t device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* params,
-            tk::Plan* plan) {
+            tk::Plan* plan, bool with_device) {
   int rc = check_shape(n, rows, k, dtype);
   if (rc) return rc;
   rc = check_params(params);
   if (rc) return rc;
   tk::ParamIn in = to_in(params);
+  in.cus = with_device ? device_cus() : 256;
   if (in.force_path == 1 && n < 2) return TOPK_EINVAL;
   tk::make_plan(n, rows, k, dtype, in, plan);
   if (plan->path == tk::PLAN_SAMPLED && (plan->S < 1 || plan->S > n || plan->t < 1 || plan->t > plan->S))
@@ -149,7 +166,7 @@ int topk_plan(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* 
   if (!out) return TOPK_EINVAL;
   try {
     tk::Plan p;
-    int rc = plan_of(n, rows, k, dtype, params, &p);
+    int rc = plan_of(n, rows, k, dtype, params, &p, false);
     if (rc) return rc;
     out->path = p.path;
     out->small_k = p.small_k ? 1 : 0;
@@ -194,7 +211,7 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
   if (!values || !out_values || !out_indices || !workspace) return TOPK_EINVAL;
   try {
     tk::Plan p;
-    int rc = plan_of(n, rows, k, dtype, params, &p);
+    int rc = plan_of(n, rows, k, dtype, params, &p, true);
     if (rc) return rc;
     const uintptr_t es = (dtype == TOPK_BF16) ? 2 : 4;
     if (reinterpret_cast<uintptr_t>(values) % es || reinterpret_cast<uintptr_t>(out_values) % es ||

@@ -284,17 +284,15 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
     p.cap = c > n ? n : c;
   }
   const int es = (dtype == 2) ? 2 : 4;
-  const int64_t target = (8192 + rows - 1) / rows;
-  const int64_t nvec = (n * es) / 16;
-  int64_t fb = (nvec + (int64_t)filter_threads() * filter_unroll() - 1) /
-               ((int64_t)filter_threads() * filter_unroll());
-  if (fb > target) fb = target;
+  // filter grid: two workgroups per compute unit over the whole call, each a
+  // contiguous slice of one row no shorter than 64 KB
+  const int64_t cus = in.cus > 0 ? in.cus : 256;
+  int64_t fb = (2 * cus + rows / 2) / rows;
+  const int64_t max_slices = (n * es) / 65536;
+  if (fb > max_slices) fb = max_slices;
   if (fb < 1) fb = 1;
   p.filter_bpr = (uint32_t)fb;
-  int64_t hb = (n + 1023) / 1024;
-  if (hb > target) hb = target;
-  if (hb < 1) hb = 1;
-  p.hist_bpr = (uint32_t)hb;
+  p.hist_bpr = 1;
 
   size_t off = 0;
   p.off_states = off;

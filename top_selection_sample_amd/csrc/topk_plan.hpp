@@ -23,6 +23,7 @@ struct ParamIn {
   int policy = 0;      // 0 exact tail, 1 Algorithm 1
   int force_path = 0;  // 0 auto, 1 filter, 2 exact
   int64_t S = 0, t = 0, M = 0;
+  int64_t cus = 256;   // compute units of the device the call runs on
 };
 
 double normal_quantile(double p);
