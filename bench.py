@@ -250,12 +250,16 @@ def pmc_run(args):
 
 
 def _rows_of(path_glob, counter):
+    """(dispatch id, kernel name, value) of every row of a rocprofv3 counter
+    CSV for one counter, in dispatch order."""
     out = []
     for f in glob.glob(path_glob, recursive=True):
         with open(f) as fh:
             for row in csv.DictReader(fh):
                 if row.get("Counter_Name") == counter:
-                    out.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+                    did = int(row.get("Dispatch_Id") or row.get("Correlation_Id") or 0)
+                    out.append((did, row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+    out.sort()
     return out
 
 
@@ -264,34 +268,48 @@ def pmc_summary(args):
     fe = _rows_of(os.path.join(fetch_dir, "**", "*counter_collection.csv"), "FETCH_SIZE")
     wr = _rows_of(os.path.join(write_dir, "**", "*counter_collection.csv"), "WRITE_SIZE")
 
-    def pick(rows, key):
-        return [v for name, v in rows if key in name]
-    copy_f = [v for name, v in fe if "copy" in name.lower() or "elementwise" in name.lower()]
-    copy_w = [v for name, v in wr if "copy" in name.lower() or "elementwise" in name.lower()]
-    filt_f = pick(fe, "k_filter")
-    filt_w = pick(wr, "k_filter")
+    def first_copy(rows):
+        for _, name, v in rows:
+            if "copy" in name.lower():
+                return v, name
+        return None, None
+
+    def filt(rows):
+        vals = sorted(v for _, name, v in rows if "k_filter" in name)
+        return vals[len(vals) // 2] if vals else None
+
     kib = 1024.0
-    # FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; the copy kernel moved
-    # COPY_BYTES each way, which calibrates both counters.
-    scale_f = COPY_BYTES / (max(copy_f) * kib) if copy_f else None
-    scale_w = COPY_BYTES / (max(copy_w) * kib) if copy_w else None
-    # the sampled pass is the first k_filter launch of each call; the exact
-    # pass is a no-op launch, so keep the largest per call
-    ff = sorted(filt_f)[-1] * kib if filt_f else None
-    fw = sorted(filt_w)[-1] * kib if filt_w else None
+    # The calibration copy is the program's first copy kernel: it reads and
+    # writes COPY_BYTES, and FETCH_SIZE / WRITE_SIZE are KiB per dispatch.
+    cf, cf_name = first_copy(fe)
+    cw, cw_name = first_copy(wr)
+    scale_f = COPY_BYTES / (cf * kib) if cf else None
+    scale_w = COPY_BYTES / (cw * kib) if cw else None
+    ff, fw = filt(fe), filt(wr)
     lines = [
-        "rocprofv3 counter summary: k_filter on workload c3k64 (2^28 fp32, k=64)",
+        "rocprofv3 counter summary: k_filter on workload c3k64 (1 row x 2^28 fp32, k=64)",
+        "",
+        "Commands (from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = output dirs):",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python3 REPO/bench.py --pmc-run --steps 3",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python3 REPO/bench.py --pmc-run --steps 3",
+        "  python3 REPO/bench.py --pmc-summary OUT_F OUT_W",
+        "",
         f"kernel_source_sha256_16: {kernel_source_hash()}",
-        f"fetch_kib_copy_kernel: {max(copy_f) if copy_f else 'n/a'}",
-        f"write_kib_copy_kernel: {max(copy_w) if copy_w else 'n/a'}",
+        f"calibration_kernel: {cf_name}",
         f"copy_bytes_known: {COPY_BYTES}",
+        f"fetch_kib_copy_kernel: {cf}",
+        f"write_kib_copy_kernel: {cw}",
         f"scale_fetch: {scale_f}",
         f"scale_write: {scale_w}",
-        f"fetch_bytes_raw_per_launch: {ff}",
-        f"write_bytes_raw_per_launch: {fw}",
+        f"k_filter_fetch_kib_median: {ff}",
+        f"k_filter_write_kib_median: {fw}",
     ]
     if ff is not None and fw is not None and scale_f and scale_w:
-        lines.append(f"hbm_bytes_per_launch: {ff * scale_f + fw * scale_w:.0f}")
+        fb, wb = ff * kib * scale_f, fw * kib * scale_w
+        lines.append(f"k_filter_fetch_bytes_scaled: {fb:.0f}")
+        lines.append(f"k_filter_write_bytes_scaled: {wb:.0f}")
+        lines.append(f"hbm_bytes_per_launch: {fb + wb:.0f}")
+        lines.append(f"algorithmic_bytes_per_launch_approx: {2 ** 28 * 4 + 16384 * 8}")
     print("\n".join(lines))
 
 
