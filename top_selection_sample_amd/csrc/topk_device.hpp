@@ -85,6 +85,20 @@ __device__ __forceinline__ uint32_t key_bf16(uint32_t h) {  // h: 16 bits
   return k;
 }
 
+// Inverse of the key for every key except the two that several bit patterns
+// share: +0's key (also -0) and the top key (every NaN).  Returns false for
+// those; the caller then reads the element itself.
+__device__ __forceinline__ bool unkey_f32(uint32_t k, uint32_t* bits) {
+  if (k == 0x80000000u || k == 0xFFFFFFFFu) return false;
+  *bits = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return true;
+}
+__device__ __forceinline__ bool unkey_bf16(uint32_t k, uint32_t* bits) {
+  if (k == 0x8000u || k == 0xFFFFu) return false;
+  *bits = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return true;
+}
+
 template <int DT> struct Dt;
 template <> struct Dt<DT_I32> {
   using raw = uint32_t;
@@ -92,16 +106,22 @@ template <> struct Dt<DT_I32> {
   static constexpr int ES = 4;       // element bytes
   static constexpr int VEC = 4;      // elements per 16-byte load
   __device__ static uint32_t key(uint32_t r) { return key_i32(r); }
+  __device__ static bool unkey(uint32_t k, uint32_t* bits) {
+    *bits = k ^ 0x80000000u;
+    return true;
+  }
 };
 template <> struct Dt<DT_F32> {
   using raw = uint32_t;
   static constexpr int KB = 32, ES = 4, VEC = 4;
   __device__ static uint32_t key(uint32_t r) { return key_f32(r); }
+  __device__ static bool unkey(uint32_t k, uint32_t* bits) { return unkey_f32(k, bits); }
 };
 template <> struct Dt<DT_BF16> {
   using raw = uint16_t;
   static constexpr int KB = 16, ES = 2, VEC = 8;
   __device__ static uint32_t key(uint32_t r) { return key_bf16(r & 0xFFFFu); }
+  __device__ static bool unkey(uint32_t k, uint32_t* bits) { return unkey_bf16(k, bits); }
 };
 
 // Raw bits of element i of a row.

@@ -143,11 +143,30 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     st0.in_lds = true;
     __syncthreads();
   }
-  SelectOut r = block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP);
+  uint32_t tau;
+  if (st0.in_lds && st0.m <= nt) {
+    // a small bucket: the wanted key is the one whose rank inside it (larger
+    // keys, then equal keys earlier in the list) is need - 1
+    if (tid == 0) s_misc[5] = 0;
+    __syncthreads();
+    if (tid < st0.m) {
+      const uint64_t mine = s_cand[tid];
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < st0.m; ++j) {
+        const uint64_t o = s_cand[j];
+        r += (o > mine || (o == mine && j < tid)) ? 1u : 0u;
+      }
+      if (r == st0.need - 1) s_misc[5] = (uint32_t)mine;
+    }
+    __syncthreads();
+    tau = s_misc[5];
+  } else {
+    tau = (uint32_t)block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP).thr;
+  }
   if (tid == 0) {
     RowState* st = states + row;
     st->status = ST_FILTER;
-    st->tau_key = (uint32_t)r.thr;
+    st->tau_key = tau;
     st->count = 0;
     st->r_sampled = 0;
     st->path = PATH_SAMPLED;
@@ -479,19 +498,60 @@ struct RowSrc {
   }
 };
 
+// The output value of a winner: the input element's own bits.  They follow
+// from the key except for +-0 and NaN, which are read from the input.
+template <int DT>
+__device__ __forceinline__ uint32_t winner_bits(uint64_t c, uint32_t B, const char* rowp,
+                                                uint32_t n, uint32_t* idx_out) {
+  const uint64_t maskB = (1ull << B) - 1ull;
+  uint32_t idx = (uint32_t)(maskB - (c & maskB));
+  if (idx >= n) idx = n - 1;   // only a padding entry could decode out of range
+  *idx_out = idx;
+  uint32_t bits;
+  if (Dt<DT>::unkey((uint32_t)(c >> B), &bits)) return bits;
+  return load_raw<DT>(rowp, idx);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_winner(void* out_values, int64_t* out_idx, size_t o,
+                                             uint32_t bits, uint32_t idx) {
+  if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = (uint16_t)bits;
+  else static_cast<uint32_t*>(out_values)[o] = bits;
+  out_idx[o] = idx;
+}
+
+// Output slot of s[i] = #{j : s[j] > s[i]}; slots >= k are dropped.
+template <int DT>
+__device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint32_t B,
+                               const char* rowp, uint32_t n, void* out_values, int64_t* out_idx,
+                               uint32_t row) {
+  for (uint32_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const uint64_t c = s[i];
+    uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    uint32_t j = 0;
+    for (; j + 4 <= cnt; j += 4) {   // four independent LDS reads per step
+      r0 += (s[j] > c) ? 1u : 0u;
+      r1 += (s[j + 1] > c) ? 1u : 0u;
+      r2 += (s[j + 2] > c) ? 1u : 0u;
+      r3 += (s[j + 3] > c) ? 1u : 0u;
+    }
+    for (; j < cnt; ++j) r0 += (s[j] > c) ? 1u : 0u;
+    const uint32_t r = r0 + r1 + r2 + r3;
+    if (r < k) {
+      uint32_t idx;
+      const uint32_t bits = winner_bits<DT>(c, B, rowp, n, &idx);
+      store_winner<DT>(out_values, out_idx, (size_t)row * k + r, bits, idx);
+    }
+  }
+}
+
 template <int DT>
 __device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t B, const char* rowp,
                               uint32_t n, void* out_values, int64_t* out_idx, uint32_t row) {
-  const uint64_t maskB = (1ull << B) - 1ull;
   for (uint32_t i = threadIdx.x; i < k; i += blockDim.x) {
-    const uint64_t c = s_w[i];
-    uint32_t idx = (uint32_t)(maskB - (c & maskB));
-    if (idx >= n) idx = n - 1;   // only a padding entry could decode out of range
-    const uint32_t raw = load_raw<DT>(rowp, idx);
-    const size_t o = (size_t)row * k + i;
-    if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = (uint16_t)raw;
-    else static_cast<uint32_t*>(out_values)[o] = raw;
-    out_idx[o] = idx;
+    uint32_t idx;
+    const uint32_t bits = winner_bits<DT>(s_w[i], B, rowp, n, &idx);
+    store_winner<DT>(out_values, out_idx, (size_t)row * k + i, bits, idx);
   }
 }
 
@@ -512,6 +572,8 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* s_tmp) {
 constexpr uint32_t RF_BITS = 11;
 constexpr uint32_t RF_BINS = 1u << RF_BITS;
 constexpr uint32_t RF_SORT_CAP = 4096;
+constexpr uint32_t RF_KCAP = 24576;     // candidate keys cached in LDS (96 KB)
+constexpr uint32_t RF_RANK_MAX = 256;   // up to this many: rank counting, else bitonic
 
 // Sort s[0..cnt) descending in LDS (cnt <= CAND_CAP), zero-padded to a power
 // of two; composites are never zero, so padding sorts last.
@@ -531,8 +593,9 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
                            uint32_t cap, uint32_t k, uint32_t B, uint32_t W, uint32_t want,
                            void* __restrict__ out_values, int64_t* __restrict__ out_idx,
                            uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
-                           uint64_t* s_cand) {
-  // LDS: s_hist[RF_BINS], s_misc[8], s_tmp[16], s_cand[CAND_CAP]
+                           uint64_t* s_cand, uint32_t* s_keys, uint32_t* s_idx) {
+  // LDS: s_hist[RF_BINS], s_misc[8], s_tmp[16], s_cand[RF_SORT_CAP],
+  //      s_keys[RF_KCAP], s_idx[RF_SORT_CAP]
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   RowState* st = states + row;
   if (st->status != want) return;
@@ -553,53 +616,87 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
   const uint32_t lo_key = (want == ST_FILTER) ? st->tau_key : st->thr_key;
   CompSrc src{cbuf + (size_t)row * cap};
 
-  // pass 1: the largest candidate key
+  // Pass 0 reads every candidate once: its key goes to the LDS key cache
+  // (the first RF_KCAP), and the largest key is kept.
+  const uint32_t Rc = R < RF_KCAP ? R : RF_KCAP;
   uint32_t mx = 0;
-  for_batched<LOADS_IN_FLIGHT, uint64_t>(
+  for_batched_i<LOADS_IN_FLIGHT, uint64_t>(
       R, [&](uint32_t i) { return src.p[i]; },
-      [&](uint64_t c, bool ok) {
+      [&](uint64_t c, bool ok, uint32_t i) {
         const uint32_t key = ok ? (uint32_t)(c >> B) : 0u;
+        if (ok && i < Rc) s_keys[i] = key;
         mx = key > mx ? key : mx;
       });
-  const uint32_t kmax = block_max_u32(mx, s_tmp);
+  const uint32_t kmax = block_max_u32(mx, s_tmp);   // (has the barrier the cache needs)
   // every candidate key lies in [lo_key, kmax]: histogram the 11 key bits
   // just below their common prefix
   const uint32_t diff = (lo_key ^ kmax) & (KB == 32 ? 0xFFFFFFFFu : 0xFFFFu);
   const uint32_t top = diff ? 31u - (uint32_t)__builtin_clz(diff) : 0u;
   const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
+  auto digit = [&](uint32_t key) { return (key >> kshift) & (RF_BINS - 1); };
   for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist[i] = 0;
   __syncthreads();
-  for_batched<LOADS_IN_FLIGHT, uint64_t>(
-      R, [&](uint32_t i) { return src.p[i]; },
-      [&](uint64_t c, bool ok) {
-        hist_add(s_hist, ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1), ok);
-      });
+  {
+    uint32_t i = tid;
+    for (; i + 3 * nt < Rc; i += 4 * nt) {   // four independent LDS reads per step
+      const uint32_t k0 = s_keys[i], k1 = s_keys[i + nt], k2 = s_keys[i + 2 * nt],
+                     k3 = s_keys[i + 3 * nt];
+      atomicAdd(&s_hist[digit(k0)], 1u);
+      atomicAdd(&s_hist[digit(k1)], 1u);
+      atomicAdd(&s_hist[digit(k2)], 1u);
+      atomicAdd(&s_hist[digit(k3)], 1u);
+    }
+    for (; i < Rc; i += nt) atomicAdd(&s_hist[digit(s_keys[i])], 1u);
+  }
+  if (R > Rc)
+    for_batched<LOADS_IN_FLIGHT, uint64_t>(
+        R - Rc, [&](uint32_t i) { return src.p[Rc + i]; },
+        [&](uint64_t c, bool ok) { hist_add(s_hist, digit((uint32_t)(c >> B)), ok); });
   __syncthreads();
   block_find_bucket(s_hist, RF_BINS, k, s_misc, s_tmp);
   const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
   __syncthreads();
   uint32_t got;
   if (acc + hb <= RF_SORT_CAP) {
-    // pass 2: everything at or above the boundary bucket, then sort in LDS
+    // pass 2: list the indices at or above the boundary bucket, then gather
+    // those composites and sort them in LDS
     if (tid == 0) s_misc[4] = 0;
     __syncthreads();
-    for_batched<LOADS_IN_FLIGHT, uint64_t>(
-        R, [&](uint32_t i) { return src.p[i]; },
-        [&](uint64_t c, bool ok) {
-          const bool keep = ok && (((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1)) >= b;
-          lds_append(s_cand, &s_misc[4], CAND_CAP, c, keep);
-        });
+    for (uint32_t i0 = 0; i0 < Rc; i0 += nt) {
+      const uint32_t i = i0 + tid;
+      const bool keep = i < Rc && digit(s_keys[i]) >= b;
+      lds_append_u32(s_idx, &s_misc[4], RF_SORT_CAP, i, keep);
+    }
+    if (R > Rc)
+      for_batched_i<LOADS_IN_FLIGHT, uint64_t>(
+          R - Rc, [&](uint32_t i) { return src.p[Rc + i]; },
+          [&](uint64_t c, bool ok, uint32_t i) {
+            lds_append_u32(s_idx, &s_misc[4], RF_SORT_CAP, Rc + i,
+                           ok && digit((uint32_t)(c >> B)) >= b);
+          });
     __syncthreads();
     got = s_misc[4] < RF_SORT_CAP ? s_misc[4] : RF_SORT_CAP;
+    for_batched_i<4, uint64_t>(
+        got, [&](uint32_t j) { return src.p[s_idx[j]]; },
+        [&](uint64_t c, bool ok, uint32_t j) {
+          if (ok) s_cand[j] = c;
+        });
     __syncthreads();
   } else {
     // heavy ties or a wide boundary bucket: radix select on the composite
-    SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
-    got = block_collect(src, R, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
+    SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
+    got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
   }
-  lds_sort_desc(s_cand, got);
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-  write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+  if (got <= RF_RANK_MAX) {
+    // few elements: each one's output slot is the number of larger
+    // composites (the rank of GPU.js Learn "Rank by Counting"; composites are
+    // unique, so the slots are a permutation)
+    rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
+  } else {
+    lds_sort_desc(s_cand, got);
+    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+  }
   __syncthreads();
   if (tid == 0) {
     if (want == ST_FILTER) st->r_sampled = R;
@@ -618,9 +715,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_refine(
   __shared__ uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
-  __shared__ uint64_t s_cand[CAND_CAP];
+  __shared__ uint64_t s_cand[RF_SORT_CAP];
+  __shared__ uint32_t s_keys[RF_KCAP];
+  __shared__ uint32_t s_idx[RF_SORT_CAP];
   refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
-                 out_idx, blockIdx.x, s_hist, s_misc, s_tmp, s_cand);
+                 out_idx, blockIdx.x, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
 }
 
 // Whole exact selection of a small row in one workgroup.  Small k: writes the
@@ -820,7 +919,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
   __shared__ uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
-  __shared__ uint64_t s_cand[CAND_CAP];
+  __shared__ uint64_t s_cand[RF_SORT_CAP];
+  __shared__ uint32_t s_keys[RF_KCAP];
+  __shared__ uint32_t s_idx[RF_SORT_CAP];
   const uint32_t nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (nf == 0) return;                        // the common case: nothing to do
   const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
@@ -920,7 +1021,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
     const uint32_t row = flagged[f];
     if (small_k) {
       refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_EXACT_READY,
-                     out_values, out_idx, row, s_hist, s_misc, s_tmp, s_cand);
+                     out_values, out_idx, row, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
     } else if (tid == 0) {
       states[row].status = ST_SORT;
     }
@@ -1001,16 +1102,11 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
   const uint32_t row = blockIdx.y;
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;
   if (i >= k) return;
-  const uint64_t maskB = (1ull << B) - 1ull;
   const uint64_t c = sorted[(size_t)row * cap + i];
-  uint32_t idx = (uint32_t)(maskB - (c & maskB));
-  if (idx >= n) idx = n - 1;   // only a padding entry could decode out of range
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-  const uint32_t raw = load_raw<DT>(rowp, idx);
-  const size_t o = (size_t)row * k + i;
-  if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = (uint16_t)raw;
-  else static_cast<uint32_t*>(out_values)[o] = raw;
-  out_idx[o] = idx;
+  uint32_t idx;
+  const uint32_t bits = winner_bits<DT>(c, B, rowp, n, &idx);
+  store_winner<DT>(out_values, out_idx, (size_t)row * k + i, bits, idx);
   if (i == 0) states[row].status = ST_DONE;
 }
 

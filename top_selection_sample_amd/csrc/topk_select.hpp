@@ -63,7 +63,38 @@ __device__ __forceinline__ void for_batched(uint32_t total, Load&& load, Proc&& 
   }
 }
 
+// Same, with the element index passed to proc(value, valid, i).
+template <int U, class T, class Load, class Proc>
+__device__ __forceinline__ void for_batched_i(uint32_t total, Load&& load, Proc&& proc) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  for (uint32_t i0 = 0; i0 < total; i0 += nt * U) {
+    T v[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + (uint32_t)u * nt + tid;
+      ok[u] = i < total;
+      v[u] = ok[u] ? load(i) : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) proc(v[u], ok[u], i0 + (uint32_t)u * nt + tid);
+  }
+}
+
 constexpr int LOADS_IN_FLIGHT = 8;
+
+// Append a 32-bit value to an LDS list (same rules as lds_append).
+__device__ __forceinline__ void lds_append_u32(uint32_t* arr, uint32_t* counter, uint32_t cap,
+                                               uint32_t v, bool keep) {
+  uint64_t m = ballot(keep);
+  if (!m) return;
+  uint32_t base = 0;
+  const uint32_t first = (uint32_t)__builtin_ctzll(m);
+  if (lane_id() == first) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(m));
+  base = __shfl(base, first, 64);
+  const uint32_t slot = base + rank_below(m);
+  if (keep && slot < cap) arr[slot] = v;
+}
 
 struct SelectOut {
   uint64_t thr;       // threshold composite: resolved top bits, zeros below
