@@ -18,6 +18,8 @@ namespace tk {
 
 enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Per-row phase of the pipeline.
 enum : uint32_t {
   ST_IDLE = 0,
@@ -45,7 +47,8 @@ struct alignas(64) RowState {
   uint32_t thr_key;     // exact threshold: key >= thr_key, and on key ==
   uint32_t thr_bound;   //   thr_key only indices <= thr_bound
   uint32_t passes;      // exact select: histogram passes used
-  uint32_t pad[2];
+  uint32_t pad1;
+  uint32_t kmax;        // largest candidate key written by a filter pass
 };
 static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");
 

@@ -69,8 +69,8 @@ constexpr uint32_t SH_BINS = 1u << SH_BITS;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_sample(const void* __restrict__ values, uint32_t n,
-                                                uint32_t S, uint64_t seed, uint32_t half_bits,
-                                                uint32_t* __restrict__ skeys,
+                                                uint32_t S, uint32_t SP, uint64_t seed,
+                                                uint32_t half_bits, uint32_t* __restrict__ skeys,
                                                 uint32_t* __restrict__ shist) {
   __shared__ uint32_t h[SH_BINS];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void k_sample(const void* __restrict__ values,
     while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
     const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
     const uint32_t key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
-    skeys[(size_t)row * S + j] = key;
+    skeys[(size_t)row * SP + j] = key;
     atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
   }
   __syncthreads();
@@ -104,8 +104,12 @@ struct KeySrc {
 constexpr uint32_t SEL_THREADS = 1024;
 constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
 
+// One workgroup per row.  The boundary bucket comes from the row's histogram;
+// one pass over the sample keys (16-byte loads, 32 keys per thread in
+// flight) copies that bucket into LDS, and the rest of the select stays there.
+// Sample-key rows are padded to a multiple of 4 keys (SP = padded length).
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
-                                                     uint32_t t, uint32_t KB,
+                                                     uint32_t SP, uint32_t t, uint32_t KB,
                                                      uint32_t* __restrict__ shist,
                                                      RowState* __restrict__ states) {
   __shared__ uint32_t s_hist[SH_BINS];
@@ -122,7 +126,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   block_find_bucket(s_hist, SH_BINS, t, s_misc, s_tmp);
   const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
   const uint32_t sh = KB - SH_BITS;
-  KeySrc src{skeys + (size_t)row * S};
+  const uint32_t* keys = skeys + (size_t)row * SP;
+  KeySrc src{keys};
   SelectStart st0;
   st0.prefix = (uint64_t)b << sh;
   st0.nb = SH_BITS;
@@ -130,13 +135,23 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   st0.above = acc;
   __syncthreads();
   if (hb <= CAND_CAP) {
-    // the boundary bucket's keys into LDS; the rest of the select stays there
+    // the boundary bucket's keys into LDS
     if (tid == 0) s_misc[3] = 0;
     __syncthreads();
-    for_batched<16, uint32_t>(
-        S, [&](uint32_t i) { return src.p[i]; },
-        [&](uint32_t key, bool ok) {
-          lds_append(s_cand, &s_misc[3], CAND_CAP, key, ok && (key >> sh) == b);
+    const u32x4* kv = reinterpret_cast<const u32x4*>(keys);
+    for_batched_i<8, u32x4>(
+        SP / 4, [&](uint32_t i) { return kv[i]; },
+        [&](const u32x4& v, bool ok, uint32_t i) {
+          bool in[4];
+          bool any = false;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            in[q] = ok && (i * 4 + q) < S && (v[q] >> sh) == b;
+            any = any || in[q];
+          }
+          if (ballot(any) == 0) return;   // the usual case: no key of the bucket
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lds_append(s_cand, &s_misc[3], CAND_CAP, v[q], in[q]);
         });
     __syncthreads();
     st0.m = s_misc[3] < CAND_CAP ? s_misc[3] : CAND_CAP;
@@ -171,6 +186,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     st->r_sampled = 0;
     st->path = PATH_SAMPLED;
     st->passes = 0;
+    st->kmax = 0;
   }
 }
 
@@ -269,8 +285,6 @@ __device__ __forceinline__ bool native_pass(uint32_t raw, const Thr& t) {
   else if constexpr (DT == DT_F32) return !(__uint_as_float(raw) < t.f);
   else return !(__uint_as_float(raw << 16) < t.f);
 }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
@@ -1162,12 +1176,12 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (p.path == PLAN_SAMPLED) {
       const dim3 sg((uint32_t)((p.S + 255) / 256), rows);
       mark(STAGE_SAMPLE, 1);
-      TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, a.seed,
-                  p.half_bits, a.skeys, a.shist);
+      TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, (uint32_t)p.SP,
+                  a.seed, p.half_bits, a.skeys, a.shist);
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
       hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
-                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states);
+                         (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states);
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);

@@ -20,7 +20,7 @@ struct Plan {
   int dtype = 0;
   int path = PLAN_SAMPLED;
   bool small_k = true;
-  int64_t S = 0, t = 0, M = 0, cap = 0;
+  int64_t S = 0, SP = 0, t = 0, M = 0, cap = 0;
   uint32_t B = 8, W = 40, KB = 32, half_bits = 1;
   uint32_t filter_bpr = 1, hist_bpr = 1;
   double p_recall = 0, p_overflow = 0;

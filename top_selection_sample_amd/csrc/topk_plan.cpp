@@ -304,9 +304,11 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   p.off_ghist = off;
   if (p.path != PLAN_EXACT_SMALL) off = align256(off + (size_t)rows * 256 * 4);
   p.off_skeys = off;
-  if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.S * 4);
+  p.SP = (p.S + 3) / 4 * 4;   // sample-key rows padded for 16-byte loads
+  if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.SP * 4);
   p.off_shist = off;
   if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 2048 * 4);
+
   p.off_cbuf = off;
   off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.off_aux = off;
