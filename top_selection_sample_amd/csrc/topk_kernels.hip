@@ -708,7 +708,20 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
     // unique, so the slots are a permutation)
     rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
   } else {
-    lds_sort_desc(s_cand, got);
+    // the key cache is free again: scratch for the sort
+    uint64_t* tmp = reinterpret_cast<uint64_t*>(s_keys);
+    if (!block_sort_unique_desc(s_cand, got, tmp, s_hist, s_misc, tmp + RF_SORT_CAP, 64u)) {
+      uint64_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t i = 4 * tid + (uint32_t)j;
+        v[j] = i < got ? s_cand[i] : 0ull;
+      }
+      block_bitonic4096_desc(v, tmp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_cand[4 * tid + j] = v[j];
+      __syncthreads();
+    }
     write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
   }
   __syncthreads();
@@ -1060,17 +1073,25 @@ constexpr uint32_t SORT_TILE = 4096;
 __global__ __launch_bounds__(SEL_THREADS) void k_tile_sort(RowState* __restrict__ states,
                                                            uint64_t* __restrict__ cbuf,
                                                            uint32_t cap) {
-  __shared__ uint64_t s[SORT_TILE];
-  const uint32_t row = blockIdx.y;
+  __shared__ uint64_t x[SORT_TILE];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x;
   const uint32_t R = min(states[row].count, cap);
   const uint32_t start = blockIdx.x * SORT_TILE;
   if (start >= R) return;
   const uint32_t len = min(SORT_TILE, R - start);
   uint64_t* p = cbuf + (size_t)row * cap + start;
-  for (uint32_t i = threadIdx.x; i < SORT_TILE; i += blockDim.x) s[i] = (i < len) ? p[i] : 0ull;
-  __syncthreads();
-  block_bitonic_desc(s, SORT_TILE);
-  for (uint32_t i = threadIdx.x; i < len; i += blockDim.x) p[i] = s[i];
+  uint64_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t i = 4 * tid + (uint32_t)j;
+    v[j] = i < len ? p[i] : 0ull;   // composites are never 0: padding sorts last
+  }
+  block_bitonic4096_desc(v, x);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t i = 4 * tid + (uint32_t)j;
+    if (i < len) p[i] = v[j];
+  }
 }
 
 __global__ __launch_bounds__(256) void k_merge(RowState* __restrict__ states,

@@ -268,6 +268,165 @@ __device__ __forceinline__ void block_bitonic_desc(uint64_t* s, uint32_t P) {
   }
 }
 
+// ---------------------------------------------------------------- LDS sort
+// Sort cnt unique 64-bit values s[0..cnt) into descending order, in LDS.
+// One counting-sort pass on the 11 bits just below the common prefix of the
+// smallest and largest value (digits taken from the top, so bucket order is
+// value order), then each element's place inside its bucket is the number of
+// larger values in that bucket.  O(cnt) LDS passes plus the sum of squared
+// bucket sizes, which is small unless the values crowd into one bucket.
+// tmp: cnt values of scratch; hist: 2048 words; misc: 8 words; red: 32
+// words.  Every thread of the workgroup calls it.  Returns false, with s
+// untouched, when the fullest bucket holds more than max_bucket values (many
+// ties in the top bits); the caller then sorts another way.
+__device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt, uint64_t* tmp,
+                                                       uint32_t* hist, uint32_t* misc,
+                                                       uint64_t* red, uint32_t max_bucket) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
+  if (cnt <= 1) {
+    __syncthreads();
+    return true;
+  }
+  // smallest and largest
+  uint64_t mn = ~0ull, mx = 0ull;
+  for (uint32_t i = tid; i < cnt; i += nt) {
+    const uint64_t v = s[i];
+    mn = v < mn ? v : mn;
+    mx = v > mx ? v : mx;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint64_t a = __shfl_xor(mn, d, 64), b = __shfl_xor(mx, d, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    red[w] = mn;
+    red[16 + w] = mx;
+  }
+  for (uint32_t i = tid; i < 2048; i += nt) hist[i] = 0;
+  __syncthreads();
+  mn = red[0];
+  mx = red[16];
+  for (uint32_t j = 1; j < (nt >> 6); ++j) {
+    mn = red[j] < mn ? red[j] : mn;
+    mx = red[16 + j] > mx ? red[16 + j] : mx;
+  }
+  const uint64_t diff = mn ^ mx;
+  const uint32_t top = 63u - (uint32_t)__builtin_clzll(diff);   // diff != 0: values unique
+  const uint32_t shift = top >= 10 ? top - 10 : 0u;
+  auto digit = [&](uint64_t v) { return (uint32_t)(v >> shift) & 2047u; };
+  for (uint32_t i = tid; i < cnt; i += nt) atomicAdd(&hist[digit(s[i])], 1u);
+  if (tid == 0) misc[0] = 0;
+  __syncthreads();
+  {
+    uint32_t big = 0;
+    for (uint32_t i = tid; i < 2048; i += nt) big = hist[i] > big ? hist[i] : big;
+    if (big > max_bucket) atomicMax(&misc[0], big);
+  }
+  __syncthreads();
+  if (misc[0] > max_bucket) {
+    __syncthreads();
+    return false;
+  }
+  // exclusive scan from bucket 2047 down: start of each bucket in the output
+  // (one wave; each lane owns 32 buckets)
+  if (w == 0) {
+    uint32_t loc = 0;
+    for (uint32_t j = 0; j < 32; ++j) loc += hist[2047 - (lane * 32 + j)];
+    uint32_t incl = loc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t v = __shfl_up(incl, d, 64);
+      if (lane >= (uint32_t)d) incl += v;
+    }
+    uint32_t run = incl - loc;
+    for (uint32_t j = 0; j < 32; ++j) {
+      const uint32_t b = 2047 - (lane * 32 + j);
+      const uint32_t h = hist[b];
+      hist[b] = run;   // now the bucket's start (used as a cursor below)
+      run += h;
+    }
+  }
+  __syncthreads();
+  // scatter into buckets (order inside a bucket arbitrary for now)
+  for (uint32_t i = tid; i < cnt; i += nt) {
+    const uint64_t v = s[i];
+    const uint32_t p = atomicAdd(&hist[digit(v)], 1u);
+    tmp[p] = v;
+  }
+  __syncthreads();
+  // hist[b] is now the end of bucket b; its start is the end of the bucket
+  // above it (b + 1), or 0 for the top bucket
+  for (uint32_t p = tid; p < cnt; p += nt) {
+    const uint64_t v = tmp[p];
+    const uint32_t b = digit(v);
+    const uint32_t end = hist[b];
+    const uint32_t beg = (b == 2047) ? 0u : hist[b + 1];
+    uint32_t r = 0;
+    for (uint32_t q = beg; q < end; ++q) r += (tmp[q] > v) ? 1u : 0u;
+    s[beg + r] = v;
+  }
+  __syncthreads();
+  return true;
+}
+
+// Bitonic sort of 4096 values into descending order by 1024 threads, four
+// consecutive positions per thread (position p = 4 * tid + j).  Pairs that
+// are in one thread swap in registers, pairs within a wave exchange through
+// cross-lane shuffles, and only strides of 256 and more go through LDS
+// (x: 4096 words of scratch).  Every thread of the workgroup calls it.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, uint32_t m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void block_bitonic4096_desc(uint64_t (&v)[4], uint64_t* x) {
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t size = 2; size <= 4096; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 256) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[4 * tid + j] = v[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t p = 4 * tid + (uint32_t)j;
+          const uint64_t o = x[p ^ stride];
+          const bool desc = (p & size) == 0, low = (p & stride) == 0;
+          const uint64_t hi = v[j] > o ? v[j] : o, lo = v[j] > o ? o : v[j];
+          v[j] = (low == desc) ? hi : lo;
+        }
+        __syncthreads();
+      } else if (stride >= 4) {
+        const uint32_t m = stride >> 2;   // partner lane distance
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t p = 4 * tid + (uint32_t)j;
+          const uint64_t o = shfl_xor_u64(v[j], m);
+          const bool desc = (p & size) == 0, low = (p & stride) == 0;
+          const uint64_t hi = v[j] > o ? v[j] : o, lo = v[j] > o ? o : v[j];
+          v[j] = (low == desc) ? hi : lo;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = j ^ (int)stride;
+          if (q > j) {
+            const uint32_t p = 4 * tid + (uint32_t)j;
+            const bool desc = (p & size) == 0;
+            const uint64_t a = v[j], b = v[q];
+            const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+            v[j] = desc ? hi : lo;
+            v[q] = desc ? lo : hi;
+          }
+        }
+      }
+    }
+  }
+}
+
 __host__ __device__ __forceinline__ uint32_t next_pow2(uint32_t v) {
   uint32_t p = 1;
   while (p < v) p <<= 1;
