@@ -14,6 +14,9 @@ Extra modes (measurement plumbing, not part of the timed line):
     --pmc-summary A B         read the rocprofv3 counter CSVs of the FETCH_SIZE
                               run (A) and the WRITE_SIZE run (B) and print the
                               traffic summary that belongs in profiles/
+    --calibrate W1,W2,...     measure the whole call over the tuned policy's
+                              grid of sample sizes on each workload and fit
+                              the cost ratio tau_B / tau_A of Eq. 13
 """
 from __future__ import annotations
 
@@ -32,7 +35,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "top-k Gelem/s and HBM GB/s (% of peak), N=2^28 fp32 k=64, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc", "topk_kernels.hip")
+CSRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "topk_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_k_filter_c3_k64.txt")
 COPY_BYTES = 1 << 30
 
@@ -51,8 +55,24 @@ WORKLOADS = {
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of everything the filter kernel is compiled from: the device
+    header, the filter's section of the kernel source, and the compile
+    flags.  Counter data taken on another version of these is stale."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    a = src.index("// Filter (Prof-K section 3")
+    b = src.index("__device__ __forceinline__ void start_exact")
+    h = hashlib.sha256()
+    with open(os.path.join(CSRC, "topk_device.hpp"), "rb") as f:
+        h.update(f.read())
+    h.update(src[a:b].encode())
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_tss_build", os.path.join(ROOT, "top_selection_sample_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    h.update(" ".join(mod.FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def load_inputs(name: str):
@@ -177,12 +197,26 @@ def run_bench(args):
     tss.profile_enable(False)
     ms_step_profiled = ev0.elapsed_time(ev1) / args.steps
 
-    # fallback rate and mean survivors, both parameter policies
-    fb_calls = args.fallback_calls
-    fb = {"exact_tail": fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_EXACT_TAIL)}
+    # fallback rate and mean survivors per parameter policy (fresh seeds)
+    fb_calls = args.fallback_calls or (1000 if rows == 1 else 100)
+    fb = {"tuned": fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_TUNED)}
     if plan["path"] == 0:
-        fb["alg1"] = fallback_rate(tss, bufs, k, rows, max(fb_calls // 2, 1), tss.POLICY_ALG1)
-    R_mean = fb["exact_tail"]["mean_R"] * rows
+        fb["exact_tail"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_EXACT_TAIL)
+        fb["alg1"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_ALG1)
+    R_mean = fb["tuned"]["mean_R"] * rows
+
+    # cost of one fallback: the exact route over the whole input
+    exact_ms = None
+    if plan["path"] == 0:
+        pe = tss.default_params(force_path=tss.PATH_EXACT)
+        tss.topk(bufs[0], k, params=pe, out=(ov, oi))
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(5):
+            tss.topk(bufs[i % 3], k, params=pe, out=(ov, oi))
+        ev1.record()
+        torch.cuda.synchronize()
+        exact_ms = ev0.elapsed_time(ev1) / 5
 
     elems = rows * n
     gelem_s = elems / (ms_step * 1e-3) / 1e9
@@ -218,13 +252,14 @@ def run_bench(args):
         "dtype": "bf16" if dt == "bf16" else ("i32" if dt == "int32" else "f32"),
         "data": "synthetic",
         "config": {"workload": desc, "rows": rows, "n": n, "k": k, "input_dtype": dt,
-                   "seed": meta["seed"], "policy": "exact_tail", "S": plan["S"],
+                   "seed": meta["seed"], "policy": "tuned", "S": plan["S"],
                    "t": plan["t"], "M": plan["M"], "route": ["sampled", "exact", "exact_small"][plan["path"]]},
         "hbm_gbs": round(e2e_gbs, 1), "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(alg_bytes),
         "roofline": roof,
         "cpu_baseline": cpu,
         "fallback": fb,
+        "exact_route_ms_per_call": round(exact_ms, 4) if exact_ms is not None else None,
         "stage_ms": stage_ms,
         "ms_per_step_with_stage_events": round(ms_step_profiled, 4),
     }
@@ -313,13 +348,90 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+def calibrate(args):
+    """Cost-ratio calibration for the tuned policy (Prof-K section 4,
+    "Optimal Sample Size": tau_B / tau_A estimated by microbenchmark).
+
+    For each workload, the mean whole-call time is measured at every sample
+    size of the policy's grid (t and M from the exact tail at that S).  Then,
+    for each candidate ratio, the policy's choice of S is looked up in the
+    measurements; the ratio whose choices lose the least time against the
+    best measured S (summed relative excess over the workloads) is
+    reported."""
+    import math
+    import torch
+    import top_selection_sample_amd as tss
+    d0 = tss.default_params()
+    names = args.calibrate.split(",")
+    meas = {}
+    for name in names:
+        x, dt, k, desc, meta = load_inputs(name)
+        rows, n = x.shape
+        x0 = to_device(x, dt)
+        del x
+        bufs = [x0] + [torch.roll(x0, shifts=s, dims=1).contiguous()
+                       for s in (n // 3 + 1, (2 * n) // 3 + 7)]
+        ov = torch.empty((rows, k), dtype=x0.dtype, device="cuda")
+        oi = torch.empty((rows, k), dtype=torch.int64, device="cuda")
+        grid, j = [], 0
+        s_hi = min(d0.s_max, n // 8)
+        while True:
+            S = int(round(d0.tuned_s_min * 2.0 ** (0.25 * j)))
+            if S > s_hi:
+                break
+            if not grid or S != grid[-1]:
+                grid.append(S)
+            j += 1
+        times = {}
+        for S in grid:
+            p = tss.default_params(S=S)
+            for i in range(3):
+                tss.topk(bufs[i % 3], k, params=p, out=(ov, oi))
+            torch.cuda.synchronize()
+            # mean over many calls with fresh seeds: the occasional fallback
+            # is part of the cost being minimised
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(150):
+                tss.topk(bufs[i % 3], k, params=p, out=(ov, oi))
+            e1.record()
+            torch.cuda.synchronize()
+            times[S] = e0.elapsed_time(e1) / 150
+            pl = tss.plan(n, rows, k, dt, params=p)
+            print(f"{name} S={S} t={pl['t']} M={pl['M']} us={times[S] * 1e3:.1f}", flush=True)
+        meas[name] = (n, rows, k, dt, times)
+        del bufs, x0, ov, oi
+        torch.cuda.empty_cache()
+    ratios = [10 ** (e / 8.0) for e in range(-24, 9)]
+    table = []
+    for rho in ratios:
+        loss = 0.0
+        picks = {}
+        for name, (n, rows, k, dt, times) in meas.items():
+            S = tss.plan(n, rows, k, dt, params=tss.default_params(tuned_ratio=rho))["S"]
+            picks[name] = S
+            loss += times[S] / min(times.values()) - 1.0
+        table.append((loss, rho, picks))
+        print(f"ratio {rho:.4g}: excess {loss * 100:.2f}% picks {picks}", flush=True)
+    best = min(l for l, _, _ in table)
+    good = [rho for l, rho, _ in table if l <= best + 1e-12]
+    print(f"best excess {best * 100:.2f}% for ratios {min(good):.4g} .. {max(good):.4g}; "
+          f"geometric middle {math.sqrt(min(good) * max(good)):.4g}")
+    for name, (n, rows, k, dt, times) in meas.items():
+        sb = min(times, key=times.get)
+        print(f"{name}: best measured S={sb} ({times[sb] * 1e3:.1f} us)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3k64", choices=sorted(WORKLOADS))
-    ap.add_argument("--fallback-calls", type=int, default=200)
+    ap.add_argument("--fallback-calls", type=int, default=0,
+                    help="calls per policy for the fallback rate (default 1000, or 100 for batched rows)")
+    ap.add_argument("--calibrate", metavar="WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -335,6 +447,9 @@ def main():
         sys.exit(2)
     if args.pmc_run:
         pmc_run(args)
+        return
+    if args.calibrate:
+        calibrate(args)
         return
     run_bench(args)
 

@@ -64,16 +64,26 @@ typedef enum {
 } topk_status;
 
 /* Parameter policy for (S, t, M).
- *  TOPK_POLICY_EXACT_TAIL (default): S from Algorithm 1; t and M the least
- *    values meeting the two conditions of Theorem 3 (recall failure R < k and
+ *  TOPK_POLICY_EXACT_TAIL: S from Algorithm 1; t and M the least values
+ *    meeting the two conditions of Theorem 3 (recall failure R < k and
  *    overflow R > M each at most eps/2), evaluated with the exact
  *    hypergeometric law that Lemma 1 gives for the threshold rank.
  *  TOPK_POLICY_ALG1: Algorithm 1 verbatim (normal approximation of Lemma 2,
- *    t = 1 when alpha*S < -ln(eps/2)). */
-typedef enum { TOPK_POLICY_EXACT_TAIL = 0, TOPK_POLICY_ALG1 = 1 } topk_policy;
+ *    t = 1 when alpha*S < -ln(eps/2)).
+ *  TOPK_POLICY_TUNED (default): t and M as in EXACT_TAIL; S minimises the
+ *    overhead of Eq. 13, tau_A*S + tau_B*M(S)*log2(k), with the exact-tail
+ *    M(S) and tau_B/tau_A = tuned_ratio, over the sample sizes
+ *    tuned_s_min * 2^(j/4) (j = 0, 1, ...) up to min(s_max, n/8).  Sets S
+ *    the way section 4 ("Optimal Sample Size") suggests, with the cost ratio
+ *    measured on this engine instead of the default 1. */
+typedef enum {
+  TOPK_POLICY_EXACT_TAIL = 0,
+  TOPK_POLICY_ALG1 = 1,
+  TOPK_POLICY_TUNED = 2
+} topk_policy;
 
-/* Route.  AUTO: the sampled filter when n >= 8*S and the buffer M is below
- * n/2, else the exact radix select.  FILTER / EXACT force one route (FILTER
+/* Route.  AUTO: the sampled filter when n >= 8*S, n >= 2^18 and the buffer
+ * M is below n/2, else the exact radix select.  FILTER / EXACT force one route (FILTER
  * still falls back to the exact select when the sample fails). */
 typedef enum { TOPK_PATH_AUTO = 0, TOPK_PATH_FILTER = 1, TOPK_PATH_EXACT = 2 } topk_path;
 
@@ -81,7 +91,7 @@ typedef struct {
   double eps;         /* failure budget, Algorithm 1 input (default 1e-3) */
   int64_t s_min;      /* sample size bounds (default 32768 and 131072) */
   int64_t s_max;
-  double cost_ratio;  /* tau_B / tau_A of Eq. 13 (default 1) */
+  double cost_ratio;  /* tau_B / tau_A of Eq. 13 in Algorithm 1 (default 1) */
   int32_t policy;     /* topk_policy */
   int32_t force_path; /* topk_path */
   uint64_t seed;      /* sampler seed when use_seed != 0 */
@@ -90,6 +100,8 @@ typedef struct {
   int64_t S;          /* > 0: override the sample size */
   int64_t t;          /* > 0: override the threshold rank */
   int64_t M;          /* > 0: override the buffer capacity */
+  double tuned_ratio; /* TUNED policy: tau_B / tau_A of this engine (default 0.13) */
+  int64_t tuned_s_min;/* TUNED policy: least sample size considered (default 1024) */
 } topk_params;
 
 /* Resolved plan of one call shape (host arithmetic only; no GPU needed). */

@@ -9,6 +9,10 @@ infrastructure; the product library has its own C++ version).
                 threshold rank (Lemma 1) instead of its normal approximation
                 (Lemma 2), which the paper itself calls unreliable when
                 alpha*S is small.
+``tuned``       t and M as in ``exact_tail``; S the point of the grid
+                s_lo * 2^(j/4) (up to s_hi) with the least overhead of Eq. 13,
+                tau_A*S + tau_B*M(S)*log2(k), written as S + ratio*M(S)*log2(k)
+                with ratio = tau_B/tau_A (section 4, "Optimal Sample Size").
 
 Lemma 1 (the t-th largest of S samples drawn without replacement from N
 ranked items has rank R with a negative hypergeometric law) gives two
@@ -173,6 +177,27 @@ def exact_tail(N: int, k: int, eps: float = EPS_DEFAULT, s_min: int = S_MIN_DEFA
     return {"S": S, "t": t, "M": M,
             "p_recall": hyper_sf(N, k - 1, S, t),
             "p_overflow": hyper_cdf(N, M, S, t - 1)}
+
+
+def tuned(N: int, k: int, eps: float = EPS_DEFAULT, s_lo: int = 1024,
+          s_hi: int = S_MAX_DEFAULT, ratio: float = 0.13) -> dict:
+    """Eq. 13 minimised over a quarter-octave grid of S, with the exact-tail
+    buffer M(S) of each grid point; the smaller S wins a tie."""
+    s_lo, s_hi = min(s_lo, N), min(s_hi, N)
+    if s_hi < s_lo:
+        return exact_tail(N, k, eps, s_min=s_lo, s_max=s_lo)
+    best = None
+    j = 0
+    while True:
+        S = int(round(s_lo * 2.0 ** (j / 4)))
+        j += 1
+        if S > s_hi:
+            break
+        r = exact_tail(N, k, eps, s_min=S, s_max=S)
+        cost = S + ratio * r["M"] * math.log2(k)
+        if best is None or cost < best[0]:
+            best = (cost, r)
+    return best[1]
 
 
 def failure_probs(N: int, k: int, S: int, t: int, M: int) -> tuple[float, float]:

@@ -15,12 +15,12 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, Params,
+from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED, Params,
                    TopkError, default_params)
 
 __all__ = ["topk", "plan", "profile_enable", "profile_read", "workspace_size", "read_stats", "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
-           "POLICY_EXACT_TAIL", "POLICY_ALG1", "dtype_code"]
+           "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code"]
 
 _TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}
 _NAME_CODES = _lib.DTYPE_CODES

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libtopk_mi355x.so")
 
 TOPK_OK, TOPK_EINVAL, TOPK_EDTYPE, TOPK_EWORKSPACE, TOPK_EHIP, TOPK_ENOTIMPL = 0, -1, -2, -3, -4, -5
 DTYPE_CODES = {"int32": 0, "float32": 1, "bf16": 2}
-POLICY_EXACT_TAIL, POLICY_ALG1 = 0, 1
+POLICY_EXACT_TAIL, POLICY_ALG1, POLICY_TUNED = 0, 1, 2
 PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
 
 # Names of every function include/topk.h declares.
@@ -29,7 +29,8 @@ class Params(ctypes.Structure):
                 ("cost_ratio", ctypes.c_double), ("policy", ctypes.c_int32),
                 ("force_path", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("use_seed", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64)]
+                ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
+                ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -92,6 +92,8 @@ tk::ParamIn to_in(const topk_params* p) {
   in.S = p->S;
   in.t = p->t;
   in.M = p->M;
+  in.tuned_ratio = p->tuned_ratio;
+  in.tuned_s_min = p->tuned_s_min;
   return in;
 }
 
@@ -100,7 +102,8 @@ int check_params(const topk_params* p) {
   if (!(p->eps > 0.0 && p->eps < 1.0)) return TOPK_EINVAL;
   if (p->s_min < 1 || p->s_max < p->s_min) return TOPK_EINVAL;
   if (!(p->cost_ratio > 0.0)) return TOPK_EINVAL;
-  if (p->policy < 0 || p->policy > 1) return TOPK_EINVAL;
+  if (p->policy < 0 || p->policy > 2) return TOPK_EINVAL;
+  if (!(p->tuned_ratio > 0.0) || p->tuned_s_min < 1) return TOPK_EINVAL;
   if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
   if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
   return TOPK_OK;
@@ -149,6 +152,8 @@ int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* pa
 
 extern "C" {
 
+static_assert(sizeof(topk_params) == 96, "topk_params layout is part of the ABI");
+
 int topk_default_params(topk_params* p) {
   if (!p) return TOPK_EINVAL;
   std::memset(p, 0, sizeof(*p));
@@ -156,8 +161,10 @@ int topk_default_params(topk_params* p) {
   p->s_min = 32768;
   p->s_max = 131072;
   p->cost_ratio = 1.0;
-  p->policy = TOPK_POLICY_EXACT_TAIL;
+  p->policy = TOPK_POLICY_TUNED;
   p->force_path = TOPK_PATH_AUTO;
+  p->tuned_ratio = 0.13;
+  p->tuned_s_min = 1024;
   return TOPK_OK;
 }
 

@@ -349,6 +349,54 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     }
   };
 
+  // Survivors of one unrolled step: each lane sets one bit per element that
+  // passes, then the wave drains the bits one survivor per lane per round
+  // (slot = set lanes below, as in push), so a lane with one survivor costs
+  // one round whatever the element's position.
+  constexpr uint32_t SPAN = FILTER_UNROLL * D::VEC;   // elements per lane per step
+  static_assert(SPAN <= 32, "one 32-bit survivor mask per lane");
+  static_assert(FILTER_UNROLL == 4, "elem() selects among four vectors");
+  auto elem = [&](const u32x4 (&v)[FILTER_UNROLL], uint32_t b) -> uint32_t {
+    const uint32_t u = b / D::VEC, e = b % D::VEC;
+    const u32x4 w = u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3];
+    if constexpr (DT == DT_BF16) {
+      const uint32_t q = e >> 1;
+      const uint32_t x = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
+      return (e & 1u) ? (x >> 16) : (x & 0xFFFFu);
+    } else {
+      return e == 0 ? w[0] : e == 1 ? w[1] : e == 2 ? w[2] : w[3];
+    }
+  };
+  auto drain = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi, uint32_t bits) {
+    uint64_t m = ballot(bits != 0u);
+    while (m) {
+      const uint32_t c = (uint32_t)__builtin_popcountll(m);
+      if (sg.fill + c > STAGE_SLOTS) sg.flush();
+      if (bits) {
+        const uint32_t b = (uint32_t)__builtin_ctz(bits);
+        bits &= bits - 1u;
+        const uint32_t u = b / D::VEC, e = b % D::VEC;
+        const uint32_t idx = head + (uint32_t)(vi + u * FILTER_THREADS) * D::VEC + e;
+        sg.stage[sg.fill + rank_below(m)] = comp_of(elem(v, b), idx);
+      }
+      sg.fill += c;
+      m = ballot(bits != 0u);
+    }
+  };
+  auto mask_of = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi) -> uint32_t {
+    uint32_t bits = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < SPAN; ++b) {
+      const uint32_t u = b / D::VEC, e = b % D::VEC;
+      uint32_t raw;
+      if constexpr (DT == DT_BF16) raw = (e & 1u) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu);
+      else raw = v[u][e];
+      const uint32_t idx = head + (uint32_t)(vi + u * FILTER_THREADS) * D::VEC + e;
+      bits |= (uint32_t)pass_of(raw, idx) << b;
+    }
+    return bits;
+  };
+
   // This workgroup's slice of the row's vectors: [vi0, vend), in steps of
   // FILTER_THREADS * FILTER_UNROLL vectors.
   const uint32_t bpr = gridDim.x;
@@ -383,16 +431,14 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
         }
       }
       if (ballot(any != 0u) == 0) continue;
-#pragma unroll
-      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) handle_vec(v[u], (uint32_t)(vi + u * stride), true);
+      drain(v, vi, mask_of(v, vi));
     }
   } else {
     for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; vi += FILTER_UNROLL * stride) {
       u32x4 v[FILTER_UNROLL];
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
-#pragma unroll
-      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) handle_vec(v[u], (uint32_t)(vi + u * stride), true);
+      drain(v, vi, mask_of(v, vi));
     }
   }
   // Remainder of the slice: the bound differs between lanes, so iterate on

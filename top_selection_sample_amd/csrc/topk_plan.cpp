@@ -14,6 +14,14 @@
 // law of the threshold rank (Lemma 1): with H(N, K, S) the number of sampled
 // items among K fixed items,
 //   P(R < k) = P(H(N, k-1, S) >= t),   P(R > M) = P(H(N, M, S) <= t-1).
+//
+// Tuned policy: t and M as in the exact-tail policy, and S the minimiser of
+// Eq. 13's overhead C(S) = tau_A S + tau_B M(S) log2 k with the exact-tail
+// M(S), over a quarter-octave grid of sample sizes, with tau_B / tau_A
+// measured on this engine.  The lower bound S_min of Algorithm 1 guards the
+// normal approximation; the exact tail needs no such guard, so the grid
+// starts lower.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -177,15 +185,43 @@ TailParams exact_tail(int64_t N, int64_t k, int64_t S, double eps) {
   return r;
 }
 
+// Quarter-octave grid s_lo * 2^(j/4), j = 0, 1, ... up to s_hi; the point
+// with the least C(S) / tau_A = S + ratio * M(S) * log2 k wins (the smaller S
+// on a tie).
+int64_t tuned_sample_size(int64_t N, int64_t k, double eps, int64_t s_lo, int64_t s_hi,
+                          double ratio) {
+  if (s_lo > N) s_lo = N;
+  if (s_hi > N) s_hi = N;
+  if (s_hi < s_lo) return s_lo;
+  const double lk = std::log2((double)k);
+  int64_t best = s_lo;
+  double best_c = 0.0;
+  int64_t prev = 0;
+  for (int j = 0;; ++j) {
+    int64_t S = (int64_t)std::llround((double)s_lo * std::exp2(0.25 * j));
+    if (S > s_hi) break;
+    if (S == prev) continue;
+    prev = S;
+    const TailParams tp = exact_tail(N, k, S, eps);
+    const double c = (double)S + ratio * (double)tp.M * lk;
+    if (j == 0 || c < best_c) {
+      best = S;
+      best_c = c;
+    }
+  }
+  return best;
+}
+
 // ---------------------------------------------------------------- cache
 namespace {
 struct Key {
-  int64_t N, k, s_min, s_max, S, t, M;
-  double eps, ratio;
+  int64_t N, k, s_min, s_max, S, t, M, tuned_s_min;
+  double eps, ratio, tuned_ratio;
   int policy;
   bool operator<(const Key& o) const {
-    return std::tie(N, k, s_min, s_max, S, t, M, eps, ratio, policy) <
-           std::tie(o.N, o.k, o.s_min, o.s_max, o.S, o.t, o.M, o.eps, o.ratio, o.policy);
+    return std::tie(N, k, s_min, s_max, S, t, M, tuned_s_min, eps, ratio, tuned_ratio, policy) <
+           std::tie(o.N, o.k, o.s_min, o.s_max, o.S, o.t, o.M, o.tuned_s_min, o.eps, o.ratio,
+                    o.tuned_ratio, o.policy);
   }
 };
 struct Val {
@@ -208,7 +244,8 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t* t, int64_t* M,
                    double* pr, double* po) {
-  Key key{N, k, in.s_min, in.s_max, in.S, in.t, in.M, in.eps, in.cost_ratio, in.policy};
+  Key key{N,      k,     in.s_min,      in.s_max,       in.S,      in.t,
+          in.M,   in.tuned_s_min, in.eps, in.cost_ratio, in.tuned_ratio, in.policy};
   {
     std::lock_guard<std::mutex> g(g_mu);
     auto it = g_cache.find(key);
@@ -222,7 +259,10 @@ void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t*
     }
   }
   const Alg1 a = algorithm1(N, k, in.eps, in.s_min, in.s_max, in.cost_ratio);
-  int64_t s = in.S > 0 ? in.S : a.S;
+  int64_t s = a.S;
+  if (in.S > 0) s = in.S;
+  else if (in.policy == 2)
+    s = tuned_sample_size(N, k, in.eps, in.tuned_s_min, std::min(in.s_max, N / 8), in.tuned_ratio);
   if (s > N) s = N;
   int64_t tt, mm;
   if (in.policy == 1) {
@@ -270,7 +310,7 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   bool sampled;
   if (in.force_path == 1) sampled = true;
   else if (in.force_path == 2) sampled = false;
-  else sampled = (n >= 8 * p.S) && (p.M < n / 2);
+  else sampled = (n >= 8 * p.S) && (n >= EXACT_SMALL_MAX) && (p.M < n / 2);
   if (sampled) {
     p.path = PLAN_SAMPLED;
     p.cap = p.M < k ? k : p.M;

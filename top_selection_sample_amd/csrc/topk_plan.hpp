@@ -20,10 +20,12 @@ struct ParamIn {
   double eps = 1e-3;
   int64_t s_min = 32768, s_max = 131072;
   double cost_ratio = 1.0;
-  int policy = 0;      // 0 exact tail, 1 Algorithm 1
+  int policy = 2;      // 0 exact tail, 1 Algorithm 1, 2 tuned sample size
   int force_path = 0;  // 0 auto, 1 filter, 2 exact
   int64_t S = 0, t = 0, M = 0;
   int64_t cus = 256;   // compute units of the device the call runs on
+  double tuned_ratio = 0.13;   // tau_B / tau_A measured for this engine
+  int64_t tuned_s_min = 1024;  // least sample size the tuned policy considers
 };
 
 double normal_quantile(double p);
@@ -31,6 +33,8 @@ Alg1 algorithm1(int64_t N, int64_t k, double eps, int64_t s_min, int64_t s_max, 
 double hyper_cdf(int64_t N, int64_t K, int64_t S, int64_t t, bool fast);
 double hyper_sf(int64_t N, int64_t K, int64_t S, int64_t t);
 TailParams exact_tail(int64_t N, int64_t k, int64_t S, double eps);
+int64_t tuned_sample_size(int64_t N, int64_t k, double eps, int64_t s_lo, int64_t s_hi,
+                          double ratio);
 void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t* t, int64_t* M,
                    double* p_recall, double* p_overflow);
 int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, Plan* out);
