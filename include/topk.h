@@ -120,7 +120,9 @@ typedef struct {
 /* Per-row record of the last call on a workspace (topk_read_stats). */
 typedef struct {
   uint32_t tau_key;   /* sampled threshold as an order-preserving key */
-  uint32_t r_sampled; /* survivors of the sampled filter pass (R) */
+  uint32_t r_sampled; /* survivors of the sampled filter pass (R); on an
+                         overflow the pass may stop early, and this is then
+                         only some count above the buffer capacity */
   uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only */
   uint32_t passes;    /* histogram passes of the exact select */
   uint32_t flags;     /* bit 0: an exact-route grid barrier gave up waiting (the

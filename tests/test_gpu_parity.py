@@ -208,6 +208,33 @@ def test_batched_rows_reduced(variant):
     assert_same(gv, gi, x, k, "float32", variant)
 
 
+def test_more_rows_than_workgroups_with_failures():
+    # rows > compute units: a finishing workgroup owns several rows; every
+    # 7th row is constant, so its sampled threshold admits the whole row
+    # (overflow) and the row takes the exact route beside refined rows
+    rows, n, k = 300, 2 ** 18, 16
+    x = workloads.normal_f32(rows, n, 91)
+    x[::7] = 1.5
+    say(f"mixed failures rows={rows}")
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", "mixed rows")
+    st = _tss().read_stats(rows)
+    assert [r["path"] for r in st[::7]] == [1] * len(st[::7])
+    assert sum(r["path"] == 0 for r in st) >= rows - len(st[::7]) - 3
+
+
+def test_rows_listed_by_check_kernel():
+    # more rows than one workgroup scans: a separate kernel lists the failures
+    rows, n, k = 1030, 2 ** 18, 8
+    x = workloads.scores_int(rows, n, -2 ** 31, 2 ** 31 - 1, 92)
+    x[5::97] = 7
+    say(f"listed failures rows={rows}")
+    gv, gi = run_gpu(x, k, "int32")
+    assert_same(gv, gi, x, k, "int32", "listed rows")
+    st = _tss().read_stats(rows)
+    assert all(r["path"] == 1 for r in st[5::97])
+
+
 def test_batched_small_rows_exact():
     x = workloads.scores_int(300, 5000, 0, 50, 62)
     gv, gi = run_gpu(x, 17, "int32")

@@ -9,10 +9,11 @@
 //   k_sample       S sample keys per row through a keyed permutation
 //   k_tau          workgroup radix select of the t-th largest sample key
 //   k_filter       the streaming pass: keep composites with key >= tau
-//   k_check        large-k: accept the candidate count or start the fallback
+//   k_check        many rows: list the rows whose candidate count fails
 //   k_setup_exact  rows that start on the exact path
-//   k_hist         exact path: one 8-bit digit histogram pass over a row
-//   k_refine       small k: select, sort and write the k winners
+//   k_finish       the check, the refine of every accepted row (small k: select,
+//                  sort and write the k winners), and the exact route for the
+//                  failed rows, in one persistent launch
 //   k_exact_small  small rows: the whole exact selection in one workgroup
 //   k_tile_sort / k_merge / k_output   large k: sort all candidates
 #include "topk_device.hpp"
@@ -194,8 +195,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
 // Filter (Prof-K section 3, stage 3; Appendix D "Efficient GPU
 // Implementation"): one streaming pass over the row that keeps every element
 // whose key is >= the threshold, appending its composite to the row's
-// candidate buffer.  The counter keeps counting past the capacity, so the
-// exact number of survivors R is known after the pass.
+// candidate buffer.  The counter keeps counting past the capacity; R is
+// exact whenever it fits, and a wave that meets a full buffer stops early
+// (the row overflows, so only R > capacity matters).
 //
 // Survivor slots come from a wave ballot and the count of set lanes below
 // each lane (the stable split's "how many earlier elements share my flag",
@@ -218,7 +220,8 @@ struct Stager {
   uint64_t* buf;     // row's candidate buffer
   uint32_t cap;
 
-  __device__ void flush() {
+  // Returns true when the buffer is full (the row overflows).
+  __device__ bool flush() {
     wave_lds_sync();
     uint32_t base = 0;
     if (lane_id() == 0) base = atomicAdd(&st->count, fill);
@@ -228,7 +231,9 @@ struct Stager {
       if (pos < cap) buf[pos] = stage[i];
     }
     wave_lds_sync();
+    const bool full = base + fill > cap;
     fill = 0;
+    return full;
   }
   // All lanes call together.
   __device__ void push(bool p, uint64_t comp) {
@@ -240,6 +245,56 @@ struct Stager {
     fill += c;
   }
 };
+
+// Element b (0 .. 4 * VEC - 1) of four 16-byte vectors as raw bits; b may
+// differ between lanes (a select chain, no indexed register access).
+template <int DT>
+__device__ __forceinline__ uint32_t elem4(const u32x4 (&v)[4], uint32_t b) {
+  using D = Dt<DT>;
+  const uint32_t u = b / D::VEC, e = b % D::VEC;
+  const u32x4 w = u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3];
+  if constexpr (DT == DT_BF16) {
+    const uint32_t q = e >> 1;
+    const uint32_t x = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
+    return (e & 1u) ? (x >> 16) : (x & 0xFFFFu);
+  } else {
+    return e == 0 ? w[0] : e == 1 ? w[1] : e == 2 ? w[2] : w[3];
+  }
+}
+
+// The same with b known at compile time (unrolled loops).
+template <int DT>
+__device__ __forceinline__ uint32_t elem4c(const u32x4 (&v)[4], uint32_t b) {
+  using D = Dt<DT>;
+  const uint32_t u = b / D::VEC, e = b % D::VEC;
+  if constexpr (DT == DT_BF16) return (e & 1u) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu);
+  else return v[u][e];
+}
+
+// Survivors of one step: each lane holds one bit per passing element; the
+// wave drains the bits one survivor per lane per round (slot = set lanes
+// below, as in push), so a lane with one survivor costs one round whatever
+// the element's position.  idx_of(b) is the index of element b, comp_of
+// builds its composite.  All lanes call together; returns true when a flush
+// found the row's buffer full.
+template <int DT, class IdxF, class CompF>
+__device__ __forceinline__ bool drain_bits(Stager& sg, const u32x4 (&v)[4], uint32_t bits,
+                                           IdxF&& idx_of, CompF&& comp_of) {
+  bool full = false;
+  uint64_t m = ballot(bits != 0u);
+  while (m) {
+    const uint32_t c = (uint32_t)__builtin_popcountll(m);
+    if (sg.fill + c > STAGE_SLOTS) full = sg.flush() || full;
+    if (bits) {
+      const uint32_t b = (uint32_t)__builtin_ctz(bits);
+      bits &= bits - 1u;
+      sg.stage[sg.fill + rank_below(m)] = comp_of(elem4<DT>(v, b), idx_of(b));
+    }
+    sg.fill += c;
+    m = ballot(bits != 0u);
+  }
+  return full;
+}
 
 // Native-domain threshold for the fast compare.  kind 0: compare in the value
 // domain; kind 1: compare keys (thresholds above +inf, or a tie cut on index).
@@ -349,50 +404,28 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     }
   };
 
-  // Survivors of one unrolled step: each lane sets one bit per element that
-  // passes, then the wave drains the bits one survivor per lane per round
-  // (slot = set lanes below, as in push), so a lane with one survivor costs
-  // one round whatever the element's position.
+  // Survivors of one unrolled step: a 32-bit mask per lane, drained by
+  // drain_bits.  A wave that finds the buffer full stops scanning: the row
+  // overflows and goes to the exact route whatever the rest would count.
   constexpr uint32_t SPAN = FILTER_UNROLL * D::VEC;   // elements per lane per step
   static_assert(SPAN <= 32, "one 32-bit survivor mask per lane");
-  static_assert(FILTER_UNROLL == 4, "elem() selects among four vectors");
-  auto elem = [&](const u32x4 (&v)[FILTER_UNROLL], uint32_t b) -> uint32_t {
-    const uint32_t u = b / D::VEC, e = b % D::VEC;
-    const u32x4 w = u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3];
-    if constexpr (DT == DT_BF16) {
-      const uint32_t q = e >> 1;
-      const uint32_t x = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
-      return (e & 1u) ? (x >> 16) : (x & 0xFFFFu);
-    } else {
-      return e == 0 ? w[0] : e == 1 ? w[1] : e == 2 ? w[2] : w[3];
-    }
-  };
+  static_assert(FILTER_UNROLL == 4, "elem4() selects among four vectors");
+  bool full = false;
   auto drain = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi, uint32_t bits) {
-    uint64_t m = ballot(bits != 0u);
-    while (m) {
-      const uint32_t c = (uint32_t)__builtin_popcountll(m);
-      if (sg.fill + c > STAGE_SLOTS) sg.flush();
-      if (bits) {
-        const uint32_t b = (uint32_t)__builtin_ctz(bits);
-        bits &= bits - 1u;
-        const uint32_t u = b / D::VEC, e = b % D::VEC;
-        const uint32_t idx = head + (uint32_t)(vi + u * FILTER_THREADS) * D::VEC + e;
-        sg.stage[sg.fill + rank_below(m)] = comp_of(elem(v, b), idx);
-      }
-      sg.fill += c;
-      m = ballot(bits != 0u);
-    }
+    const bool f = drain_bits<DT>(
+        sg, v, bits,
+        [&](uint32_t b) {
+          return head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
+        },
+        comp_of);
+    full = full || f;
   };
   auto mask_of = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi) -> uint32_t {
     uint32_t bits = 0;
 #pragma unroll
     for (uint32_t b = 0; b < SPAN; ++b) {
-      const uint32_t u = b / D::VEC, e = b % D::VEC;
-      uint32_t raw;
-      if constexpr (DT == DT_BF16) raw = (e & 1u) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu);
-      else raw = v[u][e];
-      const uint32_t idx = head + (uint32_t)(vi + u * FILTER_THREADS) * D::VEC + e;
-      bits |= (uint32_t)pass_of(raw, idx) << b;
+      const uint32_t idx = head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
+      bits |= (uint32_t)pass_of(elem4c<DT>(v, b), idx) << b;
     }
     return bits;
   };
@@ -432,6 +465,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       }
       if (ballot(any != 0u) == 0) continue;
       drain(v, vi, mask_of(v, vi));
+      if (full) break;
     }
   } else {
     for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; vi += FILTER_UNROLL * stride) {
@@ -439,8 +473,10 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
       drain(v, vi, mask_of(v, vi));
+      if (full) break;
     }
   }
+  if (full) vi = vend + lane;   // skip the remainder as well
   // Remainder of the slice: the bound differs between lanes, so iterate on
   // the wave's first lane index to keep ballots wave-uniform.
   for (;;) {
@@ -513,13 +549,11 @@ __global__ void k_check(RowState* __restrict__ states, CallState* __restrict__ c
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
   const uint32_t R = st->count;
-  st->r_sampled = R;
   if (R < k || R > cap) {
+    st->r_sampled = R;
     start_exact(st, k, PATH_FALLBACK);
     flag_row(cs, flagged, row);
-    return;
   }
-  st->status = ST_SORT;
 }
 
 __global__ void k_setup_exact(RowState* __restrict__ states, CallState* __restrict__ cs,
@@ -774,25 +808,8 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
   if (tid == 0) {
     if (want == ST_FILTER) st->r_sampled = R;
     st->status = ST_DONE;
-    st->count = 0;
   }
   __syncthreads();
-}
-
-template <int DT>
-__global__ __launch_bounds__(SEL_THREADS) void k_refine(
-    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
-    CallState* __restrict__ cs, uint32_t* __restrict__ flagged, const uint64_t* __restrict__ cbuf,
-    uint32_t cap, uint32_t k, uint32_t B, uint32_t W, void* __restrict__ out_values,
-    int64_t* __restrict__ out_idx) {
-  __shared__ uint32_t s_hist[RF_BINS];
-  __shared__ uint32_t s_misc[8];
-  __shared__ uint32_t s_tmp[16];
-  __shared__ uint64_t s_cand[RF_SORT_CAP];
-  __shared__ uint32_t s_keys[RF_KCAP];
-  __shared__ uint32_t s_idx[RF_SORT_CAP];
-  refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
-                 out_idx, blockIdx.x, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
 }
 
 // Whole exact selection of a small row in one workgroup.  Small k: writes the
@@ -871,35 +888,43 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
 // rows are refined (small k) or handed to the sort (large k).
 //
 // One launch does it all, the phases separated by grid-wide barriers.  The
-// grid is one workgroup per compute unit (each CU has room for two), so all
-// workgroups are resident together; every barrier wait is bounded, and a
-// wait that gives up sets CallState::error instead of hanging.  When no row
-// is listed every workgroup returns at once, so the route costs a single
-// empty launch on the common path.
+// grid is one workgroup per compute unit, so all workgroups are resident
+// together; every barrier wait is bounded, and a wait that gives up sets
+// CallState::error instead of hanging.  The same launch first refines the
+// rows whose sampled candidates passed the check, so when no row failed the
+// exact route costs nothing beyond that launch.
 // ======================================================================
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
+// Arrival: a release fence (this workgroup's writes reach memory), then one
+// relaxed increment of the arrival count; the last arrival acquires the
+// others' writes, resets the count and bumps the generation.  Waiting polls
+// the generation with relaxed loads and acquires once it has moved: an
+// acquiring load per poll would invalidate the L2 at every iteration, which
+// measured about four times slower on MI355X (~22 us against ~6 us per
+// barrier over 256 workgroups).
 __device__ void grid_barrier(CallState* cs, uint32_t G) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t gen = __hip_atomic_load(&cs->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t gen = __hip_atomic_load(&cs->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t arrived =
-        __hip_atomic_fetch_add(&cs->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        __hip_atomic_fetch_add(&cs->bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     if (arrived == G) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(&cs->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(&cs->bar_gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       uint32_t spins = 0;
-      while (__hip_atomic_load(&cs->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+      while (__hip_atomic_load(&cs->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins > SPIN_LIMIT) {
           __hip_atomic_fetch_or(&cs->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    __threadfence();
   }
   __syncthreads();
 }
@@ -947,47 +972,22 @@ __device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint
   return g;
 }
 
-// Calls f(raw, idx, valid) for every element of item c of a row, with every
-// lane of every wave taking part in each call (valid marks real elements).
-template <int DT, class F>
-__device__ __forceinline__ void for_item(const RowGeom& g, uint32_t n, uint32_t c, F&& f) {
-  using D = Dt<DT>;
-  const uint32_t tid = threadIdx.x;
-#pragma unroll
-  for (uint32_t j = 0; j < EX_VPT; ++j) {
-    const uint32_t v = c * EX_ITEM_VEC + j * EX_THREADS + tid;
-    const bool ok = v < g.nvec;
-    const u32x4 x = ok ? __builtin_nontemporal_load(g.vp + v) : u32x4{0u, 0u, 0u, 0u};
-    const uint32_t e0 = g.head + v * D::VEC;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (DT == DT_BF16) {
-        f(x[q] & 0xFFFFu, e0 + 2 * q, ok);
-        f(x[q] >> 16, e0 + 2 * q + 1, ok);
-      } else {
-        f(x[q], e0 + q, ok);
-      }
-    }
-  }
-  if (c == 0 && tid < 64) {   // head and tail elements, first wave
-    const uint32_t nt = n - g.tail0;
-    const uint32_t j = tid;
-    const bool ok = j < g.head + nt;
-    uint32_t idx = 0, raw = 0;
-    if (ok) {
-      idx = (j < g.head) ? j : g.tail0 + (j - g.head);
-      raw = load_raw<DT>(g.rowp, idx);
-    }
-    f(raw, idx, ok);
-  }
-}
+// How the finish kernel learns which rows failed the check.
+//  FIN_SCAN: sampled route with at most FIN_SCAN_ROWS rows: every workgroup
+//    reads every row's survivor count itself.  All reach the same verdict
+//    without waiting for one another: a count is final once the filter has
+//    run, and the only write to it here (start_exact, on a failed row) keeps
+//    the row failed.  The common case (no failure) then needs no barrier.
+//  FIN_LISTED: an earlier kernel listed the failed rows (nflag, flagged[]).
+enum : uint32_t { FIN_SCAN = 0, FIN_LISTED = 1 };
+constexpr uint32_t FIN_SCAN_ROWS = 1024;
 
 template <int DT>
-__global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
-    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+__global__ __launch_bounds__(EX_THREADS) void k_finish(
+    const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
     CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
     uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
-    uint32_t small_k, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+    uint32_t small_k, uint32_t mode, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
   using D = Dt<DT>;
   __shared__ uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -995,36 +995,178 @@ __global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
   __shared__ uint64_t s_cand[RF_SORT_CAP];
   __shared__ uint32_t s_keys[RF_KCAP];
   __shared__ uint32_t s_idx[RF_SORT_CAP];
-  const uint32_t nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (nf == 0) return;                        // the common case: nothing to do
   const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
+  static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
+
+  // ---- which rows failed the check (Prof-K section 3, stage 4)
+  __shared__ uint32_t s_bad[FIN_SCAN_ROWS / 32];   // FIN_SCAN: one bit per row
+  uint32_t nf;
+  if (mode == FIN_SCAN) {
+    const uint32_t words = (rows + 31) / 32;
+    for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
+    __syncthreads();
+    for (uint32_t r = tid; r < rows; r += blockDim.x) {
+      const uint32_t R = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (R < k || R > cap) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
+    }
+    __syncthreads();
+    nf = 0;
+    for (uint32_t i = 0; i < words; ++i) nf += __builtin_popcount(s_bad[i]);
+  } else {
+    nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- this workgroup's rows: list the failed ones, refine the others
+  for (uint32_t r = blockIdx.x; r < rows; r += G) {
+    RowState* st = states + r;
+    if (mode == FIN_SCAN && nf && (s_bad[r >> 5] >> (r & 31)) & 1u) {
+      if (tid == 0) {
+        uint32_t slot = 0;   // failed rows below r
+        for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
+        slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
+        st->r_sampled = st->count;
+        start_exact(st, k, PATH_FALLBACK);
+        flagged[slot] = r;
+      }
+      continue;
+    }
+    if (st->status != ST_FILTER) continue;
+    if (small_k) {
+      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
+                     out_idx, r, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
+    } else if (tid == 0) {
+      st->r_sampled = st->count;
+      st->status = ST_SORT;
+    }
+    __syncthreads();
+  }
+  if (nf == 0) return;                        // the common case: nothing more to do
+  if (mode == FIN_SCAN) {
+    if (blockIdx.x == 0 && tid == 0) {
+      cs->nflag = nf;
+      cs->nactive = nf;
+    }
+    grid_barrier(cs, G);   // the listed rows' states are visible to all
+  }
   uint32_t ipr = (n / D::VEC + EX_ITEM_VEC - 1) / EX_ITEM_VEC;   // items per row
   if (ipr == 0) ipr = 1;
   const uint64_t total = (uint64_t)nf * ipr;
   auto sync_all = [&]() { grid_barrier(cs, G); };
 
+  // Listed row f covers items [f * ipr, (f + 1) * ipr).  Each workgroup takes
+  // one contiguous range of items, so it streams long runs of one row and
+  // reads a row's state only when the row changes.
+  const uint64_t per = (total + G - 1) / G;
+  const uint64_t it_lo = (uint64_t)blockIdx.x * per;
+  const uint64_t it_hi = it_lo + per < total ? it_lo + per : total;
+  constexpr uint32_t SPAN = EX_VPT * D::VEC;   // elements per thread per item
+  static_assert(EX_VPT == 4, "elem4() selects among four vectors");
+  const uint32_t lane = tid & 63u;
+  auto vec_of = [&](uint32_t c, uint32_t b) { return c * EX_ITEM_VEC + (b / D::VEC) * EX_THREADS + tid; };
+  auto load_item = [&](const RowGeom& g, uint32_t c, u32x4 (&xs)[EX_VPT]) {
+#pragma unroll
+    for (uint32_t j = 0; j < EX_VPT; ++j) {
+      const uint32_t v = c * EX_ITEM_VEC + j * EX_THREADS + tid;
+      xs[j] = v < g.nvec ? __builtin_nontemporal_load(g.vp + v) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // The elements before the first and after the last 16-byte vector of a
+  // row (fewer than 2 * VEC): visited with item 0 by the first wave.
+  auto head_tail = [&](const RowGeom& g, auto&& f) {
+    if (tid < 64) {
+      const uint32_t nt = n - g.tail0;
+      const bool ok = tid < g.head + nt;
+      uint32_t idx = 0, raw = 0;
+      if (ok) {
+        idx = (tid < g.head) ? tid : g.tail0 + (tid - g.head);
+        raw = load_raw<DT>(g.rowp, idx);
+      }
+      f(raw, idx, ok);
+    }
+  };
+
   // ---- histogram passes
   for (uint32_t pass = 0; pass < W / 8; ++pass) {
     if (__hip_atomic_load(&cs->nactive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
-    for (uint64_t it = blockIdx.x; it < total; it += G) {
+    if (tid < 256) s_hist[tid] = 0;
+    __syncthreads();
+    uint32_t fcur = 0xFFFFFFFFu, nb = 0;
+    uint64_t prefix = 0;
+    bool live = false;
+    RowGeom g{};
+    // the LDS histogram collects consecutive items of one row
+    auto flush_hist = [&]() {
+      __syncthreads();
+      if (tid < 256) {
+        const uint32_t h = s_hist[tid];
+        if (h) {
+          atomicAdd(&ghist[(size_t)fcur * 256 + tid], h);
+          s_hist[tid] = 0;
+        }
+      }
+      __syncthreads();
+    };
+    for (uint64_t it = it_lo; it < it_hi; ++it) {
       const uint32_t f = (uint32_t)(it / ipr), c = (uint32_t)(it % ipr);
-      const uint32_t row = flagged[f];
-      RowState* st = states + row;
-      if (st->status != ST_EXACT) continue;
-      const uint32_t nb = st->nbits;
-      const uint64_t prefix = st->prefix;
-      if (tid < 256) s_hist[tid] = 0;
-      __syncthreads();
-      const RowGeom g = row_geom<DT>(values, n, row);
-      for_item<DT>(g, n, c, [&](uint32_t raw, uint32_t idx, bool ok) {
+      if (f != fcur) {
+        if (live) flush_hist();
+        fcur = f;
+        const uint32_t row = flagged[f];
+        const RowState* st = states + row;
+        live = st->status == ST_EXACT;
+        nb = st->nbits;
+        prefix = st->prefix;
+        g = row_geom<DT>(values, n, row);
+      }
+      if (!live) continue;
+      u32x4 xs[EX_VPT];
+      load_item(g, c, xs);
+      // Count this thread's matching elements and whether they share one
+      // digit; when the whole wave does (skewed data, late passes) one atomic
+      // adds the wave's count, else every element adds itself.
+      uint32_t my_d = 0, my_cnt = 0;
+      bool uni = true;
+#pragma unroll
+      for (uint32_t b = 0; b < SPAN; ++b) {
         uint32_t d;
-        const bool m = digit_of<D::KB>(D::key(raw), idx, nb, prefix, B, &d);
-        hist_add(s_hist, d, ok && m);
-      });
-      __syncthreads();
-      if (tid < 256 && s_hist[tid]) atomicAdd(&ghist[(size_t)f * 256 + tid], s_hist[tid]);
-      __syncthreads();
+        const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
+        const bool act = vec_of(c, b) < g.nvec &&
+                         digit_of<D::KB>(D::key(elem4c<DT>(xs, b)), e, nb, prefix, B, &d);
+        if (act) {
+          uni = uni && (my_cnt == 0 || d == my_d);
+          my_d = my_cnt == 0 ? d : my_d;
+          ++my_cnt;
+        }
+      }
+      const uint64_t has = ballot(my_cnt != 0u);
+      if (has) {
+        const uint32_t dref = __shfl(my_d, (int)__builtin_ctzll(has), 64);
+        const bool agree = my_cnt == 0u || (uni && my_d == dref);
+        if (ballot(!agree) == 0) {
+          uint32_t tcount = my_cnt;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) tcount += __shfl_xor(tcount, o, 64);
+          if (lane == 0) atomicAdd(&s_hist[dref], tcount);
+        } else {
+#pragma unroll
+          for (uint32_t b = 0; b < SPAN; ++b) {
+            uint32_t d;
+            const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
+            const bool act = vec_of(c, b) < g.nvec &&
+                             digit_of<D::KB>(D::key(elem4c<DT>(xs, b)), e, nb, prefix, B, &d);
+            if (act) atomicAdd(&s_hist[d], 1u);
+          }
+        }
+      }
+      if (c == 0) {
+        head_tail(g, [&](uint32_t raw, uint32_t idx, bool ok) {
+          uint32_t d;
+          const bool m = digit_of<D::KB>(D::key(raw), idx, nb, prefix, B, &d);
+          hist_add(s_hist, d, ok && m);
+        });
+      }
     }
+    if (live) flush_hist();
     sync_all();
     // resolve: one workgroup per listed row
     for (uint32_t f = blockIdx.x; f < nf; f += G) {
@@ -1041,12 +1183,12 @@ __global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
       if (tid < 64) wave_find_bucket(s_hist, need, s_misc);
       __syncthreads();
       if (tid == 0) {
-        const uint32_t nb = st->nbits;
-        const uint32_t shift = W - nb - 8;
+        const uint32_t nb0 = st->nbits;
+        const uint32_t shift = W - nb0 - 8;
         const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
         const uint32_t above = st->above + acc;
         const uint64_t np = st->prefix | ((uint64_t)b << shift);
-        const uint32_t nnb = nb + 8;
+        const uint32_t nnb = nb0 + 8;
         const uint64_t maskB = (1ull << B) - 1ull;
         st->above = above;
         st->need = need - acc;
@@ -1069,23 +1211,50 @@ __global__ __launch_bounds__(EX_THREADS) void k_exact_coop(
   // ---- exact filter: every element >= the exact threshold into the buffer
   {
     Stager sg{s_cand + (size_t)w * STAGE_SLOTS, 0u, nullptr, nullptr, cap};
-    for (uint64_t it = blockIdx.x; it < total; it += G) {
+    const uint64_t maskB = (1ull << B) - 1ull;
+    auto comp = [&](uint32_t raw, uint32_t idx) -> uint64_t {
+      return ((uint64_t)D::key(raw) << B) | (maskB - idx);
+    };
+    uint32_t fcur = 0xFFFFFFFFu;
+    bool live = false;
+    Thr thr{};
+    RowGeom g{};
+    for (uint64_t it = it_lo; it < it_hi; ++it) {
       const uint32_t f = (uint32_t)(it / ipr), c = (uint32_t)(it % ipr);
-      const uint32_t row = flagged[f];
-      RowState* st = states + row;
-      if (st->status != ST_EXACT_READY) continue;
-      const Thr thr = make_thr<DT>(st->thr_key, st->thr_bound);
-      const uint64_t maskB = (1ull << B) - 1ull;
-      sg.st = st;
-      sg.buf = cbuf + (size_t)row * cap;
-      const RowGeom g = row_geom<DT>(values, n, row);
-      for_item<DT>(g, n, c, [&](uint32_t raw, uint32_t idx, bool ok) {
-        const uint32_t key = D::key(raw);
-        const bool p = ok && key_pass(key, idx, thr);
-        sg.push(p, p ? (((uint64_t)key << B) | (maskB - idx)) : 0ull);
-      });
-      if (sg.fill) sg.flush();
+      if (f != fcur) {
+        if (sg.fill) sg.flush();   // to the previous row
+        fcur = f;
+        const uint32_t row = flagged[f];
+        RowState* st = states + row;
+        live = st->status == ST_EXACT_READY;
+        if (live) {
+          thr = make_thr<DT>(st->thr_key, st->thr_bound);
+          sg.st = st;
+          sg.buf = cbuf + (size_t)row * cap;
+          g = row_geom<DT>(values, n, row);
+        }
+      }
+      if (!live) continue;
+      u32x4 xs[EX_VPT];
+      load_item(g, c, xs);
+      uint32_t bits = 0;
+#pragma unroll
+      for (uint32_t b = 0; b < SPAN; ++b) {
+        const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
+        const bool p = vec_of(c, b) < g.nvec && key_pass(D::key(elem4c<DT>(xs, b)), e, thr);
+        bits |= (uint32_t)p << b;
+      }
+      drain_bits<DT>(
+          sg, xs, bits,
+          [&](uint32_t b) { return g.head + vec_of(c, b) * D::VEC + b % D::VEC; }, comp);
+      if (c == 0) {
+        head_tail(g, [&](uint32_t raw, uint32_t idx, bool ok) {
+          const bool p = ok && key_pass(D::key(raw), idx, thr);
+          sg.push(p, p ? comp(raw, idx) : 0ull);
+        });
+      }
     }
+    if (sg.fill) sg.flush();
   }
   sync_all();
 
@@ -1202,7 +1371,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
   }
 
 template <int DT>
-static hipError_t launch_exact_coop(const LaunchArgs& a, uint32_t small_k) {
+static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t mode) {
   // one workgroup per compute unit (cached per device)
   static int cached[64] = {0};
   int dev = 0;
@@ -1216,9 +1385,10 @@ static hipError_t launch_exact_coop(const LaunchArgs& a, uint32_t small_k) {
     cached[dev] = cus > 0 ? cus : 1;
   }
   const Plan& p = a.plan;
-  hipLaunchKernelGGL(k_exact_coop<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
-                     a.values, (uint32_t)p.n, a.states, a.call, a.flagged, a.ghist, a.cbuf,
-                     (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, a.out_values, a.out_idx);
+  hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
+                     a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.call, a.flagged,
+                     a.ghist, a.cbuf, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
+                     a.out_values, a.out_idx);
   return hipGetLastError();
 }
 
@@ -1255,31 +1425,32 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
                   cap, B, (uint32_t)ST_FILTER);
       mark(STAGE_FILTER, 0);
-      mark(STAGE_REFINE, 1);
-      if (p.small_k) {
-        TK_DISPATCH(dt, k_refine, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
-                    a.call, a.flagged, a.cbuf, cap, k, B, W, a.out_values, a.out_idx);
-      } else {
-        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows, k,
-                           cap);
-      }
-      mark(STAGE_REFINE, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
                          k);
     }
-    // Exact route for every listed row (a single no-op launch when none is).
+    // Check, refine, and the exact route for every failed row: one launch.
+    uint32_t mode = FIN_LISTED;
+    if (p.path == PLAN_SAMPLED) {
+      if (rows <= FIN_SCAN_ROWS) {
+        mode = FIN_SCAN;
+      } else {
+        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows, k,
+                           cap);
+      }
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    mark(STAGE_EXACT, 1);
+    const int stage = p.path == PLAN_SAMPLED ? STAGE_REFINE : STAGE_EXACT;
+    mark(stage, 1);
     const uint32_t sk = p.small_k ? 1u : 0u;
     switch (dt) {
-      case DT_I32: e = launch_exact_coop<DT_I32>(a, sk); break;
-      case DT_F32: e = launch_exact_coop<DT_F32>(a, sk); break;
-      default: e = launch_exact_coop<DT_BF16>(a, sk); break;
+      case DT_I32: e = launch_finish<DT_I32>(a, sk, mode); break;
+      case DT_F32: e = launch_finish<DT_F32>(a, sk, mode); break;
+      default: e = launch_finish<DT_BF16>(a, sk, mode); break;
     }
     if (e != hipSuccess) return e;
-    mark(STAGE_EXACT, 0);
+    mark(stage, 0);
   }
   if (!p.small_k) {
     // every row now holds R in [k, cap] candidates: sort them, keep k
