@@ -128,6 +128,8 @@ typedef struct {
   uint32_t flags;     /* bit 0: an exact-route grid barrier gave up waiting (the
                          result of that call is not trustworthy; never seen in
                          normal operation) */
+  uint32_t ties;      /* of r_sampled, the survivors equal to tau; they join the
+                         candidates only when fewer than k lie strictly above */
 } topk_row_stats;
 
 /* Fill *p with the defaults above.  Returns TOPK_OK, or TOPK_EINVAL for NULL. */

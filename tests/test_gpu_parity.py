@@ -144,8 +144,26 @@ def test_tau_and_R_match_sampler_spec(dt):
         tk, R = oracle.tau(x[0], seed, 0, pl["S"], pl["t"], dt)
         assert st["tau_key"] == tk
         assert st["r_sampled"] == R
-        exp_path = 0 if (k <= R <= pl["cap"]) else 1
-        assert st["path"] == exp_path
+        path, G, E = _expected_route(x[0], dt, tk, k, pl["cap"])
+        assert st["path"] == path and st["ties"] == E
+
+
+def _expected_path(row, dt, tau_key, k, cap):
+    return _expected_route(row, dt, tau_key, k, cap)[0]
+
+
+def _expected_route(row, dt, tau_key, k, cap):
+    """Route of a sampled row: the survivors split at tau into G above and E
+    equal; the row is accepted when G alone holds k of them within the
+    capacity, or when G < k <= G + E <= cap (the ties join the candidates)."""
+    kk = oracle.keys(row, dt).astype(np.int64)
+    G = int((kk > tau_key).sum())
+    E = int((kk == tau_key).sum())
+    if G > cap:
+        return 1, G, E
+    if G >= k:
+        return 0, G, E
+    return (0 if k <= G + E <= cap else 1), G, E
 
 
 def test_forced_overflow_fallback():
@@ -191,6 +209,64 @@ def test_exact_route_all_equal_large_row():
     assert_same(gv, gi, x, 300, "float32", "all-equal exact")
     gv, gi = run_gpu(x, 300, "float32")
     assert_same(gv, gi, x, 300, "float32", "all-equal auto")
+
+
+def _plateau_row(n, n_top, n_tie, seed):
+    # n_top distinct large values, n_tie copies of 5.0, the rest far below
+    g = workloads.rng(seed)
+    x = (g.standard_normal(n) - 1000.0).astype(np.float32)
+    pos = g.choice(n, n_top + n_tie, replace=False)
+    x[pos[:n_top]] = 10.0 + np.arange(n_top, dtype=np.float32)
+    x[pos[n_top:]] = 5.0
+    return x[None, :]
+
+
+def test_ties_join_candidates():
+    # 32 values above the plateau, k = 64: the threshold lands on the plateau
+    # (w.h.p.), so the 32 lowest-index ties complete the answer from the tie region
+    n, k = 2 ** 20, 64
+    x = _plateau_row(n, 32, 50_000, 71)
+    tss = _tss()
+    p = _seeded(11, M=100_000, force_path=1)
+    pl = tss.plan(n, 1, k, "float32", params=p)
+    say("ties join the candidates")
+    gv, gi = run_gpu(x, k, "float32", params=p)
+    assert_same(gv, gi, x, k, "float32", "ties join")
+    st = tss.read_stats(1)[0]
+    tk, R = oracle.tau(x[0], 11, 0, pl["S"], pl["t"], "float32")
+    assert st["tau_key"] == tk and st["r_sampled"] == R
+    path, G, E = _expected_route(x[0], "float32", tk, k, pl["cap"])
+    assert st["path"] == path and st["ties"] == E
+    if tk == int(oracle.keys(np.array([5.0], dtype=np.float32))[0]):
+        assert st["path"] == 0
+
+
+def test_ties_beyond_capacity_fall_back():
+    # the same, but the plateau does not fit the buffer: exact route
+    n, k = 2 ** 20, 64
+    x = _plateau_row(n, 32, 200_000, 72)
+    tss = _tss()
+    p = _seeded(12, M=100_000, force_path=1)
+    pl = tss.plan(n, 1, k, "float32", params=p)
+    say("ties beyond the capacity")
+    gv, gi = run_gpu(x, k, "float32", params=p)
+    assert_same(gv, gi, x, k, "float32", "ties overflow")
+    st = tss.read_stats(1)[0]
+    tk, R = oracle.tau(x[0], 12, 0, pl["S"], pl["t"], "float32")
+    assert st["path"] == _expected_path(x[0], "float32", tk, k, pl["cap"])
+
+
+def test_ties_ignored_when_enough_above():
+    # all zeros but k ones: tau is 0 (w.h.p.) and the k ones alone are the
+    # answer, so the row is accepted whatever the number of ties
+    rows, n, k = 4, 2 ** 20, 64
+    x = workloads.planted(rows, n, 64, 73)
+    say("ties ignored")
+    for dt in ("float32", "bf16"):
+        xx = x if dt == "float32" else workloads.f32_to_bf16_bits(x)
+        gv, gi = run_gpu(xx, k, dt)
+        assert_same(gv, gi, xx, k, dt, f"planted {dt}")
+        assert [r["path"] for r in _tss().read_stats(rows)] == [0] * rows
 
 
 # ------------------------------------------------------------ batched rows

@@ -132,7 +132,7 @@ def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> li
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
     return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes,
-             "flags": a.flags} for a in arr]
+             "flags": a.flags, "ties": a.ties} for a in arr]
 
 
 def profile_enable(on: bool = True) -> None:

@@ -48,7 +48,7 @@ class StageTimes(ctypes.Structure):
 class RowStats(ctypes.Structure):
     _fields_ = [("tau_key", ctypes.c_uint32), ("r_sampled", ctypes.c_uint32),
                 ("path", ctypes.c_uint32), ("passes", ctypes.c_uint32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("ties", ctypes.c_uint32)]
 
 
 def _load():

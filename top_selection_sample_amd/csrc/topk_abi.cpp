@@ -289,6 +289,7 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
       out[r].r_sampled = st[(size_t)r].r_sampled;
       out[r].path = st[(size_t)r].path;
       out[r].passes = st[(size_t)r].passes;
+      out[r].ties = st[(size_t)r].ties;
     }
     return TOPK_OK;
   } catch (...) {

@@ -36,8 +36,9 @@ enum : uint32_t { PATH_SAMPLED = 0, PATH_FALLBACK = 1, PATH_EXACT = 2 };
 struct alignas(64) RowState {
   uint32_t status;
   uint32_t tau_key;     // sampled threshold key (t-th largest sampled key)
-  uint32_t count;       // survivors counted by the current filter pass
-  uint32_t ticket;      // last-workgroup ticket of the current multi-WG pass
+  uint32_t count;       // candidates counted by the current filter pass (sampled
+                        //   pass: elements strictly above tau)
+  uint32_t ties;        // sampled pass: elements equal to tau (exact count)
   uint32_t r_sampled;   // survivors of the sampled pass
   uint32_t path;        // PATH_*
   uint32_t need;        // exact select: rank wanted inside the prefix bucket
@@ -47,7 +48,7 @@ struct alignas(64) RowState {
   uint32_t thr_key;     // exact threshold: key >= thr_key, and on key ==
   uint32_t thr_bound;   //   thr_key only indices <= thr_bound
   uint32_t passes;      // exact select: histogram passes used
-  uint32_t pad1;
+  uint32_t tslots;      // sampled pass: tie-region slots claimed
   uint32_t kmax;        // largest candidate key written by a filter pass
 };
 static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");

@@ -184,6 +184,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     st->status = ST_FILTER;
     st->tau_key = tau;
     st->count = 0;
+    st->ties = 0;
+    st->tslots = 0;
     st->r_sampled = 0;
     st->path = PATH_SAMPLED;
     st->passes = 0;
@@ -194,10 +196,14 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
 // ======================================================================
 // Filter (Prof-K section 3, stage 3; Appendix D "Efficient GPU
 // Implementation"): one streaming pass over the row that keeps every element
-// whose key is >= the threshold, appending its composite to the row's
-// candidate buffer.  The counter keeps counting past the capacity; R is
-// exact whenever it fits, and a wave that meets a full buffer stops early
-// (the row overflows, so only R > capacity matters).
+// whose key is >= the threshold.  The survivors are split in two: those
+// strictly above tau are appended to the row's candidate buffer, those equal
+// to tau are counted exactly and stored in a tie region of the same capacity
+// while it has room.  When at least k survivors lie strictly above tau the
+// ties cannot be among the answer, so ties alone never make a row overflow;
+// otherwise the row needs all of them (see sampled_verdict).  The counters
+// keep counting past the capacity; a wave that meets a full above-tau buffer
+// stops early (the row overflows, so only "more than the capacity" matters).
 //
 // Survivor slots come from a wave ballot and the count of set lanes below
 // each lane (the stable split's "how many earlier elements share my flag",
@@ -216,15 +222,15 @@ constexpr uint32_t FILTER_UNROLL = 4;
 struct Stager {
   uint64_t* stage;   // this wave's LDS slots
   uint32_t fill;     // wave-uniform
-  RowState* st;
-  uint64_t* buf;     // row's candidate buffer
+  uint32_t* ctr;     // the buffer's slot counter
+  uint64_t* buf;     // the buffer
   uint32_t cap;
 
-  // Returns true when the buffer is full (the row overflows).
+  // Returns true when the buffer is full.
   __device__ bool flush() {
     wave_lds_sync();
     uint32_t base = 0;
-    if (lane_id() == 0) base = atomicAdd(&st->count, fill);
+    if (lane_id() == 0) base = atomicAdd(ctr, fill);
     base = __shfl(base, 0, 64);
     for (uint32_t i = lane_id(); i < fill; i += 64) {
       const uint32_t pos = base + i;
@@ -296,6 +302,54 @@ __device__ __forceinline__ bool drain_bits(Stager& sg, const u32x4 (&v)[4], uint
   return full;
 }
 
+// The same drain with the survivors split on the way: is_tie(raw) sends an
+// element to the tie stager tg (while the tie region is not full) and counts
+// it, every other survivor goes to sg.  For sparse survivors, where a
+// per-survivor test is cheaper than a second mask over every element.
+struct SplitOut {
+  bool full;       // sg found its buffer full
+  bool tfull;      // the tie region is full
+  uint32_t ties;   // this lane's ties drained
+};
+
+template <int DT, class IdxF, class CompF, class TieF>
+__device__ __forceinline__ SplitOut drain_split(Stager& sg, Stager& tg, bool tfull,
+                                                const u32x4 (&v)[4], uint32_t bits,
+                                                IdxF&& idx_of, CompF&& comp_of, TieF&& is_tie) {
+  bool full = false;
+  uint32_t ties = 0;
+  uint64_t m = ballot(bits != 0u);
+  while (m) {
+    const bool has = bits != 0u;
+    uint32_t b = 0, raw = 0;
+    bool e = false;
+    if (has) {
+      b = (uint32_t)__builtin_ctz(bits);
+      bits &= bits - 1u;
+      raw = elem4<DT>(v, b);
+      e = is_tie(raw);
+    }
+    ties += e ? 1u : 0u;
+    const uint64_t mg = ballot(has && !e), me = ballot(e);
+    if (mg) {
+      const uint32_t c = (uint32_t)__builtin_popcountll(mg);
+      if (sg.fill + c > STAGE_SLOTS) full = sg.flush() || full;
+      if (has && !e) sg.stage[sg.fill + rank_below(mg)] = comp_of(raw, idx_of(b));
+      sg.fill += c;
+    }
+    if (me && !tfull) {
+      const uint32_t c = (uint32_t)__builtin_popcountll(me);
+      if (tg.fill + c > STAGE_SLOTS) tfull = tg.flush();
+      if (!tfull) {
+        if (e) tg.stage[tg.fill + rank_below(me)] = comp_of(raw, idx_of(b));
+        tg.fill += c;
+      }
+    }
+    m = ballot(bits != 0u);
+  }
+  return SplitOut{full, tfull, ties};
+}
+
 // Native-domain threshold for the fast compare.  kind 0: compare in the value
 // domain; kind 1: compare keys (thresholds above +inf, or a tie cut on index).
 struct Thr {
@@ -341,32 +395,44 @@ __device__ __forceinline__ bool native_pass(uint32_t raw, const Thr& t) {
   else return !(__uint_as_float(raw << 16) < t.f);
 }
 
+// Equal to the threshold value (+0 and -0 are equal, NaN equals nothing).
+template <int DT>
+__device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
+  if constexpr (DT == DT_I32) return (int32_t)raw == t.i;
+  else if constexpr (DT == DT_F32) return __uint_as_float(raw) == t.f;
+  else return __uint_as_float(raw << 16) == t.f;
+}
+
 template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
-    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t B, uint32_t want) {
+    uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t B) {
   using D = Dt<DT>;
   const uint32_t row = blockIdx.y;
   RowState* st = states + row;
-  if (st->status != want) return;
-  const bool sampled = (want == ST_FILTER);
-  const Thr thr = make_thr<DT>(sampled ? st->tau_key : st->thr_key,
-                               sampled ? 0xFFFFFFFFu : st->thr_bound);
+  if (st->status != ST_FILTER) return;
+  const Thr thr = make_thr<DT>(st->tau_key, 0xFFFFFFFFu);
 
   __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
-  __shared__ uint32_t s_fill[FILTER_WAVES];
-  __shared__ uint32_t s_base;
+  __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
+  __shared__ uint32_t s_fill[FILTER_WAVES], s_tfill[FILTER_WAVES], s_ties[FILTER_WAVES];
+  __shared__ uint32_t s_base, s_tbase;
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  Stager sg{s_stage[w], 0u, st, cbuf + (size_t)row * cap, cap};
+  Stager sg{s_stage[w], 0u, &st->count, cbuf + (size_t)row * cap, cap};    // above tau
+  Stager tg{s_tstage[w], 0u, &st->tslots, tbuf + (size_t)row * cap, cap};  // equal to tau
 
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
   const uint64_t maskB = (1ull << B) - 1ull;
   auto comp_of = [&](uint32_t raw, uint32_t idx) -> uint64_t {
     return ((uint64_t)D::key(raw) << B) | (maskB - idx);
   };
-  auto pass_of = [&](uint32_t raw, uint32_t idx) -> bool {
+  auto pass_of = [&](uint32_t raw) -> bool {
     if (thr.kind == 0) return native_pass<DT>(raw, thr);
-    return key_pass(D::key(raw), idx, thr);
+    return D::key(raw) >= thr.key;
+  };
+  auto eq_of = [&](uint32_t raw) -> bool {
+    if (thr.kind == 0) return native_eq<DT>(raw, thr);
+    return D::key(raw) == thr.key;
   };
 
   // Split the row into an unaligned head, 16-byte vectors, and a tail.
@@ -377,57 +443,58 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   const uint32_t tail0 = head + nvec * D::VEC;
   const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)head * D::ES);
 
-  // One 16-byte vector: its elements' predicates, then (rarely) survivors.
-  auto handle_vec = [&](const u32x4& v, uint32_t vi, bool valid) {
-    bool p[D::VEC];
-    bool any = false;
-    const uint32_t e0 = head + vi * D::VEC;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (DT == DT_BF16) {
-        const uint32_t lo = v[q] & 0xFFFFu, hi = v[q] >> 16;
-        p[2 * q] = valid && pass_of(lo, e0 + 2 * q);
-        p[2 * q + 1] = valid && pass_of(hi, e0 + 2 * q + 1);
-        any = any || p[2 * q] || p[2 * q + 1];
-      } else {
-        p[q] = valid && pass_of(v[q], e0 + q);
-        any = any || p[q];
-      }
-    }
-    if (ballot(any) == 0) return;
-#pragma unroll
-    for (int e = 0; e < D::VEC; ++e) {
-      uint32_t raw;
-      if constexpr (DT == DT_BF16) raw = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
-      else raw = v[e];
-      sg.push(p[e], p[e] ? comp_of(raw, e0 + e) : 0ull);
-    }
+  uint32_t ties = 0;      // this lane's elements equal to tau
+  bool full = false;      // the above-tau buffer is full: the row overflows
+  bool tfull = false;     // the tie region is full: ties are only counted
+
+  // One element outside the unrolled loop (all lanes call together).
+  auto push_one = [&](bool p, uint32_t raw, uint32_t idx) {
+    const bool e = p && eq_of(raw);
+    ties += e ? 1u : 0u;
+    const uint64_t c = p ? comp_of(raw, idx) : 0ull;
+    sg.push(p && !e, c);
+    if (!tfull) tg.push(e, c);
   };
 
   // Survivors of one unrolled step: a 32-bit mask per lane, drained by
-  // drain_bits.  A wave that finds the buffer full stops scanning: the row
-  // overflows and goes to the exact route whatever the rest would count.
+  // drain_bits.  A wave that finds the above-tau buffer full stops scanning:
+  // the row overflows and goes to the exact route whatever the rest would
+  // count.  A full tie region only stops the storing of ties.
   constexpr uint32_t SPAN = FILTER_UNROLL * D::VEC;   // elements per lane per step
   static_assert(SPAN <= 32, "one 32-bit survivor mask per lane");
   static_assert(FILTER_UNROLL == 4, "elem4() selects among four vectors");
-  bool full = false;
-  auto drain = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi, uint32_t bits) {
-    const bool f = drain_bits<DT>(
-        sg, v, bits,
-        [&](uint32_t b) {
-          return head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
-        },
-        comp_of);
-    full = full || f;
-  };
-  auto mask_of = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi) -> uint32_t {
-    uint32_t bits = 0;
+  auto step_survivors = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi) {
+    auto idx_of = [&](uint32_t b) {
+      return head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
+    };
+    uint32_t ge = 0;
 #pragma unroll
-    for (uint32_t b = 0; b < SPAN; ++b) {
-      const uint32_t idx = head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
-      bits |= (uint32_t)pass_of(elem4c<DT>(v, b), idx) << b;
+    for (uint32_t b = 0; b < SPAN; ++b) ge |= (uint32_t)pass_of(elem4c<DT>(v, b)) << b;
+    if (ballot(__builtin_popcount(ge) > 3) == 0) {
+      // sparse survivors: test each one for a tie as it is drained
+      const SplitOut o = drain_split<DT>(sg, tg, tfull, v, ge, idx_of, comp_of, eq_of);
+      full = full || o.full;
+      tfull = o.tfull;
+      ties += o.ties;
+      return;
     }
-    return bits;
+    // dense (many ties, or a threshold below most of the row): a tie mask.
+    // The empty asm on the copies keeps these compares inside this rare
+    // branch; otherwise the compiler computes them for every vector of the
+    // hot loop, which costs the bf16 loop a tenth of its speed.
+    u32x4 w[FILTER_UNROLL];
+#pragma unroll
+    for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
+      w[u] = v[u];
+      asm volatile("" : "+v"(w[u]));
+    }
+    uint32_t eq = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < SPAN; ++b) eq |= (uint32_t)eq_of(elem4c<DT>(w, b)) << b;
+    eq &= ge;
+    ties += (uint32_t)__builtin_popcount(eq);
+    full = drain_bits<DT>(sg, v, ge & ~eq, idx_of, comp_of) || full;
+    if (!tfull && ballot(eq != 0u)) tfull = drain_bits<DT>(tg, v, eq, idx_of, comp_of);
   };
 
   // This workgroup's slice of the row's vectors: [vi0, vend), in steps of
@@ -464,7 +531,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
         }
       }
       if (ballot(any != 0u) == 0) continue;
-      drain(v, vi, mask_of(v, vi));
+      step_survivors(v, vi);
       if (full) break;
     }
   } else {
@@ -472,7 +539,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       u32x4 v[FILTER_UNROLL];
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
-      drain(v, vi, mask_of(v, vi));
+      step_survivors(v, vi);
       if (full) break;
     }
   }
@@ -483,8 +550,25 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const size_t wave_first = vi - lane;
     if (wave_first >= vend) break;
     const bool valid = vi < vend;
-    u32x4 v = valid ? vp[vi] : u32x4{0u, 0u, 0u, 0u};
-    handle_vec(v, (uint32_t)vi, valid);
+    const u32x4 v = valid ? vp[vi] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t e0 = head + (uint32_t)vi * D::VEC;
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < D::VEC; ++e) {
+      uint32_t raw;
+      if constexpr (DT == DT_BF16) raw = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
+      else raw = v[e];
+      any = any || (valid && pass_of(raw));
+    }
+    if (ballot(any) != 0) {
+#pragma unroll
+      for (int e = 0; e < D::VEC; ++e) {
+        uint32_t raw;
+        if constexpr (DT == DT_BF16) raw = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
+        else raw = v[e];
+        push_one(valid && pass_of(raw), raw, e0 + e);
+      }
+    }
     vi += stride;
   }
   // Head and tail elements: the first wave of workgroup 0.
@@ -492,42 +576,79 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const uint32_t nt = n - tail0;
     for (uint32_t base = 0; base < head + nt; base += 64) {
       const uint32_t j = base + lane;
-      bool ok = j < head + nt;
+      const bool ok = j < head + nt;
       uint32_t idx = 0, raw = 0;
       if (ok) {
         idx = (j < head) ? j : tail0 + (j - head);
         raw = load_raw<DT>(rowp, idx);
       }
-      const bool p = ok && pass_of(raw, idx);
-      sg.push(p, p ? comp_of(raw, idx) : 0ull);
+      push_one(ok && pass_of(raw), raw, idx);
     }
   }
 
-  // Workgroup flush: one atomic for the whole workgroup.
-  if (lane == 0) s_fill[w] = sg.fill;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t total = 0;
-    for (uint32_t i = 0; i < FILTER_WAVES; ++i) total += s_fill[i];
-    s_base = total ? atomicAdd(&st->count, total) : 0u;
+  // Workgroup flush: one atomic per buffer, and one for the tie count.
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ties += __shfl_xor(ties, o, 64);
+  if (lane == 0) {
+    s_fill[w] = sg.fill;
+    s_tfill[w] = tg.fill;
+    s_ties[w] = ties;
   }
   __syncthreads();
-  uint32_t off = s_base;
-  for (uint32_t i = 0; i < w; ++i) off += s_fill[i];
+  if (tid == 0) {
+    uint32_t total = 0, ttotal = 0, tcount = 0;
+    for (uint32_t i = 0; i < FILTER_WAVES; ++i) {
+      total += s_fill[i];
+      ttotal += s_tfill[i];
+      tcount += s_ties[i];
+    }
+    s_base = total ? atomicAdd(&st->count, total) : 0u;
+    s_tbase = ttotal ? atomicAdd(&st->tslots, ttotal) : 0u;
+    if (tcount) atomicAdd(&st->ties, tcount);
+  }
+  __syncthreads();
+  uint32_t off = s_base, toff = s_tbase;
+  for (uint32_t i = 0; i < w; ++i) {
+    off += s_fill[i];
+    toff += s_tfill[i];
+  }
   for (uint32_t i = lane; i < sg.fill; i += 64) {
     const uint32_t pos = off + i;
     if (pos < cap) sg.buf[pos] = sg.stage[i];
+  }
+  for (uint32_t i = lane; i < tg.fill; i += 64) {
+    const uint32_t pos = toff + i;
+    if (pos < cap) tg.buf[pos] = tg.stage[i];
   }
 }
 
 // ======================================================================
 // Detection (Prof-K section 3, stage 4): R < k is a recall failure, R > M an
-// overflow; either sends the row to the exact path.
+// overflow; either sends the row to the exact path.  With the survivors split
+// at tau (G strictly above, E equal):
+//   G > cap          overflow
+//   G >= k           accepted: the k winners lie among the G, ties unused
+//   G + E < k        recall failure
+//   G + E > cap      the ties needed do not fit: overflow
+//   otherwise        accepted with every tie (all E were stored, E <= cap - G)
 // ======================================================================
+enum : uint32_t { V_FAIL = 0, V_OK = 1, V_OK_TIES = 2 };
+
+__device__ __forceinline__ uint32_t sampled_verdict(uint32_t G, uint32_t E, uint32_t k,
+                                                    uint32_t cap) {
+  if (G > cap) return V_FAIL;
+  if (G >= k) return V_OK;
+  const uint64_t R = (uint64_t)G + E;
+  if (R < k || R > cap) return V_FAIL;
+  return V_OK_TIES;
+}
+
+// Leaves count and ties alone: other workgroups may still be reading them to
+// reach the same verdict (the exact route resets count once its threshold is
+// known).
 __device__ __forceinline__ void start_exact(RowState* st, uint32_t k, uint32_t path) {
   st->status = ST_EXACT;
   st->path = path;
-  st->count = 0;
   st->need = k;
   st->above = 0;
   st->prefix = 0;
@@ -548,9 +669,9 @@ __global__ void k_check(RowState* __restrict__ states, CallState* __restrict__ c
   if (row >= rows) return;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
-  const uint32_t R = st->count;
-  if (R < k || R > cap) {
-    st->r_sampled = R;
+  const uint32_t G = st->count, E = st->ties;
+  if (sampled_verdict(G, E, k, cap) == V_FAIL) {
+    st->r_sampled = G + E;
     start_exact(st, k, PATH_FALLBACK);
     flag_row(cs, flagged, row);
   }
@@ -564,6 +685,7 @@ __global__ void k_setup_exact(RowState* __restrict__ states, CallState* __restri
   start_exact(st, k, PATH_EXACT);
   st->r_sampled = 0;
   st->tau_key = 0;
+  st->ties = 0;
   flagged[row] = row;
   if (row == 0) {
     cs->nflag = rows;
@@ -693,19 +815,8 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   RowState* st = states + row;
   if (st->status != want) return;
-  uint32_t R = st->count;
-  if (want == ST_FILTER) {
-    if (R < k || R > cap) {
-      __syncthreads();
-      if (tid == 0) {
-        st->r_sampled = R;
-        start_exact(st, k, PATH_FALLBACK);
-        flag_row(cs, flagged, row);
-      }
-      return;
-    }
-  }
-  if (R > cap) R = cap;   // the exact route never exceeds the capacity
+  uint32_t R = st->count;   // in [k, cap]: the row passed its check
+  if (R > cap) R = cap;
   const uint32_t KB = W - B;
   const uint32_t lo_key = (want == ST_FILTER) ? st->tau_key : st->thr_key;
   CompSrc src{cbuf + (size_t)row * cap};
@@ -805,10 +916,7 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
     write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
   }
   __syncthreads();
-  if (tid == 0) {
-    if (want == ST_FILTER) st->r_sampled = R;
-    st->status = ST_DONE;
-  }
+  if (tid == 0) st->status = ST_DONE;
   __syncthreads();
 }
 
@@ -842,6 +950,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       st->count = 0;
       st->r_sampled = 0;
       st->tau_key = 0;
+      st->ties = 0;
     }
     return;
   }
@@ -874,6 +983,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
     st->path = PATH_EXACT;
     st->r_sampled = 0;
     st->tau_key = 0;
+    st->ties = 0;
   }
 }
 
@@ -986,8 +1096,9 @@ template <int DT>
 __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
     CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
-    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
-    uint32_t small_k, uint32_t mode, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+    uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
+    uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode, void* __restrict__ out_values,
+    int64_t* __restrict__ out_idx) {
   using D = Dt<DT>;
   __shared__ uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -1006,8 +1117,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
     __syncthreads();
     for (uint32_t r = tid; r < rows; r += blockDim.x) {
-      const uint32_t R = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (R < k || R > cap) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
+      const uint32_t G = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t E = __hip_atomic_load(&states[r].ties, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sampled_verdict(G, E, k, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
     }
     __syncthreads();
     nf = 0;
@@ -1024,21 +1136,30 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         uint32_t slot = 0;   // failed rows below r
         for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
         slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
-        st->r_sampled = st->count;
+        st->r_sampled = st->count + st->ties;
         start_exact(st, k, PATH_FALLBACK);
         flagged[slot] = r;
       }
       continue;
     }
     if (st->status != ST_FILTER) continue;
-    if (small_k) {
-      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
-                     out_idx, r, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
-    } else if (tid == 0) {
-      st->r_sampled = st->count;
-      st->status = ST_SORT;
+    // an accepted row; when it needs the ties, they join its candidates
+    const uint32_t G = st->count, E = st->ties;
+    __syncthreads();   // every thread has read the counts
+    if (sampled_verdict(G, E, k, cap) == V_OK_TIES) {
+      uint64_t* dst = cbuf + (size_t)r * cap + G;
+      const uint64_t* src = tbuf + (size_t)r * cap;
+      for (uint32_t i = tid; i < E; i += blockDim.x) dst[i] = src[i];
+    }
+    if (tid == 0) {
+      st->r_sampled = G + E;
+      if (G < k) st->count = G + E;
+      if (!small_k) st->status = ST_SORT;
     }
     __syncthreads();
+    if (small_k)
+      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
+                     out_idx, r, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
   }
   if (nf == 0) return;                        // the common case: nothing more to do
   if (mode == FIN_SCAN) {
@@ -1229,7 +1350,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         live = st->status == ST_EXACT_READY;
         if (live) {
           thr = make_thr<DT>(st->thr_key, st->thr_bound);
-          sg.st = st;
+          sg.ctr = &st->count;
           sg.buf = cbuf + (size_t)row * cap;
           g = row_geom<DT>(values, n, row);
         }
@@ -1387,7 +1508,7 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   const Plan& p = a.plan;
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.call, a.flagged,
-                     a.ghist, a.cbuf, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
+                     a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
                      a.out_values, a.out_idx);
   return hipGetLastError();
 }
@@ -1423,7 +1544,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
-                  cap, B, (uint32_t)ST_FILTER);
+                  a.aux, cap, B);
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,

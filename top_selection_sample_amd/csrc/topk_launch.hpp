@@ -49,7 +49,7 @@ struct LaunchArgs {
   uint32_t* skeys;
   uint32_t* shist;
   uint64_t* cbuf;
-  uint64_t* aux;
+  uint64_t* aux;     // large k: merge buffer; sampled route: tie region (rows x cap)
   uint64_t seed;
   hipStream_t stream;
 };

@@ -351,8 +351,8 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
 
   p.off_cbuf = off;
   off = align256(off + (size_t)rows * (size_t)p.cap * 8);
-  p.off_aux = off;
-  if (!p.small_k) off = align256(off + (size_t)rows * (size_t)p.cap * 8);
+  p.off_aux = off;   // large k: the merge buffer; sampled route: the tie region first
+  if (!p.small_k || p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.total = off;
   *out = p;
   return 0;
