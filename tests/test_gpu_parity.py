@@ -345,6 +345,42 @@ def test_full_sort_k_equals_n():
     assert_same(gv, gi, x, 50_000, "float32", "k = n")
 
 
+def test_large_k_oversized_bucket():
+    # zeros with a few huge values: the exact route keeps the huge values and
+    # the lowest-index zeros; the zeros share one key far below the largest,
+    # so they land in one bucket too big for one LDS sort and get split on
+    # their index bits
+    n, k = 2 ** 20, 20_000
+    g = workloads.rng(75)
+    x = np.zeros((1, n), dtype=np.float32)
+    x[0, g.choice(n, 100, replace=False)] = (1e30 * (1 + g.random(100))).astype(np.float32)
+    say("large k oversized bucket")
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", "oversized bucket")
+
+
+def test_large_k_two_rows_ties_and_spread():
+    # two rows: one with heavy bf16 ties, one all-equal (every candidate in
+    # one key): both through the bucket sort
+    n, k = 2 ** 20, 9000
+    x = workloads.relu_bf16(2, n, 76)
+    x[1] = x[1, 0] if x[1, 0] != 0 else np.uint16(0x3F80)
+    say("large k ties and all-equal")
+    gv, gi = run_gpu(x, k, "bf16")
+    assert_same(gv, gi, x, k, "bf16", "large k ties")
+
+
+def test_large_k_beyond_bucket_capacity():
+    # a buffer larger than the bucket sort handles: tile sort and merges
+    n, k = 2 ** 21 + 11, 2 ** 20 + 5
+    x = workloads.normal_f32(1, n, 77)
+    say("large k merge path")
+    tss = _tss()
+    assert tss.plan(n, 1, k, "float32")["cap"] > 2 ** 21
+    gv, gi = run_gpu(x, k, "float32")
+    assert_same(gv, gi, x, k, "float32", "merge path")
+
+
 # ------------------------------------------------------------ determinism
 def test_repeat_with_fresh_seeds_is_identical():
     x = workloads.relu_bf16(1, 2 ** 22, 81)

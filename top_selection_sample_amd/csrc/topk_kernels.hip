@@ -219,12 +219,24 @@ constexpr uint32_t FILTER_WAVES = FILTER_THREADS / 64;
 constexpr uint32_t STAGE_SLOTS = 256;
 constexpr uint32_t FILTER_UNROLL = 4;
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t o = __shfl_xor(v, d, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 struct Stager {
   uint64_t* stage;   // this wave's LDS slots
   uint32_t fill;     // wave-uniform
   uint32_t* ctr;     // the buffer's slot counter
   uint64_t* buf;     // the buffer
   uint32_t cap;
+  uint32_t* kmax;    // if set: publish() raises it to the largest key stored
+  uint32_t kshift;   //   (key = comp >> kshift)
+  uint32_t km;       // wave-uniform: largest key flushed since the last publish
 
   // Returns true when the buffer is full.
   __device__ bool flush() {
@@ -232,14 +244,29 @@ struct Stager {
     uint32_t base = 0;
     if (lane_id() == 0) base = atomicAdd(ctr, fill);
     base = __shfl(base, 0, 64);
+    uint32_t m = 0;
     for (uint32_t i = lane_id(); i < fill; i += 64) {
       const uint32_t pos = base + i;
       if (pos < cap) buf[pos] = stage[i];
+      const uint32_t key = (uint32_t)(stage[i] >> kshift);
+      m = key > m ? key : m;
+    }
+    if (kmax) {
+      m = wave_max_u32(m);
+      km = m > km ? m : km;
     }
     wave_lds_sync();
     const bool full = base + fill > cap;
     fill = 0;
     return full;
+  }
+  // One wave's largest key into *kmax (a read first: most waves find it
+  // already larger and skip the contended atomic).
+  __device__ void publish() {
+    if (kmax && km && lane_id() == 0 &&
+        km > __hip_atomic_load(kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(kmax, km);
+    km = 0;
   }
   // All lanes call together.
   __device__ void push(bool p, uint64_t comp) {
@@ -406,7 +433,8 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
 template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
-    uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t B) {
+    uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t B,
+    uint32_t track_kmax) {
   using D = Dt<DT>;
   const uint32_t row = blockIdx.y;
   RowState* st = states + row;
@@ -416,10 +444,13 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
   __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
   __shared__ uint32_t s_fill[FILTER_WAVES], s_tfill[FILTER_WAVES], s_ties[FILTER_WAVES];
-  __shared__ uint32_t s_base, s_tbase;
+  __shared__ uint32_t s_base, s_tbase, s_km;
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  Stager sg{s_stage[w], 0u, &st->count, cbuf + (size_t)row * cap, cap};    // above tau
-  Stager tg{s_tstage[w], 0u, &st->tslots, tbuf + (size_t)row * cap, cap};  // equal to tau
+  if (tid == 0) s_km = 0;
+  // above tau (and, for large k, its largest key: the bucket sort's range)
+  Stager sg{s_stage[w], 0u, &st->count, cbuf + (size_t)row * cap, cap,
+            track_kmax ? &st->kmax : nullptr, B, 0u};
+  Stager tg{s_tstage[w], 0u, &st->tslots, tbuf + (size_t)row * cap, cap, nullptr, B, 0u};  // = tau
 
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
   const uint64_t maskB = (1ull << B) - 1ull;
@@ -612,13 +643,23 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     off += s_fill[i];
     toff += s_tfill[i];
   }
+  uint32_t km = 0;
   for (uint32_t i = lane; i < sg.fill; i += 64) {
     const uint32_t pos = off + i;
     if (pos < cap) sg.buf[pos] = sg.stage[i];
+    const uint32_t key = (uint32_t)(sg.stage[i] >> B);
+    km = key > km ? key : km;
   }
   for (uint32_t i = lane; i < tg.fill; i += 64) {
     const uint32_t pos = toff + i;
     if (pos < cap) tg.buf[pos] = tg.stage[i];
+  }
+  if (track_kmax) {   // one atomic per workgroup
+    km = wave_max_u32(km);
+    km = sg.km > km ? sg.km : km;
+    if (lane == 0 && km) atomicMax(&s_km, km);
+    __syncthreads();
+    if (tid == 0 && s_km) atomicMax(&st->kmax, s_km);
   }
 }
 
@@ -956,8 +997,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
   }
   // large k: scatter the k winners to global memory
   uint64_t* out = cbuf + (size_t)row * cap;
-  if (threadIdx.x == 0) s_misc[4] = 0;
+  if (threadIdx.x == 0) {
+    s_misc[4] = 0;
+    s_misc[5] = 0;
+  }
   __syncthreads();
+  uint32_t km = 0;   // largest winner key
   for (uint32_t i0 = 0; i0 < n; i0 += blockDim.x) {
     const uint32_t i = i0 + threadIdx.x;
     uint64_t c = 0;
@@ -966,6 +1011,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       c = src(i);
       keep = c >= sel.thr;
     }
+    if (keep && (uint32_t)(c >> B) > km) km = (uint32_t)(c >> B);
     const uint64_t m = ballot(keep);
     if (m) {
       const uint32_t first = (uint32_t)__builtin_ctzll(m);
@@ -976,9 +1022,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       if (keep && slot < cap) out[slot] = c;
     }
   }
+  km = wave_max_u32(km);
+  if (lane_id() == 0 && km) atomicMax(&s_misc[5], km);
   __syncthreads();
   if (threadIdx.x == 0) {
     st->count = s_misc[4] < cap ? s_misc[4] : cap;
+    st->thr_key = (uint32_t)(sel.thr >> B);   // every winner key is >= this
+    st->kmax = s_misc[5];
     st->status = ST_SORT;
     st->path = PATH_EXACT;
     st->r_sampled = 0;
@@ -1154,7 +1204,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     if (tid == 0) {
       st->r_sampled = G + E;
       if (G < k) st->count = G + E;
-      if (!small_k) st->status = ST_SORT;
+      if (!small_k) {
+        st->thr_key = st->tau_key;   // every candidate key is >= this
+        st->status = ST_SORT;
+      }
     }
     __syncthreads();
     if (small_k)
@@ -1320,6 +1373,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
           st->thr_key = (uint32_t)(np >> B);
           st->thr_bound = (uint32_t)(maskB - (np & maskB));
           st->count = 0;
+          st->kmax = 0;
           st->status = ST_EXACT_READY;
           atomicSub(&cs->nactive, 1u);
         }
@@ -1331,7 +1385,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
 
   // ---- exact filter: every element >= the exact threshold into the buffer
   {
-    Stager sg{s_cand + (size_t)w * STAGE_SLOTS, 0u, nullptr, nullptr, cap};
+    Stager sg{s_cand + (size_t)w * STAGE_SLOTS, 0u, nullptr, nullptr, cap, nullptr, B, 0u};
     const uint64_t maskB = (1ull << B) - 1ull;
     auto comp = [&](uint32_t raw, uint32_t idx) -> uint64_t {
       return ((uint64_t)D::key(raw) << B) | (maskB - idx);
@@ -1344,6 +1398,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       const uint32_t f = (uint32_t)(it / ipr), c = (uint32_t)(it % ipr);
       if (f != fcur) {
         if (sg.fill) sg.flush();   // to the previous row
+        sg.publish();
         fcur = f;
         const uint32_t row = flagged[f];
         RowState* st = states + row;
@@ -1351,6 +1406,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         if (live) {
           thr = make_thr<DT>(st->thr_key, st->thr_bound);
           sg.ctr = &st->count;
+          sg.kmax = &st->kmax;
           sg.buf = cbuf + (size_t)row * cap;
           g = row_geom<DT>(values, n, row);
         }
@@ -1376,6 +1432,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
     }
     if (sg.fill) sg.flush();
+    sg.publish();
   }
   sync_all();
 
@@ -1491,6 +1548,410 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
     default: hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__); break;         \
   }
 
+// ======================================================================
+// Large k, capacity up to LK_CAP_MAX: bucket sort of the candidates.
+// Composites are unique and every candidate key lies in [lo, kmax] (lo =
+// RowState::thr_key, the threshold the candidates passed; kmax tracked by
+// the filters), so
+//     v = (key - lo) << bl | (low bl bits of the inverted index)
+// (bl = index bits that vary, 2^bl >= n) orders the candidates exactly as
+// their composites do, with no constant bits in between.  Its top 12 bits
+// are the bucket:
+//   k_lk_hist     bucket histogram (one LDS histogram per 4096 candidates)
+//   k_lk_scatter  bucket starts (descending order), then every candidate of
+//                 a bucket that starts below k goes to its bucket in aux
+//   k_lk_sort     one workgroup per 4096 output positions sorts the buckets
+//                 starting there in LDS and writes the winners directly; a
+//                 bucket too large for LDS is split further in the
+//                 workgroup (11-bit digits below the common prefix of its
+//                 smallest and largest value, through global scratch).
+// Workspace lk (u32): [rows][4096] histogram, [rows][4096] fill counters
+// (both zero between calls), [rows][LK_STRIDE] bucket starts by rank
+// (rank r = 4095 - bucket, so starts ascend with r; entry 4096 = the total),
+// [rows][2][LK_MAXWIN] per sort window the first and last rank of the
+// non-empty buckets starting in it (first = ~0: none).
+// ======================================================================
+constexpr uint32_t LK_BITS = 12;
+constexpr uint32_t LK_BINS = 1u << LK_BITS;
+constexpr uint32_t LK_STRIDE = LK_BINS + 4;
+constexpr uint32_t LK_THREADS = 1024;
+constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
+constexpr uint32_t LK_WIN = 4096;               // output positions per sort workgroup
+constexpr uint32_t LK_LCAP = 8192;              // largest range sorted in LDS
+constexpr uint32_t LK_STACK = 256;              // pending oversized ranges per workgroup
+constexpr uint32_t LK_MAXWIN = (uint32_t)(LK_CAP_MAX / LK_WIN);
+static_assert(LK_WORDS_PER_ROW == 2 * LK_BINS + LK_STRIDE + 2 * LK_MAXWIN, "workspace layout");
+static_assert((int64_t)LK_STACK * LK_LCAP >= LK_CAP_MAX,
+              "oversized ranges are disjoint and larger than LK_LCAP, so at most "
+              "LK_CAP_MAX / LK_LCAP of them are ever pending");
+static_assert(LK_LCAP >= 2 * LK_WIN, "a window's small buckets fit one LDS sort");
+
+struct LkDigit {
+  uint32_t B, bl, lo, shift;
+  uint64_t low;
+  // v of a composite, and back
+  __device__ uint64_t compact(uint64_t c) const { return (((c >> B) - lo) << bl) | (c & low); }
+  __device__ uint64_t expand(uint64_t v) const {
+    const uint64_t mask_b = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+    return (((v >> bl) + lo) << B) | (mask_b & ~low) | (v & low);
+  }
+  __device__ uint32_t operator()(uint64_t c) const {   // bucket of a composite
+    const uint64_t d = compact(c) >> shift;
+    return d < LK_BINS ? (uint32_t)d : LK_BINS - 1;   // (always below: key <= kmax)
+  }
+};
+
+__device__ __forceinline__ LkDigit lk_digit_of(const RowState& st, uint32_t B, uint32_t bl) {
+  LkDigit g;
+  g.B = B;
+  g.bl = bl;
+  g.lo = st.thr_key;
+  g.low = (1ull << bl) - 1ull;   // bl <= 32
+  const uint32_t hi = st.kmax > g.lo ? st.kmax : g.lo;
+  const uint64_t vmax = ((uint64_t)(hi - g.lo) << bl) | g.low;
+  const uint32_t tb = vmax ? 64u - (uint32_t)__builtin_clzll(vmax) : 0u;
+  g.shift = tb > LK_BITS ? tb - LK_BITS : 0u;
+  return g;
+}
+
+__global__ __launch_bounds__(LK_THREADS) void k_lk_hist(const RowState* __restrict__ states,
+                                                        const uint64_t* __restrict__ cbuf,
+                                                        uint32_t cap, uint32_t B, uint32_t bl,
+                                                        uint32_t* __restrict__ lk) {
+  __shared__ uint32_t h[LK_BINS];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  const RowState st = states[row];
+  const uint32_t R = st.count < cap ? st.count : cap;
+  const uint32_t base = blockIdx.x * LK_CHUNK;
+  if (st.status != ST_SORT || base >= R) return;
+  const LkDigit g = lk_digit_of(st, B, bl);
+  for (uint32_t i = tid; i < LK_BINS; i += LK_THREADS) h[i] = 0;
+  __syncthreads();
+  const uint64_t* p = cbuf + (size_t)row * cap;
+  uint64_t c[4];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t i = base + j * LK_THREADS + tid;
+    c[j] = i < R ? p[i] : 0ull;
+  }
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j)
+    if (base + j * LK_THREADS + tid < R) atomicAdd(&h[g(c[j])], 1u);
+  __syncthreads();
+  uint32_t* gh = lk + (size_t)row * LK_BINS;
+  for (uint32_t i = tid; i < LK_BINS; i += LK_THREADS)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+__global__ __launch_bounds__(LK_THREADS) void k_lk_scatter(const RowState* __restrict__ states,
+                                                           const uint64_t* __restrict__ cbuf,
+                                                           uint64_t* __restrict__ aux, uint32_t cap,
+                                                           uint32_t k, uint32_t B, uint32_t bl,
+                                                           uint32_t* __restrict__ lk,
+                                                           uint32_t rows) {
+  __shared__ uint32_t s_start[LK_BINS];   // by rank
+  __shared__ uint32_t s_cnt[LK_BINS];     // this workgroup's count, then its base, per rank
+  __shared__ uint32_t s_wsum[LK_THREADS / 64];
+  __shared__ uint32_t s_win[2 * LK_MAXWIN];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+  const RowState st = states[row];
+  const uint32_t R = st.count < cap ? st.count : cap;
+  const uint32_t base = blockIdx.x * LK_CHUNK;
+  if (st.status != ST_SORT || base >= R) return;
+  const LkDigit g = lk_digit_of(st, B, bl);
+  const uint32_t* gh = lk + (size_t)row * LK_BINS;
+  uint32_t* gfill = lk + (size_t)(rows + row) * LK_BINS;
+  uint32_t* gstart = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
+
+  // bucket starts in descending bucket order: thread t owns ranks 4t..4t+3
+  uint32_t hv[4], sum = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    hv[j] = gh[LK_BINS - 1 - (4 * tid + j)];
+    sum += hv[j];
+  }
+  uint32_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, 64);
+    if (lane >= (uint32_t)d) incl += o;
+  }
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  uint32_t run = incl - sum;
+  for (uint32_t i = 0; i < w; ++i) run += s_wsum[i];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    s_start[4 * tid + j] = run;
+    s_cnt[4 * tid + j] = 0;
+    if (blockIdx.x == 0) gstart[4 * tid + j] = run;
+    run += hv[j];
+  }
+  if (blockIdx.x == 0 && tid == LK_THREADS - 1) gstart[LK_BINS] = run;
+  if (blockIdx.x == 0)
+    for (uint32_t i = tid; i < 2 * LK_MAXWIN; i += LK_THREADS) s_win[i] = i < LK_MAXWIN ? ~0u : 0u;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    // each sort window: first and last non-empty bucket starting in it
+    const uint32_t nwin = (k + LK_WIN - 1) / LK_WIN;
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+      const uint32_t rr = 4 * tid + j, b0 = s_start[rr];
+      if (hv[j] && b0 < k) {
+        atomicMin(&s_win[b0 / LK_WIN], rr);
+        atomicMax(&s_win[LK_MAXWIN + b0 / LK_WIN], rr);
+      }
+    }
+    __syncthreads();
+    uint32_t* gwin = lk + (size_t)rows * (2 * LK_BINS + LK_STRIDE) + (size_t)row * 2 * LK_MAXWIN;
+    for (uint32_t i = tid; i < nwin; i += LK_THREADS) {
+      gwin[i] = s_win[i];
+      gwin[LK_MAXWIN + i] = s_win[LK_MAXWIN + i];
+    }
+  }
+
+  // this workgroup's candidates: local rank inside its bucket
+  const uint64_t* p = cbuf + (size_t)row * cap;
+  uint64_t c[4];
+  uint32_t r[4], lr[4];
+  bool need[4];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t i = base + j * LK_THREADS + tid;
+    const bool ok = i < R;
+    c[j] = ok ? p[i] : 0ull;
+    r[j] = ok ? LK_BINS - 1 - g(c[j]) : 0u;
+    need[j] = ok && s_start[r[j]] < k;
+    lr[j] = need[j] ? atomicAdd(&s_cnt[r[j]], 1u) : 0u;
+  }
+  __syncthreads();
+  // one reservation per bucket and workgroup
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t rr = 4 * tid + j;
+    const uint32_t cnt = s_cnt[rr];
+    if (cnt) s_cnt[rr] = atomicAdd(&gfill[rr], cnt);
+  }
+  __syncthreads();
+  uint64_t* a = aux + (size_t)row * cap;   // compacted values, by bucket
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j)
+    if (need[j]) a[s_start[r[j]] + s_cnt[r[j]] + lr[j]] = g.compact(c[j]);
+}
+
+template <int DT>
+__global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
+    const void* __restrict__ values, uint32_t n, const RowState* __restrict__ states,
+    CallState* __restrict__ cs, uint64_t* __restrict__ aux, uint64_t* __restrict__ scratch,
+    uint32_t cap, uint32_t k, uint32_t B, uint32_t bl, uint32_t* __restrict__ lk, uint32_t rows,
+    void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+  __shared__ uint64_t s_a[LK_LCAP];
+  __shared__ uint64_t s_b[LK_LCAP];
+  __shared__ uint32_t s_hist[2048];
+  __shared__ uint32_t s_runs[2 * 2048];
+  __shared__ uint32_t s_frames[3 * LK_STACK];
+  __shared__ uint64_t s_red[32];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_sm[8];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x, nt = LK_THREADS;
+  const uint32_t lane = tid & 63u, w = tid >> 6;
+  if (blockIdx.x == 0) {   // histogram and fill counters: clean for the next call
+    uint32_t* gh = lk + (size_t)row * LK_BINS;
+    uint32_t* gf = lk + (size_t)(rows + row) * LK_BINS;
+    for (uint32_t i = tid; i < LK_BINS; i += nt) {
+      gh[i] = 0;
+      gf[i] = 0;
+    }
+  }
+  const RowState st = states[row];
+  if (st.status != ST_SORT) return;
+  const uint32_t* gs = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
+  const uint32_t* gwin = lk + (size_t)rows * (2 * LK_BINS + LK_STRIDE) + (size_t)row * 2 * LK_MAXWIN;
+  if (blockIdx.x * LK_WIN >= k) return;
+  // the non-empty buckets that start in this window and below k
+  const uint32_t r_lo = gwin[blockIdx.x];
+  if (r_lo == ~0u) return;
+  const uint32_t r_end = gwin[LK_MAXWIN + blockIdx.x] + 1;
+
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  uint64_t* A = aux + (size_t)row * cap;
+  uint64_t* S = scratch + (size_t)row * cap;
+  const LkDigit g = lk_digit_of(st, B, bl);
+
+  // sort [lo, lo + len) of src (compacted values, unique, len <= LK_LCAP) in
+  // LDS and write the output positions below k.  nb > 0: the range is the
+  // buckets of ranks r_last - nb + 1 .. r_last, and the sort's bins are the
+  // bucket and the bits just below the bucket digit; nb = 0: bins from the
+  // range's extremes.
+  auto sort_out = [&](const uint64_t* src, uint32_t lo, uint32_t len, uint32_t nb,
+                      uint32_t r_last) {
+    for (uint32_t i = tid; i < len; i += nt) s_a[i] = src[lo + i];
+    __syncthreads();
+    bool ok;
+    if (nb > 0 && nb <= 2048) {
+      uint32_t sb = 31u - (uint32_t)__builtin_clz(2048u / nb);   // nb << sb <= 2048
+      if (sb > g.shift) sb = g.shift;
+      const uint32_t dsh = g.shift - sb;
+      const uint64_t dbase = (uint64_t)(LK_BINS - 1 - r_last) << sb;
+      ok = block_sort_binned_desc(s_a, len, s_b, s_hist, s_sm, reinterpret_cast<uint32_t*>(s_red),
+                                  [&](uint64_t v) { return (uint32_t)((v >> dsh) - dbase); }, 64u);
+    } else {
+      ok = block_sort_unique_desc(s_a, len, s_b, s_hist, s_sm, s_red, 64u);
+    }
+    if (!ok) {
+      // crowded top bits: bitonic sort instead (zero padding sorts last; a
+      // value of 0 is the range's smallest, so it still lands in place)
+      const uint32_t P = next_pow2(len);
+      for (uint32_t i = len + tid; i < P; i += nt) s_a[i] = 0ull;
+      __syncthreads();
+      block_bitonic_desc(s_a, P);
+    }
+    for (uint32_t i = tid; i < len; i += nt) {
+      const uint32_t pos = lo + i;
+      if (pos < k) {
+        uint32_t idx;
+        const uint32_t bits = winner_bits<DT>(g.expand(s_a[i]), B, rowp, n, &idx);
+        store_winner<DT>(out_values, out_idx, (size_t)row * k + pos, bits, idx);
+      }
+    }
+    __syncthreads();
+  };
+
+  // oversized ranges, split further (frames: lo, len, 1 = data in S)
+  uint32_t sp = 0;   // uniform
+  auto push = [&](uint32_t lo, uint32_t len, uint32_t in_s) {
+    if (sp < LK_STACK) {
+      if (tid == 0) {
+        s_frames[3 * sp] = lo;
+        s_frames[3 * sp + 1] = len;
+        s_frames[3 * sp + 2] = in_s;
+      }
+      ++sp;
+    } else if (tid == 0) {
+      atomicOr(&cs->error, 2u);   // cannot happen: see LK_STACK
+    }
+  };
+
+  const uint32_t a0 = gs[r_lo], e0 = gs[r_end], last = gs[r_end - 1];
+  if (e0 - a0 <= LK_LCAP) {
+    sort_out(A, a0, e0 - a0, r_end - r_lo, r_end - 1);
+  } else {
+    // every bucket but the last starts and ends inside the window
+    if (last > a0) sort_out(A, a0, last - a0, r_end - 1 - r_lo, r_end - 2);
+    if (e0 - last <= LK_LCAP) sort_out(A, last, e0 - last, 1u, r_end - 1);
+    else push(last, e0 - last, 0u);
+  }
+  __syncthreads();
+
+  while (sp > 0) {
+    --sp;
+    const uint32_t lo = s_frames[3 * sp], len = s_frames[3 * sp + 1];
+    const bool in_s = s_frames[3 * sp + 2] != 0;
+    __syncthreads();
+    const uint64_t* src = in_s ? S : A;
+    uint64_t* dst = in_s ? A : S;
+    // 11-bit digit just below the common prefix of the range's extremes
+    uint64_t mn = ~0ull, mx = 0ull;
+    for (uint32_t i = tid; i < len; i += nt) {
+      const uint64_t v = src[lo + i];
+      mn = v < mn ? v : mn;
+      mx = v > mx ? v : mx;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint64_t x = __shfl_xor(mn, d, 64), y = __shfl_xor(mx, d, 64);
+      mn = x < mn ? x : mn;
+      mx = y > mx ? y : mx;
+    }
+    if (lane == 0) {
+      s_red[w] = mn;
+      s_red[16 + w] = mx;
+    }
+    for (uint32_t i = tid; i < 2048; i += nt) s_hist[i] = 0;
+    __syncthreads();
+    mn = s_red[0];
+    mx = s_red[16];
+    for (uint32_t j = 1; j < nt / 64; ++j) {
+      mn = s_red[j] < mn ? s_red[j] : mn;
+      mx = s_red[16 + j] > mx ? s_red[16 + j] : mx;
+    }
+    const uint32_t top = 63u - (uint32_t)__builtin_clzll(mn ^ mx);   // len >= 2: unique values differ
+    const uint32_t sh = top >= 10 ? top - 10 : 0u;
+    auto digit = [&](uint64_t v) { return (uint32_t)(v >> sh) & 2047u; };
+    for (uint32_t i = tid; i < len; i += nt) atomicAdd(&s_hist[digit(src[lo + i])], 1u);
+    __syncthreads();
+    if (w == 0) {   // exclusive scan from digit 2047 down; lane owns 32 digits
+      uint32_t loc = 0;
+      for (uint32_t j = 0; j < 32; ++j) loc += s_hist[2047 - (lane * 32 + j)];
+      uint32_t inc = loc;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, 64);
+        if (lane >= (uint32_t)d) inc += o;
+      }
+      uint32_t run = inc - loc;
+      for (uint32_t j = 0; j < 32; ++j) {
+        const uint32_t b = 2047 - (lane * 32 + j);
+        const uint32_t h = s_hist[b];
+        s_hist[b] = run;
+        run += h;
+      }
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < len; i += nt) {
+      const uint64_t v = src[lo + i];
+      dst[lo + atomicAdd(&s_hist[digit(v)], 1u)] = v;
+    }
+    __syncthreads();
+    // s_hist[b] is now the end of digit b's range; pack consecutive digits
+    // into runs of at most LK_LCAP (one thread; this path is rare)
+    if (tid == 0) {
+      uint32_t nr = 0, cur = 0, cl = 0;
+      for (int b = 2047; b >= 0; --b) {
+        const uint32_t beg = (b == 2047) ? 0u : s_hist[b + 1];
+        const uint32_t end = s_hist[b];
+        if (end == beg) continue;
+        if (lo + beg >= k) break;
+        const uint32_t h = end - beg;
+        if (h > LK_LCAP) {
+          if (cl) {
+            s_runs[2 * nr] = cur;
+            s_runs[2 * nr + 1] = cl;
+            ++nr;
+            cl = 0;
+          }
+          s_runs[2 * nr] = beg;
+          s_runs[2 * nr + 1] = h | 0x80000000u;
+          ++nr;
+          continue;
+        }
+        if (cl + h > LK_LCAP) {
+          s_runs[2 * nr] = cur;
+          s_runs[2 * nr + 1] = cl;
+          ++nr;
+          cl = 0;
+        }
+        if (cl == 0) cur = beg;
+        cl += h;
+      }
+      if (cl) {
+        s_runs[2 * nr] = cur;
+        s_runs[2 * nr + 1] = cl;
+        ++nr;
+      }
+      s_misc[2] = nr;
+    }
+    __syncthreads();
+    const uint32_t nr = s_misc[2];
+    for (uint32_t q = 0; q < nr; ++q) {
+      const uint32_t rs = s_runs[2 * q], rl = s_runs[2 * q + 1];
+      if (rl & 0x80000000u) push(lo + rs, rl & 0x7FFFFFFFu, in_s ? 0u : 1u);
+      else sort_out(dst, lo + rs, rl, 0u, 0u);
+      __syncthreads();
+    }
+  }
+}
+
 template <int DT>
 static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t mode) {
   // one workgroup per compute unit (cached per device)
@@ -1544,7 +2005,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
-                  a.aux, cap, B);
+                  a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1));
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
@@ -1573,8 +2034,21 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (e != hipSuccess) return e;
     mark(stage, 0);
   }
-  if (!p.small_k) {
-    // every row now holds R in [k, cap] candidates: sort them, keep k
+  if (!p.small_k && p.cap <= LK_CAP_MAX) {
+    // every row now holds R in [k, cap] candidates: bucket sort, keep k
+    mark(STAGE_SORT, 1);
+    uint32_t bl = 0;   // index bits that vary: 2^bl >= n
+    while (bl < 32 && (1ull << bl) < (uint64_t)n) ++bl;
+    const dim3 hg((cap + LK_CHUNK - 1) / LK_CHUNK, rows);
+    hipLaunchKernelGGL(k_lk_hist, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, cap, B, bl, a.lk);
+    hipLaunchKernelGGL(k_lk_scatter, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, a.aux, cap, k,
+                       B, bl, a.lk, rows);
+    const dim3 sgr((k + LK_WIN - 1) / LK_WIN, rows);
+    TK_DISPATCH(dt, k_lk_sort, sgr, dim3(LK_THREADS), 0, s, a.values, n, a.states, a.call, a.aux,
+                a.cbuf, cap, k, B, bl, a.lk, rows, a.out_values, a.out_idx);
+    mark(STAGE_SORT, 0);
+  } else if (!p.small_k) {
+    // capacities beyond the bucket sort's: tile sort and pairwise merges
     mark(STAGE_SORT, 1);
     const dim3 tg((cap + SORT_TILE - 1) / SORT_TILE, rows);
     hipLaunchKernelGGL(k_tile_sort, tg, dim3(SEL_THREADS), 0, s, a.states, a.cbuf, cap);

@@ -13,6 +13,8 @@ struct CallState;
 enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
 
 constexpr int64_t KSMALL = 4096;            // largest k sorted inside one workgroup
+constexpr int64_t LK_CAP_MAX = int64_t(1) << 21;  // large k: bucket sort up to this capacity
+constexpr size_t LK_WORDS_PER_ROW = 4096 + 4096 + 4100 + 2 * 512;   // its workspace (u32)
 constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workgroup
 
 struct Plan {
@@ -25,7 +27,7 @@ struct Plan {
   uint32_t filter_bpr = 1, hist_bpr = 1;
   double p_recall = 0, p_overflow = 0;
   // workspace layout (byte offsets)
-  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, total = 0;
+  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lk = 0, total = 0;
 };
 
 // Pipeline stages that can be bracketed by timing events.
@@ -50,6 +52,7 @@ struct LaunchArgs {
   uint32_t* shist;
   uint64_t* cbuf;
   uint64_t* aux;     // large k: merge buffer; sampled route: tie region (rows x cap)
+  uint32_t* lk;      // large-k bucket sort: histograms, fill counters, bucket starts
   uint64_t seed;
   hipStream_t stream;
 };

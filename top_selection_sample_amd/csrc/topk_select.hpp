@@ -269,16 +269,87 @@ __device__ __forceinline__ void block_bitonic_desc(uint64_t* s, uint32_t P) {
 }
 
 // ---------------------------------------------------------------- LDS sort
-// Sort cnt unique 64-bit values s[0..cnt) into descending order, in LDS.
-// One counting-sort pass on the 11 bits just below the common prefix of the
-// smallest and largest value (digits taken from the top, so bucket order is
-// value order), then each element's place inside its bucket is the number of
-// larger values in that bucket.  O(cnt) LDS passes plus the sum of squared
-// bucket sizes, which is small unless the values crowd into one bucket.
-// tmp: cnt values of scratch; hist: 2048 words; misc: 8 words; red: 32
-// words.  Every thread of the workgroup calls it.  Returns false, with s
-// untouched, when the fullest bucket holds more than max_bucket values (many
-// ties in the top bits); the caller then sorts another way.
+// Exclusive scan of hist[0..2048) from bin 2047 down: on return hist[b] is
+// the number of elements in the bins above b.  wsum: 16 words of scratch.
+// Every thread of the workgroup calls it.
+__device__ __forceinline__ void block_scan_desc_2048(uint32_t* hist, uint32_t* wsum) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
+  const uint32_t per = 2048u / nt;   // bins per thread, in descending order
+  uint32_t loc = 0;
+  for (uint32_t j = 0; j < per; ++j) loc += hist[2047u - (tid * per + j)];
+  uint32_t incl = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, 64);
+    if (lane >= (uint32_t)d) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  uint32_t run = incl - loc;
+  for (uint32_t i = 0; i < w; ++i) run += wsum[i];
+  for (uint32_t j = 0; j < per; ++j) {
+    const uint32_t b = 2047u - (tid * per + j);
+    const uint32_t h = hist[b];
+    hist[b] = run;
+    run += h;
+  }
+  __syncthreads();
+}
+
+// Sort cnt unique 64-bit values s[0..cnt) into descending order, in LDS,
+// given digit(v) in [0, 2048) that never decreases as v grows: a counting
+// sort on the digit, then each element's place inside its bin is the number
+// of larger values in that bin.  O(cnt) LDS passes plus the sum of squared
+// bin sizes.  tmp: cnt values of scratch; hist: 2048 words; misc: 8 words;
+// wsum: 16 words.  Every thread of the workgroup calls it.  Returns false,
+// with s untouched, when the fullest bin holds more than max_bin values; the
+// caller then sorts another way.
+template <class Digit>
+__device__ __forceinline__ bool block_sort_binned_desc(uint64_t* s, uint32_t cnt, uint64_t* tmp,
+                                                       uint32_t* hist, uint32_t* misc,
+                                                       uint32_t* wsum, Digit&& digit,
+                                                       uint32_t max_bin) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  for (uint32_t i = tid; i < 2048; i += nt) hist[i] = 0;
+  if (tid == 0) misc[0] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < cnt; i += nt) atomicAdd(&hist[digit(s[i])], 1u);
+  __syncthreads();
+  {
+    uint32_t big = 0;
+    for (uint32_t i = tid; i < 2048; i += nt) big = hist[i] > big ? hist[i] : big;
+    if (big > max_bin) atomicMax(&misc[0], big);
+  }
+  __syncthreads();
+  if (misc[0] > max_bin) {
+    __syncthreads();
+    return false;
+  }
+  block_scan_desc_2048(hist, wsum);   // hist[b] = start of bin b (a cursor below)
+  // scatter into bins (order inside a bin arbitrary for now)
+  for (uint32_t i = tid; i < cnt; i += nt) {
+    const uint64_t v = s[i];
+    tmp[atomicAdd(&hist[digit(v)], 1u)] = v;
+  }
+  __syncthreads();
+  // hist[b] is now the end of bin b; its start is the end of the bin above
+  // it (b + 1), or 0 for the top bin
+  for (uint32_t p = tid; p < cnt; p += nt) {
+    const uint64_t v = tmp[p];
+    const uint32_t b = digit(v);
+    const uint32_t end = hist[b];
+    const uint32_t beg = (b == 2047) ? 0u : hist[b + 1];
+    uint32_t r = 0;
+    for (uint32_t q = beg; q < end; ++q) r += (tmp[q] > v) ? 1u : 0u;
+    s[beg + r] = v;
+  }
+  __syncthreads();
+  return true;
+}
+
+// The same with the digit taken as the 11 bits just below the common prefix
+// of the smallest and largest value (digits from the top, so bin order is
+// value order).  red: 32 words of scratch.
 __device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt, uint64_t* tmp,
                                                        uint32_t* hist, uint32_t* misc,
                                                        uint64_t* red, uint32_t max_bucket) {
@@ -287,7 +358,6 @@ __device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt
     __syncthreads();
     return true;
   }
-  // smallest and largest
   uint64_t mn = ~0ull, mx = 0ull;
   for (uint32_t i = tid; i < cnt; i += nt) {
     const uint64_t v = s[i];
@@ -304,7 +374,6 @@ __device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt
     red[w] = mn;
     red[16 + w] = mx;
   }
-  for (uint32_t i = tid; i < 2048; i += nt) hist[i] = 0;
   __syncthreads();
   mn = red[0];
   mx = red[16];
@@ -312,63 +381,13 @@ __device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt
     mn = red[j] < mn ? red[j] : mn;
     mx = red[16 + j] > mx ? red[16 + j] : mx;
   }
+  __syncthreads();   // red is reused as scan scratch below
   const uint64_t diff = mn ^ mx;
   const uint32_t top = 63u - (uint32_t)__builtin_clzll(diff);   // diff != 0: values unique
   const uint32_t shift = top >= 10 ? top - 10 : 0u;
-  auto digit = [&](uint64_t v) { return (uint32_t)(v >> shift) & 2047u; };
-  for (uint32_t i = tid; i < cnt; i += nt) atomicAdd(&hist[digit(s[i])], 1u);
-  if (tid == 0) misc[0] = 0;
-  __syncthreads();
-  {
-    uint32_t big = 0;
-    for (uint32_t i = tid; i < 2048; i += nt) big = hist[i] > big ? hist[i] : big;
-    if (big > max_bucket) atomicMax(&misc[0], big);
-  }
-  __syncthreads();
-  if (misc[0] > max_bucket) {
-    __syncthreads();
-    return false;
-  }
-  // exclusive scan from bucket 2047 down: start of each bucket in the output
-  // (one wave; each lane owns 32 buckets)
-  if (w == 0) {
-    uint32_t loc = 0;
-    for (uint32_t j = 0; j < 32; ++j) loc += hist[2047 - (lane * 32 + j)];
-    uint32_t incl = loc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t v = __shfl_up(incl, d, 64);
-      if (lane >= (uint32_t)d) incl += v;
-    }
-    uint32_t run = incl - loc;
-    for (uint32_t j = 0; j < 32; ++j) {
-      const uint32_t b = 2047 - (lane * 32 + j);
-      const uint32_t h = hist[b];
-      hist[b] = run;   // now the bucket's start (used as a cursor below)
-      run += h;
-    }
-  }
-  __syncthreads();
-  // scatter into buckets (order inside a bucket arbitrary for now)
-  for (uint32_t i = tid; i < cnt; i += nt) {
-    const uint64_t v = s[i];
-    const uint32_t p = atomicAdd(&hist[digit(v)], 1u);
-    tmp[p] = v;
-  }
-  __syncthreads();
-  // hist[b] is now the end of bucket b; its start is the end of the bucket
-  // above it (b + 1), or 0 for the top bucket
-  for (uint32_t p = tid; p < cnt; p += nt) {
-    const uint64_t v = tmp[p];
-    const uint32_t b = digit(v);
-    const uint32_t end = hist[b];
-    const uint32_t beg = (b == 2047) ? 0u : hist[b + 1];
-    uint32_t r = 0;
-    for (uint32_t q = beg; q < end; ++q) r += (tmp[q] > v) ? 1u : 0u;
-    s[beg + r] = v;
-  }
-  __syncthreads();
-  return true;
+  return block_sort_binned_desc(
+      s, cnt, tmp, hist, misc, reinterpret_cast<uint32_t*>(red),
+      [&](uint64_t v) { return (uint32_t)(v >> shift) & 2047u; }, max_bucket);
 }
 
 // Bitonic sort of 4096 values into descending order by 1024 threads, four
