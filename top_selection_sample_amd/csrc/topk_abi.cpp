@@ -73,7 +73,7 @@ std::map<uintptr_t, uint64_t> g_ws_layout;
 uint64_t layout_signature(const tk::Plan& p) {
   uint64_t h = 0x9E3779B97F4A7C15ull;
   const uint64_t parts[] = {p.total, p.off_states, p.off_call, p.off_flag, p.off_ghist,
-                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux, p.off_lk,
+                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux, p.off_lk, p.off_rctr,
                             (uint64_t)p.rows};
   for (uint64_t v : parts) {
     h ^= v + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
@@ -241,6 +241,7 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     a.cbuf = reinterpret_cast<uint64_t*>(ws + p.off_cbuf);
     a.aux = reinterpret_cast<uint64_t*>(ws + p.off_aux);
     a.lk = reinterpret_cast<uint32_t*>(ws + p.off_lk);
+    a.rctr = reinterpret_cast<tk::RowCtr*>(ws + p.off_rctr);
     const uint64_t ctr = g_calls.fetch_add(1, std::memory_order_relaxed);
     a.seed = (params && params->use_seed) ? params->seed
                                           : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));

@@ -38,7 +38,7 @@ struct alignas(64) RowState {
   uint32_t tau_key;     // sampled threshold key (t-th largest sampled key)
   uint32_t count;       // candidates counted by the current filter pass (sampled
                         //   pass: elements strictly above tau)
-  uint32_t ties;        // sampled pass: elements equal to tau (exact count)
+  uint32_t ties;        // sampled pass: elements equal to tau (published copy)
   uint32_t r_sampled;   // survivors of the sampled pass
   uint32_t path;        // PATH_*
   uint32_t need;        // exact select: rank wanted inside the prefix bucket
@@ -48,10 +48,24 @@ struct alignas(64) RowState {
   uint32_t thr_key;     // exact threshold: key >= thr_key, and on key ==
   uint32_t thr_bound;   //   thr_key only indices <= thr_bound
   uint32_t passes;      // exact select: histogram passes used
-  uint32_t tslots;      // sampled pass: tie-region slots claimed
+  uint32_t pad1;
   uint32_t kmax;        // largest candidate key written by a filter pass
 };
 static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");
+
+// Counters that every filter workgroup updates once at its end, each on a
+// 128-byte line of its own: atomics on one line serialise, and four of them
+// per workgroup on the row's state line measured about 12 us slower over
+// 512 workgroups than one.
+struct alignas(128) RowCtr {
+  uint32_t ties;        // elements equal to tau (exact count)
+  uint32_t pad0[31];
+  uint32_t tslots;      // tie-region slots claimed
+  uint32_t pad1[31];
+  uint32_t kmax;        // largest key above tau (large k only)
+  uint32_t pad2[31];
+};
+static_assert(sizeof(RowCtr) == 384, "three 128-byte lines");
 
 // Per-call record shared by all rows: the rows sent to the exact route.
 // Zero between calls (the exact-route kernel clears it when it is done).

@@ -112,7 +112,8 @@ constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
                                                      uint32_t SP, uint32_t t, uint32_t KB,
                                                      uint32_t* __restrict__ shist,
-                                                     RowState* __restrict__ states) {
+                                                     RowState* __restrict__ states,
+                                                     RowCtr* __restrict__ rctr) {
   __shared__ uint32_t s_hist[SH_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
@@ -185,8 +186,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     st->tau_key = tau;
     st->count = 0;
     st->ties = 0;
-    st->tslots = 0;
     st->r_sampled = 0;
+    RowCtr* rc = rctr + row;
+    rc->ties = 0;
+    rc->tslots = 0;
+    rc->kmax = 0;
     st->path = PATH_SAMPLED;
     st->passes = 0;
     st->kmax = 0;
@@ -279,13 +283,15 @@ struct Stager {
   }
 };
 
-// Element b (0 .. 4 * VEC - 1) of four 16-byte vectors as raw bits; b may
+// Element b (0 .. NV * VEC - 1) of NV 16-byte vectors as raw bits; b may
 // differ between lanes (a select chain, no indexed register access).
-template <int DT>
-__device__ __forceinline__ uint32_t elem4(const u32x4 (&v)[4], uint32_t b) {
+template <int DT, int NV>
+__device__ __forceinline__ uint32_t elemv(const u32x4 (&v)[NV], uint32_t b) {
   using D = Dt<DT>;
   const uint32_t u = b / D::VEC, e = b % D::VEC;
-  const u32x4 w = u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3];
+  u32x4 w = v[0];
+#pragma unroll
+  for (int j = 1; j < NV; ++j) w = (u == (uint32_t)j) ? v[j] : w;
   if constexpr (DT == DT_BF16) {
     const uint32_t q = e >> 1;
     const uint32_t x = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
@@ -296,8 +302,8 @@ __device__ __forceinline__ uint32_t elem4(const u32x4 (&v)[4], uint32_t b) {
 }
 
 // The same with b known at compile time (unrolled loops).
-template <int DT>
-__device__ __forceinline__ uint32_t elem4c(const u32x4 (&v)[4], uint32_t b) {
+template <int DT, int NV>
+__device__ __forceinline__ uint32_t elemvc(const u32x4 (&v)[NV], uint32_t b) {
   using D = Dt<DT>;
   const uint32_t u = b / D::VEC, e = b % D::VEC;
   if constexpr (DT == DT_BF16) return (e & 1u) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu);
@@ -309,9 +315,9 @@ __device__ __forceinline__ uint32_t elem4c(const u32x4 (&v)[4], uint32_t b) {
 // below, as in push), so a lane with one survivor costs one round whatever
 // the element's position.  idx_of(b) is the index of element b, comp_of
 // builds its composite.  All lanes call together; returns true when a flush
-// found the row's buffer full.
-template <int DT, class IdxF, class CompF>
-__device__ __forceinline__ bool drain_bits(Stager& sg, const u32x4 (&v)[4], uint32_t bits,
+// found the buffer full.
+template <int DT, int NV, class IdxF, class CompF>
+__device__ __forceinline__ bool drain_bits(Stager& sg, const u32x4 (&v)[NV], uint32_t bits,
                                            IdxF&& idx_of, CompF&& comp_of) {
   bool full = false;
   uint64_t m = ballot(bits != 0u);
@@ -321,7 +327,7 @@ __device__ __forceinline__ bool drain_bits(Stager& sg, const u32x4 (&v)[4], uint
     if (bits) {
       const uint32_t b = (uint32_t)__builtin_ctz(bits);
       bits &= bits - 1u;
-      sg.stage[sg.fill + rank_below(m)] = comp_of(elem4<DT>(v, b), idx_of(b));
+      sg.stage[sg.fill + rank_below(m)] = comp_of(elemv<DT, NV>(v, b), idx_of(b));
     }
     sg.fill += c;
     m = ballot(bits != 0u);
@@ -339,9 +345,9 @@ struct SplitOut {
   uint32_t ties;   // this lane's ties drained
 };
 
-template <int DT, class IdxF, class CompF, class TieF>
+template <int DT, int NV, class IdxF, class CompF, class TieF>
 __device__ __forceinline__ SplitOut drain_split(Stager& sg, Stager& tg, bool tfull,
-                                                const u32x4 (&v)[4], uint32_t bits,
+                                                const u32x4 (&v)[NV], uint32_t bits,
                                                 IdxF&& idx_of, CompF&& comp_of, TieF&& is_tie) {
   bool full = false;
   uint32_t ties = 0;
@@ -353,7 +359,7 @@ __device__ __forceinline__ SplitOut drain_split(Stager& sg, Stager& tg, bool tfu
     if (has) {
       b = (uint32_t)__builtin_ctz(bits);
       bits &= bits - 1u;
-      raw = elem4<DT>(v, b);
+      raw = elemv<DT, NV>(v, b);
       e = is_tie(raw);
     }
     ties += e ? 1u : 0u;
@@ -433,8 +439,8 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
 template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
-    uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t B,
-    uint32_t track_kmax) {
+    RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf,
+    uint32_t cap, uint32_t B, uint32_t track_kmax) {
   using D = Dt<DT>;
   const uint32_t row = blockIdx.y;
   RowState* st = states + row;
@@ -447,10 +453,11 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   __shared__ uint32_t s_base, s_tbase, s_km;
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
   if (tid == 0) s_km = 0;
+  RowCtr* rc = rctr + row;
   // above tau (and, for large k, its largest key: the bucket sort's range)
-  Stager sg{s_stage[w], 0u, &st->count, cbuf + (size_t)row * cap, cap,
-            track_kmax ? &st->kmax : nullptr, B, 0u};
-  Stager tg{s_tstage[w], 0u, &st->tslots, tbuf + (size_t)row * cap, cap, nullptr, B, 0u};  // = tau
+  Stager sg{s_stage[w], 0u, &st->count, cbuf + (size_t)row * cap, cap, nullptr, B, 0u};
+  Stager tg{s_tstage[w], 0u, &rc->tslots, tbuf + (size_t)row * cap, cap, nullptr, B, 0u};  // = tau
+  if (track_kmax) sg.kmax = &rc->kmax;
 
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
   const uint64_t maskB = (1ull << B) - 1ull;
@@ -487,45 +494,40 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     if (!tfull) tg.push(e, c);
   };
 
-  // Survivors of one unrolled step: a 32-bit mask per lane, drained by
-  // drain_bits.  A wave that finds the above-tau buffer full stops scanning:
-  // the row overflows and goes to the exact route whatever the rest would
-  // count.  A full tie region only stops the storing of ties.
-  constexpr uint32_t SPAN = FILTER_UNROLL * D::VEC;   // elements per lane per step
-  static_assert(SPAN <= 32, "one 32-bit survivor mask per lane");
-  static_assert(FILTER_UNROLL == 4, "elem4() selects among four vectors");
-  auto step_survivors = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vi) {
-    auto idx_of = [&](uint32_t b) {
-      return head + (uint32_t)(vi + (b / D::VEC) * FILTER_THREADS) * D::VEC + b % D::VEC;
-    };
+  // Survivors of one 16-byte vector (VEC elements per lane, a bit each),
+  // drained by drain_split or drain_bits.  A wave that finds the above-tau
+  // buffer full stops scanning: the row overflows and goes to the exact route
+  // whatever the rest would count.  A full tie region only stops the storing
+  // of ties.  Per vector rather than per unrolled step: with many survivors
+  // (bf16 at large k: most 2048-element steps hold one) the masks and drains
+  // then cover 8 elements instead of 32.
+  auto vec_survivors = [&](const u32x4& v0, size_t vi_lane) {
+    const u32x4 v[1] = {v0};
+    auto idx_of = [&](uint32_t b) { return head + (uint32_t)vi_lane * D::VEC + b; };
     uint32_t ge = 0;
 #pragma unroll
-    for (uint32_t b = 0; b < SPAN; ++b) ge |= (uint32_t)pass_of(elem4c<DT>(v, b)) << b;
-    if (ballot(__builtin_popcount(ge) > 3) == 0) {
+    for (uint32_t b = 0; b < D::VEC; ++b) ge |= (uint32_t)pass_of(elemvc<DT, 1>(v, b)) << b;
+    if (ballot(__builtin_popcount(ge) > D::VEC / 2) == 0) {
       // sparse survivors: test each one for a tie as it is drained
-      const SplitOut o = drain_split<DT>(sg, tg, tfull, v, ge, idx_of, comp_of, eq_of);
+      const SplitOut o = drain_split<DT, 1>(sg, tg, tfull, v, ge, idx_of, comp_of, eq_of);
       full = full || o.full;
       tfull = o.tfull;
       ties += o.ties;
       return;
     }
     // dense (many ties, or a threshold below most of the row): a tie mask.
-    // The empty asm on the copies keeps these compares inside this rare
+    // The empty asm on the copy keeps these compares inside this rare
     // branch; otherwise the compiler computes them for every vector of the
-    // hot loop, which costs the bf16 loop a tenth of its speed.
-    u32x4 w[FILTER_UNROLL];
-#pragma unroll
-    for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
-      w[u] = v[u];
-      asm volatile("" : "+v"(w[u]));
-    }
+    // hot loop.
+    u32x4 w[1] = {v0};
+    asm volatile("" : "+v"(w[0]));
     uint32_t eq = 0;
 #pragma unroll
-    for (uint32_t b = 0; b < SPAN; ++b) eq |= (uint32_t)eq_of(elem4c<DT>(w, b)) << b;
+    for (uint32_t b = 0; b < D::VEC; ++b) eq |= (uint32_t)eq_of(elemvc<DT, 1>(w, b)) << b;
     eq &= ge;
     ties += (uint32_t)__builtin_popcount(eq);
-    full = drain_bits<DT>(sg, v, ge & ~eq, idx_of, comp_of) || full;
-    if (!tfull && ballot(eq != 0u)) tfull = drain_bits<DT>(tg, v, eq, idx_of, comp_of);
+    full = drain_bits<DT, 1>(sg, v, ge & ~eq, idx_of, comp_of) || full;
+    if (!tfull && ballot(eq != 0u)) tfull = drain_bits<DT, 1>(tg, v, eq, idx_of, comp_of);
   };
 
   // This workgroup's slice of the row's vectors: [vi0, vend), in steps of
@@ -542,15 +544,33 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // the same trip count (the ballots and the staging counter need that).
   // With a plain threshold the loop only ORs native compares and skips the
   // vectors of a wave that has no survivor.
+  // The loads of the next step are issued before the current step is
+  // examined, so a wave that is draining survivors still has a step's worth
+  // of loads in flight.
+  auto step_ok = [&](size_t at) { return (at - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; };
   if (thr.kind == 0) {
-    for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; vi += FILTER_UNROLL * stride) {
-      u32x4 v[FILTER_UNROLL];
+    u32x4 nxt[FILTER_UNROLL];
+    bool more = step_ok(vi);
+    if (more) {
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
-        v[u] = __builtin_nontemporal_load(vp + vi + u * stride);
-      uint32_t any = 0;
+        nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+    }
+    while (more) {
+      u32x4 v[FILTER_UNROLL];
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = nxt[u];
+      const size_t vc = vi;
+      vi += FILTER_UNROLL * stride;
+      more = step_ok(vi);
+      if (more) {
+#pragma unroll
+        for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+          nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+      }
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
+        uint32_t any = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if constexpr (DT == DT_BF16) {
@@ -560,9 +580,8 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
             any |= (uint32_t)native_pass<DT>(v[u][q], thr);
           }
         }
+        if (ballot(any != 0u) != 0) vec_survivors(v[u], vc + u * stride);
       }
-      if (ballot(any != 0u) == 0) continue;
-      step_survivors(v, vi);
       if (full) break;
     }
   } else {
@@ -570,7 +589,8 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       u32x4 v[FILTER_UNROLL];
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
-      step_survivors(v, vi);
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) vec_survivors(v[u], vi + u * stride);
       if (full) break;
     }
   }
@@ -634,8 +654,8 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       tcount += s_ties[i];
     }
     s_base = total ? atomicAdd(&st->count, total) : 0u;
-    s_tbase = ttotal ? atomicAdd(&st->tslots, ttotal) : 0u;
-    if (tcount) atomicAdd(&st->ties, tcount);
+    s_tbase = ttotal ? atomicAdd(&rc->tslots, ttotal) : 0u;
+    if (tcount) atomicAdd(&rc->ties, tcount);
   }
   __syncthreads();
   uint32_t off = s_base, toff = s_tbase;
@@ -659,7 +679,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     km = sg.km > km ? sg.km : km;
     if (lane == 0 && km) atomicMax(&s_km, km);
     __syncthreads();
-    if (tid == 0 && s_km) atomicMax(&st->kmax, s_km);
+    if (tid == 0 && s_km) atomicMax(&rc->kmax, s_km);
   }
 }
 
@@ -704,15 +724,17 @@ __device__ __forceinline__ void flag_row(CallState* cs, uint32_t* flagged, uint3
   flagged[slot] = row;
 }
 
-__global__ void k_check(RowState* __restrict__ states, CallState* __restrict__ cs,
-                        uint32_t* __restrict__ flagged, uint32_t rows, uint32_t k, uint32_t cap) {
+__global__ void k_check(RowState* __restrict__ states, const RowCtr* __restrict__ rctr,
+                        CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t rows,
+                        uint32_t k, uint32_t cap) {
   const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
-  const uint32_t G = st->count, E = st->ties;
+  const uint32_t G = st->count, E = rctr[row].ties;
   if (sampled_verdict(G, E, k, cap) == V_FAIL) {
     st->r_sampled = G + E;
+    st->ties = E;
     start_exact(st, k, PATH_FALLBACK);
     flag_row(cs, flagged, row);
   }
@@ -1145,7 +1167,8 @@ constexpr uint32_t FIN_SCAN_ROWS = 1024;
 template <int DT>
 __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
-    CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
+    const RowCtr* __restrict__ rctr, CallState* __restrict__ cs, uint32_t* __restrict__ flagged,
+    uint32_t* __restrict__ ghist,
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
     uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode, void* __restrict__ out_values,
     int64_t* __restrict__ out_idx) {
@@ -1168,7 +1191,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     __syncthreads();
     for (uint32_t r = tid; r < rows; r += blockDim.x) {
       const uint32_t G = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t E = __hip_atomic_load(&states[r].ties, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t E = rctr[r].ties;   // final: only the filter adds to it
       if (sampled_verdict(G, E, k, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
     }
     __syncthreads();
@@ -1186,6 +1209,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         uint32_t slot = 0;   // failed rows below r
         for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
         slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
+        st->ties = rctr[r].ties;
         st->r_sampled = st->count + st->ties;
         start_exact(st, k, PATH_FALLBACK);
         flagged[slot] = r;
@@ -1194,7 +1218,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     }
     if (st->status != ST_FILTER) continue;
     // an accepted row; when it needs the ties, they join its candidates
-    const uint32_t G = st->count, E = st->ties;
+    const uint32_t G = st->count, E = rctr[r].ties;
     __syncthreads();   // every thread has read the counts
     if (sampled_verdict(G, E, k, cap) == V_OK_TIES) {
       uint64_t* dst = cbuf + (size_t)r * cap + G;
@@ -1203,9 +1227,11 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     }
     if (tid == 0) {
       st->r_sampled = G + E;
+      st->ties = E;
       if (G < k) st->count = G + E;
       if (!small_k) {
         st->thr_key = st->tau_key;   // every candidate key is >= this
+        st->kmax = rctr[r].kmax;
         st->status = ST_SORT;
       }
     }
@@ -1234,7 +1260,6 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   const uint64_t it_lo = (uint64_t)blockIdx.x * per;
   const uint64_t it_hi = it_lo + per < total ? it_lo + per : total;
   constexpr uint32_t SPAN = EX_VPT * D::VEC;   // elements per thread per item
-  static_assert(EX_VPT == 4, "elem4() selects among four vectors");
   const uint32_t lane = tid & 63u;
   auto vec_of = [&](uint32_t c, uint32_t b) { return c * EX_ITEM_VEC + (b / D::VEC) * EX_THREADS + tid; };
   auto load_item = [&](const RowGeom& g, uint32_t c, u32x4 (&xs)[EX_VPT]) {
@@ -1305,7 +1330,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         uint32_t d;
         const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
         const bool act = vec_of(c, b) < g.nvec &&
-                         digit_of<D::KB>(D::key(elem4c<DT>(xs, b)), e, nb, prefix, B, &d);
+                         digit_of<D::KB>(D::key(elemvc<DT, EX_VPT>(xs, b)), e, nb, prefix, B, &d);
         if (act) {
           uni = uni && (my_cnt == 0 || d == my_d);
           my_d = my_cnt == 0 ? d : my_d;
@@ -1327,7 +1352,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
             uint32_t d;
             const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
             const bool act = vec_of(c, b) < g.nvec &&
-                             digit_of<D::KB>(D::key(elem4c<DT>(xs, b)), e, nb, prefix, B, &d);
+                             digit_of<D::KB>(D::key(elemvc<DT, EX_VPT>(xs, b)), e, nb, prefix, B, &d);
             if (act) atomicAdd(&s_hist[d], 1u);
           }
         }
@@ -1418,10 +1443,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
 #pragma unroll
       for (uint32_t b = 0; b < SPAN; ++b) {
         const uint32_t e = g.head + vec_of(c, b) * D::VEC + b % D::VEC;
-        const bool p = vec_of(c, b) < g.nvec && key_pass(D::key(elem4c<DT>(xs, b)), e, thr);
+        const bool p = vec_of(c, b) < g.nvec && key_pass(D::key(elemvc<DT, EX_VPT>(xs, b)), e, thr);
         bits |= (uint32_t)p << b;
       }
-      drain_bits<DT>(
+      drain_bits<DT, EX_VPT>(
           sg, xs, bits,
           [&](uint32_t b) { return g.head + vec_of(c, b) * D::VEC + b % D::VEC; }, comp);
       if (c == 0) {
@@ -1968,7 +1993,7 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   }
   const Plan& p = a.plan;
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
-                     a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.call, a.flagged,
+                     a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
                      a.out_values, a.out_idx);
   return hipGetLastError();
@@ -2000,12 +2025,13 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
       hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
-                         (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states);
+                         (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states,
+                         a.rctr);
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
-      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.cbuf,
-                  a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1));
+      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
+                  a.cbuf, a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1));
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
@@ -2017,8 +2043,8 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       if (rows <= FIN_SCAN_ROWS) {
         mode = FIN_SCAN;
       } else {
-        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows, k,
-                           cap);
+        hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.rctr, a.call, a.flagged,
+                           rows, k, cap);
       }
     }
     hipError_t e = hipGetLastError();

@@ -8,6 +8,7 @@
 namespace tk {
 
 struct RowState;
+struct RowCtr;
 struct CallState;
 
 enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
@@ -27,7 +28,7 @@ struct Plan {
   uint32_t filter_bpr = 1, hist_bpr = 1;
   double p_recall = 0, p_overflow = 0;
   // workspace layout (byte offsets)
-  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lk = 0, total = 0;
+  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lk = 0, off_rctr = 0, total = 0;
 };
 
 // Pipeline stages that can be bracketed by timing events.
@@ -45,6 +46,7 @@ struct LaunchArgs {
   void* out_values;
   int64_t* out_idx;
   RowState* states;
+  RowCtr* rctr;      // sampled route: per-row filter counters
   CallState* call;
   uint32_t* flagged;
   uint32_t* ghist;
