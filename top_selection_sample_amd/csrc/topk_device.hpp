@@ -173,6 +173,15 @@ __device__ __forceinline__ uint32_t rank_below(uint64_t m) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t o = __shfl_xor(v, d, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 // Orders this wave's earlier LDS accesses before its later ones, as seen by
 // the other lanes of the same wave.
 __device__ __forceinline__ void wave_lds_sync() {

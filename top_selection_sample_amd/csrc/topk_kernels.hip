@@ -68,29 +68,138 @@ struct Feistel {
 constexpr uint32_t SH_BITS = 11;
 constexpr uint32_t SH_BINS = 1u << SH_BITS;
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_sample(const void* __restrict__ values, uint32_t n,
-                                                uint32_t S, uint32_t SP, uint64_t seed,
-                                                uint32_t half_bits, uint32_t* __restrict__ skeys,
-                                                uint32_t* __restrict__ shist) {
-  __shared__ uint32_t h[SH_BINS];
-  const uint32_t row = blockIdx.y, tid = threadIdx.x;
-  for (uint32_t i = tid; i < SH_BINS; i += 256) h[i] = 0;
+// Small threshold ranks (t <= TOPT) skip the histogram: every sampler
+// workgroup keeps its own t largest keys, and k_tau_lists takes tau, the
+// t-th largest of their union (the union holds the t largest sampled keys),
+// reading G * t keys instead of all S.  (Letting the last sampler workgroup
+// do it saves the launch but needs an agent-scope release fence in every
+// workgroup: measured slower, much slower with many rows.)
+constexpr uint32_t TOPT = 16;
+constexpr uint32_t SAMPLE_THREADS = 256;
+static_assert((SAMPLE_THREADS / 64) * TOPT <= 64, "one wave merges the wave lists");
+
+// The t largest alive values of the wave (with multiplicity), largest first,
+// written by lane 0 to out[0..); returns how many (wave-uniform).
+__device__ __forceinline__ uint32_t wave_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* out) {
+  uint32_t c = 0;
+  for (; c < t; ++c) {
+    if (ballot(alive) == 0) break;
+    const uint32_t m = wave_max_u32(alive ? v : 0u);
+    const uint64_t hit = ballot(alive && v == m);
+    if (lane_id() == (uint32_t)__builtin_ctzll(hit)) alive = false;
+    if (lane_id() == 0) out[c] = m;
+  }
+  return c;
+}
+
+// The same over the whole workgroup (SAMPLE_THREADS); the result in out
+// (TOPT words), its length returned.  s_wl: 4 * TOPT words, s_wc: 5 words.
+__device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
+                                                uint32_t* s_wc, uint32_t* out) {
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  const uint32_t c = wave_top_t(v, alive, t, s_wl + w * TOPT);
+  if (lane == 0) s_wc[w] = c;
   __syncthreads();
-  const uint32_t j = blockIdx.x * 256u + tid;
+  if (w == 0) {
+    const uint32_t q = lane / TOPT, i = lane % TOPT;
+    const bool al = q < SAMPLE_THREADS / 64 && i < s_wc[q];
+    const uint32_t x = al ? s_wl[q * TOPT + i] : 0u;
+    const uint32_t cnt = wave_top_t(x, al, t, out);
+    if (lane == 0) s_wc[4] = cnt;
+  }
+  __syncthreads();
+  return s_wc[4];
+}
+
+// Row setup for the sampled route (threshold known).
+__device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint32_t tau) {
+  st->status = ST_FILTER;
+  st->tau_key = tau;
+  st->count = 0;
+  st->ties = 0;
+  st->r_sampled = 0;
+  rc->ties = 0;
+  rc->tslots = 0;
+  rc->kmax = 0;
+  st->path = PATH_SAMPLED;
+  st->passes = 0;
+  st->kmax = 0;
+}
+
+// fused = 1: per-workgroup top-t lists in skeys (list g at g * (t + 1): its
+// length, then its keys) for k_tau_lists; fused = 0: sample keys and the
+// histogram for k_tau.
+template <int DT>
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
+    const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
+    uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t fused,
+    uint32_t t) {
+  __shared__ uint32_t h[SH_BINS];
+  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  if (!fused) {
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
+    __syncthreads();
+  }
+  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
+  uint32_t key = 0;
   if (j < S) {
     const Feistel f(seed, row, half_bits);
     uint64_t x = f.apply(j);
     while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
     const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-    const uint32_t key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
-    skeys[(size_t)row * SP + j] = key;
-    atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
+    key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+    if (!fused) {
+      skeys[(size_t)row * SP + j] = key;
+      atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
+    }
   }
-  __syncthreads();
-  uint32_t* gh = shist + (size_t)row * SH_BINS;
-  for (uint32_t i = tid; i < SH_BINS; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  if (!fused) {
+    __syncthreads();
+    uint32_t* gh = shist + (size_t)row * SH_BINS;
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
+      if (h[i]) atomicAdd(&gh[i], h[i]);
+    return;
+  }
+
+  // this workgroup's t largest keys
+  uint32_t* lists = skeys + (size_t)row * SP;
+  const uint32_t c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
+  if (tid <= c) lists[blockIdx.x * (t + 1) + tid] = tid == 0 ? c : s_out[tid - 1];
+}
+
+// tau = the t-th largest key over the G per-workgroup lists of k_sample,
+// merged in chunks of one entry per thread into a running top-t.  One
+// workgroup per row; also starts the row.
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_tau_lists(const uint32_t* __restrict__ skeys,
+                                                               uint32_t SP, uint32_t G, uint32_t t,
+                                                               RowState* __restrict__ states,
+                                                               RowCtr* __restrict__ rctr) {
+  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_run[2 * TOPT], s_out[TOPT];
+  const uint32_t row = blockIdx.x, tid = threadIdx.x, L = t + 1;
+  const uint32_t* lists = skeys + (size_t)row * SP;
+  uint32_t rc_n = 0;   // running list length (uniform)
+  const uint32_t total = G * t;
+  for (uint32_t base = 0; base < total; base += SAMPLE_THREADS) {
+    const uint32_t e = base + tid, g = e / t, i = e % t;
+    bool al = false;
+    uint32_t x = 0;
+    if (e < total) {
+      al = i < lists[g * L];
+      if (al) x = lists[g * L + 1 + i];
+    }
+    const uint32_t cc = block_top_t(x, al, t, s_wl, s_wc, s_out);
+    if (tid < 64) {   // merge the running list with this chunk's
+      const bool a2 = tid < rc_n + cc;
+      const uint32_t y = tid < rc_n ? s_run[tid] : (a2 ? s_out[tid - rc_n] : 0u);
+      const uint32_t m = wave_top_t(y, a2, t, s_run);
+      if (tid == 0) s_wc[5] = m;
+    }
+    __syncthreads();
+    rc_n = s_wc[5];
+    __syncthreads();
+  }
+  if (tid == 0) start_sampled_row(states + row, rctr + row, s_run[t - 1]);   // S >= t keys
 }
 
 // ======================================================================
@@ -180,21 +289,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   } else {
     tau = (uint32_t)block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP).thr;
   }
-  if (tid == 0) {
-    RowState* st = states + row;
-    st->status = ST_FILTER;
-    st->tau_key = tau;
-    st->count = 0;
-    st->ties = 0;
-    st->r_sampled = 0;
-    RowCtr* rc = rctr + row;
-    rc->ties = 0;
-    rc->tslots = 0;
-    rc->kmax = 0;
-    st->path = PATH_SAMPLED;
-    st->passes = 0;
-    st->kmax = 0;
-  }
+  if (tid == 0) start_sampled_row(states + row, rctr + row, tau);
 }
 
 // ======================================================================
@@ -222,15 +317,6 @@ constexpr uint32_t FILTER_THREADS = 512;
 constexpr uint32_t FILTER_WAVES = FILTER_THREADS / 64;
 constexpr uint32_t STAGE_SLOTS = 256;
 constexpr uint32_t FILTER_UNROLL = 4;
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t o = __shfl_xor(v, d, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
 
 struct Stager {
   uint64_t* stage;   // this wave's LDS slots
@@ -2018,15 +2104,24 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     mark(STAGE_EXACT, 0);
   } else {
     if (p.path == PLAN_SAMPLED) {
-      const dim3 sg((uint32_t)((p.S + 255) / 256), rows);
+      const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
+      const dim3 sg(sgx, rows);
+      // small threshold ranks: the select happens inside the sampler
+      const bool fused = p.t <= (int64_t)TOPT && (int64_t)sgx * (p.t + 1) <= p.SP;
       mark(STAGE_SAMPLE, 1);
-      TK_DISPATCH(dt, k_sample, sg, dim3(256), 0, s, a.values, n, (uint32_t)p.S, (uint32_t)p.SP,
-                  a.seed, p.half_bits, a.skeys, a.shist);
+      TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
+                  (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(fused ? 1 : 0),
+                  (uint32_t)p.t);
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
-      hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
-                         (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states,
-                         a.rctr);
+      if (fused) {
+        hipLaunchKernelGGL(k_tau_lists, row_grid, dim3(SAMPLE_THREADS), 0, s, a.skeys,
+                           (uint32_t)p.SP, sgx, (uint32_t)p.t, a.states, a.rctr);
+      } else {
+        hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
+                           (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states,
+                           a.rctr);
+      }
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
