@@ -409,21 +409,28 @@ def calibrate(args):
         meas[name] = (n, rows, k, dt, times)
         del bufs, x0, ov, oi
         torch.cuda.empty_cache()
+    # the two refines (k <= 4096 in one workgroup, larger k by the bucket
+    # sort) have their own ratio: fit each on its own workloads
     ratios = [10 ** (e / 8.0) for e in range(-24, 9)]
-    table = []
-    for rho in ratios:
-        loss = 0.0
-        picks = {}
-        for name, (n, rows, k, dt, times) in meas.items():
-            S = tss.plan(n, rows, k, dt, params=tss.default_params(tuned_ratio=rho))["S"]
-            picks[name] = S
-            loss += times[S] / min(times.values()) - 1.0
-        table.append((loss, rho, picks))
-        print(f"ratio {rho:.4g}: excess {loss * 100:.2f}% picks {picks}", flush=True)
-    best = min(l for l, _, _ in table)
-    good = [rho for l, rho, _ in table if l <= best + 1e-12]
-    print(f"best excess {best * 100:.2f}% for ratios {min(good):.4g} .. {max(good):.4g}; "
-          f"geometric middle {math.sqrt(min(good) * max(good)):.4g}")
+    for group, field in (("k <= 4096", "tuned_ratio"), ("k > 4096", "tuned_ratio_large")):
+        names_g = [nm for nm, v in meas.items() if (v[2] <= 4096) == (field == "tuned_ratio")]
+        if not names_g:
+            continue
+        table = []
+        for rho in ratios:
+            loss = 0.0
+            picks = {}
+            for name in names_g:
+                n, rows, k, dt, times = meas[name]
+                S = tss.plan(n, rows, k, dt, params=tss.default_params(**{field: rho}))["S"]
+                picks[name] = S
+                loss += times[S] / min(times.values()) - 1.0
+            table.append((loss, rho, picks))
+            print(f"{field} {rho:.4g}: excess {loss * 100:.2f}% picks {picks}", flush=True)
+        best = min(l for l, _, _ in table)
+        good = [rho for l, rho, _ in table if l <= best + 1e-12]
+        print(f"{group}: best excess {best * 100:.2f}% for {field} {min(good):.4g} .. "
+              f"{max(good):.4g}; geometric middle {math.sqrt(min(good) * max(good)):.4g}")
     for name, (n, rows, k, dt, times) in meas.items():
         sb = min(times, key=times.get)
         print(f"{name}: best measured S={sb} ({times[sb] * 1e3:.1f} us)")

@@ -72,7 +72,9 @@ typedef enum {
  *    t = 1 when alpha*S < -ln(eps/2)).
  *  TOPK_POLICY_TUNED (default): t and M as in EXACT_TAIL; S minimises the
  *    overhead of Eq. 13, tau_A*S + tau_B*M(S)*log2(k), with the exact-tail
- *    M(S) and tau_B/tau_A = tuned_ratio, over the sample sizes
+ *    M(S) and tau_B/tau_A = tuned_ratio (k <= 4096, candidates refined in
+ *    one workgroup) or tuned_ratio_large (k > 4096, the multi-workgroup
+ *    bucket sort), over the sample sizes
  *    tuned_s_min * 2^(j/4) (j = 0, 1, ...) up to min(s_max, n/8).  Sets S
  *    the way section 4 ("Optimal Sample Size") suggests, with the cost ratio
  *    measured on this engine instead of the default 1. */
@@ -100,8 +102,9 @@ typedef struct {
   int64_t S;          /* > 0: override the sample size */
   int64_t t;          /* > 0: override the threshold rank */
   int64_t M;          /* > 0: override the buffer capacity */
-  double tuned_ratio; /* TUNED policy: tau_B / tau_A of this engine (default 0.13) */
+  double tuned_ratio; /* TUNED policy, k <= 4096: tau_B / tau_A of this engine (default 0.13) */
   int64_t tuned_s_min;/* TUNED policy: least sample size considered (default 1024) */
+  double tuned_ratio_large; /* TUNED policy, k > 4096: tau_B / tau_A (default 0.01) */
 } topk_params;
 
 /* Resolved plan of one call shape (host arithmetic only; no GPU needed). */

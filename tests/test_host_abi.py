@@ -37,11 +37,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_params_layout(lib):
-    assert ctypes.sizeof(lib.Params) == 96
+    assert ctypes.sizeof(lib.Params) == 104
     p = lib.default_params()
     assert (p.eps, p.s_min, p.s_max, p.cost_ratio) == (1e-3, 32768, 131072, 1.0)
     assert p.policy == lib.POLICY_TUNED and p.force_path == 0
-    assert (p.tuned_ratio, p.tuned_s_min) == (0.13, 1024)
+    assert (p.tuned_ratio, p.tuned_s_min, p.tuned_ratio_large) == (0.13, 1024, 0.01)
     assert (p.S, p.t, p.M, p.use_seed) == (0, 0, 0, 0)
 
 
@@ -70,11 +70,14 @@ def test_exact_tail_policy_matches_oracle(lib, n, k):
 
 
 @pytest.mark.parametrize("n,k,s_max", [(2 ** 20, 64, 131072), (2 ** 22, 100, 16384),
-                                       (2 ** 21, 1000, 32768), (2 ** 24, 1, 8192)])
+                                       (2 ** 21, 1000, 32768), (2 ** 24, 1, 8192),
+                                       (2 ** 22, 9000, 131072)])
 def test_tuned_policy_matches_oracle(lib, n, k, s_max):
     rc, info = _plan(lib, n, 3, k, 1, s_max=s_max, s_min=min(32768, s_max))
     assert rc == 0
-    e = P.tuned(n, k, s_hi=min(s_max, n // 8))
+    p = lib.default_params()
+    ratio = p.tuned_ratio if k <= 4096 else p.tuned_ratio_large   # the engine's two refines
+    e = P.tuned(n, k, s_hi=min(s_max, n // 8), ratio=ratio)
     assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
 
 

@@ -30,7 +30,8 @@ class Params(ctypes.Structure):
                 ("force_path", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("use_seed", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
-                ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64)]
+                ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64),
+                ("tuned_ratio_large", ctypes.c_double)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -95,6 +95,7 @@ tk::ParamIn to_in(const topk_params* p) {
   in.M = p->M;
   in.tuned_ratio = p->tuned_ratio;
   in.tuned_s_min = p->tuned_s_min;
+  in.tuned_ratio_large = p->tuned_ratio_large;
   return in;
 }
 
@@ -105,6 +106,7 @@ int check_params(const topk_params* p) {
   if (!(p->cost_ratio > 0.0)) return TOPK_EINVAL;
   if (p->policy < 0 || p->policy > 2) return TOPK_EINVAL;
   if (!(p->tuned_ratio > 0.0) || p->tuned_s_min < 1) return TOPK_EINVAL;
+  if (!(p->tuned_ratio_large > 0.0)) return TOPK_EINVAL;
   if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
   if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
   return TOPK_OK;
@@ -153,7 +155,7 @@ int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* pa
 
 extern "C" {
 
-static_assert(sizeof(topk_params) == 96, "topk_params layout is part of the ABI");
+static_assert(sizeof(topk_params) == 104, "topk_params layout is part of the ABI");
 
 int topk_default_params(topk_params* p) {
   if (!p) return TOPK_EINVAL;
@@ -166,6 +168,7 @@ int topk_default_params(topk_params* p) {
   p->force_path = TOPK_PATH_AUTO;
   p->tuned_ratio = 0.13;
   p->tuned_s_min = 1024;
+  p->tuned_ratio_large = 0.01;
   return TOPK_OK;
 }
 

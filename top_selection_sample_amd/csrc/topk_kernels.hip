@@ -68,12 +68,13 @@ struct Feistel {
 constexpr uint32_t SH_BITS = 11;
 constexpr uint32_t SH_BINS = 1u << SH_BITS;
 
-// Small threshold ranks (t <= TOPT) skip the histogram: every sampler
-// workgroup keeps its own t largest keys, and k_tau_lists takes tau, the
-// t-th largest of their union (the union holds the t largest sampled keys),
-// reading G * t keys instead of all S.  (Letting the last sampler workgroup
-// do it saves the launch but needs an agent-scope release fence in every
-// workgroup: measured slower, much slower with many rows.)
+// Small threshold ranks (t <= TOPT): every sampler workgroup keeps only its
+// own t largest keys (zero-padded to t), and k_tau selects from those G * t
+// keys instead of all S.  Their union holds the t largest sampled keys, and
+// padding keys of 0 cannot raise the t-th largest, so tau is unchanged.
+// (Letting the last sampler workgroup select saves the launch but needs an
+// agent-scope release fence in every workgroup: measured slower, much
+// slower with many rows.)
 constexpr uint32_t TOPT = 16;
 constexpr uint32_t SAMPLE_THREADS = 256;
 static_assert((SAMPLE_THREADS / 64) * TOPT <= 64, "one wave merges the wave lists");
@@ -126,18 +127,18 @@ __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint
   st->kmax = 0;
 }
 
-// fused = 1: per-workgroup top-t lists in skeys (list g at g * (t + 1): its
-// length, then its keys) for k_tau_lists; fused = 0: sample keys and the
-// histogram for k_tau.
+// Writes the keys k_tau selects from, and their 11-bit histogram: all S
+// sample keys (lists = 0), or each workgroup's t largest at g * t (lists = 1).
 template <int DT>
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
-    uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t fused,
+    uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
     uint32_t t) {
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
-  if (!fused) {
+  uint32_t* gh = shist + (size_t)row * SH_BINS;
+  if (!lists) {
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
     __syncthreads();
   }
@@ -149,57 +150,24 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
     const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
     key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
-    if (!fused) {
+    if (!lists) {
       skeys[(size_t)row * SP + j] = key;
       atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
     }
   }
-  if (!fused) {
+  if (!lists) {
     __syncthreads();
-    uint32_t* gh = shist + (size_t)row * SH_BINS;
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
       if (h[i]) atomicAdd(&gh[i], h[i]);
     return;
   }
-
-  // this workgroup's t largest keys
-  uint32_t* lists = skeys + (size_t)row * SP;
+  // this workgroup's t largest keys, zero-padded
   const uint32_t c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
-  if (tid <= c) lists[blockIdx.x * (t + 1) + tid] = tid == 0 ? c : s_out[tid - 1];
-}
-
-// tau = the t-th largest key over the G per-workgroup lists of k_sample,
-// merged in chunks of one entry per thread into a running top-t.  One
-// workgroup per row; also starts the row.
-__global__ __launch_bounds__(SAMPLE_THREADS) void k_tau_lists(const uint32_t* __restrict__ skeys,
-                                                               uint32_t SP, uint32_t G, uint32_t t,
-                                                               RowState* __restrict__ states,
-                                                               RowCtr* __restrict__ rctr) {
-  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_run[2 * TOPT], s_out[TOPT];
-  const uint32_t row = blockIdx.x, tid = threadIdx.x, L = t + 1;
-  const uint32_t* lists = skeys + (size_t)row * SP;
-  uint32_t rc_n = 0;   // running list length (uniform)
-  const uint32_t total = G * t;
-  for (uint32_t base = 0; base < total; base += SAMPLE_THREADS) {
-    const uint32_t e = base + tid, g = e / t, i = e % t;
-    bool al = false;
-    uint32_t x = 0;
-    if (e < total) {
-      al = i < lists[g * L];
-      if (al) x = lists[g * L + 1 + i];
-    }
-    const uint32_t cc = block_top_t(x, al, t, s_wl, s_wc, s_out);
-    if (tid < 64) {   // merge the running list with this chunk's
-      const bool a2 = tid < rc_n + cc;
-      const uint32_t y = tid < rc_n ? s_run[tid] : (a2 ? s_out[tid - rc_n] : 0u);
-      const uint32_t m = wave_top_t(y, a2, t, s_run);
-      if (tid == 0) s_wc[5] = m;
-    }
-    __syncthreads();
-    rc_n = s_wc[5];
-    __syncthreads();
+  if (tid < t) {
+    const uint32_t kv = tid < c ? s_out[tid] : 0u;
+    skeys[(size_t)row * SP + blockIdx.x * t + tid] = kv;
+    atomicAdd(&gh[kv >> (Dt<DT>::KB - SH_BITS)], 1u);
   }
-  if (tid == 0) start_sampled_row(states + row, rctr + row, s_run[t - 1]);   // S >= t keys
 }
 
 // ======================================================================
@@ -250,8 +218,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     if (tid == 0) s_misc[3] = 0;
     __syncthreads();
     const u32x4* kv = reinterpret_cast<const u32x4*>(keys);
-    for_batched_i<8, u32x4>(
-        SP / 4, [&](uint32_t i) { return kv[i]; },
+    for_batched_i<12, u32x4>(
+        (S + 3) / 4, [&](uint32_t i) { return kv[i]; },
         [&](const u32x4& v, bool ok, uint32_t i) {
           bool in[4];
           bool any = false;
@@ -2106,22 +2074,17 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (p.path == PLAN_SAMPLED) {
       const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
       const dim3 sg(sgx, rows);
-      // small threshold ranks: the select happens inside the sampler
-      const bool fused = p.t <= (int64_t)TOPT && (int64_t)sgx * (p.t + 1) <= p.SP;
+      // small threshold ranks: select from per-workgroup top-t lists
+      const bool lists = p.t <= (int64_t)TOPT && (int64_t)sgx * p.t <= p.S;
+      const uint32_t ns = lists ? sgx * (uint32_t)p.t : (uint32_t)p.S;   // keys to select from
       mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
-                  (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(fused ? 1 : 0),
+                  (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
                   (uint32_t)p.t);
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
-      if (fused) {
-        hipLaunchKernelGGL(k_tau_lists, row_grid, dim3(SAMPLE_THREADS), 0, s, a.skeys,
-                           (uint32_t)p.SP, sgx, (uint32_t)p.t, a.states, a.rctr);
-      } else {
-        hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, (uint32_t)p.S,
-                           (uint32_t)p.SP, (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states,
-                           a.rctr);
-      }
+      hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, ns, (uint32_t)p.SP,
+                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states, a.rctr);
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);

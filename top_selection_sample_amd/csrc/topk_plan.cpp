@@ -244,8 +244,9 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t* t, int64_t* M,
                    double* pr, double* po) {
+  const double tratio = k > KSMALL ? in.tuned_ratio_large : in.tuned_ratio;
   Key key{N,      k,     in.s_min,      in.s_max,       in.S,      in.t,
-          in.M,   in.tuned_s_min, in.eps, in.cost_ratio, in.tuned_ratio, in.policy};
+          in.M,   in.tuned_s_min, in.eps, in.cost_ratio, tratio, in.policy};
   {
     std::lock_guard<std::mutex> g(g_mu);
     auto it = g_cache.find(key);
@@ -262,7 +263,7 @@ void sample_params(int64_t N, int64_t k, const ParamIn& in, int64_t* S, int64_t*
   int64_t s = a.S;
   if (in.S > 0) s = in.S;
   else if (in.policy == 2)
-    s = tuned_sample_size(N, k, in.eps, in.tuned_s_min, std::min(in.s_max, N / 8), in.tuned_ratio);
+    s = tuned_sample_size(N, k, in.eps, in.tuned_s_min, std::min(in.s_max, N / 8), tratio);
   if (s > N) s = N;
   int64_t tt, mm;
   if (in.policy == 1) {

@@ -24,8 +24,12 @@ struct ParamIn {
   int force_path = 0;  // 0 auto, 1 filter, 2 exact
   int64_t S = 0, t = 0, M = 0;
   int64_t cus = 256;   // compute units of the device the call runs on
-  double tuned_ratio = 0.13;   // tau_B / tau_A measured for this engine
+  // tau_B / tau_A measured for this engine (calibrated on MI355X over the
+  // sample-size grid): k <= KSMALL refines in one workgroup, larger k runs
+  // the bucket sort, whose cost per candidate is lower relative to sampling
+  double tuned_ratio = 0.13;
   int64_t tuned_s_min = 1024;  // least sample size the tuned policy considers
+  double tuned_ratio_large = 0.01;
 };
 
 double normal_quantile(double p);
