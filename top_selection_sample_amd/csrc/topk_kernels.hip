@@ -127,8 +127,10 @@ __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint
   st->kmax = 0;
 }
 
-// Writes the keys k_tau selects from, and their 11-bit histogram: all S
-// sample keys (lists = 0), or each workgroup's t largest at g * t (lists = 1).
+// Writes the keys k_tau selects from: all S sample keys and their 11-bit
+// histogram (lists = 0), or each workgroup's t largest at g * t (lists = 1;
+// k_tau histograms those itself: the largest keys of every workgroup share
+// a few top bins, and global atomics on them would serialise).
 template <int DT>
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
@@ -163,11 +165,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
   }
   // this workgroup's t largest keys, zero-padded
   const uint32_t c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
-  if (tid < t) {
-    const uint32_t kv = tid < c ? s_out[tid] : 0u;
-    skeys[(size_t)row * SP + blockIdx.x * t + tid] = kv;
-    atomicAdd(&gh[kv >> (Dt<DT>::KB - SH_BITS)], 1u);
-  }
+  if (tid < t) skeys[(size_t)row * SP + blockIdx.x * t + tid] = tid < c ? s_out[tid] : 0u;
 }
 
 // ======================================================================
@@ -189,6 +187,7 @@ constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
                                                      uint32_t SP, uint32_t t, uint32_t KB,
                                                      uint32_t* __restrict__ shist,
+                                                     uint32_t own_hist,
                                                      RowState* __restrict__ states,
                                                      RowCtr* __restrict__ rctr) {
   __shared__ uint32_t s_hist[SH_BINS];
@@ -196,10 +195,17 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   __shared__ uint32_t s_tmp[16];
   __shared__ uint64_t s_cand[CAND_CAP];
   const uint32_t row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  uint32_t* gh = shist + (size_t)row * SH_BINS;
-  for (uint32_t i = tid; i < SH_BINS; i += nt) {
-    s_hist[i] = gh[i];
-    gh[i] = 0;                      // ready for the next call
+  if (own_hist) {   // few keys: histogram them here
+    for (uint32_t i = tid; i < SH_BINS; i += nt) s_hist[i] = 0;
+    __syncthreads();
+    const uint32_t* kr = skeys + (size_t)row * SP;
+    for (uint32_t i = tid; i < S; i += nt) atomicAdd(&s_hist[kr[i] >> (KB - SH_BITS)], 1u);
+  } else {
+    uint32_t* gh = shist + (size_t)row * SH_BINS;
+    for (uint32_t i = tid; i < SH_BINS; i += nt) {
+      s_hist[i] = gh[i];
+      gh[i] = 0;                      // ready for the next call
+    }
   }
   __syncthreads();
   block_find_bucket(s_hist, SH_BINS, t, s_misc, s_tmp);
@@ -2084,7 +2090,8 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_SAMPLE, 0);
       mark(STAGE_TAU, 1);
       hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, ns, (uint32_t)p.SP,
-                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, a.states, a.rctr);
+                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, (uint32_t)(lists ? 1 : 0),
+                         a.states, a.rctr);
       mark(STAGE_TAU, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
