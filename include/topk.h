@@ -90,7 +90,8 @@ typedef enum {
 typedef enum { TOPK_PATH_AUTO = 0, TOPK_PATH_FILTER = 1, TOPK_PATH_EXACT = 2 } topk_path;
 
 typedef struct {
-  double eps;         /* failure budget, Algorithm 1 input (default 1e-3) */
+  double eps;         /* failure budget, Algorithm 1 input (default 1e-3); EXACT_TAIL
+                         and TUNED spend it per call: each of `rows` rows gets eps/rows */
   int64_t s_min;      /* sample size bounds (default 32768 and 131072) */
   int64_t s_max;
   double cost_ratio;  /* tau_B / tau_A of Eq. 13 in Algorithm 1 (default 1) */
@@ -115,8 +116,8 @@ typedef struct {
   int64_t cap;        /* candidate buffer capacity per row */
   int32_t index_bits; /* B: bits of the index field of the composite */
   int32_t key_bits;   /* 32 (int32, float32) or 16 (bf16) */
-  double p_recall;    /* P(R < k) for distinct values (Lemma 1), sampled route */
-  double p_overflow;  /* P(R > M) for distinct values (Lemma 1), sampled route */
+  double p_recall;    /* P(R < k) per row for distinct values (Lemma 1), sampled route */
+  double p_overflow;  /* P(R > M) per row for distinct values (Lemma 1), sampled route */
   size_t workspace_bytes;
 } topk_plan_info;
 

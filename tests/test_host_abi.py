@@ -77,8 +77,22 @@ def test_tuned_policy_matches_oracle(lib, n, k, s_max):
     assert rc == 0
     p = lib.default_params()
     ratio = p.tuned_ratio if k <= 4096 else p.tuned_ratio_large   # the engine's two refines
-    e = P.tuned(n, k, s_hi=min(s_max, n // 8), ratio=ratio)
+    e = P.tuned(n, k, eps=1e-3 / 3, s_hi=min(s_max, n // 8), ratio=ratio)   # eps per call, 3 rows
     assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
+
+
+def test_eps_is_spent_per_call(lib):
+    # a batch of independent rows shares the budget: each row gets eps / rows
+    n, k, rows = 2 ** 20, 64, 128
+    rc, info = _plan(lib, n, rows, k, 1, policy=lib.POLICY_EXACT_TAIL)
+    assert rc == 0
+    e = P.exact_tail(n, k, eps=1e-3 / rows)
+    assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
+    assert info.p_recall + info.p_overflow <= 1e-3 / rows * (1 + 1e-9)
+    # Algorithm 1 verbatim keeps its per-selection eps
+    rc, info = _plan(lib, n, rows, k, 1, policy=lib.POLICY_ALG1)
+    a = P.alg1(n, k)
+    assert (info.S, info.t, info.M) == (a["S"], a["t"], a["M"])
 
 
 def test_tuned_policy_limits(lib):

@@ -307,7 +307,12 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   p.half_bits = (b + 1u) / 2u;
   p.small_k = k <= KSMALL;
 
-  sample_params(n, k, in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
+  // eps bounds the fallback probability of the whole call: the rows of a
+  // batch are independent selections, so each gets eps / rows (Algorithm 1
+  // verbatim keeps its per-selection eps)
+  ParamIn row_in = in;
+  if (rows > 1 && in.policy != 1) row_in.eps = in.eps / (double)rows;
+  sample_params(n, k, row_in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
   bool sampled;
   if (in.force_path == 1) sampled = true;
   else if (in.force_path == 2) sampled = false;
