@@ -93,6 +93,56 @@ __device__ __forceinline__ uint32_t wave_top_t(uint32_t v, bool alive, uint32_t 
   return c;
 }
 
+// The same with four values per lane, v[0..cnt) sorted largest first: each
+// round takes the largest head and advances that lane.
+__device__ __forceinline__ uint32_t wave_top_t4(const uint32_t (&v)[4], uint32_t cnt, uint32_t t,
+                                                uint32_t* out) {
+  uint32_t c = 0, cur = 0;
+  for (; c < t; ++c) {
+    const bool alive = cur < cnt;
+    if (ballot(alive) == 0) break;
+    const uint32_t head = cur == 0 ? v[0] : cur == 1 ? v[1] : cur == 2 ? v[2] : v[3];
+    const uint32_t m = wave_max_u32(alive ? head : 0u);
+    const uint64_t hit = ballot(alive && head == m);
+    if (lane_id() == (uint32_t)__builtin_ctzll(hit)) ++cur;
+    if (lane_id() == 0) out[c] = m;
+  }
+  return c;
+}
+
+// The t largest of up to four values per thread over a workgroup of NW
+// waves (t <= CAP): per-wave lists, then one wave merges them.  s_wl: NW *
+// CAP words, s_wc: NW + 1 words, out: CAP words; returns the length.
+template <uint32_t NW, uint32_t CAP>
+__device__ __forceinline__ uint32_t block_top_t4(uint32_t (&v)[4], uint32_t cnt, uint32_t t,
+                                                 uint32_t* s_wl, uint32_t* s_wc, uint32_t* out) {
+  static_assert(NW * CAP <= 64, "one wave merges the wave lists");
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  auto cswap = [&](int a, int b) {
+    const uint32_t hi = v[a] > v[b] ? v[a] : v[b], lo = v[a] > v[b] ? v[b] : v[a];
+    v[a] = hi;
+    v[b] = lo;
+  };
+  // largest first; the cnt valid values must be the largest (invalid = 0)
+  cswap(0, 1);
+  cswap(2, 3);
+  cswap(0, 2);
+  cswap(1, 3);
+  cswap(1, 2);
+  const uint32_t c = wave_top_t4(v, cnt, t, s_wl + w * CAP);
+  if (lane == 0) s_wc[w] = c;
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t q = lane / CAP, i = lane % CAP;
+    const bool al = q < NW && i < s_wc[q];
+    const uint32_t x = al ? s_wl[q * CAP + i] : 0u;
+    const uint32_t m = wave_top_t(x, al, t, out);
+    if (lane == 0) s_wc[NW] = m;
+  }
+  __syncthreads();
+  return s_wc[NW];
+}
+
 // The same over the whole workgroup (SAMPLE_THREADS); the result in out
 // (TOPT words), its length returned.  s_wl: 4 * TOPT words, s_wc: 5 words.
 __device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
@@ -135,10 +185,12 @@ template <int DT>
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
     uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
-    uint32_t t) {
+    uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr) {
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  // the filter selects tau itself: start the row here (tau set there)
+  if (states && blockIdx.x == 0 && tid == 0) start_sampled_row(states + row, rctr + row, 0u);
   uint32_t* gh = shist + (size_t)row * SH_BINS;
   if (!lists) {
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
@@ -500,12 +552,13 @@ template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
     RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf,
-    uint32_t cap, uint32_t B, uint32_t track_kmax) {
+    uint32_t cap, uint32_t B, uint32_t track_kmax, const uint32_t* __restrict__ tlist,
+    uint32_t tlist_n, uint32_t tlist_stride, uint32_t t) {
   using D = Dt<DT>;
   const uint32_t row = blockIdx.y;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
-  const Thr thr = make_thr<DT>(st->tau_key, 0xFFFFFFFFu);
+  Thr thr;   // set below, once tau is known
 
   __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
   __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
@@ -606,16 +659,36 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // vectors of a wave that has no survivor.
   // The loads of the next step are issued before the current step is
   // examined, so a wave that is draining survivors still has a step's worth
-  // of loads in flight.
+  // of loads in flight.  The first step's loads go out before tau is known.
   auto step_ok = [&](size_t at) { return (at - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; };
-  if (thr.kind == 0) {
-    u32x4 nxt[FILTER_UNROLL];
-    bool more = step_ok(vi);
-    if (more) {
+  u32x4 nxt[FILTER_UNROLL];
+  bool more = step_ok(vi);
+  if (more) {
 #pragma unroll
-      for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
-        nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+    for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+      nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+  }
+  // tau: given by k_tau, or (tlist_n > 0) the t-th largest of the sampler's
+  // per-workgroup top-t lists, selected here by every workgroup
+  uint32_t tau;
+  if (tlist_n) {
+    __shared__ uint32_t s_tl[FILTER_WAVES * 8], s_tc[FILTER_WAVES + 1], s_to[8];
+    const uint32_t* kl = tlist + (size_t)row * tlist_stride;
+    uint32_t v[4], cnt = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+      const uint32_t i = q * FILTER_THREADS + tid;
+      v[q] = i < tlist_n ? kl[i] : 0u;
+      cnt += i < tlist_n ? 1u : 0u;
     }
+    block_top_t4<FILTER_WAVES, 8>(v, cnt, t, s_tl, s_tc, s_to);
+    tau = s_to[t - 1];   // the lists hold at least t keys
+    if (blockIdx.x == 0 && tid == 0) st->tau_key = tau;
+  } else {
+    tau = st->tau_key;
+  }
+  thr = make_thr<DT>(tau, 0xFFFFFFFFu);
+  if (thr.kind == 0) {
     while (more) {
       u32x4 v[FILTER_UNROLL];
 #pragma unroll
@@ -2080,23 +2153,28 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (p.path == PLAN_SAMPLED) {
       const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
       const dim3 sg(sgx, rows);
-      // small threshold ranks: select from per-workgroup top-t lists
+      // small threshold ranks: select from per-workgroup top-t lists; for
+      // t <= 8 and few lists every filter workgroup does that itself
       const bool lists = p.t <= (int64_t)TOPT && (int64_t)sgx * p.t <= p.S;
       const uint32_t ns = lists ? sgx * (uint32_t)p.t : (uint32_t)p.S;   // keys to select from
+      const bool in_filter = lists && p.t <= 8 && ns <= 4 * FILTER_THREADS;
       mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
                   (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
-                  (uint32_t)p.t);
+                  (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr);
       mark(STAGE_SAMPLE, 0);
-      mark(STAGE_TAU, 1);
-      hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, ns, (uint32_t)p.SP,
-                         (uint32_t)p.t, (uint32_t)p.KB, a.shist, (uint32_t)(lists ? 1 : 0),
-                         a.states, a.rctr);
-      mark(STAGE_TAU, 0);
+      if (!in_filter) {
+        mark(STAGE_TAU, 1);
+        hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, ns, (uint32_t)p.SP,
+                           (uint32_t)p.t, (uint32_t)p.KB, a.shist, (uint32_t)(lists ? 1 : 0),
+                           a.states, a.rctr);
+        mark(STAGE_TAU, 0);
+      }
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
-                  a.cbuf, a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1));
+                  a.cbuf, a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1), a.skeys,
+                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t);
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
