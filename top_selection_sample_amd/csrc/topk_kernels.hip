@@ -1718,7 +1718,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
 //   k_lk_hist     bucket histogram (one LDS histogram per 4096 candidates)
 //   k_lk_scatter  bucket starts (descending order), then every candidate of
 //                 a bucket that starts below k goes to its bucket in aux
-//   k_lk_sort     one workgroup per 4096 output positions sorts the buckets
+//   k_lk_sort     one workgroup per LK_WIN output positions sorts the buckets
 //                 starting there in LDS and writes the winners directly; a
 //                 bucket too large for LDS is split further in the
 //                 workgroup (11-bit digits below the common prefix of its
@@ -1734,9 +1734,9 @@ constexpr uint32_t LK_BINS = 1u << LK_BITS;
 constexpr uint32_t LK_STRIDE = LK_BINS + 4;
 constexpr uint32_t LK_THREADS = 1024;
 constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
-constexpr uint32_t LK_WIN = 4096;               // output positions per sort workgroup
-constexpr uint32_t LK_LCAP = 8192;              // largest range sorted in LDS
-constexpr uint32_t LK_STACK = 256;              // pending oversized ranges per workgroup
+constexpr uint32_t LK_WIN = 1024;               // output positions per sort workgroup
+constexpr uint32_t LK_LCAP = 2048;              // largest range sorted in LDS
+constexpr uint32_t LK_STACK = 1024;             // pending oversized ranges per workgroup
 constexpr uint32_t LK_MAXWIN = (uint32_t)(LK_CAP_MAX / LK_WIN);
 static_assert(LK_WORDS_PER_ROW == 2 * LK_BINS + LK_STRIDE + 2 * LK_MAXWIN, "workspace layout");
 static_assert((int64_t)LK_STACK * LK_LCAP >= LK_CAP_MAX,
@@ -1820,6 +1820,14 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_scatter(const RowState* __res
   const uint32_t* gh = lk + (size_t)row * LK_BINS;
   uint32_t* gfill = lk + (size_t)(rows + row) * LK_BINS;
   uint32_t* gstart = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
+  // this workgroup's candidates, loaded first so the histogram read overlaps
+  const uint64_t* p = cbuf + (size_t)row * cap;
+  uint64_t c[4];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t i = base + j * LK_THREADS + tid;
+    c[j] = i < R ? p[i] : 0ull;
+  }
 
   // bucket starts in descending bucket order: thread t owns ranks 4t..4t+3
   uint32_t hv[4], sum = 0;
@@ -1869,15 +1877,12 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_scatter(const RowState* __res
   }
 
   // this workgroup's candidates: local rank inside its bucket
-  const uint64_t* p = cbuf + (size_t)row * cap;
-  uint64_t c[4];
   uint32_t r[4], lr[4];
   bool need[4];
 #pragma unroll
   for (uint32_t j = 0; j < 4; ++j) {
     const uint32_t i = base + j * LK_THREADS + tid;
     const bool ok = i < R;
-    c[j] = ok ? p[i] : 0ull;
     r[j] = ok ? LK_BINS - 1 - g(c[j]) : 0u;
     need[j] = ok && s_start[r[j]] < k;
     lr[j] = need[j] ? atomicAdd(&s_cnt[r[j]], 1u) : 0u;

@@ -15,7 +15,7 @@ enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
 
 constexpr int64_t KSMALL = 4096;            // largest k sorted inside one workgroup
 constexpr int64_t LK_CAP_MAX = int64_t(1) << 21;  // large k: bucket sort up to this capacity
-constexpr size_t LK_WORDS_PER_ROW = 4096 + 4096 + 4100 + 2 * 512;   // its workspace (u32)
+constexpr size_t LK_WORDS_PER_ROW = 4096 + 4096 + 4100 + 2 * 2048;   // its workspace (u32)
 constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workgroup
 
 struct Plan {
