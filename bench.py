@@ -136,6 +136,18 @@ def cpu_baseline(x, dt, k, budget_s=12.0, max_calls=5):
     return med, len(times)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def fallback_rate(tss, bufs, k, rows, calls, policy):
     p = tss.default_params(policy=policy)
     cap = tss.plan(bufs[0].shape[1], rows, k, bufs[0].dtype, params=p)["cap"]
@@ -247,7 +259,8 @@ def run_bench(args):
         cpu = {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": 1,
                "kind": "oracle",
                "sample": f"the full workload ({desc}); {calls} oracle calls, median "
-                         f"{med:.2f} s each, single-threaded partial sort"}
+                         f"{med:.2f} s each, single-threaded partial sort on {cpu_model()} "
+                         f"({os.cpu_count()} logical CPUs on the host)"}
 
     stage_ms = {name: round(v["ms"] / v["count"], 4) if v["count"] else None
                 for name, v in stages.items()}
