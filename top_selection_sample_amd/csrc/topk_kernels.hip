@@ -335,10 +335,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
 // GPU.js Learn "One Bit at a Time"); they are staged per wave in LDS and each
 // workgroup appends its survivors with one atomic at the end.
 // ======================================================================
-// Launch shape (measured on MI355X): 512-thread workgroups, two per compute
-// unit, each streaming one contiguous slice of its row with four 16-byte
-// nontemporal loads in flight per lane; long per-workgroup streams beat a
-// grid-stride sweep by about 20%.
+// Launch shape (measured on MI355X): 512-thread workgroups, one per compute
+// unit (two when survivors are dense), each streaming one contiguous slice
+// of its row with four 16-byte nontemporal loads per lane and the next four
+// issued before the current ones are examined; long per-workgroup streams
+// beat a grid-stride sweep by about 20%.
 constexpr uint32_t FILTER_THREADS = 512;
 constexpr uint32_t FILTER_WAVES = FILTER_THREADS / 64;
 constexpr uint32_t STAGE_SLOTS = 256;

@@ -330,10 +330,15 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
     p.cap = c > n ? n : c;
   }
   const int es = (dtype == 2) ? 2 : 4;
-  // filter grid: two workgroups per compute unit over the whole call, each a
-  // contiguous slice of one row no shorter than 64 KB
+  // filter grid: one or two workgroups per compute unit over the whole call,
+  // each a contiguous slice of one row no shorter than 64 KB.  With few
+  // survivors one 512-thread workgroup per CU is faster (the next step's
+  // loads are in flight while a step is examined; 2.5% on 2^28 fp32 at
+  // t/S = 4e-5); with many (t/S ~ 1e-3: bf16 BatchTopK, 128 short rows) two
+  // hide the survivor handling better (4% and 16% faster there)
   const int64_t cus = in.cus > 0 ? in.cus : 256;
-  int64_t fb = (2 * cus + rows / 2) / rows;
+  const bool dense = (double)p.t > 2e-4 * (double)p.S;
+  int64_t fb = ((dense ? 2 : 1) * cus + rows / 2) / rows;
   const int64_t max_slices = (n * es) / 65536;
   if (fb > max_slices) fb = max_slices;
   if (fb < 1) fb = 1;
