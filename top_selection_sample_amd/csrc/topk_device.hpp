@@ -19,6 +19,7 @@ namespace tk {
 enum : int { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // Per-row phase of the pipeline.
 enum : uint32_t {
@@ -173,13 +174,52 @@ __device__ __forceinline__ uint32_t rank_below(uint64_t m) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t o = __shfl_xor(v, d, 64);
-    v = o > v ? o : v;
-  }
+// A uniform lane's value, read into a scalar register.
+__device__ __forceinline__ uint32_t wave_bcast(uint32_t v, uint32_t lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
+}
+
+// Inclusive scans over the 64 lanes of a wave with DPP moves: shifts by 1,
+// 2, 4 and 8 lanes inside each row of 16, then lane 15 of each row into the
+// next row and lane 31 into the upper half.  A lane whose source is outside
+// its row (or whose row is masked off) takes the identity 0.  Every lane of
+// the wave must be active: the moves read the other lanes' registers, so
+// each one is taken into a temporary before it is combined (a combine that
+// re-reads it could be turned into a branch with lanes switched off).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_take(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  uint32_t t;
+  t = dpp_take<0x111, 0xf>(v); v += t;
+  t = dpp_take<0x112, 0xf>(v); v += t;
+  t = dpp_take<0x114, 0xf>(v); v += t;
+  t = dpp_take<0x118, 0xf>(v); v += t;
+  t = dpp_take<0x142, 0xa>(v); v += t;
+  t = dpp_take<0x143, 0xc>(v); v += t;
   return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+  uint32_t t;
+  t = dpp_take<0x111, 0xf>(v); v = __builtin_elementwise_max(v, t);
+  t = dpp_take<0x112, 0xf>(v); v = __builtin_elementwise_max(v, t);
+  t = dpp_take<0x114, 0xf>(v); v = __builtin_elementwise_max(v, t);
+  t = dpp_take<0x118, 0xf>(v); v = __builtin_elementwise_max(v, t);
+  t = dpp_take<0x142, 0xa>(v); v = __builtin_elementwise_max(v, t);
+  t = dpp_take<0x143, 0xc>(v); v = __builtin_elementwise_max(v, t);
+  return v;
+}
+
+// Sum and maximum over the wave, uniform (lane 63's inclusive scan).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return wave_bcast(wave_incl_sum(v), 63u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_bcast(wave_incl_max(v), 63u);
 }
 
 // Orders this wave's earlier LDS accesses before its later ones, as seen by
@@ -201,12 +241,7 @@ __device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, uint32_t 
   const uint32_t b3 = 255u - 4u * l;
   uint32_t c3 = hist[b3], c2 = hist[b3 - 1], c1 = hist[b3 - 2], c0 = hist[b3 - 3];
   uint32_t s = c3 + c2 + c1 + c0;
-  uint32_t incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t v = __shfl_up(incl, d, 64);
-    if (l >= (uint32_t)d) incl += v;
-  }
+  const uint32_t incl = wave_incl_sum(s);
   uint64_t m = ballot(incl >= need);
   uint32_t first = m ? (uint32_t)__builtin_ctzll(m) : 63u;
   if (l == first) {

@@ -360,7 +360,7 @@ struct Stager {
     wave_lds_sync();
     uint32_t base = 0;
     if (lane_id() == 0) base = atomicAdd(ctr, fill);
-    base = __shfl(base, 0, 64);
+    base = wave_bcast(base, 0u);
     uint32_t m = 0;
     for (uint32_t i = lane_id(); i < fill; i += 64) {
       const uint32_t pos = base + i;
@@ -772,8 +772,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   }
 
   // Workgroup flush: one atomic per buffer, and one for the tie count.
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ties += __shfl_xor(ties, o, 64);
+  ties = wave_sum_u32(ties);
   if (lane == 0) {
     s_fill[w] = sg.fill;
     s_tfill[w] = tg.fill;
@@ -968,16 +967,18 @@ __device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t B, const
   }
 }
 
+// s_tmp: 16 words (at most 1024 threads).
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* s_tmp) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t o = __shfl_xor(v, d, 64);
-    v = o > v ? o : v;
-  }
+  v = wave_max_u32(v);
   if ((threadIdx.x & 63u) == 0) s_tmp[threadIdx.x >> 6] = v;
   __syncthreads();
+  const uint32_t nw = blockDim.x >> 6;
   uint32_t m = 0;
-  for (uint32_t j = 0; j < (blockDim.x >> 6); ++j) m = s_tmp[j] > m ? s_tmp[j] : m;
+#pragma unroll
+  for (uint32_t j = 0; j < 16; ++j) {   // independent reads
+    const uint32_t x = j < nw ? s_tmp[j] : 0u;
+    m = x > m ? x : m;
+  }
   __syncthreads();
   return m;
 }
@@ -995,6 +996,37 @@ __device__ __forceinline__ void lds_sort_desc(uint64_t* s, uint32_t cnt) {
   for (uint32_t i = cnt + threadIdx.x; i < P; i += blockDim.x) s[i] = 0ull;
   __syncthreads();
   block_bitonic_desc(s, P);
+}
+
+// The k largest of the `got` unique composites in s_cand (got >= k) to the
+// output, in rank order.  tmp: LDS scratch of 2 * RF_SORT_CAP + 64 words.
+template <int DT>
+__device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32_t k, uint32_t B,
+                             void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+                             uint32_t row, uint64_t* s_cand, uint32_t got, uint32_t* s_hist,
+                             uint32_t* s_misc, uint64_t* tmp) {
+  const uint32_t tid = threadIdx.x;
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  if (got <= RF_RANK_MAX) {
+    // few elements: each one's output slot is the number of larger
+    // composites (the rank of GPU.js Learn "Rank by Counting"; composites are
+    // unique, so the slots are a permutation)
+    rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
+  } else {
+    if (!block_sort_unique_desc(s_cand, got, tmp, s_hist, s_misc, tmp + RF_SORT_CAP, 64u)) {
+      uint64_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t i = 4 * tid + (uint32_t)j;
+        v[j] = i < got ? s_cand[i] : 0ull;
+      }
+      block_bitonic4096_desc(v, tmp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_cand[4 * tid + j] = v[j];
+      __syncthreads();
+    }
+    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+  }
 }
 
 // One row, one workgroup (1024 threads).  want = ST_FILTER: the sampled
@@ -1089,29 +1121,97 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
     SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
     got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
   }
-  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-  if (got <= RF_RANK_MAX) {
-    // few elements: each one's output slot is the number of larger
-    // composites (the rank of GPU.js Learn "Rank by Counting"; composites are
-    // unique, so the slots are a permutation)
-    rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
-  } else {
-    // the key cache is free again: scratch for the sort
-    uint64_t* tmp = reinterpret_cast<uint64_t*>(s_keys);
-    if (!block_sort_unique_desc(s_cand, got, tmp, s_hist, s_misc, tmp + RF_SORT_CAP, 64u)) {
-      uint64_t v[4];
+  emit_winners<DT>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
+                   reinterpret_cast<uint64_t*>(s_keys));
+  __syncthreads();
+  if (tid == 0) st->status = ST_DONE;
+  __syncthreads();
+}
+
+// The sampled route's refine (Prof-K section 3, stage 4: the exact top-k of
+// the candidates), one row per workgroup of RS_THREADS.  The candidates are
+// read from global memory once and stay in registers (RS_VEC pairs per
+// thread; a longer buffer streams its remainder).  Their keys lie in
+// [tau, kmax], kmax being the largest key the filter stored, so the 11 key
+// bits just below the common prefix of tau and kmax order them: one LDS
+// histogram finds the bin holding rank k, and the candidates from that bin
+// up go straight from registers to LDS for the final rank or sort.
+constexpr uint32_t RS_VEC = 12;
+template <int DT>
+__device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowState* st,
+                               const uint64_t* __restrict__ cb, uint32_t R, uint32_t lo,
+                               uint32_t kmax, uint32_t k, uint32_t B, uint32_t W,
+                               void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+                               uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
+                               uint64_t* s_cand, uint64_t* s_scratch) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t KB = W - B;
+  const uint32_t hi = kmax > lo ? kmax : lo;
+  const uint32_t diff = (lo ^ hi) & (KB == 32 ? 0xFFFFFFFFu : 0xFFFFu);
+  const uint32_t top = diff ? 31u - (uint32_t)__builtin_clz(diff) : 0u;
+  const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
+  auto digit = [&](uint64_t c) { return ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1); };
+
+  // Issue every load first.  The row's buffer starts 8-byte aligned: an odd
+  // start leaves one leading composite to thread 0; then 16-byte pairs; a
+  // remainder (an odd last one, or beyond the registers) is streamed.
+  const uint32_t nh = (R && ((reinterpret_cast<uintptr_t>(cb) >> 3) & 1u)) ? 1u : 0u;
+  const uint32_t pairs = (R - nh) / 2;
+  const uint32_t nvr = pairs < RS_VEC * nt ? pairs : RS_VEC * nt;
+  const uint32_t r0 = nh + 2 * nvr;   // first streamed index
+  const u64x2* vp = reinterpret_cast<const u64x2*>(cb + nh);
+  u64x2 x[RS_VEC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t i = 4 * tid + (uint32_t)j;
-        v[j] = i < got ? s_cand[i] : 0ull;
-      }
-      block_bitonic4096_desc(v, tmp);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s_cand[4 * tid + j] = v[j];
-      __syncthreads();
-    }
-    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+  for (uint32_t j = 0; j < RS_VEC; ++j) {
+    const uint32_t v = j * nt + tid;
+    x[j] = v < nvr ? __builtin_nontemporal_load(vp + v) : u64x2{0ull, 0ull};
   }
+  const bool has1 = tid == 0 && nh;
+  const uint64_t x1 = has1 ? cb[0] : 0ull;
+  for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist[i] = 0;
+  __syncthreads();
+  hist_add(s_hist, digit(x1), has1);
+#pragma unroll
+  for (uint32_t j = 0; j < RS_VEC; ++j) {
+    const bool ok = j * nt + tid < nvr;
+    hist_add(s_hist, digit(x[j].x), ok);
+    hist_add(s_hist, digit(x[j].y), ok);
+  }
+  if (r0 < R)
+    for_batched<LOADS_IN_FLIGHT, uint64_t>(
+        R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+        [&](uint64_t c, bool ok) { hist_add(s_hist, digit(c), ok); });
+  __syncthreads();
+  block_find_bucket(s_hist, RF_BINS, k, s_misc, s_tmp);
+  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+  __syncthreads();
+  uint32_t got;
+  if (acc + hb <= RF_SORT_CAP) {
+    if (tid == 0) s_misc[4] = 0;
+    __syncthreads();
+    lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x1, has1 && digit(x1) >= b);
+#pragma unroll
+    for (uint32_t j = 0; j < RS_VEC; ++j) {
+      const bool ok = j * nt + tid < nvr;
+      lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x[j].x, ok && digit(x[j].x) >= b);
+      lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x[j].y, ok && digit(x[j].y) >= b);
+    }
+    if (r0 < R)
+      for_batched<LOADS_IN_FLIGHT, uint64_t>(
+          R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+          [&](uint64_t c, bool ok) {
+            lds_append(s_cand, &s_misc[4], RF_SORT_CAP, c, ok && digit(c) >= b);
+          });
+    __syncthreads();
+    got = s_misc[4] < RF_SORT_CAP ? s_misc[4] : RF_SORT_CAP;
+  } else {
+    // heavy ties or a wide boundary bin: radix select on the composite
+    CompSrc src{cb};
+    SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
+    got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
+  }
+  emit_winners<DT>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
+                   s_scratch);
   __syncthreads();
   if (tid == 0) st->status = ST_DONE;
   __syncthreads();
@@ -1173,7 +1273,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       const uint32_t first = (uint32_t)__builtin_ctzll(m);
       uint32_t base = 0;
       if (lane_id() == first) base = atomicAdd(&s_misc[4], (uint32_t)__builtin_popcountll(m));
-      base = __shfl(base, first, 64);
+      base = wave_bcast(base, first);
       const uint32_t slot = base + rank_below(m);
       if (keep && slot < cap) out[slot] = c;
     }
@@ -1352,7 +1452,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     }
     if (st->status != ST_FILTER) continue;
     // an accepted row; when it needs the ties, they join its candidates
-    const uint32_t G = st->count, E = rctr[r].ties;
+    const uint32_t G = st->count, E = rctr[r].ties, kmx = rctr[r].kmax, tau = st->tau_key;
     __syncthreads();   // every thread has read the counts
     if (sampled_verdict(G, E, k, cap) == V_OK_TIES) {
       uint64_t* dst = cbuf + (size_t)r * cap + G;
@@ -1370,9 +1470,13 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
     }
     __syncthreads();
-    if (small_k)
-      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_FILTER, out_values,
-                     out_idx, r, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
+    if (small_k) {
+      uint32_t R = G < k ? G + E : G;
+      if (R > cap) R = cap;
+      refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, k, B, W, out_values,
+                         out_idx, r, s_hist, s_misc, s_tmp, s_cand,
+                         reinterpret_cast<uint64_t*>(s_keys));
+    }
   }
   if (nf == 0) return;                        // the common case: nothing more to do
   if (mode == FIN_SCAN) {
@@ -1473,12 +1577,11 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
       const uint64_t has = ballot(my_cnt != 0u);
       if (has) {
-        const uint32_t dref = __shfl(my_d, (int)__builtin_ctzll(has), 64);
+        const uint32_t dref = wave_bcast(my_d, (uint32_t)__builtin_ctzll(has));
         const bool agree = my_cnt == 0u || (uni && my_d == dref);
         if (ballot(!agree) == 0) {
           uint32_t tcount = my_cnt;
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) tcount += __shfl_xor(tcount, o, 64);
+          tcount = wave_sum_u32(tcount);
           if (lane == 0) atomicAdd(&s_hist[dref], tcount);
         } else {
 #pragma unroll
@@ -1837,16 +1940,12 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_scatter(const RowState* __res
     hv[j] = gh[LK_BINS - 1 - (4 * tid + j)];
     sum += hv[j];
   }
-  uint32_t incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d, 64);
-    if (lane >= (uint32_t)d) incl += o;
-  }
+  const uint32_t incl = wave_incl_sum(sum);
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
   uint32_t run = incl - sum;
-  for (uint32_t i = 0; i < w; ++i) run += s_wsum[i];
+#pragma unroll
+  for (uint32_t i = 0; i < LK_THREADS / 64; ++i) run += i < w ? s_wsum[i] : 0u;
 #pragma unroll
   for (uint32_t j = 0; j < 4; ++j) {
     s_start[4 * tid + j] = run;
@@ -2047,12 +2146,7 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
     if (w == 0) {   // exclusive scan from digit 2047 down; lane owns 32 digits
       uint32_t loc = 0;
       for (uint32_t j = 0; j < 32; ++j) loc += s_hist[2047 - (lane * 32 + j)];
-      uint32_t inc = loc;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d, 64);
-        if (lane >= (uint32_t)d) inc += o;
-      }
+      const uint32_t inc = wave_incl_sum(loc);
       uint32_t run = inc - loc;
       for (uint32_t j = 0; j < 32; ++j) {
         const uint32_t b = 2047 - (lane * 32 + j);
@@ -2179,7 +2273,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
-                  a.cbuf, a.aux, cap, B, (uint32_t)(p.small_k ? 0 : 1), a.skeys,
+                  a.cbuf, a.aux, cap, B, 1u, a.skeys,
                   in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t);
       mark(STAGE_FILTER, 0);
     } else {

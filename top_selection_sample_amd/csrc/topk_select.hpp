@@ -19,7 +19,7 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t d, bool active) {
   uint64_t act = ballot(active);
   if (!act) return;
   const uint32_t first = (uint32_t)__builtin_ctzll(act);
-  const uint32_t d0 = __shfl(d, first, 64);
+  const uint32_t d0 = wave_bcast(d, first);
   const uint64_t same = ballot(active && d == d0);
   if (same == act) {
     if (lane_id() == first) atomicAdd(&h[d0], (uint32_t)__builtin_popcountll(act));
@@ -38,7 +38,7 @@ __device__ __forceinline__ void lds_append(uint64_t* arr, uint32_t* counter, uin
   uint32_t base = 0;
   const uint32_t first = (uint32_t)__builtin_ctzll(m);
   if (lane_id() == first) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(m));
-  base = __shfl(base, first, 64);
+  base = wave_bcast(base, first);
   const uint32_t slot = base + rank_below(m);
   if (keep && slot < cap) arr[slot] = c;
 }
@@ -91,7 +91,7 @@ __device__ __forceinline__ void lds_append_u32(uint32_t* arr, uint32_t* counter,
   uint32_t base = 0;
   const uint32_t first = (uint32_t)__builtin_ctzll(m);
   if (lane_id() == first) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(m));
-  base = __shfl(base, first, 64);
+  base = wave_bcast(base, first);
   const uint32_t slot = base + rank_below(m);
   if (keep && slot < cap) arr[slot] = v;
 }
@@ -202,16 +202,12 @@ __device__ __forceinline__ void block_find_bucket(const uint32_t* hist, uint32_t
   if (tid < used) {
     for (uint32_t j = 0; j < per; ++j) s += hist[nbins - 1 - (tid * per + j)];
   }
-  uint32_t incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t v = __shfl_up(incl, d, 64);
-    if (lane >= (uint32_t)d) incl += v;
-  }
+  uint32_t incl = wave_incl_sum(s);
   if (lane == 63) s_tmp[w] = incl;
   __syncthreads();
   uint32_t base = 0;
-  for (uint32_t j = 0; j < w; ++j) base += s_tmp[j];
+#pragma unroll
+  for (uint32_t j = 0; j < 16; ++j) base += j < w ? s_tmp[j] : 0u;   // independent reads
   incl += base;
   const uint32_t excl = incl - s;
   if (tid < used && excl < need && need <= incl) {
@@ -277,16 +273,12 @@ __device__ __forceinline__ void block_scan_desc_2048(uint32_t* hist, uint32_t* w
   const uint32_t per = 2048u / nt;   // bins per thread, in descending order
   uint32_t loc = 0;
   for (uint32_t j = 0; j < per; ++j) loc += hist[2047u - (tid * per + j)];
-  uint32_t incl = loc;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d, 64);
-    if (lane >= (uint32_t)d) incl += o;
-  }
+  const uint32_t incl = wave_incl_sum(loc);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   uint32_t run = incl - loc;
-  for (uint32_t i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+  for (uint32_t i = 0; i < 16; ++i) run += i < w ? wsum[i] : 0u;
   for (uint32_t j = 0; j < per; ++j) {
     const uint32_t b = 2047u - (tid * per + j);
     const uint32_t h = hist[b];
