@@ -256,4 +256,68 @@ __device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, uint32_t 
   }
 }
 
+// The same over a 2048-bin histogram.  Read step j gives lane l the four
+// bins 256j + 4l .. 256j + 4l + 3 (consecutive lanes read consecutive 16-byte
+// words: no bank conflicts).  The group of 256 bins holding the rank is
+// found from the group totals, then the lane inside it from a suffix sum
+// over the lanes (higher lanes hold higher bins).
+__device__ __forceinline__ void wave_find_bucket_2048(const uint32_t* hist, uint32_t need,
+                                                      uint32_t* out) {
+  const uint32_t l = lane_id();
+  const uint4* hp = reinterpret_cast<const uint4*>(hist);
+  uint4 h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = hp[64 * j + l];
+  uint32_t s[8], tot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s[j] = h[j].x + h[j].y + h[j].z + h[j].w;
+    tot[j] = wave_sum_u32(s[j]);
+  }
+  // the group, from the top (uniform)
+  uint32_t acc = 0, g = 0;
+  bool gfound = false;
+#pragma unroll
+  for (int j = 7; j >= 0; --j) {
+    if (!gfound && acc + tot[j] >= need) {
+      gfound = true;
+      g = (uint32_t)j;
+    } else if (!gfound) {
+      acc += tot[j];
+    }
+  }
+  uint4 hg = h[0];
+  uint32_t sg = s[0], tg = tot[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    if (g == (uint32_t)j) {
+      hg = h[j];
+      sg = s[j];
+      tg = tot[j];
+    }
+  }
+  // elements in this lane's bins and every higher lane's, within the group
+  const uint32_t suffix = tg - wave_incl_sum(sg) + sg;
+  const uint64_t m = ballot(acc + suffix >= need);
+  const uint32_t lf = m ? 63u - (uint32_t)__builtin_clzll(m) : 0u;
+  if (l == lf) {
+    uint32_t a = acc + suffix - sg, b = 256u * g + 4u * l, hb = hg.x;
+    const uint32_t v[4] = {hg.w, hg.z, hg.y, hg.x};
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && a + v[q] >= need) {
+        found = true;
+        b = 256u * g + 4u * l + 3u - (uint32_t)q;
+        hb = v[q];
+      } else if (!found) {
+        a += v[q];
+      }
+    }
+    out[0] = b;
+    out[1] = a;
+    out[2] = hb;
+  }
+}
+
 }  // namespace tk

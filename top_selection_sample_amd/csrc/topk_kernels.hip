@@ -932,28 +932,30 @@ __device__ __forceinline__ void store_winner(void* out_values, int64_t* out_idx,
   out_idx[o] = idx;
 }
 
-// Output slot of s[i] = #{j : s[j] > s[i]}; slots >= k are dropped.
+// Output slot of s[i] = #{j : s[j] > s[i]}; slots >= k are dropped.  Four
+// neighbouring lanes share an element, each counting a quarter of the list;
+// their counts are summed with two quad moves.  Needs cnt <= blockDim.x / 4
+// and every thread of the workgroup.
 template <int DT>
 __device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint32_t B,
                                const char* rowp, uint32_t n, void* out_values, int64_t* out_idx,
                                uint32_t row) {
-  for (uint32_t i = threadIdx.x; i < cnt; i += blockDim.x) {
-    const uint64_t c = s[i];
-    uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-    uint32_t j = 0;
-    for (; j + 4 <= cnt; j += 4) {   // four independent LDS reads per step
-      r0 += (s[j] > c) ? 1u : 0u;
-      r1 += (s[j + 1] > c) ? 1u : 0u;
-      r2 += (s[j + 2] > c) ? 1u : 0u;
-      r3 += (s[j + 3] > c) ? 1u : 0u;
-    }
-    for (; j < cnt; ++j) r0 += (s[j] > c) ? 1u : 0u;
-    const uint32_t r = r0 + r1 + r2 + r3;
-    if (r < k) {
-      uint32_t idx;
-      const uint32_t bits = winner_bits<DT>(c, B, rowp, n, &idx);
-      store_winner<DT>(out_values, out_idx, (size_t)row * k + r, bits, idx);
-    }
+  const uint32_t i = threadIdx.x >> 2, q = threadIdx.x & 3u;
+  const uint64_t c = i < cnt ? s[i] : ~0ull;
+  uint32_t r0 = 0, r1 = 0;
+  uint32_t j = q;
+  for (; j + 4 < cnt; j += 8) {   // two independent LDS reads per step
+    r0 += (s[j] > c) ? 1u : 0u;
+    r1 += (s[j + 4] > c) ? 1u : 0u;
+  }
+  if (j < cnt) r0 += (s[j] > c) ? 1u : 0u;
+  uint32_t r = r0 + r1;
+  r += dpp_take<0xB1, 0xf>(r);   // lanes 1,0,3,2 of each quad
+  r += dpp_take<0x4E, 0xf>(r);   // lanes 2,3,0,1
+  if (q == 0 && i < cnt && r < k) {
+    uint32_t idx;
+    const uint32_t bits = winner_bits<DT>(c, B, rowp, n, &idx);
+    store_winner<DT>(out_values, out_idx, (size_t)row * k + r, bits, idx);
   }
 }
 
@@ -1153,12 +1155,14 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
   auto digit = [&](uint64_t c) { return ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1); };
 
   // Issue every load first.  The row's buffer starts 8-byte aligned: an odd
-  // start leaves one leading composite to thread 0; then 16-byte pairs; a
-  // remainder (an odd last one, or beyond the registers) is streamed.
+  // start leaves one leading composite to thread 0, then come 16-byte pairs,
+  // and an odd last one goes to thread 1.  Candidates beyond the registers
+  // are streamed.
   const uint32_t nh = (R && ((reinterpret_cast<uintptr_t>(cb) >> 3) & 1u)) ? 1u : 0u;
   const uint32_t pairs = (R - nh) / 2;
   const uint32_t nvr = pairs < RS_VEC * nt ? pairs : RS_VEC * nt;
-  const uint32_t r0 = nh + 2 * nvr;   // first streamed index
+  const uint32_t tl = (nvr == pairs && ((R - nh) & 1u)) ? 1u : 0u;
+  const uint32_t r0 = nh + 2 * nvr, re = R - tl;   // the streamed range [r0, re)
   const u64x2* vp = reinterpret_cast<const u64x2*>(cb + nh);
   u64x2 x[RS_VEC];
 #pragma unroll
@@ -1166,9 +1170,10 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
     const uint32_t v = j * nt + tid;
     x[j] = v < nvr ? __builtin_nontemporal_load(vp + v) : u64x2{0ull, 0ull};
   }
-  const bool has1 = tid == 0 && nh;
-  const uint64_t x1 = has1 ? cb[0] : 0ull;
+  const bool has1 = (tid == 0 && nh) || (tid == 1 && tl);
+  const uint64_t x1 = has1 ? cb[tid == 0 ? 0u : R - 1] : 0ull;
   for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist[i] = 0;
+  if (tid == 0) s_misc[4] = 0;
   __syncthreads();
   hist_add(s_hist, digit(x1), has1);
 #pragma unroll
@@ -1177,28 +1182,45 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
     hist_add(s_hist, digit(x[j].x), ok);
     hist_add(s_hist, digit(x[j].y), ok);
   }
-  if (r0 < R)
+  if (r0 < re)
     for_batched<LOADS_IN_FLIGHT, uint64_t>(
-        R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+        re - r0, [&](uint32_t i) { return cb[r0 + i]; },
         [&](uint64_t c, bool ok) { hist_add(s_hist, digit(c), ok); });
   __syncthreads();
-  block_find_bucket(s_hist, RF_BINS, k, s_misc, s_tmp);
-  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+  if (tid < 64) wave_find_bucket_2048(s_hist, k, s_misc);
   __syncthreads();
+  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
   uint32_t got;
   if (acc + hb <= RF_SORT_CAP) {
-    if (tid == 0) s_misc[4] = 0;
-    __syncthreads();
-    lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x1, has1 && digit(x1) >= b);
+    // the register-held ones: one slot reservation per wave
+    auto keep = [&](uint64_t c, bool ok) { return ok && digit(c) >= b; };
+    uint32_t mine = keep(x1, has1) ? 1u : 0u;
 #pragma unroll
     for (uint32_t j = 0; j < RS_VEC; ++j) {
       const bool ok = j * nt + tid < nvr;
-      lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x[j].x, ok && digit(x[j].x) >= b);
-      lds_append(s_cand, &s_misc[4], RF_SORT_CAP, x[j].y, ok && digit(x[j].y) >= b);
+      mine += (keep(x[j].x, ok) ? 1u : 0u) + (keep(x[j].y, ok) ? 1u : 0u);
     }
-    if (r0 < R)
+    const uint32_t incl = wave_incl_sum(mine);
+    const uint32_t wtot = wave_bcast(incl, 63u);
+    uint32_t wbase = 0;
+    if ((tid & 63u) == 0 && wtot) wbase = atomicAdd(&s_misc[4], wtot);
+    uint32_t pos = wave_bcast(wbase, 0u) + incl - mine;
+    auto put = [&](uint64_t c, bool k) {
+      if (k) {
+        if (pos < RF_SORT_CAP) s_cand[pos] = c;
+        ++pos;
+      }
+    };
+    put(x1, keep(x1, has1));
+#pragma unroll
+    for (uint32_t j = 0; j < RS_VEC; ++j) {
+      const bool ok = j * nt + tid < nvr;
+      put(x[j].x, keep(x[j].x, ok));
+      put(x[j].y, keep(x[j].y, ok));
+    }
+    if (r0 < re)
       for_batched<LOADS_IN_FLIGHT, uint64_t>(
-          R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+          re - r0, [&](uint32_t i) { return cb[r0 + i]; },
           [&](uint64_t c, bool ok) {
             lds_append(s_cand, &s_misc[4], RF_SORT_CAP, c, ok && digit(c) >= b);
           });
@@ -1206,6 +1228,7 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
     got = s_misc[4] < RF_SORT_CAP ? s_misc[4] : RF_SORT_CAP;
   } else {
     // heavy ties or a wide boundary bin: radix select on the composite
+    __syncthreads();   // every thread has read the bin
     CompSrc src{cb};
     SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
     got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
@@ -1346,6 +1369,7 @@ __device__ void grid_barrier(CallState* cs, uint32_t G) {
 }
 
 constexpr uint32_t EX_THREADS = 1024;
+static_assert(RF_RANK_MAX * 4 <= EX_THREADS, "rank counting: four lanes per element");
 constexpr uint32_t EX_VPT = 4;                            // vectors per thread per item
 constexpr uint32_t EX_ITEM_VEC = EX_THREADS * EX_VPT;     // vectors per item
 
@@ -1407,13 +1431,26 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode, void* __restrict__ out_values,
     int64_t* __restrict__ out_idx) {
   using D = Dt<DT>;
-  __shared__ uint32_t s_hist[RF_BINS];
+  __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
   __shared__ uint64_t s_cand[RF_SORT_CAP];
   __shared__ uint32_t s_keys[RF_KCAP];
   __shared__ uint32_t s_idx[RF_SORT_CAP];
   const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
+
+  // FIN_SCAN (a sampled call): this workgroup's first row's state is read
+  // here, in the same round trip as the check's reads below.
+  const uint32_t r_first = blockIdx.x;
+  const bool pre = mode == FIN_SCAN && r_first < rows;
+  uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
+  if (pre) {
+    f_status = states[r_first].status;
+    f_count = states[r_first].count;
+    f_tau = states[r_first].tau_key;
+    f_ties = rctr[r_first].ties;
+    f_kmax = rctr[r_first].kmax;
+  }
   static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
 
   // ---- which rows failed the check (Prof-K section 3, stage 4)
@@ -1450,11 +1487,14 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
       continue;
     }
-    if (st->status != ST_FILTER) continue;
+    const bool fr = pre && r == r_first;
+    if ((fr ? f_status : st->status) != ST_FILTER) continue;
     // an accepted row; when it needs the ties, they join its candidates
-    const uint32_t G = st->count, E = rctr[r].ties, kmx = rctr[r].kmax, tau = st->tau_key;
-    __syncthreads();   // every thread has read the counts
-    if (sampled_verdict(G, E, k, cap) == V_OK_TIES) {
+    const uint32_t G = fr ? f_count : st->count, E = fr ? f_ties : rctr[r].ties;
+    const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
+    const bool ties_in = sampled_verdict(G, E, k, cap) == V_OK_TIES;
+    if (!fr) __syncthreads();   // every thread has read the counts
+    if (ties_in) {
       uint64_t* dst = cbuf + (size_t)r * cap + G;
       const uint64_t* src = tbuf + (size_t)r * cap;
       for (uint32_t i = tid; i < E; i += blockDim.x) dst[i] = src[i];
@@ -1469,7 +1509,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         st->status = ST_SORT;
       }
     }
-    __syncthreads();
+    if (ties_in) __syncthreads();   // the copied ties are visible to every thread
     if (small_k) {
       uint32_t R = G < k ? G + E : G;
       if (R > cap) R = cap;
