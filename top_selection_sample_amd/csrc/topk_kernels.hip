@@ -232,26 +232,50 @@ struct KeySrc {
 constexpr uint32_t SEL_THREADS = 1024;
 constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
 
-// One workgroup per row.  The boundary bucket comes from the row's histogram;
-// one pass over the sample keys (16-byte loads, 32 keys per thread in
-// flight) copies that bucket into LDS, and the rest of the select stays there.
+// One workgroup per row.  The sample keys are loaded into registers first
+// (TAU_VEC 16-byte words per thread), so their loads overlap the histogram:
+// the row's global one (built by the sampler), or for few keys one built
+// here.  One wave finds the bin holding rank t; the keys of that bin go
+// from registers to LDS (one slot reservation per wave), and the select
+// finishes there.  Longer key lists take a streaming pass instead.
 // Sample-key rows are padded to a multiple of 4 keys (SP = padded length).
+constexpr uint32_t TAU_VEC = 8;
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
                                                      uint32_t SP, uint32_t t, uint32_t KB,
                                                      uint32_t* __restrict__ shist,
                                                      uint32_t own_hist,
                                                      RowState* __restrict__ states,
                                                      RowCtr* __restrict__ rctr) {
-  __shared__ uint32_t s_hist[SH_BINS];
+  static_assert(SH_BINS == 2048, "one wave searches 2048 bins");
+  __shared__ __align__(16) uint32_t s_hist[SH_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
   __shared__ uint64_t s_cand[CAND_CAP];
   const uint32_t row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t sh = KB - SH_BITS;
+  const uint32_t* keys = skeys + (size_t)row * SP;
+  const u32x4* kv4 = reinterpret_cast<const u32x4*>(keys);
+  const uint32_t nv = (S + 3) / 4;
+  const bool regs = nv <= TAU_VEC * nt;   // every key fits the registers
+  u32x4 kv[TAU_VEC];
+#pragma unroll
+  for (uint32_t j = 0; j < TAU_VEC; ++j) {
+    const uint32_t v = j * nt + tid;
+    kv[j] = (regs && v < nv) ? kv4[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+  auto valid = [&](uint32_t j, int q) { return (j * nt + tid) * 4u + (uint32_t)q < S; };
+  if (tid == 0) s_misc[3] = 0;
   if (own_hist) {   // few keys: histogram them here
     for (uint32_t i = tid; i < SH_BINS; i += nt) s_hist[i] = 0;
     __syncthreads();
-    const uint32_t* kr = skeys + (size_t)row * SP;
-    for (uint32_t i = tid; i < S; i += nt) atomicAdd(&s_hist[kr[i] >> (KB - SH_BITS)], 1u);
+    if (regs) {
+#pragma unroll
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist_add(s_hist, kv[j][q] >> sh, valid(j, q));
+    } else {
+      for (uint32_t i = tid; i < S; i += nt) atomicAdd(&s_hist[keys[i] >> sh], 1u);
+    }
   } else {
     uint32_t* gh = shist + (size_t)row * SH_BINS;
     for (uint32_t i = tid; i < SH_BINS; i += nt) {
@@ -260,59 +284,75 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     }
   }
   __syncthreads();
-  block_find_bucket(s_hist, SH_BINS, t, s_misc, s_tmp);
+  if (tid < 64) wave_find_bucket_2048(s_hist, t, s_misc);
+  __syncthreads();
   const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
-  const uint32_t sh = KB - SH_BITS;
-  const uint32_t* keys = skeys + (size_t)row * SP;
   KeySrc src{keys};
   SelectStart st0;
   st0.prefix = (uint64_t)b << sh;
   st0.nb = SH_BITS;
   st0.need = t - acc;
   st0.above = acc;
-  __syncthreads();
   if (hb <= CAND_CAP) {
-    // the boundary bucket's keys into LDS
-    if (tid == 0) s_misc[3] = 0;
-    __syncthreads();
-    const u32x4* kv = reinterpret_cast<const u32x4*>(keys);
-    for_batched_i<12, u32x4>(
-        (S + 3) / 4, [&](uint32_t i) { return kv[i]; },
-        [&](const u32x4& v, bool ok, uint32_t i) {
-          bool in[4];
-          bool any = false;
+    // the boundary bin's keys into LDS
+    if (regs) {
+      uint32_t mine = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            in[q] = ok && (i * 4 + q) < S && (v[q] >> sh) == b;
-            any = any || in[q];
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine += (valid(j, q) && (kv[j][q] >> sh) == b) ? 1u : 0u;
+      const uint32_t incl = wave_incl_sum(mine);
+      const uint32_t wtot = wave_bcast(incl, 63u);
+      uint32_t wbase = 0;
+      if ((tid & 63u) == 0 && wtot) wbase = atomicAdd(&s_misc[3], wtot);
+      uint32_t pos = wave_bcast(wbase, 0u) + incl - mine;
+#pragma unroll
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (valid(j, q) && (kv[j][q] >> sh) == b) {
+            if (pos < CAND_CAP) s_cand[pos] = kv[j][q];
+            ++pos;
           }
-          if (ballot(any) == 0) return;   // the usual case: no key of the bucket
+    } else {
+      for_batched_i<12, u32x4>(
+          nv, [&](uint32_t i) { return kv4[i]; },
+          [&](const u32x4& v, bool ok, uint32_t i) {
+            bool in[4];
+            bool any = false;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) lds_append(s_cand, &s_misc[3], CAND_CAP, v[q], in[q]);
-        });
+            for (int q = 0; q < 4; ++q) {
+              in[q] = ok && (i * 4 + q) < S && (v[q] >> sh) == b;
+              any = any || in[q];
+            }
+            if (ballot(any) == 0) return;   // the usual case: no key of the bin
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lds_append(s_cand, &s_misc[3], CAND_CAP, v[q], in[q]);
+          });
+    }
     __syncthreads();
     st0.m = s_misc[3] < CAND_CAP ? s_misc[3] : CAND_CAP;
     st0.in_lds = true;
-    __syncthreads();
   }
   uint32_t tau;
-  if (st0.in_lds && st0.m <= nt) {
-    // a small bucket: the wanted key is the one whose rank inside it (larger
-    // keys, then equal keys earlier in the list) is need - 1
-    if (tid == 0) s_misc[5] = 0;
-    __syncthreads();
-    if (tid < st0.m) {
-      const uint64_t mine = s_cand[tid];
-      uint32_t r = 0;
-      for (uint32_t j = 0; j < st0.m; ++j) {
-        const uint64_t o = s_cand[j];
-        r += (o > mine || (o == mine && j < tid)) ? 1u : 0u;
-      }
-      if (r == st0.need - 1) s_misc[5] = (uint32_t)mine;
+  if (st0.in_lds && st0.m <= nt / 4) {
+    // a small bin: the wanted key is the one whose rank inside it (larger
+    // keys, then equal keys earlier in the list) is need - 1; four lanes
+    // share each key, each counting a quarter of the list
+    const uint32_t i = tid >> 2, q = tid & 3u;
+    const uint64_t mine = i < st0.m ? s_cand[i] : 0ull;
+    uint32_t r = 0;
+    for (uint32_t j = q; j < st0.m; j += 4) {
+      const uint64_t o = s_cand[j];
+      r += (o > mine || (o == mine && j < i)) ? 1u : 0u;
     }
+    r += dpp_take<0xB1, 0xf>(r);
+    r += dpp_take<0x4E, 0xf>(r);
+    if (q == 0 && i < st0.m && r == st0.need - 1) s_misc[5] = (uint32_t)mine;
     __syncthreads();
     tau = s_misc[5];
   } else {
+    __syncthreads();   // every thread has read the bin
     tau = (uint32_t)block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP).thr;
   }
   if (tid == 0) start_sampled_row(states + row, rctr + row, tau);
