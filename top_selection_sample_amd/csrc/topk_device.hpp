@@ -213,6 +213,38 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
   return v;
 }
 
+// 64-bit minimum and maximum over the wave, uniform: the same scan on both
+// halves of each value (identity ~0 for the minimum, 0 for the maximum).
+template <int CTRL, int ROWS, int ID>
+__device__ __forceinline__ uint64_t dpp_take64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(ID, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t bcast64(uint64_t v, uint32_t lane) {
+  return ((uint64_t)wave_bcast((uint32_t)(v >> 32), lane) << 32) | wave_bcast((uint32_t)v, lane);
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  uint64_t t;
+  t = dpp_take64<0x111, 0xf, -1>(v); v = t < v ? t : v;
+  t = dpp_take64<0x112, 0xf, -1>(v); v = t < v ? t : v;
+  t = dpp_take64<0x114, 0xf, -1>(v); v = t < v ? t : v;
+  t = dpp_take64<0x118, 0xf, -1>(v); v = t < v ? t : v;
+  t = dpp_take64<0x142, 0xa, -1>(v); v = t < v ? t : v;
+  t = dpp_take64<0x143, 0xc, -1>(v); v = t < v ? t : v;
+  return bcast64(v, 63u);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t t;
+  t = dpp_take64<0x111, 0xf, 0>(v); v = t > v ? t : v;
+  t = dpp_take64<0x112, 0xf, 0>(v); v = t > v ? t : v;
+  t = dpp_take64<0x114, 0xf, 0>(v); v = t > v ? t : v;
+  t = dpp_take64<0x118, 0xf, 0>(v); v = t > v ? t : v;
+  t = dpp_take64<0x142, 0xa, 0>(v); v = t > v ? t : v;
+  t = dpp_take64<0x143, 0xc, 0>(v); v = t > v ? t : v;
+  return bcast64(v, 63u);
+}
+
 // Sum and maximum over the wave, uniform (lane 63's inclusive scan).
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return wave_bcast(wave_incl_sum(v), 63u);
@@ -265,15 +297,14 @@ __device__ __forceinline__ void wave_find_bucket_2048(const uint32_t* hist, uint
                                                       uint32_t* out) {
   const uint32_t l = lane_id();
   const uint4* hp = reinterpret_cast<const uint4*>(hist);
-  uint4 h[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) h[j] = hp[64 * j + l];
   uint32_t s[8], tot[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    s[j] = h[j].x + h[j].y + h[j].z + h[j].w;
-    tot[j] = wave_sum_u32(s[j]);
+    const uint4 h = hp[64 * j + l];
+    s[j] = h.x + h.y + h.z + h.w;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tot[j] = wave_sum_u32(s[j]);
   // the group, from the top (uniform)
   uint32_t acc = 0, g = 0;
   bool gfound = false;
@@ -286,16 +317,15 @@ __device__ __forceinline__ void wave_find_bucket_2048(const uint32_t* hist, uint
       acc += tot[j];
     }
   }
-  uint4 hg = h[0];
   uint32_t sg = s[0], tg = tot[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) {
     if (g == (uint32_t)j) {
-      hg = h[j];
       sg = s[j];
       tg = tot[j];
     }
   }
+  const uint4 hg = hp[64 * g + l];   // the group's four bins, read again
   // elements in this lane's bins and every higher lane's, within the group
   const uint32_t suffix = tg - wave_incl_sum(sg) + sg;
   const uint64_t m = ballot(acc + suffix >= need);

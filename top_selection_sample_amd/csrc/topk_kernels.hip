@@ -1042,11 +1042,13 @@ __device__ __forceinline__ void lds_sort_desc(uint64_t* s, uint32_t cnt) {
 
 // The k largest of the `got` unique composites in s_cand (got >= k) to the
 // output, in rank order.  tmp: LDS scratch of 2 * RF_SORT_CAP + 64 words.
-template <int DT>
+// digit: a bin of 11 key bits that never decreases as the composite grows,
+// or null to take one from the list's own range.
+template <int DT, class Digit>
 __device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32_t k, uint32_t B,
                              void* __restrict__ out_values, int64_t* __restrict__ out_idx,
                              uint32_t row, uint64_t* s_cand, uint32_t got, uint32_t* s_hist,
-                             uint32_t* s_misc, uint64_t* tmp) {
+                             uint32_t* s_misc, uint64_t* tmp, const Digit* digit) {
   const uint32_t tid = threadIdx.x;
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
   if (got <= RF_RANK_MAX) {
@@ -1055,7 +1057,10 @@ __device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32
     // unique, so the slots are a permutation)
     rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
   } else {
-    if (!block_sort_unique_desc(s_cand, got, tmp, s_hist, s_misc, tmp + RF_SORT_CAP, 64u)) {
+    uint32_t* wsum = reinterpret_cast<uint32_t*>(tmp + RF_SORT_CAP);
+    bool sorted = digit && block_sort_binned_desc(s_cand, got, tmp, s_hist, s_misc, wsum, *digit, 64u);
+    if (!sorted) sorted = block_sort_unique_desc(s_cand, got, tmp, s_hist, s_misc, tmp + RF_SORT_CAP, 64u);
+    if (!sorted) {
       uint64_t v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1070,6 +1075,10 @@ __device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32
     write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
   }
 }
+
+struct NoDigit {
+  __device__ uint32_t operator()(uint64_t) const { return 0u; }
+};
 
 // One row, one workgroup (1024 threads).  want = ST_FILTER: the sampled
 // candidates (a failed check sends the row to the exact route instead);
@@ -1163,8 +1172,8 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
     SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
     got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
   }
-  emit_winners<DT>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
-                   reinterpret_cast<uint64_t*>(s_keys));
+  emit_winners<DT, NoDigit>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
+                            reinterpret_cast<uint64_t*>(s_keys), nullptr);
   __syncthreads();
   if (tid == 0) st->status = ST_DONE;
   __syncthreads();
@@ -1273,8 +1282,15 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
     SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
     got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
   }
-  emit_winners<DT>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
-                   s_scratch);
+  // the collected candidates keep the histogram's bins: sort on them
+  struct BinOf {
+    uint32_t B, kshift;
+    __device__ uint32_t operator()(uint64_t c) const {
+      return ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1);
+    }
+  } bin_of{B, kshift};
+  emit_winners<DT, BinOf>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
+                          s_scratch, &bin_of);
   __syncthreads();
   if (tid == 0) st->status = ST_DONE;
   __syncthreads();

@@ -356,22 +356,19 @@ __device__ __forceinline__ bool block_sort_unique_desc(uint64_t* s, uint32_t cnt
     mn = v < mn ? v : mn;
     mx = v > mx ? v : mx;
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint64_t a = __shfl_xor(mn, d, 64), b = __shfl_xor(mx, d, 64);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
+  mn = wave_min_u64(mn);
+  mx = wave_max_u64(mx);
   if (lane == 0) {
     red[w] = mn;
     red[16 + w] = mx;
   }
   __syncthreads();
-  mn = red[0];
-  mx = red[16];
-  for (uint32_t j = 1; j < (nt >> 6); ++j) {
-    mn = red[j] < mn ? red[j] : mn;
-    mx = red[16 + j] > mx ? red[16 + j] : mx;
+  const uint32_t nw = nt >> 6;
+#pragma unroll
+  for (uint32_t j = 0; j < 16; ++j) {   // independent reads
+    const uint64_t a = j < nw ? red[j] : ~0ull, b = j < nw ? red[16 + j] : 0ull;
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
   }
   __syncthreads();   // red is reused as scan scratch below
   const uint64_t diff = mn ^ mx;
