@@ -236,6 +236,25 @@ def run_bench(args):
         torch.cuda.synchronize()
         exact_ms = ev0.elapsed_time(ev1) / 5
 
+    # read ceiling: the same input read once per launch with the filter's
+    # access pattern and nothing else (k_stream_read), same K
+    ceiling = None
+    if plan["path"] == 0:
+        sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        for i in range(3):
+            tss.stream_read(bufs[i % 3], sink)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            tss.stream_read(bufs[i % 3], sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        t_read = ev0.elapsed_time(ev1) / args.steps * 1e-3
+        read_bytes = rows * n * es
+        ceiling = {"kernel": "k_stream_read", "unit": "GB/s",
+                   "achieved": round(read_bytes / t_read / 1e9, 1),
+                   "avg_launch_us": round(t_read * 1e6, 2), "bytes_per_launch": int(read_bytes)}
+
     elems = rows * n
     gelem_s = elems / (ms_step * 1e-3) / 1e9
     alg_bytes = algorithmic_bytes(rows, n, k, es, plan, R_mean)
@@ -252,6 +271,8 @@ def run_bench(args):
                 "traffic": traffic, "kernel": "k_filter",
                 "avg_launch_us": round(t_filter * 1e6, 2),
                 "algorithmic_bytes_per_launch": int(filt_bytes)}
+        if ceiling:
+            ceiling["filter_frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -276,6 +297,7 @@ def run_bench(args):
         "hbm_gbs": round(e2e_gbs, 1), "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(alg_bytes),
         "roofline": roof,
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "fallback": fb,
         "exact_route_ms_per_call": round(exact_ms, 4) if exact_ms is not None else None,

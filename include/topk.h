@@ -181,6 +181,18 @@ typedef struct {
 int topk_profile_enable(int on);
 int topk_profile_read(topk_stage_times* out);
 
+/* Read ceiling (measurement aid, not part of a selection).  Reads
+ * data[0..bytes) once on `stream` with the filter's access pattern: one
+ * 512-thread workgroup per compute unit, each streaming a contiguous slice
+ * with four 16-byte nontemporal loads per lane in flight and the next four
+ * issued before the current ones are used.  Nothing is written except,
+ * with negligible probability, one word of sink[0..64) (caller-owned device
+ * memory of 64 words).  Timing it gives the achievable read bandwidth of that
+ * pattern, against which the filter's bandwidth is judged.  data must be
+ * device memory, 16-byte aligned, bytes a non-zero multiple of 16; otherwise
+ * TOPK_EINVAL.  Asynchronous; TOPK_EHIP if the launch fails. */
+int topk_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
 /* Short English text for a status code (static storage). */
 const char* topk_status_string(int status);
 

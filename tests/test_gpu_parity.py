@@ -401,3 +401,21 @@ def test_argument_errors():
         tss.topk(x, 0)
     with pytest.raises(TypeError):
         tss.topk(x.double(), 5)
+
+
+def test_stream_read_reads_and_writes_nothing():
+    # the read-ceiling aid: valid sizes run, a ragged or misaligned buffer
+    # is refused, and the data and the sink are left as they were
+    tss = _tss()
+    x = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    before = x.clone()
+    tss.stream_read(x, sink)
+    tss.stream_read(x[: (1 << 20) - 4 * 1000 - 4], sink)   # a ragged last step
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)
+    assert bool((sink == -7).all())
+    with pytest.raises(tss.TopkError):
+        tss.stream_read(x[1:5], sink)   # 4-byte aligned only
+    with pytest.raises(tss.TopkError):
+        tss.stream_read(x[:3], sink)    # 12 bytes

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED, Params,
                    TopkError, default_params)
 
-__all__ = ["topk", "plan", "profile_enable", "profile_read", "workspace_size", "read_stats", "Workspace", "Params",
+__all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "workspace_size", "read_stats",
+           "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code"]
 
@@ -146,3 +147,17 @@ def profile_read() -> dict:
     t = _lib.StageTimes()
     _lib.check(_lib.lib.topk_profile_read(ctypes.byref(t)), "topk_profile_read")
     return {name: {"ms": t.ms[i], "count": t.count[i]} for i, name in enumerate(_lib.STAGES)}
+
+
+def stream_read(x: torch.Tensor, sink: torch.Tensor) -> None:
+    """One read of ``x`` with the filter's access pattern (a measurement aid:
+    its time is the achievable read time of that pattern).  ``x``: contiguous
+    GPU tensor, 16-byte aligned, a multiple of 16 bytes; ``sink``: int32 GPU
+    tensor of at least 64 elements."""
+    if not (x.is_cuda and x.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+            and sink.numel() >= 64):
+        raise ValueError("x: contiguous GPU tensor; sink: int32 GPU tensor of >= 64 elements")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _lib.check(_lib.lib.topk_stream_read(x.data_ptr(), x.numel() * x.element_size(),
+                                             sink.data_ptr(), stream), "topk_stream_read")

@@ -326,6 +326,14 @@ int topk_profile_read(topk_stage_times* out) {
   return rc;
 }
 
+int topk_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  if (!data || !sink || bytes == 0) return TOPK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(data) % 16 || bytes % 16 || reinterpret_cast<uintptr_t>(sink) % 4)
+    return TOPK_EINVAL;
+  const hipError_t e = tk::launch_stream_read(data, bytes, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
+}
+
 const char* topk_status_string(int status) {
   switch (status) {
     case TOPK_OK: return "ok";

@@ -2306,6 +2306,68 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
   }
 }
 
+// Measurement aid: one read of a buffer with the filter's access pattern
+// (a contiguous slice per 512-thread workgroup, one workgroup per compute
+// unit, FILTER_UNROLL 16-byte nontemporal loads per lane, the next step's
+// loads issued before the current ones are used).  It keeps nothing but an
+// XOR of the data, so its duration is the achievable time of that read
+// pattern on the device, the ceiling the filter is measured against.
+__global__ __launch_bounds__(FILTER_THREADS) void k_stream_read(const u32x4* __restrict__ p,
+                                                                size_t nvec,
+                                                                uint32_t* __restrict__ sink) {
+  constexpr size_t step = (size_t)FILTER_THREADS * FILTER_UNROLL;
+  const size_t per = ((nvec + gridDim.x - 1) / gridDim.x + step - 1) / step * step;
+  const size_t v0 = (size_t)blockIdx.x * per;
+  const size_t v1 = v0 + per < nvec ? v0 + per : nvec;
+  const uint32_t tid = threadIdx.x;
+  uint32_t acc = 0;
+  size_t b = v0;   // the current whole step starts here
+  u32x4 ra[FILTER_UNROLL], rb[FILTER_UNROLL];
+  auto load = [&](u32x4 (&r)[FILTER_UNROLL], size_t at) {
+#pragma unroll
+    for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+      r[u] = __builtin_nontemporal_load(p + at + tid + u * FILTER_THREADS);
+  };
+  auto fold = [&](const u32x4 (&r)[FILTER_UNROLL]) {
+#pragma unroll
+    for (uint32_t u = 0; u < FILTER_UNROLL; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+  };
+  if (b + step <= v1) {
+    load(ra, b);
+    for (;;) {
+      const bool more = b + 2 * step <= v1;
+      load(rb, more ? b + step : b);
+      fold(ra);
+      if (!more) break;
+      b += step;
+      const bool more2 = b + 2 * step <= v1;
+      load(ra, more2 ? b + step : b);
+      fold(rb);
+      if (!more2) break;
+      b += step;
+    }
+    b += step;
+  }
+  // the part of the slice after its last whole step
+  for (size_t i = b + tid; i < v1; i += FILTER_THREADS) {
+    const u32x4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 63u] = acc;   // keeps the loads
+}
+
+hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (cus <= 0) cus = 1;
+  hipLaunchKernelGGL(k_stream_read, dim3((uint32_t)cus), dim3(FILTER_THREADS), 0, s,
+                     static_cast<const u32x4*>(data), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t mode) {
   // one workgroup per compute unit (cached per device)

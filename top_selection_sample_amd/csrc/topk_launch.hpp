@@ -61,6 +61,7 @@ struct LaunchArgs {
 
 hipError_t launch_pipeline(const LaunchArgs& a);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
 uint32_t filter_threads();
 uint32_t filter_unroll();
 uint32_t sort_tile();
