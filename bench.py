@@ -255,6 +255,37 @@ def run_bench(args):
                    "achieved": round(read_bytes / t_read / 1e9, 1),
                    "avg_launch_us": round(t_read * 1e6, 2), "bytes_per_launch": int(read_bytes)}
 
+    # BatchTopK consumer (c5): the selection turned into the sparse
+    # activation (zero fill of the [B, d] output, then the K winners written
+    # back), alone and after the top-k in one step
+    consumer = None
+    if args.workload == "c5":
+        dense = torch.empty((rows, n), dtype=x0.dtype, device="cuda")
+        for i in range(3):
+            tss.scatter(ov, oi, n, out=dense)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            tss.scatter(ov, oi, n, out=dense)
+        ev1.record()
+        torch.cuda.synchronize()
+        t_cons = ev0.elapsed_time(ev1) / args.steps * 1e-3
+        ev0.record()
+        for i in range(args.steps):
+            tss.topk(bufs[i % 3], k, out=(ov, oi))
+            tss.scatter(ov, oi, n, out=dense)
+        ev1.record()
+        torch.cuda.synchronize()
+        t_both = ev0.elapsed_time(ev1) / args.steps * 1e-3
+        cbytes = rows * n * es + rows * k * (es + 8) + rows * k * es
+        consumer = {"kernels": "k_fill_zero + k_scatter_winners", "bound": "hbm", "unit": "GB/s",
+                    "avg_us": round(t_cons * 1e6, 2),
+                    "achieved": round(cbytes / t_cons / 1e9, 1), "peak": HBM_PEAK_GBS,
+                    "frac": round(cbytes / t_cons / 1e9 / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_launch": int(cbytes),
+                    "batchtopk_ms_per_step": round(t_both * 1e3, 4)}
+        del dense
+
     elems = rows * n
     gelem_s = elems / (ms_step * 1e-3) / 1e9
     alg_bytes = algorithmic_bytes(rows, n, k, es, plan, R_mean)
@@ -298,6 +329,7 @@ def run_bench(args):
         "algorithmic_bytes_per_step": int(alg_bytes),
         "roofline": roof,
         "read_ceiling": ceiling,
+        "batchtopk_consumer": consumer,
         "cpu_baseline": cpu,
         "fallback": fb,
         "exact_route_ms_per_call": round(exact_ms, 4) if exact_ms is not None else None,

@@ -181,6 +181,23 @@ typedef struct {
 int topk_profile_enable(int on);
 int topk_profile_read(topk_stage_times* out);
 
+/* BatchTopK consumer (Prof-K section 5, "Application: BatchTopK Sparse
+ * Autoencoders": the batch-global top-k keeps the K largest of the flattened
+ * B x d_dict activations).  Turns a selection into the sparse activation:
+ * for every row r < rows and j < k, out_dense[r*n + indices[r*k + j]] =
+ * values[r*k + j]; every other element of out_dense[0 .. rows*n) becomes 0.
+ * out_mask, if not null, gets 1 at the same places and 0 elsewhere (one byte
+ * per element).  values / indices are laid out as topk writes them (for the
+ * flattened call rows = 1, n = B*d_dict, k = K); out_dense has the dtype of
+ * values.  Either output may be null, not both.  An index outside [0, n) is
+ * skipped.  All pointers are device memory; values and out_dense aligned to
+ * the element size, indices to 8 bytes; the outputs must not overlap the
+ * inputs.  Two kernels on `stream` (a zero fill, then one thread per
+ * winner), asynchronous.  Errors: TOPK_EDTYPE, TOPK_EINVAL (sizes, k > n,
+ * no output, alignment), TOPK_EHIP. */
+int topk_scatter(const void* values, const int64_t* indices, int64_t rows, int64_t k, int64_t n,
+                 int dtype, void* out_dense, uint8_t* out_mask, void* stream);
+
 /* Read ceiling (measurement aid, not part of a selection).  Reads
  * data[0..bytes) once on `stream` with the filter's access pattern: one
  * 512-thread workgroup per compute unit, each streaming a contiguous slice

@@ -21,6 +21,9 @@ Contents
                       (Prof-K section 3, stages 1 and 2); C++ core.
 * ``params``          Algorithm 1 and the exact-tail reading of Theorem 3
                       (submodule ``oracle.params``).
+* ``sparse_activation``  the BatchTopK consumer (Prof-K section 5): the
+                      selected activations kept in place, zero elsewhere,
+                      and the mask of the kept places.
 
 bf16 data is carried as its uint16 bit patterns with ``dtype="bf16"``.
 """
@@ -214,3 +217,22 @@ def tau(row_values: np.ndarray, seed: int, row: int, S: int, t: int,
     if with_sample:
         return tk.value, R.value, sk
     return tk.value, R.value
+
+
+def sparse_activation(values: np.ndarray, indices: np.ndarray, n: int):
+    """BatchTopK consumer (Prof-K section 5, "Application: BatchTopK Sparse
+    Autoencoders": the largest K of the flattened activations are selected;
+    the sparse activation keeps them and is zero elsewhere).  values,
+    indices: [rows, k] as ``topk`` returns them (bf16 as uint16 bits).
+    Returns (dense [rows, n] of the values' dtype, mask [rows, n] uint8)."""
+    values = np.asarray(values)
+    indices = np.asarray(indices, dtype=np.int64)
+    if values.ndim == 1:
+        values, indices = values[None, :], indices[None, :]
+    rows = values.shape[0]
+    out = np.zeros((rows, n), dtype=values.dtype)
+    mask = np.zeros((rows, n), dtype=np.uint8)
+    for r in range(rows):
+        out[r, indices[r]] = values[r]
+        mask[r, indices[r]] = 1
+    return out, mask

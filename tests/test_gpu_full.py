@@ -2,8 +2,10 @@
 benchmark times (default parameters, fresh sampler seed per call).  The CPU
 oracle computes every one of these in seconds, so the comparison is complete:
 every index and every value bit of every row."""
+import numpy as np
 import pytest
 
+import oracle
 import workloads
 from gpu_util import assert_same, run_gpu, say, to_dev
 
@@ -43,3 +45,24 @@ def test_config5_batchtopk_bf16():
     xt = to_dev(flat, dt)
     gv, gi = run_gpu(flat, ks[0], dt, xt=xt)
     assert_same(gv, gi, flat, ks[0], dt, "c5")
+
+
+def test_config5_batchtopk_sparse_activation():
+    # the BatchTopK consumer at full size: the [4096, 65536] bf16 activations
+    # with their 131072 largest kept and zeros elsewhere, and the mask
+    import torch
+    import top_selection_sample_amd as tss
+    x, dt, ks, _ = workloads.config("c5")
+    K = ks[0]
+    say("config 5 consumer: batchtopk [4096, 65536] bf16, K=131072")
+    acts = to_dev(x, dt)
+    out, m = tss.batchtopk(acts, K, mask=True)
+    torch.cuda.synchronize()
+    ov, oi = oracle.topk(x.reshape(1, -1), K, dt)
+    flat = out.reshape(-1)
+    assert int(m.sum()) == K
+    assert int(torch.count_nonzero(flat)) == K   # every kept ReLU activation is positive
+    idx = torch.from_numpy(oi.reshape(-1)).cuda()
+    got = flat[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert got.tobytes() == ov.reshape(-1).tobytes()
+    assert int(m.reshape(-1)[idx].sum()) == K

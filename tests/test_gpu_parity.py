@@ -419,3 +419,76 @@ def test_stream_read_reads_and_writes_nothing():
         tss.stream_read(x[1:5], sink)   # 4-byte aligned only
     with pytest.raises(tss.TopkError):
         tss.stream_read(x[:3], sink)    # 12 bytes
+
+
+# ------------------------------------------------- BatchTopK consumer
+def _dense_to_host(t, dt):
+    import numpy as np
+    if dt == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("dt,rows,n,k", [("float32", 3, 5000, 37), ("bf16", 2, 70001, 900),
+                                         ("int32", 1, 4096, 4096), ("float32", 4, 300000, 5000)])
+def test_scatter_matches_oracle(dt, rows, n, k):
+    from gpu_util import vals_to_host
+    tss = _tss()
+    g = np.random.default_rng(rows * 1000 + k)
+    if dt == "float32":
+        x = np.maximum(g.standard_normal((rows, n)), 0).astype(np.float32)
+    elif dt == "bf16":
+        x = workloads.f32_to_bf16_bits(np.maximum(g.standard_normal((rows, n)), 0).astype(np.float32))
+    else:
+        x = g.integers(-50, 50, size=(rows, n)).astype(np.int32)
+    say(f"scatter {dt} rows={rows} n={n} k={k}")
+    xt = to_dev(x, dt)
+    v, i = tss.topk(xt, k)
+    out, m = tss.scatter(v, i, n, mask=True)
+    torch.cuda.synchronize()
+    ov, oi = oracle.topk(x, k, dt)
+    edense, emask = oracle.sparse_activation(ov, oi, n)
+    assert _dense_to_host(out, dt).tobytes() == edense.tobytes()
+    assert np.array_equal(m.cpu().numpy(), emask)
+
+
+def test_batchtopk_flattened_matches_oracle():
+    tss = _tss()
+    g = np.random.default_rng(77)
+    B, d, K = 64, 4096, 2048
+    x = workloads.f32_to_bf16_bits(np.maximum(g.standard_normal((B, d)), 0).astype(np.float32))
+    say(f"batchtopk bf16 [{B}, {d}] K={K}")
+    acts = to_dev(x, "bf16")
+    out, m = tss.batchtopk(acts, K, mask=True)
+    torch.cuda.synchronize()
+    ov, oi = oracle.topk(x.reshape(1, -1), K, "bf16")
+    edense, emask = oracle.sparse_activation(ov, oi, B * d)
+    assert out.shape == (B, d) and m.shape == (B, d)
+    assert _dense_to_host(out, "bf16").reshape(-1).tobytes() == edense.reshape(-1).tobytes()
+    assert np.array_equal(m.cpu().numpy().reshape(-1), emask.reshape(-1))
+
+
+def test_scatter_unaligned_output_and_errors():
+    # an output that starts 2 bytes past a 16-byte boundary: head and tail
+    # bytes of the zero fill; stale data must not survive
+    tss = _tss()
+    n, k = 1000, 10
+    x = torch.arange(n, dtype=torch.float32, device="cuda").reshape(1, n)
+    v, i = tss.topk(x, k)
+    big = torch.full((1 + n + 15,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = v.to(torch.bfloat16)
+    out = big[1:1 + n]
+    tss.scatter(vb, i, n, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    expect = np.zeros(n, dtype=np.float32)
+    expect[i.cpu().numpy().reshape(-1)] = vb.float().cpu().numpy().reshape(-1)   # bf16-rounded
+    assert np.array_equal(got, expect)
+    assert int(np.count_nonzero(got)) == k
+    assert bool(torch.isnan(big[0].float())) and bool(torch.isnan(big[1 + n].float()))
+    lib = tss._lib.lib
+    with pytest.raises(tss.TopkError):
+        tss._lib.check(lib.topk_scatter(v.data_ptr(), i.data_ptr(), 1, k, n, 1, None, None, None), "s")
+    with pytest.raises(tss.TopkError):
+        tss._lib.check(lib.topk_scatter(v.data_ptr(), i.data_ptr(), 1, n + 1, n, 1, out.data_ptr(),
+                                        None, None), "s")

@@ -185,3 +185,46 @@ def test_bf16_rounding_matches_torch():
     ours = workloads.f32_to_bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------- BatchTopK consumer
+@pytest.mark.parametrize("dtype,seed", [("f32", 5), ("bf16", 6), ("i32", 7)])
+def test_sparse_activation_is_the_rank_mask(dtype, seed):
+    # Prof-K section 5: the kept activations are the K largest of the
+    # flattened matrix.  The expected sparse activation is built straight
+    # from the rank definition (elements of rank < K keep their bits, the
+    # rest are zero), with no top-k or scatter involved.
+    g = np.random.default_rng(seed)
+    B, d, K = 12, 40, 37
+    if dtype == "f32":
+        x = np.maximum(g.standard_normal((B, d)).astype(np.float32), 0)   # ReLU: many ties at 0
+        dt = None
+    elif dtype == "bf16":
+        x = workloads.f32_to_bf16_bits(np.maximum(g.standard_normal((B, d)), 0).astype(np.float32))
+        dt = "bf16"
+    else:
+        x = g.integers(-5, 6, size=(B, d)).astype(np.int32)
+        dt = None
+    flat = x.reshape(-1)
+    ranks = oracle.rank_by_counting(flat, dt)
+    expect = np.where(ranks < K, flat, np.zeros_like(flat)).reshape(B, d)
+    vals, idx = oracle.topk(flat, K, dt)
+    dense, mask = oracle.sparse_activation(vals, idx, B * d)
+    assert np.array_equal(dense.reshape(B, d).view(np.uint8), expect.view(np.uint8))
+    assert np.array_equal(mask.reshape(-1), (ranks < K).astype(np.uint8))
+    assert int(mask.sum()) == K
+
+
+def test_sparse_activation_brute_force_rows():
+    # a second, loop-by-loop construction on tiny batched rows
+    g = np.random.default_rng(11)
+    vals = g.standard_normal((3, 4)).astype(np.float32)
+    idx = np.stack([g.permutation(9)[:4] for _ in range(3)]).astype(np.int64)
+    dense, mask = oracle.sparse_activation(vals, idx, 9)
+    for r in range(3):
+        for c in range(9):
+            hit = [j for j in range(4) if idx[r, j] == c]
+            if hit:
+                assert dense[r, c] == vals[r, hit[0]] and mask[r, c] == 1
+            else:
+                assert dense[r, c] == 0 and mask[r, c] == 0

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED, Params,
                    TopkError, default_params)
 
-__all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "workspace_size", "read_stats",
+__all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "scatter", "batchtopk",
+           "workspace_size", "read_stats",
            "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code"]
@@ -161,3 +162,57 @@ def stream_read(x: torch.Tensor, sink: torch.Tensor) -> None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
         _lib.check(_lib.lib.topk_stream_read(x.data_ptr(), x.numel() * x.element_size(),
                                              sink.data_ptr(), stream), "topk_stream_read")
+
+
+def scatter(values: torch.Tensor, indices: torch.Tensor, n: int, out: torch.Tensor | None = None,
+            mask: torch.Tensor | bool | None = None):
+    """Sparse activation from a selection: ``out[r, indices[r, j]] = values[r, j]``,
+    every other element zero (BatchTopK, Prof-K section 5).  ``values`` and
+    ``indices`` are [rows, k] (or [k]) as ``topk`` returns them; ``out`` is
+    [rows, n] of the values' dtype (allocated when None).  ``mask=True`` also
+    returns a uint8 [rows, n] mask of the kept places (or pass a tensor to fill).
+    Returns ``out``, or ``(out, mask)`` when a mask is asked for."""
+    squeeze = values.dim() == 1
+    v2 = values.reshape(1, -1) if squeeze else values
+    i2 = indices.reshape(1, -1) if squeeze else indices
+    if not (v2.is_cuda and i2.is_cuda and v2.is_contiguous() and i2.is_contiguous()
+            and i2.dtype == torch.int64 and v2.shape == i2.shape):
+        raise ValueError("values, indices: contiguous GPU tensors of one shape, indices int64")
+    rows, k = v2.shape
+    dev = v2.device
+    if out is None:
+        out = torch.empty((rows, n), dtype=v2.dtype, device=dev)
+    m = None
+    if mask is True:
+        m = torch.empty((rows, n), dtype=torch.uint8, device=dev)
+    elif isinstance(mask, torch.Tensor):
+        m = mask
+    if not (out.is_cuda and out.is_contiguous() and out.dtype == v2.dtype and out.numel() == rows * n):
+        raise ValueError("out: contiguous GPU tensor of rows * n elements, the values' dtype")
+    if m is not None and not (m.is_cuda and m.is_contiguous() and m.dtype == torch.uint8
+                              and m.numel() == rows * n):
+        raise ValueError("mask: contiguous uint8 GPU tensor of rows * n elements")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.check(_lib.lib.topk_scatter(v2.data_ptr(), i2.data_ptr(), rows, k, n, dtype_code(v2.dtype),
+                                         out.data_ptr(), m.data_ptr() if m is not None else None,
+                                         stream), "topk_scatter")
+    if squeeze:
+        out = out.reshape(-1)
+        m = m.reshape(-1) if m is not None else None
+    return (out, m) if m is not None else out
+
+
+def batchtopk(acts: torch.Tensor, k_total: int, params: Params | None = None, mask: bool = False):
+    """BatchTopK (Prof-K section 5): keep the ``k_total`` largest entries of the
+    whole [B, d] activation matrix (one flattened top-k) and zero the rest.
+    Returns the sparse [B, d] activation, and its uint8 mask if asked."""
+    if acts.dim() != 2 or not acts.is_contiguous():
+        raise ValueError("acts must be a contiguous [B, d] tensor")
+    flat = acts.reshape(1, -1)
+    vals, idx = topk(flat, k_total, params=params)
+    res = scatter(vals, idx, flat.shape[1], mask=mask)
+    if mask:
+        out, m = res
+        return out.reshape(acts.shape), m.reshape(acts.shape)
+    return res.reshape(acts.shape)

@@ -20,7 +20,7 @@ PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
            "topk", "topk_ex", "topk_read_stats", "topk_profile_enable", "topk_profile_read",
-           "topk_stream_read", "topk_status_string")
+           "topk_scatter", "topk_stream_read", "topk_status_string")
 STAGES = ("sample", "tau", "filter", "refine", "exact", "sort")
 
 
@@ -70,6 +70,7 @@ def _load():
     L.topk_profile_enable.argtypes = [i32]
     L.topk_profile_read.argtypes = [P(StageTimes)]
     L.topk_stream_read.argtypes = [vp, sz, vp, vp]
+    L.topk_scatter.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
     L.topk_status_string.argtypes = [i32]
     L.topk_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:

@@ -326,6 +326,22 @@ int topk_profile_read(topk_stage_times* out) {
   return rc;
 }
 
+int topk_scatter(const void* values, const int64_t* indices, int64_t rows, int64_t k, int64_t n,
+                 int dtype, void* out_dense, uint8_t* out_mask, void* stream) {
+  if (dtype != TOPK_I32 && dtype != TOPK_F32 && dtype != TOPK_BF16) return TOPK_EDTYPE;
+  if (rows < 0 || k < 0 || n < 0 || k > n || (!out_dense && !out_mask)) return TOPK_EINVAL;
+  if (rows * k > 0 && (!values || !indices)) return TOPK_EINVAL;
+  const uintptr_t es = (dtype == TOPK_BF16) ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(values) % es || reinterpret_cast<uintptr_t>(out_dense) % es ||
+      reinterpret_cast<uintptr_t>(indices) % 8)
+    return TOPK_EINVAL;
+  if ((uint64_t)rows * (uint64_t)k > 0xFFFFFFFFull * 256ull) return TOPK_EINVAL;
+  const hipError_t e = tk::launch_scatter(values, indices, (uint64_t)rows, (uint64_t)k, (uint64_t)n,
+                                          dtype,
+                                          out_dense, out_mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
+}
+
 int topk_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
   if (!data || !sink || bytes == 0) return TOPK_EINVAL;
   if (reinterpret_cast<uintptr_t>(data) % 16 || bytes % 16 || reinterpret_cast<uintptr_t>(sink) % 4)

@@ -2523,6 +2523,102 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ======================================================================
+// BatchTopK consumer (Prof-K section 5, "Application: BatchTopK Sparse
+// Autoencoders": the batch-global selection keeps the K largest of the
+// flattened B x d_dict activations).  The kept activations stay where they
+// were and every other entry becomes zero; a mask marks the kept ones.
+// Two launches on the caller's stream: a zero fill of the outputs, then one
+// thread per winner writes it back.
+// ======================================================================
+constexpr uint32_t FILL_THREADS = 512;
+constexpr uint32_t FILL_UNROLL = 4;
+
+// Zero bytes [0, bytes) of p: the 16-byte aligned middle with nontemporal
+// 16-byte stores, one contiguous slice per workgroup (FILL_UNROLL stores per
+// lane per step); the unaligned head and tail bytes by workgroup 0.  Swept on
+// MI355X over 512 MB followed by a 131072-element scatter: every
+// nontemporal shape ends at 103-104 us (as does the runtime's memset), while
+// plain stores, faster alone, end at 112-124 us because the fill's dirty L2
+// lines are written back before the scatter runs.
+__global__ __launch_bounds__(FILL_THREADS) void k_fill_zero(unsigned char* __restrict__ p,
+                                                             size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  size_t head = (16u - (a & 15u)) & 15u;
+  if (head > bytes) head = bytes;
+  const size_t nvec = (bytes - head) / 16;
+  const size_t tail0 = head + nvec * 16;
+  u32x4* vp = reinterpret_cast<u32x4*>(p + head);
+  constexpr size_t step = (size_t)FILL_THREADS * FILL_UNROLL;
+  const size_t per = ((nvec + gridDim.x - 1) / gridDim.x + step - 1) / step * step;
+  const size_t v0 = (size_t)blockIdx.x * per;
+  const size_t v1 = v0 + per < nvec ? v0 + per : nvec;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  size_t b = v0;
+  for (; b + step <= v1; b += step) {
+#pragma unroll
+    for (uint32_t u = 0; u < FILL_UNROLL; ++u)
+      __builtin_nontemporal_store(z, vp + b + threadIdx.x + u * FILL_THREADS);
+  }
+  for (size_t i = b + threadIdx.x; i < v1; i += FILL_THREADS) __builtin_nontemporal_store(z, vp + i);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < head) p[threadIdx.x] = 0;
+    if (threadIdx.x < bytes - tail0) p[tail0 + threadIdx.x] = 0;
+  }
+}
+
+template <int DT>
+__global__ void k_scatter_winners(const void* __restrict__ values, const int64_t* __restrict__ idx,
+                                  uint64_t rows, uint64_t k, uint64_t n,
+                                  void* __restrict__ out_dense, unsigned char* __restrict__ out_mask) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * k) return;
+  const uint64_t r = i / k;
+  const int64_t j = idx[i];
+  if (j < 0 || (uint64_t)j >= n) return;   // not an index of the row: skipped
+  const uint64_t o = r * n + (uint64_t)j;
+  if (out_dense) {
+    if constexpr (DT == DT_BF16)
+      static_cast<uint16_t*>(out_dense)[o] = static_cast<const uint16_t*>(values)[i];
+    else
+      static_cast<uint32_t*>(out_dense)[o] = static_cast<const uint32_t*>(values)[i];
+  }
+  if (out_mask) out_mask[o] = 1;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (!bytes) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (cus <= 0) cus = 1;
+  size_t grid = (size_t)cus * 2;
+  const size_t vecs = bytes / 16;
+  const size_t want = (vecs + (size_t)FILL_THREADS * FILL_UNROLL - 1) / ((size_t)FILL_THREADS * FILL_UNROLL);
+  if (want < grid) grid = want ? want : 1;
+  hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)grid), dim3(FILL_THREADS), 0, s,
+                     static_cast<unsigned char*>(p), bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const void* values, const int64_t* idx, uint64_t rows, uint64_t k,
+                          uint64_t n, int dtype, void* out_dense, unsigned char* out_mask,
+                          hipStream_t s) {
+  const uint64_t es = dtype == DT_BF16 ? 2 : 4;
+  hipError_t e = hipSuccess;
+  if (out_dense) e = launch_fill_zero(out_dense, rows * n * es, s);
+  if (e == hipSuccess && out_mask) e = launch_fill_zero(out_mask, rows * n, s);
+  if (e != hipSuccess) return e;
+  const uint64_t total = rows * k;
+  if (!total) return hipSuccess;
+  const dim3 grid((uint32_t)((total + 255) / 256));
+  TK_DISPATCH(dtype, k_scatter_winners, grid, dim3(256), 0, s, values, idx, rows, k, n, out_dense,
+              out_mask);
+  return hipGetLastError();
+}
+
 uint32_t filter_threads() { return FILTER_THREADS; }
 uint32_t filter_unroll() { return FILTER_UNROLL; }
 uint32_t sort_tile() { return SORT_TILE; }

@@ -62,6 +62,9 @@ struct LaunchArgs {
 hipError_t launch_pipeline(const LaunchArgs& a);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_scatter(const void* values, const int64_t* idx, uint64_t rows, uint64_t k,
+                          uint64_t n, int dtype, void* out_dense, unsigned char* out_mask,
+                          hipStream_t s);
 uint32_t filter_threads();
 uint32_t filter_unroll();
 uint32_t sort_tile();
