@@ -63,10 +63,12 @@ struct alignas(128) RowCtr {
   uint32_t pad0[31];
   uint32_t tslots;      // tie-region slots claimed
   uint32_t pad1[31];
-  uint32_t kmax;        // largest key above tau (large k only)
+  uint32_t kmax;        // largest key above tau
   uint32_t pad2[31];
+  uint32_t above;       // elements above tau (a count the finish kernel never rewrites)
+  uint32_t pad3[31];
 };
-static_assert(sizeof(RowCtr) == 384, "three 128-byte lines");
+static_assert(sizeof(RowCtr) == 512, "four 128-byte lines");
 
 // Per-call record shared by all rows: the rows sent to the exact route.
 // Zero between calls (the exact-route kernel clears it when it is done).

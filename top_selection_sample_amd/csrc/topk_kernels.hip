@@ -172,6 +172,7 @@ __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint
   rc->ties = 0;
   rc->tslots = 0;
   rc->kmax = 0;
+  rc->above = 0;
   st->path = PATH_SAMPLED;
   st->passes = 0;
   st->kmax = 0;
@@ -829,6 +830,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     s_base = total ? atomicAdd(&st->count, total) : 0u;
     s_tbase = ttotal ? atomicAdd(&rc->tslots, ttotal) : 0u;
     if (tcount) atomicAdd(&rc->ties, tcount);
+    if (total) atomicAdd(&rc->above, total);
   }
   __syncthreads();
   uint32_t off = s_base, toff = s_tbase;
@@ -1468,6 +1470,101 @@ __device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint
   return g;
 }
 
+// ======================================================================
+// Large k, capacity up to LK_CAP_MAX: bucket sort of the candidates.
+// Composites are unique and every candidate key lies in [lo, kmax] (lo =
+// RowState::thr_key, the threshold the candidates passed; kmax tracked by
+// the filters), so
+//     v = (key - lo) << bl | (low bl bits of the inverted index)
+// (bl = index bits that vary, 2^bl >= n) orders the candidates exactly as
+// their composites do, with no constant bits in between.  Its top 12 bits
+// are the bucket:
+//   k_lk_hist     bucket histogram (one LDS histogram per 4096 candidates)
+//   k_lk_scatter  bucket starts (descending order), then every candidate of
+//                 a bucket that starts below k goes to its bucket in aux
+//   k_lk_sort     one workgroup per LK_WIN output positions sorts the buckets
+//                 starting there in LDS and writes the winners directly; a
+//                 bucket too large for LDS is split further in the
+//                 workgroup (11-bit digits below the common prefix of its
+//                 smallest and largest value, through global scratch).
+// Workspace lk (u32): [rows][4096] histogram, [rows][4096] fill counters
+// (both zero between calls), [rows][LK_STRIDE] bucket starts by rank
+// (rank r = 4095 - bucket, so starts ascend with r; entry 4096 = the total),
+// [rows][2][LK_MAXWIN] per sort window the first and last rank of the
+// non-empty buckets starting in it (first = ~0: none).
+// ======================================================================
+constexpr uint32_t LK_BITS = 12;
+constexpr uint32_t LK_BINS = 1u << LK_BITS;
+constexpr uint32_t LK_STRIDE = LK_BINS + 4;
+constexpr uint32_t LK_THREADS = 1024;
+constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
+constexpr uint32_t LK_WIN = 1024;               // output positions per sort workgroup
+constexpr uint32_t LK_LCAP = 2048;              // largest range sorted in LDS
+constexpr uint32_t LK_STACK = 1024;             // pending oversized ranges per workgroup
+constexpr uint32_t LK_MAXWIN = (uint32_t)(LK_CAP_MAX / LK_WIN);
+static_assert(LK_WORDS_PER_ROW == 2 * LK_BINS + LK_STRIDE + 2 * LK_MAXWIN, "workspace layout");
+static_assert((int64_t)LK_STACK * LK_LCAP >= LK_CAP_MAX,
+              "oversized ranges are disjoint and larger than LK_LCAP, so at most "
+              "LK_CAP_MAX / LK_LCAP of them are ever pending");
+static_assert(LK_LCAP >= 2 * LK_WIN, "a window's small buckets fit one LDS sort");
+
+struct LkDigit {
+  uint32_t B, bl, lo, shift;
+  uint64_t low;
+  // v of a composite, and back
+  __device__ uint64_t compact(uint64_t c) const { return (((c >> B) - lo) << bl) | (c & low); }
+  __device__ uint64_t expand(uint64_t v) const {
+    const uint64_t mask_b = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+    return (((v >> bl) + lo) << B) | (mask_b & ~low) | (v & low);
+  }
+  __device__ uint32_t operator()(uint64_t c) const {   // bucket of a composite
+    const uint64_t d = compact(c) >> shift;
+    return d < LK_BINS ? (uint32_t)d : LK_BINS - 1;   // (always below: key <= kmax)
+  }
+};
+
+__device__ __forceinline__ LkDigit lk_digit(uint32_t lo, uint32_t kmax, uint32_t B, uint32_t bl) {
+  LkDigit g;
+  g.B = B;
+  g.bl = bl;
+  g.lo = lo;
+  g.low = (1ull << bl) - 1ull;   // bl <= 32
+  const uint32_t hi = kmax > g.lo ? kmax : g.lo;
+  const uint64_t vmax = ((uint64_t)(hi - g.lo) << bl) | g.low;
+  const uint32_t tb = vmax ? 64u - (uint32_t)__builtin_clzll(vmax) : 0u;
+  g.shift = tb > LK_BITS ? tb - LK_BITS : 0u;
+  return g;
+}
+
+__device__ __forceinline__ LkDigit lk_digit_of(const RowState& st, uint32_t B, uint32_t bl) {
+  return lk_digit(st.thr_key, st.kmax, B, bl);
+}
+
+// One LK_CHUNK of a row's candidates into the row's bucket histogram (lk):
+// an LDS histogram, then one global atomic per non-empty bucket.  Candidate
+// i is cb[i] below G and tb[i - G] from G on (the tie region, for a row
+// whose ties join its candidates before they are copied over).  Every
+// thread of the workgroup calls it; h: LK_BINS words of LDS.
+__device__ void lk_hist_chunk(const uint64_t* __restrict__ cb, const uint64_t* __restrict__ tb,
+                              uint32_t G, uint32_t R, uint32_t base, const LkDigit& g,
+                              uint32_t* __restrict__ gh, uint32_t* h) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  for (uint32_t i = tid; i < LK_BINS; i += nt) h[i] = 0;
+  uint64_t c[4];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t i = base + j * nt + tid;
+    c[j] = i < R ? (i < G ? cb[i] : tb[i - G]) : 0ull;
+  }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) hist_add(h, g(c[j]), base + j * nt + tid < R);
+  __syncthreads();
+  for (uint32_t i = tid; i < LK_BINS; i += nt)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+  __syncthreads();
+}
+
 // How the finish kernel learns which rows failed the check.
 //  FIN_SCAN: sampled route with at most FIN_SCAN_ROWS rows: every workgroup
 //    reads every row's survivor count itself.  All reach the same verdict
@@ -1476,6 +1573,9 @@ __device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint
 //    the row failed.  The common case (no failure) then needs no barrier.
 //  FIN_LISTED: an earlier kernel listed the failed rows (nflag, flagged[]).
 enum : uint32_t { FIN_SCAN = 0, FIN_LISTED = 1 };
+// k_finish builds the large-k bucket histograms of the accepted sampled rows
+// and/or of the exact route's rows (the first step of the bucket sort).
+enum : uint32_t { LK_HIST_SAMPLED = 1, LK_HIST_EXACT = 2 };
 constexpr uint32_t FIN_SCAN_ROWS = 1024;
 
 template <int DT>
@@ -1485,7 +1585,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     uint32_t* __restrict__ ghist,
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
     uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode, void* __restrict__ out_values,
-    int64_t* __restrict__ out_idx) {
+    int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk, uint32_t bl, uint32_t lk_flags) {
   using D = Dt<DT>;
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -1572,6 +1672,28 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, k, B, W, out_values,
                          out_idx, r, s_hist, s_misc, s_tmp, s_cand,
                          reinterpret_cast<uint64_t*>(s_keys));
+    }
+  }
+  // Large k: the bucket histograms of the accepted sampled rows (the first
+  // step of the bucket sort), LK_CHUNK candidates per workgroup and step.
+  // Every count read here is final: the filter's above-tau count and tie
+  // count, tau and the largest key (the row's owner rewrites only the
+  // RowState count, and copies the ties later; they are read from the tie
+  // region).
+  if (lk_flags & LK_HIST_SAMPLED) {
+    const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
+    const uint64_t npairs = (uint64_t)rows * maxch;
+    for (uint64_t q = blockIdx.x; q < npairs; q += G) {
+      const uint32_t r = (uint32_t)(q / maxch), c = (uint32_t)(q % maxch);
+      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
+      const uint32_t v = sampled_verdict(Ga, E, k, cap);
+      if (v == V_FAIL) continue;   // the exact route's rows: below
+      uint32_t R = v == V_OK_TIES ? Ga + E : Ga;
+      if (R > cap) R = cap;
+      if ((uint64_t)c * LK_CHUNK >= R) continue;
+      const LkDigit g = lk_digit(states[r].tau_key, rctr[r].kmax, B, bl);
+      lk_hist_chunk(cbuf + (size_t)r * cap, tbuf + (size_t)r * cap, Ga, R, c * LK_CHUNK, g,
+                    lk + (size_t)r * LK_BINS, s_keys);
     }
   }
   if (nf == 0) return;                        // the common case: nothing more to do
@@ -1809,6 +1931,20 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     cs->nflag = 0;
     cs->nactive = 0;
   }
+  // Large k: the exact route's rows into their bucket histograms (their
+  // count, threshold and largest key were final at the last grid barrier)
+  if (!small_k && (lk_flags & LK_HIST_EXACT)) {
+    const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
+    const uint64_t npairs = (uint64_t)nf * maxch;
+    for (uint64_t q = blockIdx.x; q < npairs; q += G) {
+      const uint32_t row = flagged[q / maxch], c = (uint32_t)(q % maxch);
+      const RowState st = states[row];
+      const uint32_t R = st.count < cap ? st.count : cap;
+      if ((uint64_t)c * LK_CHUNK >= R) continue;
+      lk_hist_chunk(cbuf + (size_t)row * cap, cbuf + (size_t)row * cap, R, R, c * LK_CHUNK,
+                    lk_digit_of(st, B, bl), lk + (size_t)row * LK_BINS, s_keys);
+    }
+  }
 }
 
 // ======================================================================
@@ -1905,72 +2041,6 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
     case DT_F32: hipLaunchKernelGGL(KERNEL<DT_F32>, __VA_ARGS__); break;      \
     default: hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__); break;         \
   }
-
-// ======================================================================
-// Large k, capacity up to LK_CAP_MAX: bucket sort of the candidates.
-// Composites are unique and every candidate key lies in [lo, kmax] (lo =
-// RowState::thr_key, the threshold the candidates passed; kmax tracked by
-// the filters), so
-//     v = (key - lo) << bl | (low bl bits of the inverted index)
-// (bl = index bits that vary, 2^bl >= n) orders the candidates exactly as
-// their composites do, with no constant bits in between.  Its top 12 bits
-// are the bucket:
-//   k_lk_hist     bucket histogram (one LDS histogram per 4096 candidates)
-//   k_lk_scatter  bucket starts (descending order), then every candidate of
-//                 a bucket that starts below k goes to its bucket in aux
-//   k_lk_sort     one workgroup per LK_WIN output positions sorts the buckets
-//                 starting there in LDS and writes the winners directly; a
-//                 bucket too large for LDS is split further in the
-//                 workgroup (11-bit digits below the common prefix of its
-//                 smallest and largest value, through global scratch).
-// Workspace lk (u32): [rows][4096] histogram, [rows][4096] fill counters
-// (both zero between calls), [rows][LK_STRIDE] bucket starts by rank
-// (rank r = 4095 - bucket, so starts ascend with r; entry 4096 = the total),
-// [rows][2][LK_MAXWIN] per sort window the first and last rank of the
-// non-empty buckets starting in it (first = ~0: none).
-// ======================================================================
-constexpr uint32_t LK_BITS = 12;
-constexpr uint32_t LK_BINS = 1u << LK_BITS;
-constexpr uint32_t LK_STRIDE = LK_BINS + 4;
-constexpr uint32_t LK_THREADS = 1024;
-constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
-constexpr uint32_t LK_WIN = 1024;               // output positions per sort workgroup
-constexpr uint32_t LK_LCAP = 2048;              // largest range sorted in LDS
-constexpr uint32_t LK_STACK = 1024;             // pending oversized ranges per workgroup
-constexpr uint32_t LK_MAXWIN = (uint32_t)(LK_CAP_MAX / LK_WIN);
-static_assert(LK_WORDS_PER_ROW == 2 * LK_BINS + LK_STRIDE + 2 * LK_MAXWIN, "workspace layout");
-static_assert((int64_t)LK_STACK * LK_LCAP >= LK_CAP_MAX,
-              "oversized ranges are disjoint and larger than LK_LCAP, so at most "
-              "LK_CAP_MAX / LK_LCAP of them are ever pending");
-static_assert(LK_LCAP >= 2 * LK_WIN, "a window's small buckets fit one LDS sort");
-
-struct LkDigit {
-  uint32_t B, bl, lo, shift;
-  uint64_t low;
-  // v of a composite, and back
-  __device__ uint64_t compact(uint64_t c) const { return (((c >> B) - lo) << bl) | (c & low); }
-  __device__ uint64_t expand(uint64_t v) const {
-    const uint64_t mask_b = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
-    return (((v >> bl) + lo) << B) | (mask_b & ~low) | (v & low);
-  }
-  __device__ uint32_t operator()(uint64_t c) const {   // bucket of a composite
-    const uint64_t d = compact(c) >> shift;
-    return d < LK_BINS ? (uint32_t)d : LK_BINS - 1;   // (always below: key <= kmax)
-  }
-};
-
-__device__ __forceinline__ LkDigit lk_digit_of(const RowState& st, uint32_t B, uint32_t bl) {
-  LkDigit g;
-  g.B = B;
-  g.bl = bl;
-  g.lo = st.thr_key;
-  g.low = (1ull << bl) - 1ull;   // bl <= 32
-  const uint32_t hi = st.kmax > g.lo ? st.kmax : g.lo;
-  const uint64_t vmax = ((uint64_t)(hi - g.lo) << bl) | g.low;
-  const uint32_t tb = vmax ? 64u - (uint32_t)__builtin_clzll(vmax) : 0u;
-  g.shift = tb > LK_BITS ? tb - LK_BITS : 0u;
-  return g;
-}
 
 __global__ __launch_bounds__(LK_THREADS) void k_lk_hist(const RowState* __restrict__ states,
                                                         const uint64_t* __restrict__ cbuf,
@@ -2369,7 +2439,8 @@ hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hi
 }
 
 template <int DT>
-static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t mode) {
+static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t mode,
+                                uint32_t bl, uint32_t lk_flags) {
   // one workgroup per compute unit (cached per device)
   static int cached[64] = {0};
   int dev = 0;
@@ -2386,13 +2457,17 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
-                     a.out_values, a.out_idx);
+                     a.out_values, a.out_idx, a.lk, bl, lk_flags);
   return hipGetLastError();
 }
 
 hipError_t launch_pipeline(const LaunchArgs& a) {
   const Plan& p = a.plan;
   const uint32_t rows = (uint32_t)p.rows, n = (uint32_t)p.n, k = (uint32_t)p.k;
+  const bool bucket_sort = !p.small_k && p.cap <= LK_CAP_MAX;
+  uint32_t bl = 0;   // index bits that vary: 2^bl >= n
+  while (bl < 32 && (1ull << bl) < (uint64_t)n) ++bl;
+  bool hist_done = false;
   const uint32_t cap = (uint32_t)p.cap, B = p.B, W = p.W;
   hipStream_t s = a.stream;
   const int dt = p.dtype;
@@ -2453,21 +2528,24 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     const int stage = p.path == PLAN_SAMPLED ? STAGE_REFINE : STAGE_EXACT;
     mark(stage, 1);
     const uint32_t sk = p.small_k ? 1u : 0u;
+    // large k: the first bucket-sort step (histograms) runs inside k_finish
+    uint32_t lkf = 0;
+    if (bucket_sort) lkf = LK_HIST_EXACT | (p.path == PLAN_SAMPLED ? LK_HIST_SAMPLED : 0u);
     switch (dt) {
-      case DT_I32: e = launch_finish<DT_I32>(a, sk, mode); break;
-      case DT_F32: e = launch_finish<DT_F32>(a, sk, mode); break;
-      default: e = launch_finish<DT_BF16>(a, sk, mode); break;
+      case DT_I32: e = launch_finish<DT_I32>(a, sk, mode, bl, lkf); break;
+      case DT_F32: e = launch_finish<DT_F32>(a, sk, mode, bl, lkf); break;
+      default: e = launch_finish<DT_BF16>(a, sk, mode, bl, lkf); break;
     }
+    hist_done = lkf != 0;
     if (e != hipSuccess) return e;
     mark(stage, 0);
   }
-  if (!p.small_k && p.cap <= LK_CAP_MAX) {
+  if (bucket_sort) {
     // every row now holds R in [k, cap] candidates: bucket sort, keep k
     mark(STAGE_SORT, 1);
-    uint32_t bl = 0;   // index bits that vary: 2^bl >= n
-    while (bl < 32 && (1ull << bl) < (uint64_t)n) ++bl;
     const dim3 hg((cap + LK_CHUNK - 1) / LK_CHUNK, rows);
-    hipLaunchKernelGGL(k_lk_hist, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, cap, B, bl, a.lk);
+    if (!hist_done)
+      hipLaunchKernelGGL(k_lk_hist, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, cap, B, bl, a.lk);
     hipLaunchKernelGGL(k_lk_scatter, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, a.aux, cap, k,
                        B, bl, a.lk, rows);
     const dim3 sgr((k + LK_WIN - 1) / LK_WIN, rows);

@@ -366,8 +366,8 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   if (!p.small_k || p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.off_lk = off;   // large k: bucket histogram, fill counters, starts, sort windows
   if (!p.small_k && p.cap <= LK_CAP_MAX) off = align256(off + (size_t)rows * LK_WORDS_PER_ROW * 4);
-  p.off_rctr = off;   // sampled route: three 128-byte counter lines per row
-  if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 384);
+  p.off_rctr = off;   // sampled route: four 128-byte counter lines per row
+  if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 512);
   p.total = off;
   *out = p;
   return 0;
