@@ -106,6 +106,16 @@ typedef struct {
   double tuned_ratio; /* TUNED policy, k <= 4096: tau_B / tau_A of this engine (default 0.13) */
   int64_t tuned_s_min;/* TUNED policy: least sample size considered (default 1024) */
   double tuned_ratio_large; /* TUNED policy, k > 4096: tau_B / tau_A (default 0.01) */
+  double recall;      /* recall target rho in (0, 1] (default 1: exact).  Prof-K's
+                         relaxed-recall trade (abstract; section 1): below 1 the
+                         parameters are chosen for k_eff = ceil(rho * k) instead of
+                         k, and a row where at least k_eff but fewer than k
+                         elements reach tau (and they fit the buffer) keeps them
+                         instead of taking the exact route.  Every one of them is a
+                         true top-k element; they fill the first slots of the row
+                         in rank order, and the remaining slots get index -1 and
+                         the dtype's lowest value (-inf, or INT32_MIN).  Rows with
+                         k or more survivors are exact as before. */
 } topk_params;
 
 /* Resolved plan of one call shape (host arithmetic only; no GPU needed). */
@@ -116,9 +126,12 @@ typedef struct {
   int64_t cap;        /* candidate buffer capacity per row */
   int32_t index_bits; /* B: bits of the index field of the composite */
   int32_t key_bits;   /* 32 (int32, float32) or 16 (bf16) */
-  double p_recall;    /* P(R < k) per row for distinct values (Lemma 1), sampled route */
+  double p_recall;    /* P(R < k_eff) per row for distinct values (Lemma 1), sampled
+                         route; k_eff = k unless params.recall < 1 */
   double p_overflow;  /* P(R > M) per row for distinct values (Lemma 1), sampled route */
   size_t workspace_bytes;
+  int64_t k_eff;      /* the selection size the parameters were chosen for: k, or
+                         ceil(params.recall * k) below recall 1 */
 } topk_plan_info;
 
 /* Per-row record of the last call on a workspace (topk_read_stats). */
@@ -127,7 +140,8 @@ typedef struct {
   uint32_t r_sampled; /* survivors of the sampled filter pass (R); on an
                          overflow the pass may stop early, and this is then
                          only some count above the buffer capacity */
-  uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only */
+  uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only,
+                         3 sampled with fewer than k survivors kept (recall < 1) */
   uint32_t passes;    /* histogram passes of the exact select */
   uint32_t flags;     /* bit 0: an exact-route grid barrier gave up waiting (the
                          result of that call is not trustworthy; never seen in
@@ -190,7 +204,8 @@ int topk_profile_read(topk_stage_times* out);
  * per element).  values / indices are laid out as topk writes them (for the
  * flattened call rows = 1, n = B*d_dict, k = K); out_dense has the dtype of
  * values.  Either output may be null, not both.  An index outside [0, n) is
- * skipped.  All pointers are device memory; values and out_dense aligned to
+ * skipped (so the padded slots of a relaxed-recall selection, index -1,
+ * write nothing).  All pointers are device memory; values and out_dense aligned to
  * the element size, indices to 8 bytes; the outputs must not overlap the
  * inputs.  Two kernels on `stream` (a zero fill, then one thread per
  * winner), asynchronous.  Errors: TOPK_EDTYPE, TOPK_EINVAL (sizes, k > n,

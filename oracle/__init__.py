@@ -24,6 +24,10 @@ Contents
 * ``sparse_activation``  the BatchTopK consumer (Prof-K section 5): the
                       selected activations kept in place, zero elsewhere,
                       and the mask of the kept places.
+* ``relaxed_selection``  the relaxed-recall trade (Prof-K abstract and
+                      section 1): a row whose survivors number at least
+                      k_eff but fewer than k keeps them, in rank order, and
+                      pads the other slots.
 
 bf16 data is carried as its uint16 bit patterns with ``dtype="bf16"``.
 """
@@ -236,3 +240,37 @@ def sparse_activation(values: np.ndarray, indices: np.ndarray, n: int):
         out[r, indices[r]] = values[r]
         mask[r, indices[r]] = 1
     return out, mask
+
+
+# lowest value of each dtype, the padding of a slot no winner fills (bf16 as
+# its bit pattern)
+PAD_VALUE = {"float32": np.float32(-np.inf), "int32": np.int32(-2 ** 31),
+             "bf16": np.uint16(0xFF80)}
+
+
+def relaxed_selection(row: np.ndarray, k: int, k_eff: int, tau_key: int, cap: int,
+                      dtype: str | None = None):
+    """One row under a relaxed recall target (Prof-K abstract and section 1:
+    recall traded for speed, e.g. 95% of the true top-k).
+
+    Reading: the survivors are the elements whose key is at least tau
+    (stage 3), R of them.  When k_eff <= R < k and R <= cap the row keeps
+    them: sorted by key descending, ties by lower index, they fill slots
+    0..R-1, and slots R..k-1 get index -1 and the dtype's lowest value.
+    Any other row ends with the exact top-k (accepted with R >= k, or taken
+    by the exact fallback).  Returns (values [k], indices [k], partial).
+    """
+    dt = _dtype_name(row, dtype)
+    rv = np.ascontiguousarray(np.asarray(row).reshape(-1))
+    kk = keys(rv, dt).astype(np.int64)
+    surv = np.flatnonzero(kk >= int(tau_key))
+    R = int(surv.size)
+    if not (k_eff <= R < k and R <= cap):
+        v, i = topk(rv, k, dt)
+        return v[0], i[0], False
+    order = surv[np.lexsort((surv, -kk[surv]))]   # key descending, then index
+    vals = np.full(k, PAD_VALUE[dt], dtype=_NP[dt])
+    idx = np.full(k, -1, dtype=np.int64)
+    vals[:R] = rv[order]
+    idx[:R] = order
+    return vals, idx, True

@@ -492,3 +492,111 @@ def test_scatter_unaligned_output_and_errors():
     with pytest.raises(tss.TopkError):
         tss._lib.check(lib.topk_scatter(v.data_ptr(), i.data_ptr(), 1, n + 1, n, 1, out.data_ptr(),
                                         None, None), "s")
+
+
+# ------------------------------------------------------------ relaxed recall
+def _relaxed_case(x, dt, k, S, seed, recall=None, M=100_000):
+    """Run one relaxed-recall call with the sampler forced to t = 1 (tau is
+    the sample maximum, so few elements survive) and compare every row with
+    the oracle's relaxed selection for the same threshold.  recall=None sets
+    the target so that k_eff equals the first row's survivor count."""
+    tss = _tss()
+    rows, n = x.shape
+    kw = dict(S=S, t=1, M=M, force_path=1)
+    pl = tss.plan(n, rows, k, dt, params=_seeded(seed, **kw))
+    taus = [oracle.tau(x[r], seed, r, pl["S"], pl["t"], dt) for r in range(rows)]
+    if recall is None:
+        recall = taus[0][1] / k
+    p = _seeded(seed, recall=recall, **kw)
+    pl = tss.plan(n, rows, k, dt, params=p)
+    k_eff = pl["k_eff"]
+    say(f"relaxed recall {dt} rows={rows} n={n} k={k} k_eff={k_eff} S={S} seed={seed}")
+    gv, gi = run_gpu(x, k, dt, params=p)
+    st = tss.read_stats(rows)
+    gv, gi = gv.reshape(rows, k), gi.reshape(rows, k)
+    kinds = []
+    for r in range(rows):
+        tk, R = taus[r]
+        ov, oi, part = oracle.relaxed_selection(x[r], k, k_eff, tk, pl["cap"], dt)
+        if not np.array_equal(gi[r], oi):
+            c = int(np.argwhere(gi[r] != oi)[0][0])
+            raise AssertionError(f"row {r} R={R}: index differs at slot {c}: gpu {gi[r, c]} "
+                                 f"oracle {oi[c]}")
+        assert gv[r].tobytes() == ov.tobytes(), f"row {r}: value bits differ"
+        assert st[r]["tau_key"] == tk and st[r]["r_sampled"] == R
+        assert st[r]["path"] == (3 if part else (0 if R >= k else 1)), (r, R, st[r])
+        kinds.append("partial" if part else ("accepted" if R >= k else "fallback"))
+    return kinds
+
+
+@pytest.mark.parametrize("dt,gen_seed", [("float32", 301), ("int32", 301), ("bf16", 301)])
+def test_relaxed_recall_keeps_partial_row(dt, gen_seed):
+    # k = 4096, about n/S = 1000 survivors: the row keeps them (sorted in
+    # the workgroup) and pads the remaining slots
+    n = 2 ** 21 + 9
+    if dt == "float32":
+        x = workloads.normal_f32(1, n, gen_seed)
+    elif dt == "int32":
+        x = workloads.scores_int(1, n, -10 ** 6, 10 ** 6, gen_seed)
+    else:
+        x = workloads.relu_bf16(1, n, gen_seed)
+    assert _relaxed_case(x, dt, 4096, 2048, 31) == ["partial"]
+
+
+def test_relaxed_recall_few_survivors_ranked():
+    # fewer than 256 survivors: the rank-by-counting writer
+    x = workloads.normal_f32(1, 2 ** 21 + 9, 302)
+    assert _relaxed_case(x, "float32", 512, 16384, 32) == ["partial"]
+
+
+@pytest.mark.parametrize("dt,gen_seed,seed", [("float32", 303, 33), ("bf16", 304, 34)])
+def test_relaxed_recall_large_k_bucket_sort(dt, gen_seed, seed):
+    # k = 20000 with a few hundred survivors: the bucket sort writes them and
+    # every later sort window is padding
+    n = 2 ** 21 + 9
+    x = workloads.normal_f32(1, n, gen_seed) if dt == "float32" else workloads.relu_bf16(1, n, gen_seed)
+    assert _relaxed_case(x, dt, 20_000, 1024, seed) == ["partial"]
+
+
+def test_relaxed_recall_merge_path():
+    # k beyond the bucket sort's capacity: tile sort, merges, padded output
+    x = workloads.normal_f32(1, 2 ** 22 + 3, 305)
+    assert _tss().plan(2 ** 22 + 3, 1, 2 ** 21 + 1, "float32")["cap"] > 2 ** 21
+    assert _relaxed_case(x, "float32", 2 ** 21 + 1, 1024, 35) == ["partial"]
+
+
+def test_relaxed_recall_mixed_rows():
+    # recall 0.5, k = n/S: rows with k or more survivors are exact, rows with
+    # at least k/2 keep theirs, rows with fewer fall back to the exact route
+    x = workloads.normal_f32(12, 2 ** 20, 306)
+    kinds = _relaxed_case(x, "float32", 1024, 1024, 36, recall=0.5)
+    assert {"partial", "accepted", "fallback"} <= set(kinds), kinds
+
+
+def test_relaxed_recall_rows_listed_by_check_kernel():
+    # more rows than one workgroup scans: the check kernel applies the same
+    # three-way verdict
+    x = workloads.scores_int(1030, 2 ** 16, -2 ** 31, 2 ** 31 - 1, 307)
+    kinds = _relaxed_case(x, "int32", 512, 128, 37, recall=0.5)
+    assert {"partial", "accepted", "fallback"} <= set(kinds)
+
+
+def test_relaxed_selection_scatters_kept_slots_only():
+    # a partial row's padded slots (index -1) write nothing in the consumer
+    tss = _tss()
+    n, k, S, seed = 2 ** 21 + 9, 4096, 2048, 31
+    x = workloads.normal_f32(1, n, 301)
+    kw = dict(S=S, t=1, M=100_000, force_path=1)
+    pl = tss.plan(n, 1, k, "float32", params=_seeded(seed, **kw))
+    tk, R = oracle.tau(x[0], seed, 0, pl["S"], pl["t"], "float32")
+    p = _seeded(seed, recall=R / k, **kw)
+    say(f"relaxed selection into the consumer, R={R}")
+    xt = to_dev(x, "float32")
+    v, i = tss.topk(xt, k, params=p)
+    out, m = tss.scatter(v, i, n, mask=True)
+    torch.cuda.synchronize()
+    ov, oi, part = oracle.relaxed_selection(x[0], k, R, tk, tss.plan(n, 1, k, "float32", params=p)["cap"])
+    assert part and (oi[R:] == -1).all()
+    edense, emask = oracle.sparse_activation(ov[None, :R], oi[None, :R], n)
+    assert _dense_to_host(out, "float32").tobytes() == edense.tobytes()
+    assert np.array_equal(m.cpu().numpy(), emask)

@@ -37,8 +37,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_params_layout(lib):
-    assert ctypes.sizeof(lib.Params) == 104
+    assert ctypes.sizeof(lib.Params) == 112
     p = lib.default_params()
+    assert p.recall == 1.0
     assert (p.eps, p.s_min, p.s_max, p.cost_ratio) == (1e-3, 32768, 131072, 1.0)
     assert p.policy == lib.POLICY_TUNED and p.force_path == 0
     assert (p.tuned_ratio, p.tuned_s_min, p.tuned_ratio_large) == (0.13, 1024, 0.01)
@@ -140,9 +141,30 @@ def test_shape_errors(lib, args, status):
 @pytest.mark.parametrize("kw", [dict(eps=0.0), dict(eps=1.0), dict(s_min=0), dict(s_max=10),
                                 dict(cost_ratio=0.0), dict(policy=3), dict(policy=-1),
                                 dict(force_path=3), dict(S=-1), dict(tuned_ratio=0.0),
-                                dict(tuned_s_min=0)])
+                                dict(tuned_s_min=0), dict(recall=0.0), dict(recall=1.5),
+                                dict(recall=-0.5), dict(recall=float("nan"))])
 def test_param_errors(lib, kw):
     assert _plan(lib, 2 ** 20, 1, 64, 1, **kw)[0] == -1
+
+
+@pytest.mark.parametrize("n,k,recall", [(2 ** 28, 64, 0.95), (2 ** 24, 1000, 0.9),
+                                        (2 ** 24, 10_000, 0.5), (2 ** 22, 7, 0.01)])
+def test_relaxed_recall_plans_for_k_eff(lib, n, k, recall):
+    # the parameters are chosen for k_eff = ceil(recall * k), priced with the
+    # refine that runs for k; the buffer still holds k winners
+    rc, info = _plan(lib, n, 1, k, 1, recall=recall)
+    assert rc == 0
+    k_eff = max(1, math.ceil(recall * k - 1e-9))
+    assert info.k_eff == k_eff
+    p = lib.default_params()
+    ratio = p.tuned_ratio if k <= 4096 else p.tuned_ratio_large
+    e = P.tuned(n, k_eff, eps=1e-3, s_hi=min(131072, n // 8), ratio=ratio)
+    assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
+    assert info.cap >= k
+    # recall 1 plans for k itself
+    assert _plan(lib, n, 1, k, 1)[1].k_eff == k
+    # the recall failure it bounds is R < k_eff
+    assert info.p_recall <= 5e-4 * (1 + 1e-9) and info.p_overflow <= 5e-4 * (1 + 1e-9)
 
 
 def test_null_pointers_rejected_before_any_launch(lib):

@@ -228,3 +228,59 @@ def test_sparse_activation_brute_force_rows():
                 assert dense[r, c] == vals[r, hit[0]] and mask[r, c] == 1
             else:
                 assert dense[r, c] == 0 and mask[r, c] == 0
+
+
+def test_relaxed_selection_worked_example():
+    # values 1 5 3 4 2, tau at 3.0: three survivors (5, 4, 3).  With k = 4
+    # and k_eff = 3 they are kept and the fourth slot is padding; with
+    # k_eff = 4 the row falls back to the exact answer; beyond the capacity
+    # too.
+    row = np.array([1, 5, 3, 4, 2], dtype=np.float32)
+    tau = int(oracle.keys(np.array([3.0], dtype=np.float32))[0])
+    v, i, part = oracle.relaxed_selection(row, 4, 3, tau, 10)
+    assert part and i.tolist() == [1, 3, 2, -1]
+    assert v[:3].tolist() == [5.0, 4.0, 3.0] and np.isneginf(v[3])
+    v, i, part = oracle.relaxed_selection(row, 4, 4, tau, 10)
+    assert not part and i.tolist() == [1, 3, 2, 4]
+    v, i, part = oracle.relaxed_selection(row, 4, 3, tau, 2)
+    assert not part and i.tolist() == [1, 3, 2, 4]
+    # enough survivors: exact whatever k_eff
+    tau2 = int(oracle.keys(np.array([2.0], dtype=np.float32))[0])
+    v, i, part = oracle.relaxed_selection(row, 4, 1, tau2, 10)
+    assert not part and i.tolist() == [1, 3, 2, 4]
+
+
+@pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])
+def test_relaxed_selection_brute_force(dt):
+    # every threshold a tiny row can have, against the rank definition: a
+    # partial row keeps exactly the elements of rank < R, element of rank r
+    # in slot r, so at least k_eff of the true top-k are returned; the pad
+    # is the dtype's lowest value
+    g = np.random.default_rng({"float32": 21, "int32": 22, "bf16": 23}[dt])
+    for trial in range(30):
+        n = int(g.integers(1, 40))
+        base = g.integers(-4, 5, n)
+        if dt == "int32":
+            row = base.astype(np.int32)
+        elif dt == "float32":
+            row = (base * 0.5).astype(np.float32)
+        else:
+            row = workloads.f32_to_bf16_bits((base * 0.5).astype(np.float32))
+        ranks = oracle.rank_by_counting(row, dt)
+        kr = oracle.keys(row, dt).astype(np.int64)
+        for tau in sorted(set(kr.tolist())) + [int(kr.max()) + 1]:
+            R = int((kr >= tau).sum())
+            for k in range(1, n + 1):
+                for k_eff in range(1, k + 1):
+                    cap = int(g.integers(1, n + 2))
+                    v, i, part = oracle.relaxed_selection(row, k, k_eff, tau, cap, dt)
+                    assert part == (k_eff <= R < k and R <= cap)
+                    if not part:
+                        assert i.tolist() == np.argsort(ranks, kind="stable")[:k].tolist()
+                        continue
+                    assert [int(ranks[j]) for j in i[:R]] == list(range(R))
+                    assert (i[R:] == -1).all() and R >= k_eff
+                    assert v[:R].tobytes() == row[i[:R]].tobytes()
+                    pad = {"float32": np.float32(-np.inf), "int32": np.int32(-2 ** 31),
+                           "bf16": np.uint16(0xFF80)}[dt]
+                    assert (v[R:].tobytes() == np.full(k - R, pad).tobytes())

@@ -15,13 +15,15 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED, Params,
+from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED,
+                   ROUTE_EXACT, ROUTE_FALLBACK, ROUTE_PARTIAL, ROUTE_SAMPLED, Params,
                    TopkError, default_params)
 
 __all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "scatter", "batchtopk",
            "workspace_size", "read_stats",
            "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
+           "ROUTE_SAMPLED", "ROUTE_FALLBACK", "ROUTE_EXACT", "ROUTE_PARTIAL",
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code"]
 
 _TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}

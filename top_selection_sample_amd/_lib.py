@@ -16,6 +16,9 @@ TOPK_OK, TOPK_EINVAL, TOPK_EDTYPE, TOPK_EWORKSPACE, TOPK_EHIP, TOPK_ENOTIMPL = 0
 DTYPE_CODES = {"int32": 0, "float32": 1, "bf16": 2}
 POLICY_EXACT_TAIL, POLICY_ALG1, POLICY_TUNED = 0, 1, 2
 PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
+# per-row route in read_stats: sampled accepted, sampled then exact fallback,
+# exact only, sampled with fewer than k survivors kept (recall < 1)
+ROUTE_SAMPLED, ROUTE_FALLBACK, ROUTE_EXACT, ROUTE_PARTIAL = 0, 1, 2, 3
 
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
@@ -31,7 +34,7 @@ class Params(ctypes.Structure):
                 ("use_seed", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
                 ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64),
-                ("tuned_ratio_large", ctypes.c_double)]
+                ("tuned_ratio_large", ctypes.c_double), ("recall", ctypes.c_double)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -39,7 +42,7 @@ class PlanInfo(ctypes.Structure):
                 ("t", ctypes.c_int64), ("M", ctypes.c_int64), ("cap", ctypes.c_int64),
                 ("index_bits", ctypes.c_int32), ("key_bits", ctypes.c_int32),
                 ("p_recall", ctypes.c_double), ("p_overflow", ctypes.c_double),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("k_eff", ctypes.c_int64)]
 
 
 class StageTimes(ctypes.Structure):

@@ -96,6 +96,7 @@ tk::ParamIn to_in(const topk_params* p) {
   in.tuned_ratio = p->tuned_ratio;
   in.tuned_s_min = p->tuned_s_min;
   in.tuned_ratio_large = p->tuned_ratio_large;
+  in.recall = p->recall;
   return in;
 }
 
@@ -107,6 +108,7 @@ int check_params(const topk_params* p) {
   if (p->policy < 0 || p->policy > 2) return TOPK_EINVAL;
   if (!(p->tuned_ratio > 0.0) || p->tuned_s_min < 1) return TOPK_EINVAL;
   if (!(p->tuned_ratio_large > 0.0)) return TOPK_EINVAL;
+  if (!(p->recall > 0.0 && p->recall <= 1.0)) return TOPK_EINVAL;
   if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
   if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
   return TOPK_OK;
@@ -155,7 +157,7 @@ int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* pa
 
 extern "C" {
 
-static_assert(sizeof(topk_params) == 104, "topk_params layout is part of the ABI");
+static_assert(sizeof(topk_params) == 112, "topk_params layout is part of the ABI");
 
 int topk_default_params(topk_params* p) {
   if (!p) return TOPK_EINVAL;
@@ -169,6 +171,7 @@ int topk_default_params(topk_params* p) {
   p->tuned_ratio = 0.13;
   p->tuned_s_min = 1024;
   p->tuned_ratio_large = 0.01;
+  p->recall = 1.0;
   return TOPK_OK;
 }
 
@@ -187,6 +190,7 @@ int topk_plan(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* 
     out->cap = p.cap;
     out->index_bits = (int32_t)p.B;
     out->key_bits = (int32_t)p.KB;
+    out->k_eff = p.k_eff;
     out->p_recall = p.p_recall;
     out->p_overflow = p.p_overflow;
     out->workspace_bytes = p.total;

@@ -32,7 +32,7 @@ enum : uint32_t {
 };
 
 // Which route produced a row's answer (reported through the stats call).
-enum : uint32_t { PATH_SAMPLED = 0, PATH_FALLBACK = 1, PATH_EXACT = 2 };
+enum : uint32_t { PATH_SAMPLED = 0, PATH_FALLBACK = 1, PATH_EXACT = 2, PATH_PARTIAL = 3 };
 
 struct alignas(64) RowState {
   uint32_t status;

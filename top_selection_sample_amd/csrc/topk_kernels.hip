@@ -864,19 +864,23 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 // at tau (G strictly above, E equal):
 //   G > cap          overflow
 //   G >= k           accepted: the k winners lie among the G, ties unused
-//   G + E < k        recall failure
 //   G + E > cap      the ties needed do not fit: overflow
-//   otherwise        accepted with every tie (all E were stored, E <= cap - G)
+//   G + E >= k       accepted with every tie (all E were stored, E <= cap - G)
+//   G + E >= k_eff   relaxed recall (k_eff < k): fewer than k reach tau, and
+//                    every one of them is a top-k element; they are kept
+//   otherwise        recall failure
 // ======================================================================
-enum : uint32_t { V_FAIL = 0, V_OK = 1, V_OK_TIES = 2 };
+enum : uint32_t { V_FAIL = 0, V_OK = 1, V_OK_TIES = 2, V_PARTIAL = 3 };
 
 __device__ __forceinline__ uint32_t sampled_verdict(uint32_t G, uint32_t E, uint32_t k,
-                                                    uint32_t cap) {
+                                                    uint32_t k_eff, uint32_t cap) {
   if (G > cap) return V_FAIL;
   if (G >= k) return V_OK;
   const uint64_t R = (uint64_t)G + E;
-  if (R < k || R > cap) return V_FAIL;
-  return V_OK_TIES;
+  if (R > cap) return V_FAIL;
+  if (R >= k) return V_OK_TIES;
+  if (R >= k_eff) return V_PARTIAL;
+  return V_FAIL;
 }
 
 // Leaves count and ties alone: other workgroups may still be reading them to
@@ -901,13 +905,13 @@ __device__ __forceinline__ void flag_row(CallState* cs, uint32_t* flagged, uint3
 
 __global__ void k_check(RowState* __restrict__ states, const RowCtr* __restrict__ rctr,
                         CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t rows,
-                        uint32_t k, uint32_t cap) {
+                        uint32_t k, uint32_t k_eff, uint32_t cap) {
   const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
   const uint32_t G = st->count, E = rctr[row].ties;
-  if (sampled_verdict(G, E, k, cap) == V_FAIL) {
+  if (sampled_verdict(G, E, k, k_eff, cap) == V_FAIL) {
     st->r_sampled = G + E;
     st->ties = E;
     start_exact(st, k, PATH_FALLBACK);
@@ -974,14 +978,14 @@ __device__ __forceinline__ void store_winner(void* out_values, int64_t* out_idx,
   out_idx[o] = idx;
 }
 
-// Output slot of s[i] = #{j : s[j] > s[i]}; slots >= k are dropped.  Four
-// neighbouring lanes share an element, each counting a quarter of the list;
-// their counts are summed with two quad moves.  Needs cnt <= blockDim.x / 4
-// and every thread of the workgroup.
+// Output slot of s[i] = #{j : s[j] > s[i]}; slots >= k are dropped, and a
+// row's slots start at row * ks.  Four neighbouring lanes share an element,
+// each counting a quarter of the list; their counts are summed with two quad
+// moves.  Needs cnt <= blockDim.x / 4 and every thread of the workgroup.
 template <int DT>
-__device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint32_t B,
-                               const char* rowp, uint32_t n, void* out_values, int64_t* out_idx,
-                               uint32_t row) {
+__device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint32_t ks,
+                               uint32_t B, const char* rowp, uint32_t n, void* out_values,
+                               int64_t* out_idx, uint32_t row) {
   const uint32_t i = threadIdx.x >> 2, q = threadIdx.x & 3u;
   const uint64_t c = i < cnt ? s[i] : ~0ull;
   uint32_t r0 = 0, r1 = 0;
@@ -997,18 +1001,38 @@ __device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint
   if (q == 0 && i < cnt && r < k) {
     uint32_t idx;
     const uint32_t bits = winner_bits<DT>(c, B, rowp, n, &idx);
-    store_winner<DT>(out_values, out_idx, (size_t)row * k + r, bits, idx);
+    store_winner<DT>(out_values, out_idx, (size_t)row * ks + r, bits, idx);
   }
 }
 
+// The first k of the sorted list s_w to the row's slots (which start at
+// row * ks).
 template <int DT>
-__device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t B, const char* rowp,
-                              uint32_t n, void* out_values, int64_t* out_idx, uint32_t row) {
+__device__ void write_winners(const uint64_t* s_w, uint32_t k, uint32_t ks, uint32_t B,
+                              const char* rowp, uint32_t n, void* out_values, int64_t* out_idx,
+                              uint32_t row) {
   for (uint32_t i = threadIdx.x; i < k; i += blockDim.x) {
     uint32_t idx;
     const uint32_t bits = winner_bits<DT>(s_w[i], B, rowp, n, &idx);
-    store_winner<DT>(out_values, out_idx, (size_t)row * k + i, bits, idx);
+    store_winner<DT>(out_values, out_idx, (size_t)row * ks + i, bits, idx);
   }
+}
+
+// An output slot no winner fills (a row that keeps fewer than k): index -1
+// and the dtype's lowest value (-inf for the floats, INT32_MIN for int32).
+template <int DT>
+__device__ __forceinline__ void store_pad(void* out_values, int64_t* out_idx, size_t o) {
+  if constexpr (DT == DT_BF16) static_cast<uint16_t*>(out_values)[o] = 0xFF80u;
+  else static_cast<uint32_t*>(out_values)[o] = DT == DT_I32 ? 0x80000000u : 0xFF800000u;
+  out_idx[o] = -1;
+}
+
+// Slots [from, ks) of the row, padded.
+template <int DT>
+__device__ void pad_slots(uint32_t from, uint32_t ks, void* out_values, int64_t* out_idx,
+                          uint32_t row) {
+  for (uint32_t i = from + threadIdx.x; i < ks; i += blockDim.x)
+    store_pad<DT>(out_values, out_idx, (size_t)row * ks + i);
 }
 
 // s_tmp: 16 words (at most 1024 threads).
@@ -1043,12 +1067,12 @@ __device__ __forceinline__ void lds_sort_desc(uint64_t* s, uint32_t cnt) {
 }
 
 // The k largest of the `got` unique composites in s_cand (got >= k) to the
-// output, in rank order.  tmp: LDS scratch of 2 * RF_SORT_CAP + 64 words.
+// output, in rank order; the row's slots start at row * ks (ks >= k).  tmp: LDS scratch of 2 * RF_SORT_CAP + 64 words.
 // digit: a bin of 11 key bits that never decreases as the composite grows,
 // or null to take one from the list's own range.
 template <int DT, class Digit>
-__device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32_t k, uint32_t B,
-                             void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+__device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32_t k, uint32_t ks,
+                             uint32_t B, void* __restrict__ out_values, int64_t* __restrict__ out_idx,
                              uint32_t row, uint64_t* s_cand, uint32_t got, uint32_t* s_hist,
                              uint32_t* s_misc, uint64_t* tmp, const Digit* digit) {
   const uint32_t tid = threadIdx.x;
@@ -1057,7 +1081,7 @@ __device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32
     // few elements: each one's output slot is the number of larger
     // composites (the rank of GPU.js Learn "Rank by Counting"; composites are
     // unique, so the slots are a permutation)
-    rank_and_write<DT>(s_cand, got, k, B, rowp, n, out_values, out_idx, row);
+    rank_and_write<DT>(s_cand, got, k, ks, B, rowp, n, out_values, out_idx, row);
   } else {
     uint32_t* wsum = reinterpret_cast<uint32_t*>(tmp + RF_SORT_CAP);
     bool sorted = digit && block_sort_binned_desc(s_cand, got, tmp, s_hist, s_misc, wsum, *digit, 64u);
@@ -1074,7 +1098,7 @@ __device__ void emit_winners(const void* __restrict__ values, uint32_t n, uint32
       for (int j = 0; j < 4; ++j) s_cand[4 * tid + j] = v[j];
       __syncthreads();
     }
-    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+    write_winners<DT>(s_cand, k, ks, B, rowp, n, out_values, out_idx, row);
   }
 }
 
@@ -1082,9 +1106,11 @@ struct NoDigit {
   __device__ uint32_t operator()(uint64_t) const { return 0u; }
 };
 
-// One row, one workgroup (1024 threads).  want = ST_FILTER: the sampled
-// candidates (a failed check sends the row to the exact route instead);
-// want = ST_EXACT_READY: the exact route's candidates.
+// One row, one workgroup (1024 threads): the exact route's candidates
+// (want = ST_EXACT_READY; the sampled route's rows use refine_sampled).
+// A key pass fills an LDS key cache and finds the largest key, the
+// histogram and the boundary bin come from the cache, and the candidates
+// from the boundary bin up are gathered from the buffer.
 template <int DT>
 __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
                            CallState* cs, uint32_t* flagged, const uint64_t* __restrict__ cbuf,
@@ -1174,7 +1200,7 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
     SelectOut sel = block_select(src, R, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
     got = block_collect(src, R, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
   }
-  emit_winners<DT, NoDigit>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
+  emit_winners<DT, NoDigit>(values, n, k, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
                             reinterpret_cast<uint64_t*>(s_keys), nullptr);
   __syncthreads();
   if (tid == 0) st->status = ST_DONE;
@@ -1188,12 +1214,14 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
 // [tau, kmax], kmax being the largest key the filter stored, so the 11 key
 // bits just below the common prefix of tau and kmax order them: one LDS
 // histogram finds the bin holding rank k, and the candidates from that bin
-// up go straight from registers to LDS for the final rank or sort.
+// up go straight from registers to LDS for the final rank or sort.  The k
+// winners fill the row's first k slots of ks; a row that keeps fewer than ks
+// (k = R) gets the rest padded.
 constexpr uint32_t RS_VEC = 12;
 template <int DT>
 __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowState* st,
                                const uint64_t* __restrict__ cb, uint32_t R, uint32_t lo,
-                               uint32_t kmax, uint32_t k, uint32_t B, uint32_t W,
+                               uint32_t kmax, uint32_t k, uint32_t ks, uint32_t B, uint32_t W,
                                void* __restrict__ out_values, int64_t* __restrict__ out_idx,
                                uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
                                uint64_t* s_cand, uint64_t* s_scratch) {
@@ -1291,8 +1319,9 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
       return ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1);
     }
   } bin_of{B, kshift};
-  emit_winners<DT, BinOf>(values, n, k, B, out_values, out_idx, row, s_cand, got, s_hist, s_misc,
-                          s_scratch, &bin_of);
+  emit_winners<DT, BinOf>(values, n, k, ks, B, out_values, out_idx, row, s_cand, got, s_hist,
+                          s_misc, s_scratch, &bin_of);
+  if (k < ks) pad_slots<DT>(k, ks, out_values, out_idx, row);
   __syncthreads();
   if (tid == 0) st->status = ST_DONE;
   __syncthreads();
@@ -1320,7 +1349,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
     for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
     __syncthreads();
     block_bitonic_desc(s_cand, P);
-    write_winners<DT>(s_cand, k, B, rowp, n, out_values, out_idx, row);
+    write_winners<DT>(s_cand, k, k, B, rowp, n, out_values, out_idx, row);
     __syncthreads();
     if (threadIdx.x == 0) {
       st->status = ST_DONE;
@@ -1584,8 +1613,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const RowCtr* __restrict__ rctr, CallState* __restrict__ cs, uint32_t* __restrict__ flagged,
     uint32_t* __restrict__ ghist,
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
-    uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode, void* __restrict__ out_values,
-    int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk, uint32_t bl, uint32_t lk_flags) {
+    uint32_t k_eff, uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode,
+    void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk,
+    uint32_t bl, uint32_t lk_flags) {
   using D = Dt<DT>;
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -1619,7 +1649,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     for (uint32_t r = tid; r < rows; r += blockDim.x) {
       const uint32_t G = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint32_t E = rctr[r].ties;   // final: only the filter adds to it
-      if (sampled_verdict(G, E, k, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
+      if (sampled_verdict(G, E, k, k_eff, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
     }
     __syncthreads();
     nf = 0;
@@ -1648,7 +1678,8 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     // an accepted row; when it needs the ties, they join its candidates
     const uint32_t G = fr ? f_count : st->count, E = fr ? f_ties : rctr[r].ties;
     const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
-    const bool ties_in = sampled_verdict(G, E, k, cap) == V_OK_TIES;
+    const uint32_t verdict = sampled_verdict(G, E, k, k_eff, cap);
+    const bool ties_in = verdict == V_OK_TIES || verdict == V_PARTIAL;
     if (!fr) __syncthreads();   // every thread has read the counts
     if (ties_in) {
       uint64_t* dst = cbuf + (size_t)r * cap + G;
@@ -1659,6 +1690,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       st->r_sampled = G + E;
       st->ties = E;
       if (G < k) st->count = G + E;
+      if (verdict == V_PARTIAL) st->path = PATH_PARTIAL;
       if (!small_k) {
         st->thr_key = st->tau_key;   // every candidate key is >= this
         st->kmax = rctr[r].kmax;
@@ -1669,8 +1701,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     if (small_k) {
       uint32_t R = G < k ? G + E : G;
       if (R > cap) R = cap;
-      refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, k, B, W, out_values,
-                         out_idx, r, s_hist, s_misc, s_tmp, s_cand,
+      // a partial row (fewer than k reach tau) keeps all R and pads the rest
+      const uint32_t kk = R < k ? R : k;
+      refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, kk, k, B, W,
+                         out_values, out_idx, r, s_hist, s_misc, s_tmp, s_cand,
                          reinterpret_cast<uint64_t*>(s_keys));
     }
   }
@@ -1686,9 +1720,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     for (uint64_t q = blockIdx.x; q < npairs; q += G) {
       const uint32_t r = (uint32_t)(q / maxch), c = (uint32_t)(q % maxch);
       const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
-      const uint32_t v = sampled_verdict(Ga, E, k, cap);
+      const uint32_t v = sampled_verdict(Ga, E, k, k_eff, cap);
       if (v == V_FAIL) continue;   // the exact route's rows: below
-      uint32_t R = v == V_OK_TIES ? Ga + E : Ga;
+      uint32_t R = (v == V_OK_TIES || v == V_PARTIAL) ? Ga + E : Ga;
       if (R > cap) R = cap;
       if ((uint64_t)c * LK_CHUNK >= R) continue;
       const LkDigit g = lk_digit(states[r].tau_key, rctr[r].kmax, B, bl);
@@ -2024,6 +2058,10 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
   const uint32_t row = blockIdx.y;
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;
   if (i >= k) return;
+  if (i >= min(states[row].count, cap)) {   // a row that keeps fewer than k
+    store_pad<DT>(out_values, out_idx, (size_t)row * k + i);
+    return;
+  }
   const uint64_t c = sorted[(size_t)row * cap + i];
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
   uint32_t idx;
@@ -2194,6 +2232,12 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
   }
   const RowState st = states[row];
   if (st.status != ST_SORT) return;
+  const uint32_t R = st.count < cap ? st.count : cap;
+  if (R < k) {   // a row that keeps fewer than k: pad this window's slots past R
+    const uint32_t w0 = blockIdx.x * LK_WIN, w1 = w0 + LK_WIN < k ? w0 + LK_WIN : k;
+    for (uint32_t i = (w0 > R ? w0 : R) + tid; i < w1; i += nt)
+      store_pad<DT>(out_values, out_idx, (size_t)row * k + i);
+  }
   const uint32_t* gs = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
   const uint32_t* gwin = lk + (size_t)rows * (2 * LK_BINS + LK_STRIDE) + (size_t)row * 2 * LK_MAXWIN;
   if (blockIdx.x * LK_WIN >= k) return;
@@ -2456,8 +2500,8 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   const Plan& p = a.plan;
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
-                     a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, p.B, p.W, small_k, mode,
-                     a.out_values, a.out_idx, a.lk, bl, lk_flags);
+                     a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
+                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags);
   return hipGetLastError();
 }
 
@@ -2520,7 +2564,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
         mode = FIN_SCAN;
       } else {
         hipLaunchKernelGGL(k_check, tiny, dim3(64), 0, s, a.states, a.rctr, a.call, a.flagged,
-                           rows, k, cap);
+                           rows, k, (uint32_t)p.k_eff, cap);
       }
     }
     hipError_t e = hipGetLastError();

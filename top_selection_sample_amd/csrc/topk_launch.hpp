@@ -20,6 +20,7 @@ constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workg
 
 struct Plan {
   int64_t n = 0, rows = 0, k = 0;
+  int64_t k_eff = 0;   // k, or ceil(recall * k) in relaxed-recall mode
   int dtype = 0;
   int path = PLAN_SAMPLED;
   bool small_k = true;

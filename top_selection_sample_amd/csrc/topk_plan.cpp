@@ -312,7 +312,17 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   // verbatim keeps its per-selection eps)
   ParamIn row_in = in;
   if (rows > 1 && in.policy != 1) row_in.eps = in.eps / (double)rows;
-  sample_params(n, k, row_in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
+  // relaxed recall: the parameters are those of the smaller selection
+  // k_eff = ceil(recall * k) (a row keeps its survivors once it has k_eff)
+  p.k_eff = k;
+  if (in.recall < 1.0) {
+    p.k_eff = (int64_t)std::ceil(in.recall * (double)k - 1e-9);
+    if (p.k_eff < 1) p.k_eff = 1;
+    if (p.k_eff > k) p.k_eff = k;
+  }
+  // the refine that runs is the one for k: its cost ratio prices the buffer
+  if (k > KSMALL) row_in.tuned_ratio = in.tuned_ratio_large;
+  sample_params(n, p.k_eff, row_in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
   bool sampled;
   if (in.force_path == 1) sampled = true;
   else if (in.force_path == 2) sampled = false;

@@ -30,6 +30,9 @@ struct ParamIn {
   double tuned_ratio = 0.13;
   int64_t tuned_s_min = 1024;  // least sample size the tuned policy considers
   double tuned_ratio_large = 0.01;
+  // recall target (relaxed-recall mode below 1): parameters for
+  // ceil(recall * k), and rows with at least that many survivors keep them
+  double recall = 1.0;
 };
 
 double normal_quantile(double p);
