@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "topk_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_k_filter_c3_k64.txt")
+TRAFFIC_WORKLOAD = "c3k64"   # the workload those counters were taken on
 COPY_BYTES = 1 << 30
 
 WORKLOADS = {
@@ -105,10 +106,11 @@ def algorithmic_bytes(rows, n, k, es, plan, R_mean):
     return b
 
 
-def read_traffic(launch_bytes_alg):
+def read_traffic(workload):
     """Traffic measured by rocprofv3 counters for the filter kernel, if the
-    committed summary was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    committed summary was taken on this workload and the current kernel
+    source."""
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
     for line in open(TRAFFIC_FILE):
@@ -339,7 +341,7 @@ def run_bench(args):
         t_filter = stages["filter"]["ms"] / stages["filter"]["count"] * 1e-3
         filt_bytes = elems * es + R_mean * 8
         achieved = filt_bytes / t_filter / 1e9
-        traffic = read_traffic(filt_bytes)
+        traffic = read_traffic(args.workload)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "k_filter",

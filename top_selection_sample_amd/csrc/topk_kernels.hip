@@ -1217,7 +1217,7 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
 // up go straight from registers to LDS for the final rank or sort.  The k
 // winners fill the row's first k slots of ks; a row that keeps fewer than ks
 // (k = R) gets the rest padded.
-constexpr uint32_t RS_VEC = 12;
+constexpr uint32_t RS_VEC = 11;
 template <int DT>
 __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowState* st,
                                const uint64_t* __restrict__ cb, uint32_t R, uint32_t lo,
