@@ -125,14 +125,20 @@ def read_traffic(workload):
         return None
 
 
-def cpu_baseline(x, dt, k, budget_s=12.0, max_calls=5):
+def cpu_baseline(x, dt, k, budget_s=12.0, max_calls=5, threads=1):
+    """Median seconds of the oracle's selection on the whole workload (inputs
+    in host memory): the plain partial sort, or its chunked form on
+    `threads` threads."""
     import oracle
     oracle.lib()
     times = []
     t_start = time.time()
     while len(times) < max_calls and (time.time() - t_start) < budget_s:
         t0 = time.perf_counter()
-        oracle.topk(x, k, dt)
+        if threads == 1:
+            oracle.topk(x, k, dt)
+        else:
+            oracle.topk_chunked(x, k, threads, dt)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return med, len(times)
@@ -150,9 +156,28 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def fallback_rate(tss, bufs, k, rows, calls, policy):
+def fallback_rate(tss, bufs, k, rows, calls, policy, steps=0):
+    """Fallback rate and survivors of one parameter policy over `calls` calls
+    with fresh seeds; with steps > 0 also the time per call over that many
+    calls (fresh seeds, fallbacks included as they come)."""
+    import torch
     p = tss.default_params(policy=policy)
-    cap = tss.plan(bufs[0].shape[1], rows, k, bufs[0].dtype, params=p)["cap"]
+    n = bufs[0].shape[1]
+    cap = tss.plan(n, rows, k, bufs[0].dtype, params=p)["cap"]
+    timed = {}
+    if steps:
+        tss.topk(bufs[0], k, params=p)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(steps):
+            tss.topk(bufs[i % len(bufs)], k, params=p)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        timed = {"ms_per_call_with_fallbacks": round(ms, 4),
+                 "gelem_s_with_fallbacks": round(rows * n / (ms * 1e-3) / 1e9, 3)}
     fb = 0
     r_sum = 0
     w_sum = 0
@@ -169,7 +194,7 @@ def fallback_rate(tss, bufs, k, rows, calls, policy):
             nrow += 1
     return {"calls": calls, "row_selections": nrow, "fallbacks": fb,
             "rate": fb / max(nrow, 1), "mean_R": r_sum / max(nrow, 1),
-            "mean_written": w_sum / max(nrow, 1)}
+            "mean_written": w_sum / max(nrow, 1), **timed}
 
 
 def relaxed_trade(tss, bufs, k, rows, steps, calls, ov, oi, recall=0.95):
@@ -256,8 +281,9 @@ def run_bench(args):
     fb_calls = args.fallback_calls or (1000 if rows == 1 else 100)
     fb = {"tuned": fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_TUNED)}
     if plan["path"] == 0:
-        fb["exact_tail"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_EXACT_TAIL)
-        fb["alg1"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_ALG1)
+        fb["exact_tail"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_EXACT_TAIL,
+                                         args.steps)
+        fb["alg1"] = fallback_rate(tss, bufs, k, rows, fb_calls, tss.POLICY_ALG1, args.steps)
     R_mean = fb["tuned"]["mean_written"] * rows
 
     # cost of one fallback: the exact route over the whole input
@@ -350,7 +376,7 @@ def run_bench(args):
         if ceiling:
             ceiling["filter_frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
 
-    cpu = None
+    cpu = cpu_chunked = None
     if not args.no_cpu_baseline:
         med, calls = cpu_baseline(x, dt, k)
         cpu = {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": 1,
@@ -358,6 +384,14 @@ def run_bench(args):
                "sample": f"the full workload ({desc}); {calls} oracle calls, median "
                          f"{med:.2f} s each, single-threaded partial sort on {cpu_model()} "
                          f"({os.cpu_count()} logical CPUs on the host)"}
+        # the same on every core the process may use (at most 16)
+        T = max(1, min(len(os.sched_getaffinity(0)), 16))
+        med, calls = cpu_baseline(x, dt, k, threads=T)
+        cpu_chunked = {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": T,
+                       "kind": "oracle",
+                       "sample": f"the full workload; {calls} calls, median {med:.3f} s each, "
+                                 f"{T} threads each taking a contiguous chunk of the row and "
+                                 f"keeping its own top-k, then one partial sort of the union"}
 
     stage_ms = {name: round(v["ms"] / v["count"], 4) if v["count"] else None
                 for name, v in stages.items()}
@@ -377,6 +411,7 @@ def run_bench(args):
         "batchtopk_consumer": consumer,
         "relaxed_recall": relaxed,
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_chunked,
         "fallback": fb,
         "exact_route_ms_per_call": round(exact_ms, 4) if exact_ms is not None else None,
         "stage_ms": stage_ms,

@@ -10,6 +10,9 @@ Contents
 * ``topk``            exact top-k of each row: partial sort on (key desc,
                       index asc) (Prof-K paper, section 3; GPU.js Learn
                       "Rank by Counting" for the tie rule).  C++ core.
+* ``topk_chunked``    the same selection on several threads (chunks of each
+                      row, then one selection over the chunks' own top-k),
+                      for the CPU timing.
 * ``keys``            order-preserving unsigned keys, written with numpy.
 * ``rank_by_counting``  O(n^2) rank of every element: strictly larger
                       anywhere, or equal at a lower index (GPU.js Learn
@@ -53,7 +56,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
-            ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, _SRC])
+            ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", tmp, _SRC])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -69,6 +72,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, u64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int
         L.oracle_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp]
+        L.oracle_topk_chunked.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp]
         L.oracle_keys.argtypes = [vp, i64, i32, vp]
         L.oracle_sample_indices.argtypes = [u64, u64, u64, u64, vp]
         L.oracle_feistel_raw.argtypes = [u64, u64, u64, u64, vp]
@@ -144,6 +148,21 @@ def topk(x: np.ndarray, k: int, dtype: str | None = None):
     rc = lib().oracle_topk(_ptr(x2), n, rows, k, DTYPES[dt], _ptr(ov), _ptr(oi))
     if rc != 0:
         raise ValueError(f"oracle_topk rejected arguments (rc={rc})")
+    return ov, oi
+
+
+def topk_chunked(x: np.ndarray, k: int, threads: int, dtype: str | None = None):
+    """``topk`` on `threads` CPU threads (contiguous chunks of each row, each
+    keeps its own top-k, then one selection over the union); for timing the
+    CPU side with every core."""
+    dt = _dtype_name(x, dtype)
+    x2 = np.ascontiguousarray(x.reshape(1, -1) if x.ndim == 1 else x)
+    rows, n = x2.shape
+    ov = np.empty((rows, k), dtype=_NP[dt])
+    oi = np.empty((rows, k), dtype=np.int64)
+    rc = lib().oracle_topk_chunked(_ptr(x2), n, rows, k, DTYPES[dt], threads, _ptr(ov), _ptr(oi))
+    if rc != 0:
+        raise ValueError(f"oracle_topk_chunked rejected arguments (rc={rc})")
     return ov, oi
 
 

@@ -33,6 +33,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -166,6 +167,54 @@ int oracle_topk(const void* values, int64_t n, int64_t rows, int64_t k, int dtyp
     for (int64_t j = 0; j < k; ++j) {
       std::memcpy(ov + (r * k + j) * es, row + static_cast<int64_t>(order[j]) * es, es);
       out_indices[r * k + j] = order[j];
+    }
+  }
+  return 0;
+}
+
+// The same selection on T threads, for timing the CPU side: each thread
+// takes a contiguous chunk of the row and keeps its own first min(k, chunk)
+// in rank order; then the union of those lists is partially sorted again.
+// Exact, because the k best of a row lie among the k best of whichever chunk
+// holds each of them.
+int oracle_topk_chunked(const void* values, int64_t n, int64_t rows, int64_t k, int dtype,
+                        int threads, void* out_values, int64_t* out_indices) {
+  const int es = elem_size(dtype);
+  if (!es) return -2;
+  if (n < 1 || rows < 1 || k < 1 || k > n || threads < 1) return -1;
+  const unsigned char* base = static_cast<const unsigned char*>(values);
+  unsigned char* ov = static_cast<unsigned char*>(out_values);
+  std::vector<uint32_t> keys(n);
+  const int64_t T = threads;
+  const int64_t chunk = (n + T - 1) / T;
+  std::vector<std::vector<uint32_t>> best(T);
+  for (int64_t r = 0; r < rows; ++r) {
+    const unsigned char* row = base + r * n * es;
+    auto outranks = [&](uint32_t a, uint32_t b) {
+      return keys[a] > keys[b] || (keys[a] == keys[b] && a < b);
+    };
+    std::vector<std::thread> pool;
+    for (int64_t c = 0; c < T; ++c) {
+      pool.emplace_back([&, c]() {
+        const int64_t lo = c * chunk, hi = std::min(n, lo + chunk);
+        std::vector<uint32_t>& mine = best[c];
+        mine.clear();
+        for (int64_t i = lo; i < hi; ++i) {
+          keys[i] = key_at(row, i, dtype);
+          mine.push_back(static_cast<uint32_t>(i));
+        }
+        const int64_t keep = std::min<int64_t>(k, static_cast<int64_t>(mine.size()));
+        std::partial_sort(mine.begin(), mine.begin() + keep, mine.end(), outranks);
+        mine.resize(keep);
+      });
+    }
+    for (auto& th : pool) th.join();
+    std::vector<uint32_t> all;
+    for (auto& b : best) all.insert(all.end(), b.begin(), b.end());
+    std::partial_sort(all.begin(), all.begin() + k, all.end(), outranks);
+    for (int64_t j = 0; j < k; ++j) {
+      std::memcpy(ov + (r * k + j) * es, row + static_cast<int64_t>(all[j]) * es, es);
+      out_indices[r * k + j] = all[j];
     }
   }
   return 0;

@@ -284,3 +284,28 @@ def test_relaxed_selection_brute_force(dt):
                     pad = {"float32": np.float32(-np.inf), "int32": np.int32(-2 ** 31),
                            "bf16": np.uint16(0xFF80)}[dt]
                     assert (v[R:].tobytes() == np.full(k - R, pad).tobytes())
+
+
+@pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])
+def test_chunked_selection_equals_single_thread(dt):
+    # the threaded variant used for the CPU timing returns the same bits and
+    # indices as the plain partial sort: heavy ties across chunk borders,
+    # more threads than elements, k larger than a chunk, k = n
+    g = np.random.default_rng({"float32": 31, "int32": 32, "bf16": 33}[dt])
+    for n, k, threads in [(1, 1, 4), (5, 3, 8), (1000, 10, 7), (1000, 300, 16), (4099, 4099, 3),
+                          (20000, 64, 16)]:
+        base = g.integers(-3, 4, size=(2, n))
+        if dt == "int32":
+            x = base.astype(np.int32)
+        elif dt == "float32":
+            x = (base * 0.25).astype(np.float32)
+        else:
+            x = workloads.f32_to_bf16_bits((base * 0.25).astype(np.float32))
+        v1, i1 = oracle.topk(x, k, dt)
+        v2, i2 = oracle.topk_chunked(x, k, threads, dt)
+        assert np.array_equal(i1, i2) and v1.tobytes() == v2.tobytes(), (n, k, threads)
+    # and against the rank definition on one tiny row
+    row = x[0, :50]
+    ranks = oracle.rank_by_counting(row, dt)
+    _, ic = oracle.topk_chunked(row, 20, 6, dt)
+    assert ic[0].tolist() == np.argsort(ranks, kind="stable")[:20].tolist()
