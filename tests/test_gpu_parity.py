@@ -403,6 +403,30 @@ def test_argument_errors():
         tss.topk(x.double(), 5)
 
 
+def test_out_tensors_checked_and_empty_batch():
+    tss = _tss()
+    x = torch.randn(3, 1000, device="cuda")
+    good = (torch.empty(3, 7, device="cuda"), torch.empty(3, 7, dtype=torch.int64, device="cuda"))
+    v, i = tss.topk(x, 7, out=good)
+    assert v.data_ptr() == good[0].data_ptr() and i.data_ptr() == good[1].data_ptr()
+    ov, oi = oracle.topk(x.cpu().numpy(), 7)
+    assert np.array_equal(i.cpu().numpy(), oi)
+    bad = [(torch.empty(3, 6, device="cuda"), good[1]),                        # too small
+           (good[0], torch.empty(3, 7, dtype=torch.int32, device="cuda")),     # index dtype
+           (torch.empty(3, 7, dtype=torch.bfloat16, device="cuda"), good[1]),  # value dtype
+           (torch.empty(7, 3, device="cuda").t(), good[1]),                    # not contiguous
+           (torch.empty(3, 7), good[1])]                                       # host memory
+    for o in bad:
+        with pytest.raises(ValueError):
+            tss.topk(x, 7, out=o)
+    # an empty batch gives empty outputs, and still checks k
+    e = torch.empty(0, 1000, device="cuda")
+    v, i = tss.topk(e, 5)
+    assert v.shape == (0, 5) and i.shape == (0, 5) and i.dtype == torch.int64
+    with pytest.raises(tss.TopkError):
+        tss.topk(e, 1001)
+
+
 def test_stream_read_reads_and_writes_nothing():
     # the read-ceiling aid: valid sizes run, a ragged or misaligned buffer
     # is refused, and the data and the sink are left as they were

@@ -97,7 +97,10 @@ def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Works
          out: tuple | None = None):
     """Exact top-k of each row of ``x`` ([rows, n] or [n], contiguous rows).
 
-    Returns (values, indices) shaped [rows, k] (or [k] for 1-D input)."""
+    Returns (values, indices) shaped [rows, k] (or [k] for 1-D input).  An
+    empty batch (rows = 0) returns empty outputs.  ``out`` = (values,
+    indices): contiguous tensors of rows * k elements on x's device, of x's
+    dtype and int64; anything else raises ValueError before any launch."""
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
     squeeze = x.dim() == 1
@@ -107,16 +110,30 @@ def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Works
     rows, n = x2.shape
     code = dtype_code(x2.dtype)
     dev = x2.device
+    if out is not None:
+        vals, idx = out
+        for t, dt, name in ((vals, x2.dtype, "values"), (idx, torch.int64, "indices")):
+            if (t.device != dev or t.dtype != dt or not t.is_contiguous()
+                    or t.numel() != rows * k):
+                raise ValueError(f"out {name}: need a contiguous {dt} tensor of {rows} x {k} "
+                                 f"elements on {dev}")
+    if rows == 0:   # an empty batch: nothing to select
+        if not 1 <= k <= n:
+            raise _lib.TopkError(_lib.TOPK_EINVAL, "topk")
+        if out is None:
+            vals = torch.empty((0, k), dtype=x2.dtype, device=dev)
+            idx = torch.empty((0, k), dtype=torch.int64, device=dev)
+        return vals, idx
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         ws = workspace if workspace is not None else _workspace_for(dev)
+        if _norm_device(ws.device) != dev:
+            raise ValueError(f"workspace is on {ws.device}, x on {dev}")
         need = workspace_size(n, rows, k, code, params)
         buf = ws.get(need, stream)
         if out is None:
             vals = torch.empty((rows, k), dtype=x2.dtype, device=dev)
             idx = torch.empty((rows, k), dtype=torch.int64, device=dev)
-        else:
-            vals, idx = out
         st = _lib.lib.topk_ex(x2.data_ptr(), n, rows, k, code, vals.data_ptr(), idx.data_ptr(),
                               buf.data_ptr(), buf.numel(), stream, _pp(params))
         _lib.check(st, "topk")
@@ -189,11 +206,12 @@ def scatter(values: torch.Tensor, indices: torch.Tensor, n: int, out: torch.Tens
         m = torch.empty((rows, n), dtype=torch.uint8, device=dev)
     elif isinstance(mask, torch.Tensor):
         m = mask
-    if not (out.is_cuda and out.is_contiguous() and out.dtype == v2.dtype and out.numel() == rows * n):
-        raise ValueError("out: contiguous GPU tensor of rows * n elements, the values' dtype")
-    if m is not None and not (m.is_cuda and m.is_contiguous() and m.dtype == torch.uint8
+    if not (out.device == dev and out.is_contiguous() and out.dtype == v2.dtype
+            and out.numel() == rows * n):
+        raise ValueError("out: contiguous tensor of rows * n elements, the values' dtype and device")
+    if m is not None and not (m.device == dev and m.is_contiguous() and m.dtype == torch.uint8
                               and m.numel() == rows * n):
-        raise ValueError("mask: contiguous uint8 GPU tensor of rows * n elements")
+        raise ValueError("mask: contiguous uint8 tensor of rows * n elements on the values' device")
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.lib.topk_scatter(v2.data_ptr(), i2.data_ptr(), rows, k, n, dtype_code(v2.dtype),
