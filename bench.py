@@ -265,6 +265,30 @@ def run_bench(args):
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
 
+    # the same K calls captured in one HIP graph (own workspace, sized by
+    # eager calls first) and replayed: what remains without host launches
+    gws = tss.Workspace()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            tss.topk(bufs[i % 3], k, workspace=gws, out=(ov, oi))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            tss.topk(bufs[i % 3], k, workspace=gws, out=(ov, oi))
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    graph_replay = {"ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4),
+                    "calls_per_graph": args.steps}
+    del graph, gws
+
     # stage timing: HIP events on the launch stream around each stage
     tss.profile_enable(True)
     tss.profile_read()
@@ -416,6 +440,7 @@ def run_bench(args):
         "exact_route_ms_per_call": round(exact_ms, 4) if exact_ms is not None else None,
         "stage_ms": stage_ms,
         "ms_per_step_with_stage_events": round(ms_step_profiled, 4),
+        "graph_replay": graph_replay,
     }
     print(json.dumps(line), flush=True)
 

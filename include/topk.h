@@ -84,8 +84,12 @@ typedef enum {
   TOPK_POLICY_TUNED = 2
 } topk_policy;
 
-/* Route.  AUTO: the sampled filter when n >= 8*S, n >= 2^18 and the buffer
- * M is below n/2, else the exact radix select.  FILTER / EXACT force one route (FILTER
+/* Route.  AUTO: the sampled filter when n >= 8*S and the buffer M is below
+ * n/2, except for rows of at most 2^18 elements where one workgroup per row
+ * (exact, no sample) is estimated cheaper: about 8 us + 0.84 ns per element
+ * per round of rows (a row per compute unit) against about 22 us + 0.025 us
+ * per row + the input at 7 TB/s for the sampled route (MI355X timings).
+ * Otherwise the exact radix select.  FILTER / EXACT force one route (FILTER
  * still falls back to the exact select when the sample fails). */
 typedef enum { TOPK_PATH_AUTO = 0, TOPK_PATH_FILTER = 1, TOPK_PATH_EXACT = 2 } topk_path;
 

@@ -326,6 +326,21 @@ def test_large_k_bf16_sampled():
     assert_same(gv, gi, x, k, "bf16", "large k")
 
 
+@pytest.mark.parametrize("dt,S", [("bf16", 1024), ("bf16", 2048), ("float32", 1024)])
+def test_large_k_sampled_short_row(dt, S):
+    # a short row filtered by two workgroups: each wave stages hundreds of
+    # candidates and flushes its stage several times on the way; the bucket
+    # histogram's candidate count must include those flushes (the row is
+    # accepted for these seeds: 6,000-7,300 candidates, buffer 7,884-9,278)
+    n, k = 70_000, 5000
+    x = workloads.relu_bf16(1, n, 9) if dt == "bf16" else workloads.normal_f32(1, n, 9)
+    for seed in (0, 1):
+        say(f"large k short row {dt} S={S} seed={seed}")
+        gv, gi = run_gpu(x, k, dt, params=_seeded(seed, S=S, force_path=1))
+        assert_same(gv, gi, x, k, dt, f"short row {dt} S={S} seed={seed}")
+        assert _tss().read_stats(1)[0]["path"] == 0
+
+
 def test_large_k_batched_fp32():
     x = workloads.normal_f32(3, 2 ** 20 + 3, 72)
     k = 20000
@@ -624,3 +639,47 @@ def test_relaxed_selection_scatters_kept_slots_only():
     edense, emask = oracle.sparse_activation(ov[None, :R], oi[None, :R], n)
     assert _dense_to_host(out, "float32").tobytes() == edense.tobytes()
     assert np.array_equal(m.cpu().numpy(), emask)
+
+
+@pytest.mark.parametrize("case", ["sampled", "large_k", "small_rows"])
+def test_graph_capture_replays_match(case):
+    # one topk call captured in a HIP graph (on its own workspace, allocated
+    # before the capture), replayed several times with eager work and
+    # synchronisations in between; every replay must equal the oracle
+    tss = _tss()
+    if case == "sampled":
+        x, k = workloads.normal_f32(2, 2 ** 21 + 7, 401), 64
+    elif case == "large_k":
+        x, k = workloads.normal_f32(1, 2 ** 21 + 7, 402), 5000
+    else:
+        x, k = workloads.scores_int(5, 3000, 0, 40, 403), 17
+    dt = "int32" if x.dtype == np.int32 else "float32"
+    say(f"graph capture: {case} rows={x.shape[0]} n={x.shape[1]} k={k}")
+    xt = to_dev(x, dt)
+    ev, ei = oracle.topk(x, k, dt)
+    ws = tss.Workspace()
+    ov = torch.empty((x.shape[0], k), dtype=xt.dtype, device="cuda")
+    oi = torch.empty((x.shape[0], k), dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tss.topk(xt, k, workspace=ws, out=(ov, oi))   # sizes the workspace
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tss.topk(xt, k, workspace=ws, out=(ov, oi))
+    torch.cuda.synchronize()
+    other = torch.randn(3, 50_000, device="cuda")
+    for rep in range(4):
+        ov.zero_()
+        oi.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(oi.cpu().numpy(), ei), f"replay {rep}: indices differ"
+        assert ov.cpu().numpy().tobytes() == ev.tobytes(), f"replay {rep}: values differ"
+        # eager work between replays, on the default workspace
+        v2, i2 = tss.topk(other, 9)
+        torch.cuda.synchronize()
+        assert np.array_equal(i2.cpu().numpy(), oracle.topk(other.cpu().numpy(), 9)[1])
+    del g

@@ -110,9 +110,15 @@ def test_tuned_policy_limits(lib):
 
 
 def test_route_rules(lib):
-    # small rows: one workgroup per row; large: the sampled filter
+    # short rows: one workgroup per row while that is estimated cheaper than
+    # the sampled route (the pass costs about 22 us whatever the size); long
+    # or few rows: the sampled filter
     assert _plan(lib, 4096, 1, 10, 0)[1].path == 2
-    assert _plan(lib, 2 ** 18 - 1, 1, 10, 1)[1].path == 2
+    assert _plan(lib, 5000, 300, 17, 0)[1].path == 2          # n < 8 S
+    assert _plan(lib, 16384, 256, 16, 1)[1].path == 2         # one round of rows
+    assert _plan(lib, 65536, 1, 10, 0)[1].path == 0           # config 2: 64 us vs 21 us
+    assert _plan(lib, 65536, 64, 64, 1)[1].path == 0
+    assert _plan(lib, 2 ** 18 - 1, 1, 10, 1)[1].path == 0
     assert _plan(lib, 2 ** 18, 1, 10, 1)[1].path == 0
     assert _plan(lib, 2 ** 28, 1, 64, 1)[1].path == 0
     # a buffer of half the row or more: exact select over the row

@@ -61,7 +61,11 @@ def workspace_size(n: int, rows: int, k: int, dtype, params: Params | None = Non
 
 class Workspace:
     """Device scratch for topk calls on one device; grows on demand.  A
-    workspace serves one stream at a time."""
+    workspace serves one stream at a time.  The library allocates nothing and
+    records no memset, so a call can be captured in a HIP graph; the graph
+    keeps the workspace's address, so give captured calls a workspace of
+    their own, sized by an eager call of the same shape before the capture
+    (a later, larger call would reallocate it under the graph)."""
 
     def __init__(self, device=None):
         self.device = torch.device(device if device is not None else "cuda")

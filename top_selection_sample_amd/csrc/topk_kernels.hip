@@ -372,8 +372,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
 // stops early (the row overflows, so only "more than the capacity" matters).
 //
 // Survivor slots come from a wave ballot and the count of set lanes below
-// each lane (the stable split's "how many earlier elements share my flag",
-// GPU.js Learn "One Bit at a Time"); they are staged per wave in LDS and each
+// each lane (the stable split's count of earlier elements with the same
+// flag, GPU.js Learn "One Bit at a Time"); they are staged per wave in LDS and each
 // workgroup appends its survivors with one atomic at the end.
 // ======================================================================
 // Launch shape (measured on MI355X): 512-thread workgroups, one per compute
@@ -395,6 +395,7 @@ struct Stager {
   uint32_t* kmax;    // if set: publish() raises it to the largest key stored
   uint32_t kshift;   //   (key = comp >> kshift)
   uint32_t km;       // wave-uniform: largest key flushed since the last publish
+  uint32_t flushed = 0;   // wave-uniform: entries counted by flush() so far
 
   // Returns true when the buffer is full.
   __device__ bool flush() {
@@ -415,6 +416,7 @@ struct Stager {
     }
     wave_lds_sync();
     const bool full = base + fill > cap;
+    flushed += fill;
     fill = 0;
     return full;
   }
@@ -604,7 +606,8 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 
   __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
   __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
-  __shared__ uint32_t s_fill[FILTER_WAVES], s_tfill[FILTER_WAVES], s_ties[FILTER_WAVES];
+  __shared__ uint32_t s_fill[FILTER_WAVES], s_tfill[FILTER_WAVES], s_ties[FILTER_WAVES],
+      s_flushed[FILTER_WAVES];
   __shared__ uint32_t s_base, s_tbase, s_km;
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
   if (tid == 0) s_km = 0;
@@ -812,25 +815,30 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     }
   }
 
-  // Workgroup flush: one atomic per buffer, and one for the tie count.
+  // Workgroup flush: one atomic per buffer, one for the tie count, and one
+  // for the above-tau total (the staged entries plus those the waves
+  // flushed on the way; the count the finish kernel reads, which no other
+  // kernel rewrites).
   ties = wave_sum_u32(ties);
   if (lane == 0) {
     s_fill[w] = sg.fill;
     s_tfill[w] = tg.fill;
     s_ties[w] = ties;
+    s_flushed[w] = sg.flushed;
   }
   __syncthreads();
   if (tid == 0) {
-    uint32_t total = 0, ttotal = 0, tcount = 0;
+    uint32_t total = 0, ttotal = 0, tcount = 0, earlier = 0;
     for (uint32_t i = 0; i < FILTER_WAVES; ++i) {
       total += s_fill[i];
       ttotal += s_tfill[i];
       tcount += s_ties[i];
+      earlier += s_flushed[i];
     }
     s_base = total ? atomicAdd(&st->count, total) : 0u;
     s_tbase = ttotal ? atomicAdd(&rc->tslots, ttotal) : 0u;
     if (tcount) atomicAdd(&rc->ties, tcount);
-    if (total) atomicAdd(&rc->above, total);
+    if (total + earlier) atomicAdd(&rc->above, total + earlier);
   }
   __syncthreads();
   uint32_t off = s_base, toff = s_tbase;

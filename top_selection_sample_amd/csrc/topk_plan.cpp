@@ -323,10 +323,25 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   // the refine that runs is the one for k: its cost ratio prices the buffer
   if (k > KSMALL) row_in.tuned_ratio = in.tuned_ratio_large;
   sample_params(n, p.k_eff, row_in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
+  const int es = (dtype == 2) ? 2 : 4;
+  const int64_t cus = in.cus > 0 ? in.cus : 256;
+  // Rows up to EXACT_SMALL_MAX can instead be selected one workgroup per
+  // row, exactly and with no sample.  Measured on MI355X, that costs about
+  // 8 us + 0.84 ns per element for each round of rows (one row per compute
+  // unit), and the sampled route about 22 us + 0.025 us per row + the input
+  // read at 7 TB/s; the cheaper one runs.  (One row of 2^16 elements: 64 us
+  // in one workgroup, 21 us sampled; one row of 4096: 12 against 22.)
+  bool small_cheaper = false;
+  if (n <= EXACT_SMALL_MAX) {
+    const double rounds = (double)((rows + cus - 1) / cus);
+    const double t_small = (8.0 + 8.4e-4 * (double)n) * rounds;
+    const double t_sampled = 22.0 + 0.025 * (double)rows + (double)rows * (double)n * es / 7.0e6;
+    small_cheaper = t_small <= t_sampled;
+  }
   bool sampled;
   if (in.force_path == 1) sampled = true;
   else if (in.force_path == 2) sampled = false;
-  else sampled = (n >= 8 * p.S) && (n >= EXACT_SMALL_MAX) && (p.M < n / 2);
+  else sampled = (n >= 8 * p.S) && (p.M < n / 2) && !small_cheaper;
   if (sampled) {
     p.path = PLAN_SAMPLED;
     p.cap = p.M < k ? k : p.M;
@@ -339,14 +354,12 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
     int64_t c = 2 * k > 16384 ? 2 * k : 16384;
     p.cap = c > n ? n : c;
   }
-  const int es = (dtype == 2) ? 2 : 4;
   // filter grid: one or two workgroups per compute unit over the whole call,
   // each a contiguous slice of one row no shorter than 64 KB.  With few
   // survivors one 512-thread workgroup per CU is faster (the next step's
   // loads are in flight while a step is examined; 2.5% on 2^28 fp32 at
   // t/S = 4e-5); with many (t/S ~ 1e-3: bf16 BatchTopK, 128 short rows) two
   // hide the survivor handling better (4% and 16% faster there)
-  const int64_t cus = in.cus > 0 ? in.cus : 256;
   const bool dense = (double)p.t > 2e-4 * (double)p.S;
   int64_t fb = ((dense ? 2 : 1) * cus + rows / 2) / rows;
   const int64_t max_slices = (n * es) / 65536;
