@@ -1335,6 +1335,81 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
   __syncthreads();
 }
 
+// A short row (n <= ER_VEC * blockDim.x) and k <= RF_RANK_MAX: the row is
+// read once into registers; a block min and max of its keys give the 11 key
+// bits just below their common prefix, whose LDS histogram finds the bin
+// holding rank k; the elements from that bin up go to LDS and, when there
+// are at most RF_RANK_MAX of them, are ranked by counting and written.
+// Returns false, having written nothing, when more elements reach that bin
+// (heavy ties); the caller then runs the radix select.  s_tmp: 32 words;
+// s_hist2048: RF_BINS words, 16-byte aligned, apart from s_cand[0 ..
+// RF_RANK_MAX).  Every thread of the workgroup calls it.
+constexpr uint32_t ER_VEC = 8;
+template <int DT>
+__device__ bool exact_row_in_registers(const char* rowp, uint32_t n, uint32_t k, uint32_t B,
+                                       void* out_values, int64_t* out_idx, uint32_t row,
+                                       uint32_t* s_tmp, uint32_t* s_misc, uint32_t* s_hist2048,
+                                       uint64_t* s_cand) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
+  uint32_t key[ER_VEC];
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (uint32_t j = 0; j < ER_VEC; ++j) {
+    const uint32_t i = j * nt + tid;
+    key[j] = i < n ? Dt<DT>::key(load_raw<DT>(rowp, i)) : 0u;
+    if (i < n) {
+      mx = key[j] > mx ? key[j] : mx;
+      mn = key[j] < mn ? key[j] : mn;
+    }
+  }
+  for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist2048[i] = 0;
+  if (tid == 0) s_misc[4] = 0;
+  mx = wave_max_u32(mx);
+  mn = ~wave_max_u32(~mn);
+  if (lane == 0) {
+    s_tmp[w] = mx;
+    s_tmp[16 + w] = mn;
+  }
+  __syncthreads();
+  const uint32_t nw = nt >> 6;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (uint32_t j = 0; j < 16; ++j) {   // independent reads
+    const uint32_t a = j < nw ? s_tmp[j] : 0u, c = j < nw ? s_tmp[16 + j] : 0xFFFFFFFFu;
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  const uint32_t diff = kmin ^ kmax;
+  const uint32_t top = diff ? 31u - (uint32_t)__builtin_clz(diff) : 0u;
+  const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
+  auto digit = [&](uint32_t x) { return (x >> kshift) & (RF_BINS - 1); };
+#pragma unroll
+  for (uint32_t j = 0; j < ER_VEC; ++j) hist_add(s_hist2048, digit(key[j]), j * nt + tid < n);
+  __syncthreads();
+  if (tid < 64) wave_find_bucket_2048(s_hist2048, k, s_misc);
+  __syncthreads();
+  const uint32_t b = s_misc[0], got = s_misc[1] + s_misc[2];
+  if (got > RF_RANK_MAX) return false;   // (uniform)
+  // the elements from the bin up, one slot reservation per wave
+  const uint64_t maskB = (1ull << B) - 1ull;
+  uint32_t mine = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < ER_VEC; ++j) mine += (j * nt + tid < n && digit(key[j]) >= b) ? 1u : 0u;
+  const uint32_t incl = wave_incl_sum(mine);
+  const uint32_t wtot = wave_bcast(incl, 63u);
+  uint32_t wbase = 0;
+  if (lane == 0 && wtot) wbase = atomicAdd(&s_misc[4], wtot);
+  uint32_t pos = wave_bcast(wbase, 0u) + incl - mine;
+#pragma unroll
+  for (uint32_t j = 0; j < ER_VEC; ++j) {
+    const uint32_t i = j * nt + tid;
+    if (i < n && digit(key[j]) >= b) s_cand[pos++] = ((uint64_t)key[j] << B) | (maskB - i);
+  }
+  __syncthreads();
+  rank_and_write<DT>(s_cand, got, k, k, B, rowp, n, out_values, out_idx, row);
+  return true;
+}
+
 // Whole exact selection of a small row in one workgroup.  Small k: writes the
 // answer.  Large k: leaves exactly k winners in the candidate buffer for the
 // multi-workgroup sort.
@@ -1345,19 +1420,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
     uint32_t small_k, void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_misc[8];
-  __shared__ uint64_t s_cand[CAND_CAP];
+  __shared__ __align__(16) uint64_t s_cand[CAND_CAP];
+  static_assert(CAND_CAP * 2 >= RF_RANK_MAX * 2 + RF_BINS, "bins beside the ranked candidates");
   const uint32_t row = blockIdx.x;
   RowState* st = states + row;
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-  RowSrc<DT> src{rowp, B, (1ull << B) - 1ull};
-  SelectOut sel = block_select(src, n, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
-  if (small_k) {
-    const uint32_t got = block_collect(src, n, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
-    const uint32_t P = next_pow2(got);
-    for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
-    __syncthreads();
-    block_bitonic_desc(s_cand, P);
-    write_winners<DT>(s_cand, k, k, B, rowp, n, out_values, out_idx, row);
+  auto finish_row = [&]() {
     __syncthreads();
     if (threadIdx.x == 0) {
       st->status = ST_DONE;
@@ -1367,6 +1435,26 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       st->tau_key = 0;
       st->ties = 0;
     }
+  };
+  if (small_k && k <= RF_RANK_MAX && n <= ER_VEC * blockDim.x) {
+    uint32_t* s_hist2048 = reinterpret_cast<uint32_t*>(s_cand + CAND_CAP / 2);
+    if (exact_row_in_registers<DT>(rowp, n, k, B, out_values, out_idx, row, s_hist, s_misc,
+                                   s_hist2048, s_cand)) {
+      finish_row();
+      return;
+    }
+    __syncthreads();   // every thread has read the bin search's result
+  }
+  RowSrc<DT> src{rowp, B, (1ull << B) - 1ull};
+  SelectOut sel = block_select(src, n, W, k, k, s_hist, s_misc, s_cand, CAND_CAP);
+  if (small_k) {
+    const uint32_t got = block_collect(src, n, sel.thr, s_cand, CAND_CAP, &s_misc[4]);
+    const uint32_t P = next_pow2(got);
+    for (uint32_t i = got + threadIdx.x; i < P; i += blockDim.x) s_cand[i] = 0ull;
+    __syncthreads();
+    block_bitonic_desc(s_cand, P);
+    write_winners<DT>(s_cand, k, k, B, rowp, n, out_values, out_idx, row);
+    finish_row();
     return;
   }
   // large k: scatter the k winners to global memory
