@@ -683,3 +683,26 @@ def test_graph_capture_replays_match(case):
         torch.cuda.synchronize()
         assert np.array_equal(i2.cpu().numpy(), oracle.topk(other.cpu().numpy(), 9)[1])
     del g
+
+
+def test_two_streams_default_workspaces():
+    # calls on two streams at once, each with its stream's default workspace:
+    # both answers exact
+    tss = _tss()
+    xa = workloads.normal_f32(2, 2 ** 21 + 1, 501)
+    xb = workloads.pareto_signed(3, 2 ** 20 + 3, 502)
+    ta, tb = to_dev(xa, "float32"), to_dev(xb, "float32")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("two streams, default workspaces")
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(sa):
+            va, ia = tss.topk(ta, 64)
+        with torch.cuda.stream(sb):
+            vb, ib = tss.topk(tb, 300)
+        torch.cuda.synchronize()
+        outs.append((ia.cpu().numpy(), ib.cpu().numpy()))
+    ea, eb = oracle.topk(xa, 64)[1], oracle.topk(xb, 300)[1]
+    for ia, ib in outs:
+        assert np.array_equal(ia, ea) and np.array_equal(ib, eb)

@@ -89,9 +89,11 @@ def _norm_device(device) -> torch.device:
     return dev
 
 
-def _workspace_for(device) -> Workspace:
+def _workspace_for(device, stream: int) -> Workspace:
+    """The default workspace of a (device, stream) pair: calls on different
+    streams never share scratch memory."""
     device = _norm_device(device)
-    key = (device.type, device.index)
+    key = (device.type, device.index, stream)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
@@ -130,7 +132,7 @@ def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Works
         return vals, idx
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        ws = workspace if workspace is not None else _workspace_for(dev)
+        ws = workspace if workspace is not None else _workspace_for(dev, stream)
         if _norm_device(ws.device) != dev:
             raise ValueError(f"workspace is on {ws.device}, x on {dev}")
         need = workspace_size(n, rows, k, code, params)
@@ -147,14 +149,16 @@ def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Works
 
 
 def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> list:
-    """Per-row records of the last call on a workspace (synchronises)."""
+    """Per-row records of the last call on a workspace (synchronises).  With
+    no workspace given: the default one of the current stream, the one that
+    stream's last call used."""
     dev = _norm_device(device)
-    ws = workspace if workspace is not None else _workspace_for(dev)
-    if ws.buf is None:
-        raise RuntimeError("no call has used this workspace yet")
-    arr = (_lib.RowStats * rows)()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
+        ws = workspace if workspace is not None else _workspace_for(dev, stream)
+        if ws.buf is None:
+            raise RuntimeError("no call has used this workspace yet")
+        arr = (_lib.RowStats * rows)()
         _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
     return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes,
              "flags": a.flags, "ties": a.ties} for a in arr]
