@@ -11,6 +11,7 @@ device memory and the stream; the selection runs in libtopk_mi355x.so.
 from __future__ import annotations
 
 import ctypes
+from contextlib import nullcontext
 
 import torch
 
@@ -52,11 +53,19 @@ def plan(n: int, rows: int, k: int, dtype, params: Params | None = None) -> dict
     return {f: getattr(info, f) for f, _ in _lib.PlanInfo._fields_}
 
 
+_ws_sizes: dict = {}
+
+
 def workspace_size(n: int, rows: int, k: int, dtype, params: Params | None = None) -> int:
-    out = ctypes.c_size_t()
-    _lib.check(_lib.lib.topk_workspace_size(n, rows, k, dtype_code(dtype), _pp(params),
-                                            ctypes.byref(out)), "topk_workspace_size")
-    return out.value
+    code = dtype_code(dtype)
+    key = (n, rows, k, code, bytes(params) if params is not None else None)
+    size = _ws_sizes.get(key)
+    if size is None:
+        out = ctypes.c_size_t()
+        _lib.check(_lib.lib.topk_workspace_size(n, rows, k, code, _pp(params), ctypes.byref(out)),
+                   "topk_workspace_size")
+        size = _ws_sizes[key] = out.value
+    return size
 
 
 class Workspace:
@@ -68,7 +77,7 @@ class Workspace:
     (a later, larger call would reallocate it under the graph)."""
 
     def __init__(self, device=None):
-        self.device = torch.device(device if device is not None else "cuda")
+        self.device = _norm_device(device)
         self.buf = None
 
     def get(self, nbytes: int, stream) -> torch.Tensor:
@@ -130,10 +139,13 @@ def topk(x: torch.Tensor, k: int, params: Params | None = None, workspace: Works
             vals = torch.empty((0, k), dtype=x2.dtype, device=dev)
             idx = torch.empty((0, k), dtype=torch.int64, device=dev)
         return vals, idx
-    with torch.cuda.device(dev):
+    # the library launches on the current device: switch only when x lives
+    # elsewhere (the switch costs more than the rest of a small call)
+    ctx = torch.cuda.device(dev) if dev.index != torch.cuda.current_device() else nullcontext()
+    with ctx:
         stream = torch.cuda.current_stream(dev).cuda_stream
         ws = workspace if workspace is not None else _workspace_for(dev, stream)
-        if _norm_device(ws.device) != dev:
+        if ws.device != dev:
             raise ValueError(f"workspace is on {ws.device}, x on {dev}")
         need = workspace_size(n, rows, k, code, params)
         buf = ws.get(need, stream)
