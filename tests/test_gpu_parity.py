@@ -706,3 +706,18 @@ def test_two_streams_default_workspaces():
     ea, eb = oracle.topk(xa, 64)[1], oracle.topk(xb, 300)[1]
     for ia, ib in outs:
         assert np.array_equal(ia, ea) and np.array_equal(ib, eb)
+
+
+@pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "equal", "asc", "special"])
+@pytest.mark.parametrize("n,k", [(8193, 1), (30001, 10), (65536, 256), (65535, 64)])
+def test_short_rows_one_workgroup(dt, kind, n, k):
+    # rows up to 65,536 through the one-workgroup route (forced): read in
+    # 16-byte vectors with an unaligned head and tail (three rows of odd
+    # length start at different alignments), binned on the key range, ranked;
+    # heavy ties take the radix select instead
+    x = np.concatenate([_edge_rows(dt, n, kind, 600 + r) for r in range(3)])
+    p = _tss().default_params(force_path=2)
+    say(f"short rows one workgroup {dt} {kind} n={n} k={k}")
+    gv, gi = run_gpu(x, k, dt, params=p)
+    assert_same(gv, gi, x, k, dt, f"short rows {dt} {kind} n={n} k={k}")

@@ -1335,7 +1335,7 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
   __syncthreads();
 }
 
-// A short row (n <= ER_VEC * blockDim.x) and k <= RF_RANK_MAX: the row is
+// A short row (n <= NV * blockDim.x) and k <= RF_RANK_MAX: the row is
 // read once into registers; a block min and max of its keys give the 11 key
 // bits just below their common prefix, whose LDS histogram finds the bin
 // holding rank k; the elements from that bin up go to LDS and, when there
@@ -1344,17 +1344,16 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
 // (heavy ties); the caller then runs the radix select.  s_tmp: 32 words;
 // s_hist2048: RF_BINS words, 16-byte aligned, apart from s_cand[0 ..
 // RF_RANK_MAX).  Every thread of the workgroup calls it.
-constexpr uint32_t ER_VEC = 8;
-template <int DT>
+template <int DT, uint32_t NV>
 __device__ bool exact_row_in_registers(const char* rowp, uint32_t n, uint32_t k, uint32_t B,
                                        void* out_values, int64_t* out_idx, uint32_t row,
                                        uint32_t* s_tmp, uint32_t* s_misc, uint32_t* s_hist2048,
                                        uint64_t* s_cand) {
   const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
-  uint32_t key[ER_VEC];
+  uint32_t key[NV];
   uint32_t mx = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
-  for (uint32_t j = 0; j < ER_VEC; ++j) {
+  for (uint32_t j = 0; j < NV; ++j) {
     const uint32_t i = j * nt + tid;
     key[j] = i < n ? Dt<DT>::key(load_raw<DT>(rowp, i)) : 0u;
     if (i < n) {
@@ -1384,7 +1383,7 @@ __device__ bool exact_row_in_registers(const char* rowp, uint32_t n, uint32_t k,
   const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
   auto digit = [&](uint32_t x) { return (x >> kshift) & (RF_BINS - 1); };
 #pragma unroll
-  for (uint32_t j = 0; j < ER_VEC; ++j) hist_add(s_hist2048, digit(key[j]), j * nt + tid < n);
+  for (uint32_t j = 0; j < NV; ++j) hist_add(s_hist2048, digit(key[j]), j * nt + tid < n);
   __syncthreads();
   if (tid < 64) wave_find_bucket_2048(s_hist2048, k, s_misc);
   __syncthreads();
@@ -1394,17 +1393,108 @@ __device__ bool exact_row_in_registers(const char* rowp, uint32_t n, uint32_t k,
   const uint64_t maskB = (1ull << B) - 1ull;
   uint32_t mine = 0;
 #pragma unroll
-  for (uint32_t j = 0; j < ER_VEC; ++j) mine += (j * nt + tid < n && digit(key[j]) >= b) ? 1u : 0u;
+  for (uint32_t j = 0; j < NV; ++j) mine += (j * nt + tid < n && digit(key[j]) >= b) ? 1u : 0u;
   const uint32_t incl = wave_incl_sum(mine);
   const uint32_t wtot = wave_bcast(incl, 63u);
   uint32_t wbase = 0;
   if (lane == 0 && wtot) wbase = atomicAdd(&s_misc[4], wtot);
   uint32_t pos = wave_bcast(wbase, 0u) + incl - mine;
 #pragma unroll
-  for (uint32_t j = 0; j < ER_VEC; ++j) {
+  for (uint32_t j = 0; j < NV; ++j) {
     const uint32_t i = j * nt + tid;
     if (i < n && digit(key[j]) >= b) s_cand[pos++] = ((uint64_t)key[j] << B) | (maskB - i);
   }
+  __syncthreads();
+  rank_and_write<DT>(s_cand, got, k, k, B, rowp, n, out_values, out_idx, row);
+  return true;
+}
+
+// The same for rows too long for the registers (n <= ER_STREAM_MAX): three
+// reads of the row in 16-byte vectors (its key range, the histogram, the
+// collection), the last two from L2.  values: the whole input (the row's
+// unaligned head and tail elements are visited by the first wave).
+constexpr uint32_t ER_STREAM_MAX = 1u << 16;
+template <int DT>
+__device__ bool exact_row_streamed(const void* values, uint32_t n, uint32_t k, uint32_t B,
+                                   void* out_values, int64_t* out_idx, uint32_t row,
+                                   uint32_t* s_tmp, uint32_t* s_misc, uint32_t* s_hist2048,
+                                   uint64_t* s_cand) {
+  using D = Dt<DT>;
+  constexpr uint32_t U = 4;               // 16-byte loads in flight per thread
+  constexpr uint32_t E = U * D::VEC;      // elements per thread per step
+  const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(rowp);
+  uint32_t head = (uint32_t)(((16u - (addr & 15u)) & 15u) / D::ES);
+  if (head > n) head = n;
+  const uint32_t nvec = (n - head) / D::VEC;
+  const uint32_t tail0 = head + nvec * D::VEC;
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + (size_t)head * D::ES);
+  // f(key, index, valid) for every element; every thread calls it the same
+  // number of times within a wave, so f may use wave operations
+  auto visit = [&](auto&& f) {
+    for (uint32_t v0 = 0; v0 < nvec; v0 += U * nt) {
+      u32x4 x[U];
+#pragma unroll
+      for (uint32_t j = 0; j < U; ++j) {
+        const uint32_t v = v0 + j * nt + tid;
+        x[j] = v < nvec ? vp[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (uint32_t b = 0; b < E; ++b) {
+        const uint32_t v = v0 + (b / D::VEC) * nt + tid;
+        f(D::key(elemvc<DT, U>(x, b)), head + v * D::VEC + b % D::VEC, v < nvec);
+      }
+    }
+    if (tid < 64) {   // fewer than 2 * VEC elements outside the vectors
+      const bool ok = tid < head + (n - tail0);
+      uint32_t idx = 0, key = 0;
+      if (ok) {
+        idx = tid < head ? tid : tail0 + (tid - head);
+        key = D::key(load_raw<DT>(rowp, idx));
+      }
+      f(key, idx, ok);
+    }
+  };
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+  visit([&](uint32_t key, uint32_t, bool ok) {
+    if (ok) {
+      mx = key > mx ? key : mx;
+      mn = key < mn ? key : mn;
+    }
+  });
+  for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist2048[i] = 0;
+  if (tid == 0) s_misc[4] = 0;
+  mx = wave_max_u32(mx);
+  mn = ~wave_max_u32(~mn);
+  if (lane == 0) {
+    s_tmp[w] = mx;
+    s_tmp[16 + w] = mn;
+  }
+  __syncthreads();
+  const uint32_t nw = nt >> 6;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (uint32_t j = 0; j < 16; ++j) {   // independent reads
+    const uint32_t a = j < nw ? s_tmp[j] : 0u, c = j < nw ? s_tmp[16 + j] : 0xFFFFFFFFu;
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  const uint32_t diff = kmin ^ kmax;
+  const uint32_t top = diff ? 31u - (uint32_t)__builtin_clz(diff) : 0u;
+  const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
+  auto digit = [&](uint32_t x) { return (x >> kshift) & (RF_BINS - 1); };
+  visit([&](uint32_t key, uint32_t, bool ok) { hist_add(s_hist2048, digit(key), ok); });
+  __syncthreads();
+  if (tid < 64) wave_find_bucket_2048(s_hist2048, k, s_misc);
+  __syncthreads();
+  const uint32_t b = s_misc[0], got = s_misc[1] + s_misc[2];
+  if (got > RF_RANK_MAX) return false;   // (uniform)
+  const uint64_t maskB = (1ull << B) - 1ull;
+  visit([&](uint32_t key, uint32_t idx, bool ok) {
+    lds_append(s_cand, &s_misc[4], RF_RANK_MAX, ((uint64_t)key << B) | (maskB - idx),
+               ok && digit(key) >= b);
+  });
   __syncthreads();
   rank_and_write<DT>(s_cand, got, k, k, B, rowp, n, out_values, out_idx, row);
   return true;
@@ -1436,10 +1526,15 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
       st->ties = 0;
     }
   };
-  if (small_k && k <= RF_RANK_MAX && n <= ER_VEC * blockDim.x) {
+  if (small_k && k <= RF_RANK_MAX && n <= ER_STREAM_MAX) {
     uint32_t* s_hist2048 = reinterpret_cast<uint32_t*>(s_cand + CAND_CAP / 2);
-    if (exact_row_in_registers<DT>(rowp, n, k, B, out_values, out_idx, row, s_hist, s_misc,
-                                   s_hist2048, s_cand)) {
+    const bool done =
+        n <= 8 * blockDim.x
+            ? exact_row_in_registers<DT, 8>(rowp, n, k, B, out_values, out_idx, row, s_hist,
+                                            s_misc, s_hist2048, s_cand)
+            : exact_row_streamed<DT>(values, n, k, B, out_values, out_idx, row, s_hist, s_misc,
+                                     s_hist2048, s_cand);
+    if (done) {
       finish_row();
       return;
     }
