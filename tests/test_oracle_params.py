@@ -108,15 +108,22 @@ def test_exact_tail_conditions_and_minimality(N, k):
         assert st.hypergeom.cdf(t - 1, N, M - 1, S) > half * (1 - 1e-6)
 
 
-def test_survey_table_values():
-    # regression values for the five shapes (Algorithm 1 verbatim and the
-    # exact-tail reading)
+def test_five_workload_shapes():
+    # the benchmark's five shapes: Algorithm 1 verbatim (regression values),
+    # and the exact-tail (t, M), each checked here to be the least meeting its
+    # bound by scipy's hypergeometric law (Lemma 1)
     cases = {(2 ** 28, 16): (32768, 1, 2399, 2, 81894),
              (2 ** 28, 64): (32768, 1, 4829, 2, 81894),
              (2 ** 28, 2048): (89638, 1, 18344, 6, 52130),
              (2 ** 20, 64): (32768, 1, 358, 9, 704),
              (2 ** 28, 131072): (131072, 91, 238844, 93, 262172)}
+    st = pytest.importorskip("scipy.stats")
+    half = 1e-3 / 2
     for (N, k), (S, t1, M1, te, Me) in cases.items():
         a, e = P.alg1(N, k), P.exact_tail(N, k)
         assert (a["S"], a["t"], a["M"]) == (S, t1, M1)
         assert (e["S"], e["t"], e["M"]) == (S, te, Me)
+        # recall failure R < k is H(N, k - 1, S) >= t; overflow R > M is H(N, M, S) <= t - 1
+        assert st.hypergeom.sf(te - 1, N, k - 1, S) <= half
+        assert te == 1 or st.hypergeom.sf(te - 2, N, k - 1, S) > half
+        assert st.hypergeom.cdf(te - 1, N, Me, S) <= half < st.hypergeom.cdf(te - 1, N, Me - 1, S)
