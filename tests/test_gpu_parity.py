@@ -721,3 +721,14 @@ def test_short_rows_one_workgroup(dt, kind, n, k):
     say(f"short rows one workgroup {dt} {kind} n={n} k={k}")
     gv, gi = run_gpu(x, k, dt, params=p)
     assert_same(gv, gi, x, k, dt, f"short rows {dt} {kind} n={n} k={k}")
+
+
+def test_max_rows():
+    # the largest batch the library accepts (65,535 rows: one grid dimension)
+    rows, n, k = 65_535, 100, 7
+    x = workloads.scores_int(rows, n, -50, 50, 601)
+    say(f"max rows {rows} x {n} k={k}")
+    gv, gi = run_gpu(x, k, "int32")
+    assert_same(gv, gi, x, k, "int32", "max rows")
+    with pytest.raises(_tss().TopkError):
+        _tss().topk(torch.zeros(rows + 1, 8, device="cuda"), 2)
