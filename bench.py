@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "top-k Gelem/s and HBM GB/s (% of peak), N=2^28 fp32 k=64, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc")
-KERNEL_SRC = os.path.join(CSRC, "topk_kernels.hip")
+KERNEL_SRC = os.path.join(CSRC, "topk_part_filter.hpp")   # the filter kernel's source
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_k_filter_c3_k64.txt")
 TRAFFIC_WORKLOAD = "c3k64"   # the workload those counters were taken on
 COPY_BYTES = 1 << 30

@@ -1,0 +1,342 @@
+// Sampler and threshold kernels (k_sample, k_tau).
+// A part of topk_kernels.hip, included there in order inside namespace tk;
+// it relies on the definitions of the parts before it and is not a
+// stand-alone header.
+#pragma once
+
+// ======================================================================
+// Sampler: S indices drawn without replacement (Prof-K, section 3, stage 1).
+// The first S images of a keyed permutation of [0, n): a balanced 4-round
+// Feistel network over 2h bits whose round function is the SplitMix64 output
+// mixer (Steele, Lea & Flood 2014), walked back into [0, n) ("cycle walking",
+// Black & Rogaway 2002).  Round keys for (seed, row) are outputs 4*row..4*row+3
+// of the SplitMix64 stream seeded with `seed`.
+// ======================================================================
+__device__ __forceinline__ uint64_t sm64_finalize(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z;
+}
+
+struct Feistel {
+  uint64_t rk[4];
+  uint64_t mask;
+  uint32_t h;
+  __device__ Feistel(uint64_t seed, uint64_t row, uint32_t half_bits) {
+    h = half_bits;
+    mask = (1ull << h) - 1ull;
+    const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rk[r] = sm64_finalize(seed + (4ull * row + (uint64_t)r + 1ull) * gamma);
+  }
+  __device__ uint64_t apply(uint64_t x) const {
+    uint64_t L = x >> h, R = x & mask;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t t = L ^ (sm64_finalize(R ^ rk[r]) & mask);
+      L = R;
+      R = t;
+    }
+    return (L << h) | R;
+  }
+};
+
+// Sample keys also land in an 11-bit histogram of their top bits (LDS per
+// workgroup, merged into the row's global histogram), the first level of the
+// threshold's radix select.
+constexpr uint32_t SH_BITS = 11;
+constexpr uint32_t SH_BINS = 1u << SH_BITS;
+
+// Small threshold ranks (t <= TOPT): every sampler workgroup keeps only its
+// own t largest keys (zero-padded to t), and k_tau selects from those G * t
+// keys instead of all S.  Their union holds the t largest sampled keys, and
+// padding keys of 0 cannot raise the t-th largest, so tau is unchanged.
+// (Letting the last sampler workgroup select saves the launch but needs an
+// agent-scope release fence in every workgroup: measured slower, much
+// slower with many rows.)
+constexpr uint32_t TOPT = 16;
+constexpr uint32_t SAMPLE_THREADS = 256;
+static_assert((SAMPLE_THREADS / 64) * TOPT <= 64, "one wave merges the wave lists");
+
+// The t largest alive values of the wave (with multiplicity), largest first,
+// written by lane 0 to out[0..); returns how many (wave-uniform).
+__device__ __forceinline__ uint32_t wave_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* out) {
+  uint32_t c = 0;
+  for (; c < t; ++c) {
+    if (ballot(alive) == 0) break;
+    const uint32_t m = wave_max_u32(alive ? v : 0u);
+    const uint64_t hit = ballot(alive && v == m);
+    if (lane_id() == (uint32_t)__builtin_ctzll(hit)) alive = false;
+    if (lane_id() == 0) out[c] = m;
+  }
+  return c;
+}
+
+// The same with four values per lane, v[0..cnt) sorted largest first: each
+// round takes the largest head and advances that lane.
+__device__ __forceinline__ uint32_t wave_top_t4(const uint32_t (&v)[4], uint32_t cnt, uint32_t t,
+                                                uint32_t* out) {
+  uint32_t c = 0, cur = 0;
+  for (; c < t; ++c) {
+    const bool alive = cur < cnt;
+    if (ballot(alive) == 0) break;
+    const uint32_t head = cur == 0 ? v[0] : cur == 1 ? v[1] : cur == 2 ? v[2] : v[3];
+    const uint32_t m = wave_max_u32(alive ? head : 0u);
+    const uint64_t hit = ballot(alive && head == m);
+    if (lane_id() == (uint32_t)__builtin_ctzll(hit)) ++cur;
+    if (lane_id() == 0) out[c] = m;
+  }
+  return c;
+}
+
+// The t largest of up to four values per thread over a workgroup of NW
+// waves (t <= CAP): per-wave lists, then one wave merges them.  s_wl: NW *
+// CAP words, s_wc: NW + 1 words, out: CAP words; returns the length.
+template <uint32_t NW, uint32_t CAP>
+__device__ __forceinline__ uint32_t block_top_t4(uint32_t (&v)[4], uint32_t cnt, uint32_t t,
+                                                 uint32_t* s_wl, uint32_t* s_wc, uint32_t* out) {
+  static_assert(NW * CAP <= 64, "one wave merges the wave lists");
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  auto cswap = [&](int a, int b) {
+    const uint32_t hi = v[a] > v[b] ? v[a] : v[b], lo = v[a] > v[b] ? v[b] : v[a];
+    v[a] = hi;
+    v[b] = lo;
+  };
+  // largest first; the cnt valid values must be the largest (invalid = 0)
+  cswap(0, 1);
+  cswap(2, 3);
+  cswap(0, 2);
+  cswap(1, 3);
+  cswap(1, 2);
+  const uint32_t c = wave_top_t4(v, cnt, t, s_wl + w * CAP);
+  if (lane == 0) s_wc[w] = c;
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t q = lane / CAP, i = lane % CAP;
+    const bool al = q < NW && i < s_wc[q];
+    const uint32_t x = al ? s_wl[q * CAP + i] : 0u;
+    const uint32_t m = wave_top_t(x, al, t, out);
+    if (lane == 0) s_wc[NW] = m;
+  }
+  __syncthreads();
+  return s_wc[NW];
+}
+
+// The same over the whole workgroup (SAMPLE_THREADS); the result in out
+// (TOPT words), its length returned.  s_wl: 4 * TOPT words, s_wc: 5 words.
+__device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
+                                                uint32_t* s_wc, uint32_t* out) {
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  const uint32_t c = wave_top_t(v, alive, t, s_wl + w * TOPT);
+  if (lane == 0) s_wc[w] = c;
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t q = lane / TOPT, i = lane % TOPT;
+    const bool al = q < SAMPLE_THREADS / 64 && i < s_wc[q];
+    const uint32_t x = al ? s_wl[q * TOPT + i] : 0u;
+    const uint32_t cnt = wave_top_t(x, al, t, out);
+    if (lane == 0) s_wc[4] = cnt;
+  }
+  __syncthreads();
+  return s_wc[4];
+}
+
+// Row setup for the sampled route (threshold known).
+__device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint32_t tau) {
+  st->status = ST_FILTER;
+  st->tau_key = tau;
+  st->count = 0;
+  st->ties = 0;
+  st->r_sampled = 0;
+  rc->ties = 0;
+  rc->tslots = 0;
+  rc->kmax = 0;
+  rc->above = 0;
+  st->path = PATH_SAMPLED;
+  st->passes = 0;
+  st->kmax = 0;
+}
+
+// Writes the keys k_tau selects from: all S sample keys and their 11-bit
+// histogram (lists = 0), or each workgroup's t largest at g * t (lists = 1;
+// k_tau histograms those itself: the largest keys of every workgroup share
+// a few top bins, and global atomics on them would serialise).
+template <int DT>
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
+    const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
+    uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
+    uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr) {
+  __shared__ uint32_t h[SH_BINS];
+  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
+  const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  // the filter selects tau itself: start the row here (tau set there)
+  if (states && blockIdx.x == 0 && tid == 0) start_sampled_row(states + row, rctr + row, 0u);
+  uint32_t* gh = shist + (size_t)row * SH_BINS;
+  if (!lists) {
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
+    __syncthreads();
+  }
+  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
+  uint32_t key = 0;
+  if (j < S) {
+    const Feistel f(seed, row, half_bits);
+    uint64_t x = f.apply(j);
+    while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
+    const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+    key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+    if (!lists) {
+      skeys[(size_t)row * SP + j] = key;
+      atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
+    }
+  }
+  if (!lists) {
+    __syncthreads();
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
+      if (h[i]) atomicAdd(&gh[i], h[i]);
+    return;
+  }
+  // this workgroup's t largest keys, zero-padded
+  const uint32_t c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
+  if (tid < t) skeys[(size_t)row * SP + blockIdx.x * t + tid] = tid < c ? s_out[tid] : 0u;
+}
+
+// ======================================================================
+// Threshold (Prof-K section 3, stage 2): tau = the t-th largest sampled key,
+// found by a workgroup radix select instead of a sort.  Also starts the row.
+// ======================================================================
+struct KeySrc {
+  const uint32_t* p;
+  __device__ uint64_t operator()(uint32_t i) const { return p[i]; }
+};
+
+constexpr uint32_t SEL_THREADS = 1024;
+constexpr uint32_t CAND_CAP = 8192;   // LDS candidates (64 KB)
+
+// One workgroup per row.  The sample keys are loaded into registers first
+// (TAU_VEC 16-byte words per thread), so their loads overlap the histogram:
+// the row's global one (built by the sampler), or for few keys one built
+// here.  One wave finds the bin holding rank t; the keys of that bin go
+// from registers to LDS (one slot reservation per wave), and the select
+// finishes there.  Longer key lists take a streaming pass instead.
+// Sample-key rows are padded to a multiple of 4 keys (SP = padded length).
+constexpr uint32_t TAU_VEC = 8;
+__global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
+                                                     uint32_t SP, uint32_t t, uint32_t KB,
+                                                     uint32_t* __restrict__ shist,
+                                                     uint32_t own_hist,
+                                                     RowState* __restrict__ states,
+                                                     RowCtr* __restrict__ rctr) {
+  static_assert(SH_BINS == 2048, "one wave searches 2048 bins");
+  __shared__ __align__(16) uint32_t s_hist[SH_BINS];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint64_t s_cand[CAND_CAP];
+  const uint32_t row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t sh = KB - SH_BITS;
+  const uint32_t* keys = skeys + (size_t)row * SP;
+  const u32x4* kv4 = reinterpret_cast<const u32x4*>(keys);
+  const uint32_t nv = (S + 3) / 4;
+  const bool regs = nv <= TAU_VEC * nt;   // every key fits the registers
+  u32x4 kv[TAU_VEC];
+#pragma unroll
+  for (uint32_t j = 0; j < TAU_VEC; ++j) {
+    const uint32_t v = j * nt + tid;
+    kv[j] = (regs && v < nv) ? kv4[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+  auto valid = [&](uint32_t j, int q) { return (j * nt + tid) * 4u + (uint32_t)q < S; };
+  if (tid == 0) s_misc[3] = 0;
+  if (own_hist) {   // few keys: histogram them here
+    for (uint32_t i = tid; i < SH_BINS; i += nt) s_hist[i] = 0;
+    __syncthreads();
+    if (regs) {
+#pragma unroll
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist_add(s_hist, kv[j][q] >> sh, valid(j, q));
+    } else {
+      for (uint32_t i = tid; i < S; i += nt) atomicAdd(&s_hist[keys[i] >> sh], 1u);
+    }
+  } else {
+    uint32_t* gh = shist + (size_t)row * SH_BINS;
+    for (uint32_t i = tid; i < SH_BINS; i += nt) {
+      s_hist[i] = gh[i];
+      gh[i] = 0;                      // ready for the next call
+    }
+  }
+  __syncthreads();
+  if (tid < 64) wave_find_bucket_2048(s_hist, t, s_misc);
+  __syncthreads();
+  const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
+  KeySrc src{keys};
+  SelectStart st0;
+  st0.prefix = (uint64_t)b << sh;
+  st0.nb = SH_BITS;
+  st0.need = t - acc;
+  st0.above = acc;
+  if (hb <= CAND_CAP) {
+    // the boundary bin's keys into LDS
+    if (regs) {
+      uint32_t mine = 0;
+#pragma unroll
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine += (valid(j, q) && (kv[j][q] >> sh) == b) ? 1u : 0u;
+      const uint32_t incl = wave_incl_sum(mine);
+      const uint32_t wtot = wave_bcast(incl, 63u);
+      uint32_t wbase = 0;
+      if ((tid & 63u) == 0 && wtot) wbase = atomicAdd(&s_misc[3], wtot);
+      uint32_t pos = wave_bcast(wbase, 0u) + incl - mine;
+#pragma unroll
+      for (uint32_t j = 0; j < TAU_VEC; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (valid(j, q) && (kv[j][q] >> sh) == b) {
+            if (pos < CAND_CAP) s_cand[pos] = kv[j][q];
+            ++pos;
+          }
+    } else {
+      for_batched_i<12, u32x4>(
+          nv, [&](uint32_t i) { return kv4[i]; },
+          [&](const u32x4& v, bool ok, uint32_t i) {
+            bool in[4];
+            bool any = false;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              in[q] = ok && (i * 4 + q) < S && (v[q] >> sh) == b;
+              any = any || in[q];
+            }
+            if (ballot(any) == 0) return;   // the usual case: no key of the bin
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lds_append(s_cand, &s_misc[3], CAND_CAP, v[q], in[q]);
+          });
+    }
+    __syncthreads();
+    st0.m = s_misc[3] < CAND_CAP ? s_misc[3] : CAND_CAP;
+    st0.in_lds = true;
+  }
+  uint32_t tau;
+  if (st0.in_lds && st0.m <= nt / 4) {
+    // a small bin: the wanted key is the one whose rank inside it (larger
+    // keys, then equal keys earlier in the list) is need - 1; four lanes
+    // share each key, each counting a quarter of the list
+    const uint32_t i = tid >> 2, q = tid & 3u;
+    const uint64_t mine = i < st0.m ? s_cand[i] : 0ull;
+    uint32_t r = 0;
+    for (uint32_t j = q; j < st0.m; j += 4) {
+      const uint64_t o = s_cand[j];
+      r += (o > mine || (o == mine && j < i)) ? 1u : 0u;
+    }
+    r += dpp_take<0xB1, 0xf>(r);
+    r += dpp_take<0x4E, 0xf>(r);
+    if (q == 0 && i < st0.m && r == st0.need - 1) s_misc[5] = (uint32_t)mine;
+    __syncthreads();
+    tau = s_misc[5];
+  } else {
+    __syncthreads();   // every thread has read the bin
+    tau = (uint32_t)block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP).thr;
+  }
+  if (tid == 0) start_sampled_row(states + row, rctr + row, tau);
+}
