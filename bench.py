@@ -9,11 +9,11 @@ resident in HBM.  Three input buffers rotate so that no call finds its input
 in the 256 MB last-level cache.  Prints one JSON line.
 
 Extra modes (measurement plumbing, not part of the timed line):
-    --pmc-run                 a short run for rocprofv3 --pmc: a plain copy of
-                              a known size, then a few steps
+    --pmc-run                 a short run for rocprofv3 --pmc: two calibration
+                              kernels of known traffic, then a few steps
     --pmc-summary A B         read the rocprofv3 counter CSVs of the FETCH_SIZE
-                              run (A) and the WRITE_SIZE run (B) and print the
-                              traffic summary that belongs in profiles/
+                              run (A) and the WRITE_SIZE run (B) of --workload
+                              and print the traffic summary for profiles/
     --calibrate W1,W2,...     measure the whole call over the tuned policy's
                               grid of sample sizes on each workload and fit
                               the cost ratio tau_B / tau_A of Eq. 13
@@ -37,9 +37,13 @@ METRIC = "top-k Gelem/s and HBM GB/s (% of peak), N=2^28 fp32 k=64, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "top_selection_sample_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "topk_part_filter.hpp")   # the filter kernel's source
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_k_filter_c3_k64.txt")
-TRAFFIC_WORKLOAD = "c3k64"   # the workload those counters were taken on
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
+
+
+def traffic_file(workload: str) -> str:
+    """The committed rocprofv3 counter summary of one workload."""
+    return os.path.join(PROFILES, f"pmc_{workload}.txt")
 
 WORKLOADS = {
     # name: (config, k, description)
@@ -107,13 +111,14 @@ def algorithmic_bytes(rows, n, k, es, plan, R_mean):
 
 
 def read_traffic(workload):
-    """Traffic measured by rocprofv3 counters for the filter kernel, if the
-    committed summary was taken on this workload and the current kernel
-    source."""
-    if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
+    """HBM bytes per launch of the filter kernel measured by rocprofv3
+    counters, if the committed summary of this workload was taken on the
+    current kernel source (else None)."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line:
             kk, vv = line.split(":", 1)
             fields[kk.strip()] = vv.strip()
@@ -446,19 +451,28 @@ def run_bench(args):
 
 
 def pmc_run(args):
-    """Short program for rocprofv3 --pmc: one plain copy of COPY_BYTES (the
-    calibration kernel) then a few steps of the workload."""
+    """Short program for rocprofv3 --pmc.  Two calibration kernels of known
+    traffic come first: k_stream_read reads COPY_BYTES with the filter's own
+    load pattern (16-byte nontemporal loads; FETCH_SIZE calibration), and a
+    plain copy writes COPY_BYTES (WRITE_SIZE calibration).  Then a few
+    steps of the workload."""
     import torch
     import top_selection_sample_amd as tss
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    tss.stream_read(src, sink)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst
     x, dt, k, desc, meta = load_inputs(args.workload)
     xd = to_device(x, dt)
+    ov = torch.empty((x.shape[0], k), dtype=xd.dtype, device="cuda")
+    oi = torch.empty((x.shape[0], k), dtype=torch.int64, device="cuda")
     for _ in range(max(args.steps, 1)):
-        tss.topk(xd, k)
+        tss.topk(xd, k, out=(ov, oi))
     torch.cuda.synchronize()
     print("pmc run done", flush=True)
 
@@ -477,53 +491,83 @@ def _rows_of(path_glob, counter):
     return out
 
 
+def _short(name: str) -> str:
+    """A kernel's name without its return type and argument list
+    (tk::k_filter<1>)."""
+    nm = name.split("(")[0].strip()
+    return nm[5:] if nm.startswith("void ") else nm
+
+
 def pmc_summary(args):
+    """The traffic summary of one workload from the FETCH_SIZE run (A) and
+    the WRITE_SIZE run (B): each counter (KiB per dispatch) scaled by what
+    it reads for its calibration kernel, per kernel of the pipeline (median
+    over its dispatches)."""
     fetch_dir, write_dir = args.pmc_summary
     fe = _rows_of(os.path.join(fetch_dir, "**", "*counter_collection.csv"), "FETCH_SIZE")
     wr = _rows_of(os.path.join(write_dir, "**", "*counter_collection.csv"), "WRITE_SIZE")
+    kib = 1024.0
 
-    def first_copy(rows):
+    def first(rows, pred):
         for _, name, v in rows:
-            if "copy" in name.lower():
-                return v, name
+            if pred(name):
+                return v, _short(name)
         return None, None
 
-    def filt(rows):
-        vals = sorted(v for _, name, v in rows if "k_filter" in name)
-        return vals[len(vals) // 2] if vals else None
-
-    kib = 1024.0
-    # The calibration copy is the program's first copy kernel: it reads and
-    # writes COPY_BYTES, and FETCH_SIZE / WRITE_SIZE are KiB per dispatch.
-    cf, cf_name = first_copy(fe)
-    cw, cw_name = first_copy(wr)
+    cf, cf_name = first(fe, lambda nm: "k_stream_read" in nm)
+    cw, cw_name = first(wr, lambda nm: "copy" in nm.lower())
     scale_f = COPY_BYTES / (cf * kib) if cf else None
     scale_w = COPY_BYTES / (cw * kib) if cw else None
-    ff, fw = filt(fe), filt(wr)
+    # the pipeline's kernels: everything after the calibration dispatches
+    # (and the input upload's own copies) whose name is one of the library's
+    per = {}
+    for rows, key in ((fe, "f"), (wr, "w")):
+        for _, name, v in rows:
+            nm = _short(name)
+            if not nm.startswith("tk::") or "k_stream_read" in nm:
+                continue
+            per.setdefault(nm, {"f": [], "w": []})[key].append(v)
+    cfg, k, desc = WORKLOADS[args.workload]
     lines = [
-        "rocprofv3 counter summary: k_filter on workload c3k64 (1 row x 2^28 fp32, k=64)",
+        f"rocprofv3 counter summary: workload {args.workload} ({desc})",
         "",
         "Commands (from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = output dirs):",
-        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python3 REPO/bench.py --pmc-run --steps 3",
-        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python3 REPO/bench.py --pmc-run --steps 3",
-        "  python3 REPO/bench.py --pmc-summary OUT_F OUT_W",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python3 REPO/bench.py --pmc-run --workload {args.workload} --steps 3",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python3 REPO/bench.py --pmc-run --workload {args.workload} --steps 3",
+        f"  python3 REPO/bench.py --pmc-summary OUT_F OUT_W --workload {args.workload}",
+        "",
+        "FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it",
+        "reads for a kernel of known traffic in the same run: k_stream_read",
+        f"(reads {COPY_BYTES} bytes with the filter's load pattern) and a plain copy",
+        f"(writes {COPY_BYTES} bytes).",
         "",
         f"kernel_source_sha256_16: {kernel_source_hash()}",
-        f"calibration_kernel: {cf_name}",
-        f"copy_bytes_known: {COPY_BYTES}",
-        f"fetch_kib_copy_kernel: {cf}",
-        f"write_kib_copy_kernel: {cw}",
+        f"calibration_fetch_kernel: {cf_name}",
+        f"calibration_write_kernel: {cw_name}",
+        f"fetch_kib_calibration: {cf}",
+        f"write_kib_calibration: {cw}",
         f"scale_fetch: {scale_f}",
         f"scale_write: {scale_w}",
-        f"k_filter_fetch_kib_median: {ff}",
-        f"k_filter_write_kib_median: {fw}",
+        "",
+        "| kernel | dispatches | FETCH KiB (median) | WRITE KiB (median) | HBM read bytes | HBM write bytes |",
+        "|---|---|---|---|---|---|",
     ]
-    if ff is not None and fw is not None and scale_f and scale_w:
-        fb, wb = ff * kib * scale_f, fw * kib * scale_w
-        lines.append(f"k_filter_fetch_bytes_scaled: {fb:.0f}")
-        lines.append(f"k_filter_write_bytes_scaled: {wb:.0f}")
-        lines.append(f"hbm_bytes_per_launch: {fb + wb:.0f}")
-        lines.append(f"algorithmic_bytes_per_launch_approx: {2 ** 28 * 4 + 16384 * 8}")
+    filt = None
+    for nm in sorted(per):
+        fv, wv = sorted(per[nm]["f"]), sorted(per[nm]["w"])
+        fm = fv[len(fv) // 2] if fv else None
+        wm = wv[len(wv) // 2] if wv else None
+        fb = fm * kib * scale_f if fm is not None and scale_f else None
+        wb = wm * kib * scale_w if wm is not None and scale_w else None
+        lines.append(f"| {nm} | {len(fv)} | {fm} | {wm} | "
+                     f"{'' if fb is None else f'{fb:.0f}'} | {'' if wb is None else f'{wb:.0f}'} |")
+        if "k_filter" in nm and fb is not None and wb is not None:
+            filt = (fb, wb)
+    lines.append("")
+    if filt:
+        lines.append(f"k_filter_fetch_bytes_scaled: {filt[0]:.0f}")
+        lines.append(f"k_filter_write_bytes_scaled: {filt[1]:.0f}")
+        lines.append(f"hbm_bytes_per_launch: {filt[0] + filt[1]:.0f}")
     print("\n".join(lines))
 
 

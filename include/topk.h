@@ -27,20 +27,33 @@
  *     pattern of the selected input element.  `out_indices`: [rows, k] int64,
  *     row-local indices.
  *   - `workspace`: device memory of at least topk_workspace_size() bytes,
- *     256-byte aligned.  The library remembers (host side) the layout of the
- *     last call on each workspace address: a call with the same layout reuses
- *     the workspace as the previous call left it (clean), and any other call,
- *     or the first call on an address not prepared by topk_workspace_init,
- *     zero-fills it first.  One workspace must not be used by two calls that
- *     may run at the same time, and its contents must not be modified
- *     between calls except through topk_workspace_init.
+ *     256-byte aligned, owned by the caller.  It needs no initialisation and
+ *     may hold anything between calls (another use of the same memory, a
+ *     fresh allocation): every call writes each region before it reads it,
+ *     resetting its per-call counters in its first kernel.  The one region
+ *     kept from call to call is a sample histogram that a call leaves zero;
+ *     the next call uses it only if the header's stamp names that call's
+ *     layout, and otherwise rebuilds it (a little slower, same result).  One
+ *     workspace must not be used by two calls that may run at the same time.
  *   - `stream`: a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously on it; no host synchronisation happens
  *     inside topk/topk_ex.
  *   - Errors: argument problems return a negative status before anything is
  *     enqueued; a HIP launch failure returns TOPK_EHIP.  No exception crosses
- *     the ABI.  After TOPK_EHIP the workspace contents are undefined: call
- *     topk_workspace_init again.
+ *     the ABI.
+ *   - Exact route and co-residency.  The exact selection of the rows that
+ *     fail the sampled check (or of every row, on the exact route) runs in one
+ *     launch of one workgroup per compute unit whose phases wait for one
+ *     another at grid barriers; that assumes all of its workgroups are
+ *     resident at once.  When they are not (other work holding compute units
+ *     for more than about 0.2 s, for instance two calls on different streams
+ *     that both take the exact route at the same moment), every wait gives up
+ *     after a bounded number of polls, the workgroups leave the shared phases,
+ *     and the last one to finish selects each of those rows again on its own,
+ *     exactly.  The answer is then still the exact top-k, the call takes far
+ *     longer, and topk_read_stats reports it (flags bit 0).  For full speed,
+ *     give calls that may run concurrently their own compute units or run
+ *     them one after the other.
  */
 #ifndef TOPK_MI355X_H
 #define TOPK_MI355X_H
@@ -120,7 +133,24 @@ typedef struct {
                          in rank order, and the remaining slots get index -1 and
                          the dtype's lowest value (-inf, or INT32_MIN).  Rows with
                          k or more survivors are exact as before. */
+  uint32_t force_tau_key; /* with use_force_tau != 0: the threshold of every row, as
+                         an order-preserving key (int32: bits ^ 0x80000000; float:
+                         negatives all bits flipped, positives the sign bit set,
+                         -0 as +0, every NaN 0xFFFFFFFF; bf16 the same on 16 bits).
+                         The sampler is skipped and the sampled route runs with this
+                         tau (Prof-K section 3, stages 3-4: filter, detection and the
+                         fallback); the result is still the exact top-k.  Meant for
+                         driving detection from the host, e.g. the largest key
+                         forces R < k (section 4, "Failure Modes and Budget
+                         Allocation").  Not allowed with force_path = EXACT. */
+  int32_t use_force_tau;
+  uint32_t test_flags;  /* test aid, 0 in normal use: TOPK_TEST_BARRIER_GIVEUP makes
+                         every grid-barrier wait of the exact route give up at once,
+                         as when workgroups are not co-resident.  Other bits: EINVAL. */
+  int32_t reserved2;
 } topk_params;
+
+enum { TOPK_TEST_BARRIER_GIVEUP = 1 };
 
 /* Resolved plan of one call shape (host arithmetic only; no GPU needed). */
 typedef struct {
@@ -147,11 +177,20 @@ typedef struct {
   uint32_t path;      /* 0 sampled accepted, 1 sampled then exact fallback, 2 exact only,
                          3 sampled with fewer than k survivors kept (recall < 1) */
   uint32_t passes;    /* histogram passes of the exact select */
-  uint32_t flags;     /* bit 0: an exact-route grid barrier gave up waiting (the
-                         result of that call is not trustworthy; never seen in
-                         normal operation) */
+  uint32_t flags;     /* of the whole call: bit 0 = an exact-route grid-barrier wait
+                         gave up (workgroups not co-resident; the rows of the exact
+                         route were then selected again by one workgroup: the
+                         result is exact, the call was slow); bit 1 = internal
+                         limit of the large-k sort exceeded (never expected) */
   uint32_t ties;      /* of r_sampled, the survivors equal to tau; they join the
                          candidates only when fewer than k lie strictly above */
+  uint32_t tau_route; /* diagnostic: how tau was selected.  Low 3 bits: 0 none (exact
+                         route), 1 per-workgroup top-t lists in the filter's prologue,
+                         2 top-t lists in the threshold kernel, 3 every sample key in
+                         registers, 4 every sample key streamed, 5 given by the caller
+                         (use_force_tau).  Bit 3: the sample bin holding rank t had more
+                         keys than LDS holds (streamed radix select); bit 4: that bin was
+                         radix-selected in LDS. */
 } topk_row_stats;
 
 /* Fill *p with the defaults above.  Returns TOPK_OK, or TOPK_EINVAL for NULL. */
@@ -168,7 +207,8 @@ int topk_workspace_size(int64_t n, int64_t rows, int64_t k, int dtype, const top
                         size_t* bytes);
 
 /* Zero-fill `bytes` of workspace on `stream` with a fill kernel (no memset
- * node, so it can sit inside a captured graph). */
+ * node, so it can sit inside a captured graph).  Optional: a workspace needs
+ * no initialisation. */
 int topk_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Exact top-k with default parameters.  See the conventions above. */

@@ -14,9 +14,10 @@ Contents
                       row, then one selection over the chunks' own top-k),
                       for the CPU timing.
 * ``keys``            order-preserving unsigned keys, written with numpy.
-* ``rank_by_counting``  O(n^2) rank of every element: strictly larger
-                      anywhere, or equal at a lower index (GPU.js Learn
-                      "Rank by Counting", Goal and Hint 2).
+* ``rank_by_counting``  O(n^2) rank of every element: how many elements
+                      precede it (a bigger key, or the same key at a
+                      smaller index; GPU.js Learn "Rank by Counting", Goal
+                      and Hint 2).
 * ``bisection_cutoff``  counting bisection on the value axis (GPU.js Learn
                       "Find the Cutoff Instead", Requirements and Hint 3).
 * ``outranking``      number of elements that outrank a given (key, index).
@@ -168,9 +169,11 @@ def topk_chunked(x: np.ndarray, k: int, threads: int, dtype: str | None = None):
 
 # ---------------------------------------------------------------- definitions
 def rank_by_counting(x: np.ndarray, dtype: str | None = None) -> np.ndarray:
-    """Rank of every element of a 1-D row: the number of elements that are
-    strictly larger anywhere, or equal at a lower index.  O(n^2) memory and
-    time: tiny rows only."""
+    """Rank of every element of a 1-D row, as GPU.js Learn "Rank by Counting"
+    (section Goal) defines the output position: count the elements that come
+    before it, i.e. every element with a bigger key, plus every element with
+    the same key and a smaller index.  O(n^2) memory and time: tiny rows
+    only."""
     k = keys(x, dtype).astype(np.int64)
     n = k.size
     assert n <= 8192, "brute force is for tiny rows"

@@ -22,3 +22,39 @@ def test_multi_rank_launch_is_refused():
     r = _run([], env=env)
     assert r.returncode == 2 and "one GPU" in r.stderr
 
+
+
+def test_pmc_summary_scales_each_kernel(tmp_path):
+    # synthetic rocprofv3 counter CSVs: the calibration kernels read / write
+    # 2^30 bytes and report half / all of it; the pipeline's kernels report
+    # their own KiB.  The summary scales each by its calibration.
+    import csv
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    fetch = [(1, "tk::k_stream_read(uint4 const*, unsigned long, unsigned int*)", 524288.0),
+             (2, "__amd_rocclr_copyBuffer", 524288.0),
+             (3, "void tk::k_sample<1>(...)", 100.0), (4, "void tk::k_filter<1>(...)", 524300.0),
+             (5, "void tk::k_sample<1>(...)", 102.0), (6, "void tk::k_filter<1>(...)", 524310.0),
+             (7, "void tk::k_filter<1>(...)", 524320.0)]
+    write = [(1, "tk::k_stream_read(uint4 const*, unsigned long, unsigned int*)", 0.0),
+             (2, "__amd_rocclr_copyBuffer", 1048576.0),
+             (3, "void tk::k_sample<1>(...)", 8.0), (4, "void tk::k_filter<1>(...)", 90.0),
+             (6, "void tk::k_filter<1>(...)", 92.0), (7, "void tk::k_filter<1>(...)", 94.0)]
+    for name, rows, counter in (("f", fetch, "FETCH_SIZE"), ("w", write, "WRITE_SIZE")):
+        d = tmp_path / name / "host"
+        d.mkdir(parents=True)
+        with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+            wr = csv.DictWriter(fh, fieldnames=fields)
+            wr.writeheader()
+            for did, kn, v in rows:
+                wr.writerow({"Dispatch_Id": did, "Kernel_Name": kn, "Counter_Name": counter,
+                             "Counter_Value": v})
+    r = _run(["--pmc-summary", str(tmp_path / "f"), str(tmp_path / "w"), "--workload", "c3k64"])
+    assert r.returncode == 0, r.stderr
+    out = dict(line.split(":", 1) for line in r.stdout.splitlines() if ": " in line and "|" not in line)
+    assert float(out["scale_fetch"]) == 2.0 and float(out["scale_write"]) == 1.0
+    assert "tk::k_stream_read" in out["calibration_fetch_kernel"]
+    # filter medians: 524310 KiB fetched (x2), 92 KiB written (x1)
+    assert int(out["k_filter_fetch_bytes_scaled"]) == 524310 * 1024 * 2
+    assert int(out["k_filter_write_bytes_scaled"]) == 92 * 1024
+    assert int(out["hbm_bytes_per_launch"]) == 524310 * 2048 + 92 * 1024
+    assert "| tk::k_sample<1> | 2 |" in r.stdout

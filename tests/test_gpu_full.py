@@ -66,3 +66,47 @@ def test_config5_batchtopk_sparse_activation():
     got = flat[idx].view(torch.int16).cpu().numpy().view(np.uint16)
     assert got.tobytes() == ov.reshape(-1).tobytes()
     assert int(m.reshape(-1)[idx].sum()) == K
+
+
+def _route(row, dt, tau_key, k, cap):
+    # the detection rule: G above tau, E equal; accepted when G holds k within
+    # the capacity, or G < k <= G + E <= cap
+    kk = oracle.keys(row, dt).astype(np.int64)
+    G, E = int((kk > tau_key).sum()), int((kk == tau_key).sum())
+    if G > cap:
+        return 1, E
+    if G >= k:
+        return 0, E
+    return (0 if k <= G + E <= cap else 1), E
+
+
+@pytest.mark.parametrize("name", ["c3k16", "c3k64", "c3k2048", "c4v1", "c4v2", "c4v3", "c5"])
+def test_full_size_threshold_and_route_seeded(name):
+    """At full size, in the benchmark's launch configuration but with a fixed
+    sampler seed: every row's tau key, survivor count R, tie count and route
+    equal what the oracle's sampler and the detection rule predict, and the
+    answer is exact."""
+    import top_selection_sample_amd as tss
+    cfg = {"c3k16": ("c3", 16), "c3k64": ("c3", 64), "c3k2048": ("c3", 2048), "c4v1": ("c4v1", 64),
+           "c4v2": ("c4v2", 64), "c4v3": ("c4v3", 64), "c5": ("c5", 131072)}[name]
+    x, dt, _, _ = workloads.config(cfg[0])
+    k = cfg[1]
+    if cfg[0] == "c5":
+        x = x.reshape(1, -1)
+    rows, n = x.shape
+    seed = 4242
+    p = tss.default_params(seed=seed, use_seed=1)
+    pl = tss.plan(n, rows, k, dt, params=p)
+    assert pl["path"] == 0
+    say(f"full-size seeded route {name}: rows={rows} n={n} k={k} S={pl['S']} t={pl['t']} cap={pl['cap']}")
+    gv, gi = run_gpu(x, k, dt, params=p)
+    assert_same(gv, gi, x, k, dt, f"{name} seeded")
+    st = tss.read_stats(rows)
+    for r in range(rows):
+        tk, R = oracle.tau(x[r], seed, r, pl["S"], pl["t"], dt)
+        path, E = _route(x[r], dt, tk, k, pl["cap"])
+        assert st[r]["tau_key"] == tk, (r, hex(st[r]["tau_key"]), hex(tk))
+        assert st[r]["path"] == path, (r, st[r], path)
+        if path == 0:
+            assert st[r]["r_sampled"] == R and st[r]["ties"] == E, (r, st[r], R, E)
+        assert st[r]["flags"] == 0

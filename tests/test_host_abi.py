@@ -37,8 +37,10 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_params_layout(lib):
-    assert ctypes.sizeof(lib.Params) == 112
+    assert ctypes.sizeof(lib.Params) == 128
+    assert ctypes.sizeof(lib.RowStats) == 28
     p = lib.default_params()
+    assert (p.use_force_tau, p.force_tau_key, p.test_flags) == (0, 0, 0)
     assert p.recall == 1.0
     assert (p.eps, p.s_min, p.s_max, p.cost_ratio) == (1e-3, 32768, 131072, 1.0)
     assert p.policy == lib.POLICY_TUNED and p.force_path == 0
@@ -151,6 +153,17 @@ def test_shape_errors(lib, args, status):
                                 dict(recall=-0.5), dict(recall=float("nan"))])
 def test_param_errors(lib, kw):
     assert _plan(lib, 2 ** 20, 1, 64, 1, **kw)[0] == -1
+
+
+def test_forced_threshold_plans_the_sampled_route(lib):
+    # a caller-given threshold runs the filter route whatever the shape (the
+    # sampler is skipped), and cannot be combined with the forced exact route
+    for n, rows, k in [(4096, 1, 10), (2 ** 28, 1, 64), (5000, 300, 17)]:
+        rc, info = _plan(lib, n, rows, k, 1, use_force_tau=1, force_tau_key=0x80000000)
+        assert rc == 0 and info.path == 0 and k <= info.cap <= n
+    assert _plan(lib, 2 ** 20, 1, 64, 1, use_force_tau=1, force_path=2)[0] == -1
+    assert _plan(lib, 2 ** 20, 1, 64, 1, test_flags=lib.TEST_BARRIER_GIVEUP)[0] == 0
+    assert _plan(lib, 2 ** 20, 1, 64, 1, test_flags=2)[0] == -1
 
 
 @pytest.mark.parametrize("n,k,recall", [(2 ** 28, 64, 0.95), (2 ** 24, 1000, 0.9),

@@ -127,3 +127,95 @@ def test_five_workload_shapes():
         assert st.hypergeom.sf(te - 1, N, k - 1, S) <= half
         assert te == 1 or st.hypergeom.sf(te - 2, N, k - 1, S) > half
         assert st.hypergeom.cdf(te - 1, N, Me, S) <= half < st.hypergeom.cdf(te - 1, N, Me - 1, S)
+
+
+# ------------------------------------------------------------ the tuned policy
+def _scipy_tail(N, k, S, eps):
+    """(t, M) of the exact-tail reading computed with scipy's hypergeometric
+    law only: the least t with P(H(N, k-1, S) >= t) <= eps/2 and the least
+    M >= k with P(H(N, M, S) <= t-1) <= eps/2, both by bisection (the first
+    tail falls as t grows, the second as M grows)."""
+    H = pytest.importorskip("scipy.stats").hypergeom
+    half = eps / 2
+    lo, hi = 1, S
+    if k > 1:
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if H.sf(mid - 1, N, k - 1, S) <= half:
+                hi = mid
+            else:
+                lo = mid + 1
+    t = lo
+    if H.cdf(t - 1, N, N, S) > half:
+        return t, N
+    lo, hi = k, N
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if H.cdf(t - 1, N, mid, S) <= half:
+            hi = mid
+        else:
+            lo = mid + 1
+    return t, lo
+
+
+@pytest.mark.parametrize("N,k,eps,ratio", [(2 ** 28, 64, 1e-3, 0.13), (2 ** 28, 16, 1e-3, 0.13),
+                                           (2 ** 28, 2048, 1e-3, 0.13),
+                                           (2 ** 20, 64, 1e-3 / 128, 0.13),
+                                           (2 ** 28, 131072, 1e-3, 0.01),
+                                           (2 ** 22, 100, 1e-3, 0.13), (2 ** 24, 1, 1e-3, 0.13)])
+def test_tuned_policy_brute_force(N, k, eps, ratio):
+    """Eq. 13's overhead S + ratio * M(S) * log2(k) (section 4, "Optimal
+    Sample Size") minimised by brute force over the quarter-octave grid
+    1024 * 2^(j/4) <= min(2^17, N/8), with M(S) and t(S) from scipy's
+    hypergeometric law (Lemma 1), independently of the oracle's own tail
+    arithmetic; the first grid point wins a tie."""
+    s_hi = min(131072, N // 8)
+    best, j, prev = None, 0, None
+    while True:
+        S = int(round(1024 * 2 ** (j / 4)))
+        j += 1
+        if S > s_hi:
+            break
+        if S == prev:
+            continue
+        prev = S
+        t, M = _scipy_tail(N, k, S, eps)
+        cost = S + ratio * M * math.log2(k)
+        if best is None or cost < best[0]:
+            best = (cost, S, t, M)
+    got = P.tuned(N, k, eps, s_lo=1024, s_hi=s_hi, ratio=ratio)
+    assert (got["S"], got["t"], got["M"]) == best[1:]
+
+
+def test_tuned_optimum_approaches_theorem5():
+    """Theorem 5 (Eq. 14) gives the minimiser of Eq. 13 with Eq. 12's M.  In
+    the Gaussian regime (alpha * S >> 1, the BatchTopK shape) the exact-tail
+    M(S) follows Eq. 12 to first order, with a second-order excess that a
+    normal expansion of Lemma 1's tails fixes: t ~ alpha S + (z/2) sqrt(alpha S)
+    and the buffer's expected sample count mu = M S / N solves
+    mu = t - 1 + (z/2) sqrt(mu), so
+        (M - k) / (M_Eq12 - k) ~ 1 + (z / 4) / sqrt(alpha S).
+    The exact tails must show that excess, shrinking as 1/sqrt(alpha S); and
+    the minimiser of the exact-tail cost on a fine grid lies a little above
+    S*, approaching it as the cost ratio (and with it alpha * S) grows."""
+    N, k, eps = 2 ** 28, 131072, 1e-3
+    z = P.alg1(N, k)["z"]
+    prev = None
+    for S in (32768, 131072, 524288):
+        f = 1 - S / N
+        m12 = k + z * math.sqrt(k * (N - k) / S * f)
+        me = P.exact_tail(N, k, eps, s_min=S, s_max=S)["M"]
+        c = ((me - k) / (m12 - k) - 1) * math.sqrt(k / N * S)
+        assert abs(c - z / 4) < 0.15, (S, c, z / 4)
+        assert prev is None or abs(c - z / 4) < prev
+        prev = abs(c - z / 4)
+    prev = None
+    for ratio in (0.01, 0.05, 1.0):
+        s_star = (z * ratio * math.log2(k) / 2) ** (2 / 3) * (k * (N - k)) ** (1 / 3)
+        grid = np.unique(np.round(s_star * np.exp(np.linspace(-0.7, 0.7, 57))).astype(int))
+        cost = [S + ratio * P.exact_tail(N, k, eps, s_min=int(S), s_max=int(S))["M"] * math.log2(k)
+                for S in grid]
+        q = grid[int(np.argmin(cost))] / s_star
+        assert 1.0 < q < 1.5, (ratio, q)
+        assert prev is None or q < prev
+        prev = q

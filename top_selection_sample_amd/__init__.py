@@ -17,15 +17,19 @@ import torch
 
 from . import _lib
 from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED,
-                   ROUTE_EXACT, ROUTE_FALLBACK, ROUTE_PARTIAL, ROUTE_SAMPLED, Params,
-                   TopkError, default_params)
+                   ROUTE_EXACT, ROUTE_FALLBACK, ROUTE_PARTIAL, ROUTE_SAMPLED, TAU_BIN_RADIX,
+                   TAU_BIN_STREAMED, TAU_FILTER_LISTS, TAU_FORCED, TAU_KTAU_LISTS, TAU_KTAU_REGS,
+                   TAU_KTAU_STREAM, TAU_NONE, TEST_BARRIER_GIVEUP, Params, TopkError,
+                   default_params)
 
 __all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "scatter", "batchtopk",
            "workspace_size", "read_stats",
            "Workspace", "Params",
            "default_params", "TopkError", "PATH_AUTO", "PATH_FILTER", "PATH_EXACT",
            "ROUTE_SAMPLED", "ROUTE_FALLBACK", "ROUTE_EXACT", "ROUTE_PARTIAL",
-           "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code"]
+           "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code",
+           "TAU_NONE", "TAU_FILTER_LISTS", "TAU_KTAU_LISTS", "TAU_KTAU_REGS", "TAU_KTAU_STREAM",
+           "TAU_FORCED", "TAU_BIN_STREAMED", "TAU_BIN_RADIX", "TEST_BARRIER_GIVEUP"]
 
 _TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}
 _NAME_CODES = _lib.DTYPE_CODES
@@ -70,11 +74,13 @@ def workspace_size(n: int, rows: int, k: int, dtype, params: Params | None = Non
 
 class Workspace:
     """Device scratch for topk calls on one device; grows on demand.  A
-    workspace serves one stream at a time.  The library allocates nothing and
-    records no memset, so a call can be captured in a HIP graph; the graph
-    keeps the workspace's address, so give captured calls a workspace of
-    their own, sized by an eager call of the same shape before the capture
-    (a later, larger call would reallocate it under the graph)."""
+    workspace serves one stream at a time.  It needs no initialisation (every
+    call writes what it reads), so a new buffer is used as torch hands it
+    out.  The library allocates nothing and records no memset, so a call can
+    be captured in a HIP graph; the graph keeps the workspace's address, so
+    give captured calls a workspace of their own, sized by an eager call of
+    the same shape before the capture (a later, larger call would reallocate
+    it under the graph)."""
 
     def __init__(self, device=None):
         self.device = _norm_device(device)
@@ -83,8 +89,6 @@ class Workspace:
     def get(self, nbytes: int, stream) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
-            _lib.check(_lib.lib.topk_workspace_init(self.buf.data_ptr(), self.buf.numel(), stream),
-                       "topk_workspace_init")
         return self.buf
 
 
@@ -173,7 +177,7 @@ def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> li
         arr = (_lib.RowStats * rows)()
         _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
     return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes,
-             "flags": a.flags, "ties": a.ties} for a in arr]
+             "flags": a.flags, "ties": a.ties, "tau_route": a.tau_route} for a in arr]
 
 
 def profile_enable(on: bool = True) -> None:

@@ -19,6 +19,12 @@ PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
 # per-row route in read_stats: sampled accepted, sampled then exact fallback,
 # exact only, sampled with fewer than k survivors kept (recall < 1)
 ROUTE_SAMPLED, ROUTE_FALLBACK, ROUTE_EXACT, ROUTE_PARTIAL = 0, 1, 2, 3
+# how the threshold was selected (read_stats "tau_route"): the source in the
+# low 3 bits, plus flags for a boundary bin beyond LDS / radix-selected in LDS
+TAU_NONE, TAU_FILTER_LISTS, TAU_KTAU_LISTS, TAU_KTAU_REGS, TAU_KTAU_STREAM, TAU_FORCED = range(6)
+TAU_BIN_STREAMED, TAU_BIN_RADIX = 8, 16
+# topk_params.test_flags: every exact-route grid-barrier wait gives up at once
+TEST_BARRIER_GIVEUP = 1
 
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
@@ -34,7 +40,9 @@ class Params(ctypes.Structure):
                 ("use_seed", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
                 ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64),
-                ("tuned_ratio_large", ctypes.c_double), ("recall", ctypes.c_double)]
+                ("tuned_ratio_large", ctypes.c_double), ("recall", ctypes.c_double),
+                ("force_tau_key", ctypes.c_uint32), ("use_force_tau", ctypes.c_int32),
+                ("test_flags", ctypes.c_uint32), ("reserved2", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -52,7 +60,8 @@ class StageTimes(ctypes.Structure):
 class RowStats(ctypes.Structure):
     _fields_ = [("tau_key", ctypes.c_uint32), ("r_sampled", ctypes.c_uint32),
                 ("path", ctypes.c_uint32), ("passes", ctypes.c_uint32),
-                ("flags", ctypes.c_uint32), ("ties", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("ties", ctypes.c_uint32),
+                ("tau_route", ctypes.c_uint32)]
 
 
 def _load():

@@ -5,7 +5,6 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -60,27 +59,6 @@ void mark_stage(void*, int stage, int begin, hipStream_t s) {
   }
 }
 
-// ---- workspace layouts
-// Regions that must start at zero (sample histogram, exact-route histogram,
-// call record) sit at offsets that depend on the call shape.  Every completed
-// call leaves its own layout's zero regions clean, so a workspace can be
-// reused as is while the layout stays the same; when it changes, the
-// workspace is zero-filled again first.  The layout last used on each
-// workspace address is kept here (0 = freshly zero-filled).
-std::mutex g_ws_mu;
-std::map<uintptr_t, uint64_t> g_ws_layout;
-
-uint64_t layout_signature(const tk::Plan& p) {
-  uint64_t h = 0x9E3779B97F4A7C15ull;
-  const uint64_t parts[] = {p.total, p.off_states, p.off_call, p.off_flag, p.off_ghist,
-                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux, p.off_lk, p.off_rctr,
-                            (uint64_t)p.rows};
-  for (uint64_t v : parts) {
-    h ^= v + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
-  }
-  return h | 1ull;   // never 0
-}
-
 tk::ParamIn to_in(const topk_params* p) {
   tk::ParamIn in;
   if (!p) return in;
@@ -97,6 +75,7 @@ tk::ParamIn to_in(const topk_params* p) {
   in.tuned_s_min = p->tuned_s_min;
   in.tuned_ratio_large = p->tuned_ratio_large;
   in.recall = p->recall;
+  in.force_tau = p->use_force_tau != 0;
   return in;
 }
 
@@ -111,6 +90,8 @@ int check_params(const topk_params* p) {
   if (!(p->recall > 0.0 && p->recall <= 1.0)) return TOPK_EINVAL;
   if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
   if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
+  if (p->use_force_tau && p->force_path == TOPK_PATH_EXACT) return TOPK_EINVAL;
+  if (p->test_flags & ~(uint32_t)TOPK_TEST_BARRIER_GIVEUP) return TOPK_EINVAL;
   return TOPK_OK;
 }
 
@@ -157,7 +138,9 @@ int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* pa
 
 extern "C" {
 
-static_assert(sizeof(topk_params) == 112, "topk_params layout is part of the ABI");
+static_assert(sizeof(topk_params) == 128, "topk_params layout is part of the ABI");
+static_assert(sizeof(topk_row_stats) == 28, "topk_row_stats layout is part of the ABI");
+static_assert(sizeof(tk::WsHeader) == 256 && sizeof(tk::RowState) == 64, "workspace header and rows");
 
 int topk_default_params(topk_params* p) {
   if (!p) return TOPK_EINVAL;
@@ -214,10 +197,7 @@ int topk_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace && bytes) return TOPK_EINVAL;
   if (!bytes) return TOPK_OK;
   hipError_t e = tk::launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return TOPK_EHIP;
-  std::lock_guard<std::mutex> g(g_ws_mu);
-  g_ws_layout[reinterpret_cast<uintptr_t>(workspace)] = 0;
-  return TOPK_OK;
+  return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
 }
 
 int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
@@ -236,6 +216,9 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     char* ws = static_cast<char*>(workspace);
     tk::LaunchArgs a;
     a.plan = p;
+    a.hdr = reinterpret_cast<tk::WsHeader*>(ws);
+    a.tau_key = (params && params->use_force_tau) ? params->force_tau_key : 0u;
+    if (params && (params->test_flags & TOPK_TEST_BARRIER_GIVEUP)) a.spin_limit = 0;
     a.values = values;
     a.out_values = out_values;
     a.out_idx = out_indices;
@@ -253,16 +236,6 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     a.seed = (params && params->use_seed) ? params->seed
                                           : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));
     a.stream = static_cast<hipStream_t>(stream);
-    {
-      const uint64_t sig = layout_signature(p);
-      std::lock_guard<std::mutex> g(g_ws_mu);
-      auto it = g_ws_layout.find(reinterpret_cast<uintptr_t>(workspace));
-      const bool fresh = (it != g_ws_layout.end()) && (it->second == 0 || it->second == sig);
-      if (!fresh) {
-        if (tk::launch_zero_fill(workspace, p.total, a.stream) != hipSuccess) return TOPK_EHIP;
-      }
-      g_ws_layout[reinterpret_cast<uintptr_t>(workspace)] = sig;
-    }
     if (g_prof.load(std::memory_order_relaxed)) a.mark = mark_stage;
     hipError_t e = tk::launch_pipeline(a);
     return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
@@ -284,11 +257,13 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
   try {
     std::vector<tk::RowState> st((size_t)rows);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(st.data(), workspace, sizeof(tk::RowState) * (size_t)rows,
-                       hipMemcpyDeviceToHost, s) != hipSuccess)
+    // the row records follow the 256-byte header; the call record follows them
+    const size_t off_states = sizeof(tk::WsHeader);
+    if (hipMemcpyAsync(st.data(), static_cast<const char*>(workspace) + off_states,
+                       sizeof(tk::RowState) * (size_t)rows, hipMemcpyDeviceToHost, s) != hipSuccess)
       return TOPK_EHIP;
     tk::CallState cs;
-    const size_t off_call = ((size_t)rows * sizeof(tk::RowState) + 255) & ~(size_t)255;
+    const size_t off_call = (off_states + (size_t)rows * sizeof(tk::RowState) + 255) & ~(size_t)255;
     if (hipMemcpyAsync(&cs, static_cast<const char*>(workspace) + off_call, sizeof(cs),
                        hipMemcpyDeviceToHost, s) != hipSuccess)
       return TOPK_EHIP;
@@ -300,6 +275,7 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
       out[r].path = st[(size_t)r].path;
       out[r].passes = st[(size_t)r].passes;
       out[r].ties = st[(size_t)r].ties;
+      out[r].tau_route = st[(size_t)r].tau_route;
     }
     return TOPK_OK;
   } catch (...) {

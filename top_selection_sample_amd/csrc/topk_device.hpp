@@ -49,7 +49,7 @@ struct alignas(64) RowState {
   uint32_t thr_key;     // exact threshold: key >= thr_key, and on key ==
   uint32_t thr_bound;   //   thr_key only indices <= thr_bound
   uint32_t passes;      // exact select: histogram passes used
-  uint32_t pad1;
+  uint32_t tau_route;   // how the threshold was selected (TAU_* bits, a diagnostic)
   uint32_t kmax;        // largest candidate key written by a filter pass
 };
 static_assert(sizeof(RowState) == 64, "RowState is one 64-byte line");
@@ -70,17 +70,65 @@ struct alignas(128) RowCtr {
 };
 static_assert(sizeof(RowCtr) == 512, "four 128-byte lines");
 
-// Per-call record shared by all rows: the rows sent to the exact route.
-// Zero between calls (the exact-route kernel clears it when it is done).
+// How a row's threshold was selected (RowState::tau_route): the source in
+// the low bits, and whether the boundary bin of the sample histogram held
+// more keys than LDS (streamed radix select) or more than the rank-counting
+// limit (radix select in LDS).
+enum : uint32_t {
+  TAU_NONE = 0,          // no sampled threshold (exact route)
+  TAU_FILTER_LISTS = 1,  // per-workgroup top-t lists, selected in the filter's prologue
+  TAU_KTAU_LISTS = 2,    // per-workgroup top-t lists, selected by k_tau
+  TAU_KTAU_REGS = 3,     // every sample key, held in k_tau's registers
+  TAU_KTAU_STREAM = 4,   // every sample key, streamed by k_tau
+  TAU_FORCED = 5,        // given by the caller
+  TAU_BIN_STREAMED = 8,  // flag: the boundary bin exceeded LDS
+  TAU_BIN_RADIX = 16,    // flag: the boundary bin was radix-selected in LDS
+};
+
+// Per-call record shared by all rows: the rows sent to the exact route and
+// the exact route's grid-barrier words.  The first kernel of every call
+// writes it to zero; nothing is carried from one call to the next.
 struct alignas(64) CallState {
   uint32_t nflag;      // rows listed for the exact route
   uint32_t nactive;    // listed rows whose exact threshold is not resolved yet
-  uint32_t bar_count;  // grid barrier: arrivals in the current round (0 at rest)
+  uint32_t bar_count;  // grid barrier: arrivals in the current round
   uint32_t bar_gen;    // grid barrier: round number
-  uint32_t error;      // sticky: bit 0 = a grid barrier gave up waiting
-  uint32_t pad[11];
+  uint32_t error;      // bit 0: a grid-barrier wait gave up (the listed rows were
+                       //   then selected again by one workgroup); bit 1: the
+                       //   large-k sort's pending-range stack overflowed
+  uint32_t exit_count; // exact route: workgroups that have finished it
+  uint32_t pad[10];
 };
 static_assert(sizeof(CallState) == 64, "CallState is one 64-byte line");
+
+__device__ __forceinline__ void reset_call(CallState* cs) {
+  cs->nflag = 0;
+  cs->nactive = 0;
+  cs->bar_count = 0;
+  cs->bar_gen = 0;
+  cs->error = 0;
+  cs->exit_count = 0;
+}
+
+// Workspace header (its first 256 bytes).  `stamp` is the layout signature
+// of the call whose sample-histogram region is known to be all zero, or 0:
+// a call uses that region only when the stamp is its own signature, and
+// leaves it zero and stamped when it has used it.  Every other region is
+// written before it is read within a call, so a workspace needs no
+// initialisation and may hold anything between calls.
+struct alignas(256) WsHeader {
+  uint64_t stamp;
+  uint64_t pad[31];
+};
+static_assert(sizeof(WsHeader) == 256, "one 256-byte header");
+
+// A call that will not validate the stamp (any call whose layout differs,
+// and every call that does not build the sample histogram) clears it unless
+// it is already its own: the call may overwrite the region.  Racing readers
+// in the same kernel see either value, and neither equals `sig`.
+__device__ __forceinline__ void stamp_invalidate(WsHeader* h, uint64_t sig) {
+  if (h->stamp != sig) h->stamp = 0;
+}
 
 // ---------------------------------------------------------------- keys
 // int32: flip the sign bit.  float (32 or 16 bit): a negative value flips all

@@ -116,7 +116,7 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
-                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags);
+                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit);
   return hipGetLastError();
 }
 
@@ -136,13 +136,27 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (a.mark) a.mark(a.mark_ctx, stage, begin, s);
   };
 
+  uint32_t* lk_zero = bucket_sort ? a.lk : nullptr;   // large k: zeroed by the call's first kernel
   if (p.path == PLAN_EXACT_SMALL) {
     mark(STAGE_EXACT, 1);
     TK_DISPATCH(dt, k_exact_small, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
-                a.cbuf, cap, k, B, W, (uint32_t)(p.small_k ? 1 : 0), a.out_values, a.out_idx);
+                a.cbuf, cap, k, B, W, (uint32_t)(p.small_k ? 1 : 0), a.out_values, a.out_idx,
+                a.call, a.hdr, p.sig, lk_zero, rows);
     mark(STAGE_EXACT, 0);
   } else {
-    if (p.path == PLAN_SAMPLED) {
+    if (p.path == PLAN_SAMPLED && p.force_tau) {
+      // the caller's threshold: no sampler, no threshold select
+      mark(STAGE_SAMPLE, 1);
+      hipLaunchKernelGGL(k_force_tau, dim3(8, rows), dim3(SAMPLE_THREADS), 0, s, a.states, a.rctr,
+                         a.call, a.hdr, p.sig, a.tau_key, lk_zero, rows);
+      mark(STAGE_SAMPLE, 0);
+      const dim3 fg(p.filter_bpr, rows);
+      mark(STAGE_FILTER, 1);
+      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
+                  a.cbuf, a.aux, cap, B, 1u, a.skeys, 0u, (uint32_t)p.SP, (uint32_t)p.t,
+                  (WsHeader*)nullptr, p.sig);
+      mark(STAGE_FILTER, 0);
+    } else if (p.path == PLAN_SAMPLED) {
       const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
       const dim3 sg(sgx, rows);
       // small threshold ranks: select from per-workgroup top-t lists; for
@@ -153,24 +167,27 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
                   (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
-                  (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr);
+                  (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr, a.call, a.hdr, p.sig,
+                  lk_zero, rows);
       mark(STAGE_SAMPLE, 0);
       if (!in_filter) {
         mark(STAGE_TAU, 1);
         hipLaunchKernelGGL(k_tau, row_grid, dim3(SEL_THREADS), 0, s, a.skeys, ns, (uint32_t)p.SP,
                            (uint32_t)p.t, (uint32_t)p.KB, a.shist, (uint32_t)(lists ? 1 : 0),
-                           a.states, a.rctr);
+                           a.states, a.rctr, (const WsHeader*)a.hdr, p.sig);
         mark(STAGE_TAU, 0);
       }
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
+      // after k_tau (all keys) every row's sample histogram is zero again
+      WsHeader* validate = lists ? nullptr : a.hdr;
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
                   a.cbuf, a.aux, cap, B, 1u, a.skeys,
-                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t);
+                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, validate, p.sig);
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
-                         k);
+                         k, a.hdr, p.sig);
     }
     // Check, refine, and the exact route for every failed row: one launch.
     uint32_t mode = FIN_LISTED;

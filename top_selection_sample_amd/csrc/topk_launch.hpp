@@ -10,11 +10,13 @@ namespace tk {
 struct RowState;
 struct RowCtr;
 struct CallState;
+struct WsHeader;
 
 enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
 
 constexpr int64_t KSMALL = 4096;            // largest k sorted inside one workgroup
 constexpr int64_t LK_CAP_MAX = int64_t(1) << 21;  // large k: bucket sort up to this capacity
+constexpr uint32_t LK_HIST_BINS = 4096;     // large k: bucket-sort histogram bins per row
 constexpr size_t LK_WORDS_PER_ROW = 4096 + 4096 + 4100 + 2 * 2048;   // its workspace (u32)
 constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workgroup
 
@@ -28,7 +30,9 @@ struct Plan {
   uint32_t B = 8, W = 40, KB = 32, half_bits = 1;
   uint32_t filter_bpr = 1, hist_bpr = 1;
   double p_recall = 0, p_overflow = 0;
-  // workspace layout (byte offsets)
+  bool force_tau = false;   // the caller gives the threshold: no sampler
+  // workspace layout (byte offsets; the header is at 0)
+  uint64_t sig = 0;         // layout signature (never 0)
   size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lk = 0, off_rctr = 0, total = 0;
 };
 
@@ -39,10 +43,18 @@ enum : int { STAGE_SAMPLE = 0, STAGE_TAU = 1, STAGE_FILTER = 2, STAGE_REFINE = 3
 // Called before (begin = 1) and after (begin = 0) a stage's launches.
 typedef void (*StageMark)(void* ctx, int stage, int begin, hipStream_t s);
 
+// Test aid (topk_params.test_flags): every grid-barrier wait of the exact
+// route gives up at once.
+constexpr uint32_t TEST_BARRIER_GIVEUP = 1u;
+constexpr uint32_t SPIN_LIMIT_DEFAULT = 1u << 22;   // polls before a barrier wait gives up
+
 struct LaunchArgs {
   StageMark mark = nullptr;
   void* mark_ctx = nullptr;
   Plan plan;
+  WsHeader* hdr;
+  uint32_t tau_key = 0;          // plan.force_tau: the threshold key of every row
+  uint32_t spin_limit = SPIN_LIMIT_DEFAULT;
   const void* values;
   void* out_values;
   int64_t* out_idx;

@@ -242,9 +242,11 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
     RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf,
     uint32_t cap, uint32_t B, uint32_t track_kmax, const uint32_t* __restrict__ tlist,
-    uint32_t tlist_n, uint32_t tlist_stride, uint32_t t) {
+    uint32_t tlist_n, uint32_t tlist_stride, uint32_t t, WsHeader* validate, uint64_t sig) {
   using D = Dt<DT>;
   const uint32_t row = blockIdx.y;
+  // k_tau has left every row's sample histogram zero: stamp the workspace
+  if (validate && row == 0 && blockIdx.x == 0 && threadIdx.x == 0) validate->stamp = sig;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
   Thr thr;   // set below, once tau is known
@@ -563,7 +565,7 @@ __global__ void k_check(RowState* __restrict__ states, const RowCtr* __restrict_
   if (row >= rows) return;
   RowState* st = states + row;
   if (st->status != ST_FILTER) return;
-  const uint32_t G = st->count, E = rctr[row].ties;
+  const uint32_t G = rctr[row].above, E = rctr[row].ties;
   if (sampled_verdict(G, E, k, k_eff, cap) == V_FAIL) {
     st->r_sampled = G + E;
     st->ties = E;
@@ -572,8 +574,11 @@ __global__ void k_check(RowState* __restrict__ states, const RowCtr* __restrict_
   }
 }
 
+// The exact route's first kernel: the call's set-up (call record, stamp)
+// and every row listed.
 __global__ void k_setup_exact(RowState* __restrict__ states, CallState* __restrict__ cs,
-                              uint32_t* __restrict__ flagged, uint32_t rows, uint32_t k) {
+                              uint32_t* __restrict__ flagged, uint32_t rows, uint32_t k,
+                              WsHeader* hdr, uint64_t sig) {
   const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   RowState* st = states + row;
@@ -581,8 +586,11 @@ __global__ void k_setup_exact(RowState* __restrict__ states, CallState* __restri
   st->r_sampled = 0;
   st->tau_key = 0;
   st->ties = 0;
+  st->tau_route = TAU_NONE;
   flagged[row] = row;
   if (row == 0) {
+    reset_call(cs);
+    stamp_invalidate(hdr, sig);
     cs->nflag = rows;
     cs->nactive = rows;
   }

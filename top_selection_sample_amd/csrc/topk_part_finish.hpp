@@ -15,13 +15,17 @@
 // rows are refined (small k) or handed to the sort (large k).
 //
 // One launch does it all, the phases separated by grid-wide barriers.  The
-// grid is one workgroup per compute unit, so all workgroups are resident
-// together; every barrier wait is bounded, and a wait that gives up sets
-// CallState::error instead of hanging.  The same launch first refines the
-// rows whose sampled candidates passed the check, so when no row failed the
-// exact route costs nothing beyond that launch.
+// grid is one workgroup per compute unit, so all workgroups are normally
+// resident together.  Every barrier wait is bounded: a workgroup whose wait
+// gives up (not every workgroup is resident: other work holds compute units)
+// sets CallState::error and leaves the shared phases, which makes every
+// later barrier give up as well, so no phase ever runs on another
+// workgroup's unfinished data.  The last workgroup to finish (an exit
+// ticket) then selects every listed row again by itself, exactly: slow, but
+// the answer stays the exact top-k.  The same launch first refines the rows
+// whose sampled candidates passed the check, so when no row failed the exact
+// route costs nothing beyond that launch.
 // ======================================================================
-constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
 // Arrival: a release fence (this workgroup's writes reach memory), then one
 // relaxed increment of the arrival count; the last arrival acquires the
@@ -29,10 +33,12 @@ constexpr uint32_t SPIN_LIMIT = 1u << 22;
 // the generation with relaxed loads and acquires once it has moved: an
 // acquiring load per poll would invalidate the L2 at every iteration, which
 // measured about four times slower on MI355X (~22 us against ~6 us per
-// barrier over 256 workgroups).
-__device__ void grid_barrier(CallState* cs, uint32_t G) {
+// barrier over 256 workgroups).  Returns false (the same in every thread)
+// when the wait gave up after `spin_limit` polls.  s_flag: one LDS word.
+__device__ bool grid_barrier(CallState* cs, uint32_t G, uint32_t spin_limit, uint32_t* s_flag) {
   __syncthreads();
   if (threadIdx.x == 0) {
+    uint32_t ok = 1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t gen = __hip_atomic_load(&cs->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t arrived =
@@ -44,16 +50,22 @@ __device__ void grid_barrier(CallState* cs, uint32_t G) {
     } else {
       uint32_t spins = 0;
       while (__hip_atomic_load(&cs->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > SPIN_LIMIT) {
+        if (spins >= spin_limit) {
           __hip_atomic_fetch_or(&cs->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
           break;
         }
+        __builtin_amdgcn_s_sleep(2);
+        ++spins;
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    *s_flag = ok;
   }
   __syncthreads();
+  const bool ok = *s_flag != 0;
+  __syncthreads();
+  return ok;
 }
 
 constexpr uint32_t EX_THREADS = 1024;
@@ -125,6 +137,7 @@ __device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint
 // ======================================================================
 constexpr uint32_t LK_BITS = 12;
 constexpr uint32_t LK_BINS = 1u << LK_BITS;
+static_assert(LK_BINS == LK_HIST_BINS, "the call prologue zeroes LK_HIST_BINS words per row");
 constexpr uint32_t LK_STRIDE = LK_BINS + 4;
 constexpr uint32_t LK_THREADS = 1024;
 constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
@@ -208,6 +221,80 @@ enum : uint32_t { FIN_SCAN = 0, FIN_LISTED = 1 };
 enum : uint32_t { LK_HIST_SAMPLED = 1, LK_HIST_EXACT = 2 };
 constexpr uint32_t FIN_SCAN_ROWS = 1024;
 
+// One listed row selected again by one workgroup (every thread calls it):
+// the exact route's work for that row with no other workgroup involved, used
+// when a grid-barrier wait gave up.  A radix select of the k-th composite
+// over the whole row, then (small k) its k winners sorted in LDS and written,
+// or (large k) the k winners into the row's candidate buffer, its bucket
+// histogram rebuilt and the row handed to the sort.  LDS as in k_finish.
+template <int DT>
+__device__ __attribute__((noinline)) void reselect_row(const void* __restrict__ values, uint32_t n, RowState* st,
+                             uint32_t row, uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k,
+                             uint32_t B, uint32_t W, uint32_t small_k,
+                             void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+                             uint32_t* __restrict__ lk_row, uint32_t bl, uint32_t* s_hist,
+                             uint32_t* s_misc, uint64_t* s_cand, uint32_t* s_keys) {
+  using D = Dt<DT>;
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * D::ES;
+  const RowSrc<DT> src{rowp, B, (1ull << B) - 1ull};
+  // passes stop once exactly k composites lie at or above the bucket
+  const SelectOut sel = block_select(src, n, W, k, k, s_hist, s_misc, s_cand, RF_SORT_CAP);
+  if (small_k) {   // k <= KSMALL = RF_SORT_CAP
+    const uint32_t got = block_collect(src, n, sel.thr, s_cand, RF_SORT_CAP, &s_misc[4]);
+    const uint32_t P = next_pow2(got);
+    for (uint32_t i = got + tid; i < P; i += nt) s_cand[i] = 0ull;
+    __syncthreads();
+    block_bitonic_desc(s_cand, P);
+    write_winners<DT>(s_cand, k, k, B, rowp, n, out_values, out_idx, row);
+    __syncthreads();
+    if (tid == 0) st->status = ST_DONE;
+    __syncthreads();
+    return;
+  }
+  uint64_t* out = cbuf + (size_t)row * cap;
+  if (tid == 0) {
+    s_misc[4] = 0;
+    s_misc[5] = 0;
+  }
+  __syncthreads();
+  uint32_t km = 0;
+  for (uint32_t i0 = 0; i0 < n; i0 += nt) {
+    const uint32_t i = i0 + tid;
+    const uint64_t c = i < n ? src(i) : 0ull;
+    const bool keep = i < n && c >= sel.thr;
+    if (keep && (uint32_t)(c >> B) > km) km = (uint32_t)(c >> B);
+    const uint64_t m = ballot(keep);
+    if (m) {
+      const uint32_t first = (uint32_t)__builtin_ctzll(m);
+      uint32_t base = 0;
+      if (lane_id() == first) base = atomicAdd(&s_misc[4], (uint32_t)__builtin_popcountll(m));
+      base = wave_bcast(base, first);
+      const uint32_t slot = base + rank_below(m);
+      if (keep && slot < cap) out[slot] = c;
+    }
+  }
+  km = wave_max_u32(km);
+  if (lane_id() == 0 && km) atomicMax(&s_misc[5], km);
+  __syncthreads();
+  const uint32_t R = s_misc[4] < cap ? s_misc[4] : cap;
+  const uint32_t thr_key = (uint32_t)(sel.thr >> B), kmax = s_misc[5];
+  if (lk_row) {   // the bucket histogram, rebuilt from zero
+    for (uint32_t i = tid; i < LK_BINS; i += nt) lk_row[i] = 0u;
+    __syncthreads();
+    const LkDigit g = lk_digit(thr_key, kmax, B, bl);
+    for (uint32_t base = 0; base < R; base += LK_CHUNK)
+      lk_hist_chunk(out, out, R, R, base, g, lk_row, s_keys);
+  }
+  if (tid == 0) {
+    st->count = R;
+    st->thr_key = thr_key;   // every winner key is >= this
+    st->kmax = kmax;
+    st->status = ST_SORT;
+  }
+  __syncthreads();
+}
+
 template <int DT>
 __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
@@ -216,7 +303,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
     uint32_t k_eff, uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode,
     void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk,
-    uint32_t bl, uint32_t lk_flags) {
+    uint32_t bl, uint32_t lk_flags, uint32_t spin_limit) {
   using D = Dt<DT>;
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -224,6 +311,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   __shared__ uint64_t s_cand[RF_SORT_CAP];
   __shared__ uint32_t s_keys[RF_KCAP];
   __shared__ uint32_t s_idx[RF_SORT_CAP];
+  __shared__ uint32_t s_flag;
   const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
 
   // FIN_SCAN (a sampled call): this workgroup's first row's state is read
@@ -233,14 +321,17 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
   if (pre) {
     f_status = states[r_first].status;
-    f_count = states[r_first].count;
+    f_count = rctr[r_first].above;
     f_tau = states[r_first].tau_key;
     f_ties = rctr[r_first].ties;
     f_kmax = rctr[r_first].kmax;
   }
   static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
 
-  // ---- which rows failed the check (Prof-K section 3, stage 4)
+  // ---- which rows failed the check (Prof-K section 3, stage 4).  Every
+  // count read here is final and never rewritten in this kernel (the
+  // filter's above-tau count and tie count), so every workgroup reaches the
+  // same verdict for every row.
   __shared__ uint32_t s_bad[FIN_SCAN_ROWS / 32];   // FIN_SCAN: one bit per row
   uint32_t nf;
   if (mode == FIN_SCAN) {
@@ -248,15 +339,15 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
     __syncthreads();
     for (uint32_t r = tid; r < rows; r += blockDim.x) {
-      const uint32_t G = __hip_atomic_load(&states[r].count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t E = rctr[r].ties;   // final: only the filter adds to it
-      if (sampled_verdict(G, E, k, k_eff, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
+      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
+      if (sampled_verdict(Ga, E, k, k_eff, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
     }
     __syncthreads();
     nf = 0;
     for (uint32_t i = 0; i < words; ++i) nf += __builtin_popcount(s_bad[i]);
   } else {
     nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nf > rows) nf = rows;   // (at most one entry per row was listed)
   }
 
   // ---- this workgroup's rows: list the failed ones, refine the others
@@ -268,16 +359,18 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
         slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
         st->ties = rctr[r].ties;
-        st->r_sampled = st->count + st->ties;
+        st->r_sampled = rctr[r].above + st->ties;
         start_exact(st, k, PATH_FALLBACK);
         flagged[slot] = r;
       }
+      // large k: this row's bucket-sort counters start at zero (the sampler
+      // zeroed them; LK_HIST_SAMPLED below skips failed rows)
       continue;
     }
     const bool fr = pre && r == r_first;
     if ((fr ? f_status : st->status) != ST_FILTER) continue;
     // an accepted row; when it needs the ties, they join its candidates
-    const uint32_t G = fr ? f_count : st->count, E = fr ? f_ties : rctr[r].ties;
+    const uint32_t G = fr ? f_count : rctr[r].above, E = fr ? f_ties : rctr[r].ties;
     const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
     const uint32_t verdict = sampled_verdict(G, E, k, k_eff, cap);
     const bool ties_in = verdict == V_OK_TIES || verdict == V_PARTIAL;
@@ -332,17 +425,38 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     }
   }
   if (nf == 0) return;                        // the common case: nothing more to do
-  if (mode == FIN_SCAN) {
-    if (blockIdx.x == 0 && tid == 0) {
-      cs->nflag = nf;
-      cs->nactive = nf;
-    }
-    grid_barrier(cs, G);   // the listed rows' states are visible to all
+
+  // ======================= exact route (nf > 0 in every workgroup) =======
+  // A listed entry always names a row of this call once the barrier after
+  // the listing has passed; the bound is kept anyway for every read.
+  auto listed = [&](uint32_t f) -> uint32_t {
+    const uint32_t r = flagged[f];
+    return r < rows ? r : 0xFFFFFFFFu;
+  };
+  if (mode == FIN_SCAN && blockIdx.x == 0 && tid == 0) {
+    cs->nflag = nf;
+    cs->nactive = nf;
   }
+  // per-call scratch: the listed rows' exact-route histograms start at zero
+  for (uint32_t f = blockIdx.x; f < nf; f += G)
+    if (tid < 256) ghist[(size_t)f * 256 + tid] = 0u;
+  // (FIN_LISTED from the exact route's set-up: the bucket-sort counters of
+  // the rows too; FIN_SCAN rows had theirs zeroed by the sampler)
+  if ((lk_flags & LK_HIST_EXACT) && mode == FIN_LISTED) {
+    for (uint32_t f = blockIdx.x; f < nf; f += G) {
+      const uint32_t row = listed(f);
+      if (row == 0xFFFFFFFFu) continue;
+      for (uint32_t i = tid; i < LK_BINS; i += blockDim.x) {
+        lk[(size_t)row * LK_BINS + i] = 0u;
+        lk[(size_t)(rows + row) * LK_BINS + i] = 0u;
+      }
+    }
+  }
+  bool ok = grid_barrier(cs, G, spin_limit, &s_flag);   // the listed rows' states are visible to all
+
   uint32_t ipr = (n / D::VEC + EX_ITEM_VEC - 1) / EX_ITEM_VEC;   // items per row
   if (ipr == 0) ipr = 1;
   const uint64_t total = (uint64_t)nf * ipr;
-  auto sync_all = [&]() { grid_barrier(cs, G); };
 
   // Listed row f covers items [f * ipr, (f + 1) * ipr).  Each workgroup takes
   // one contiguous range of items, so it streams long runs of one row and
@@ -376,7 +490,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   };
 
   // ---- histogram passes
-  for (uint32_t pass = 0; pass < W / 8; ++pass) {
+  for (uint32_t pass = 0; ok && pass < W / 8; ++pass) {
     if (__hip_atomic_load(&cs->nactive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
     if (tid < 256) s_hist[tid] = 0;
     __syncthreads();
@@ -401,12 +515,14 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       if (f != fcur) {
         if (live) flush_hist();
         fcur = f;
-        const uint32_t row = flagged[f];
-        const RowState* st = states + row;
-        live = st->status == ST_EXACT;
-        nb = st->nbits;
-        prefix = st->prefix;
-        g = row_geom<DT>(values, n, row);
+        const uint32_t row = listed(f);
+        live = row != 0xFFFFFFFFu && states[row].status == ST_EXACT;
+        if (live) {
+          const RowState* st = states + row;
+          nb = st->nbits;
+          prefix = st->prefix;
+          g = row_geom<DT>(values, n, row);
+        }
       }
       if (!live) continue;
       u32x4 xs[EX_VPT];
@@ -456,10 +572,12 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
     }
     if (live) flush_hist();
-    sync_all();
+    ok = grid_barrier(cs, G, spin_limit, &s_flag);
+    if (!ok) break;
     // resolve: one workgroup per listed row
     for (uint32_t f = blockIdx.x; f < nf; f += G) {
-      const uint32_t row = flagged[f];
+      const uint32_t row = listed(f);
+      if (row == 0xFFFFFFFFu) continue;
       RowState* st = states + row;
       if (st->status != ST_EXACT) continue;
       uint32_t* gh = ghist + (size_t)f * 256;
@@ -495,11 +613,11 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
       __syncthreads();
     }
-    sync_all();
+    ok = grid_barrier(cs, G, spin_limit, &s_flag);
   }
 
   // ---- exact filter: every element >= the exact threshold into the buffer
-  {
+  if (ok) {
     Stager sg{s_cand + (size_t)w * STAGE_SLOTS, 0u, nullptr, nullptr, cap, nullptr, B, 0u};
     const uint64_t maskB = (1ull << B) - 1ull;
     auto comp = [&](uint32_t raw, uint32_t idx) -> uint64_t {
@@ -515,10 +633,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         if (sg.fill) sg.flush();   // to the previous row
         sg.publish();
         fcur = f;
-        const uint32_t row = flagged[f];
-        RowState* st = states + row;
-        live = st->status == ST_EXACT_READY;
+        const uint32_t row = listed(f);
+        live = row != 0xFFFFFFFFu && states[row].status == ST_EXACT_READY;
         if (live) {
+          RowState* st = states + row;
           thr = make_thr<DT>(st->thr_key, st->thr_bound);
           sg.ctr = &st->count;
           sg.kmax = &st->kmax;
@@ -548,36 +666,57 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     }
     if (sg.fill) sg.flush();
     sg.publish();
+    ok = grid_barrier(cs, G, spin_limit, &s_flag);
   }
-  sync_all();
 
   // ---- refine (small k) or hand over to the sort (large k)
-  for (uint32_t f = blockIdx.x; f < nf; f += G) {
-    const uint32_t row = flagged[f];
-    if (small_k) {
-      refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_EXACT_READY,
-                     out_values, out_idx, row, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
-    } else if (tid == 0) {
-      states[row].status = ST_SORT;
+  if (ok) {
+    for (uint32_t f = blockIdx.x; f < nf; f += G) {
+      const uint32_t row = listed(f);
+      if (row == 0xFFFFFFFFu) continue;
+      if (small_k) {
+        refine_row<DT>(values, n, states, cs, flagged, cbuf, cap, k, B, W, ST_EXACT_READY,
+                       out_values, out_idx, row, s_hist, s_misc, s_tmp, s_cand, s_keys, s_idx);
+      } else if (tid == 0) {
+        states[row].status = ST_SORT;
+      }
+    }
+    // Large k: the exact route's rows into their bucket histograms (their
+    // count, threshold and largest key were final at the last grid barrier)
+    if (!small_k && (lk_flags & LK_HIST_EXACT)) {
+      const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
+      const uint64_t npairs = (uint64_t)nf * maxch;
+      for (uint64_t q = blockIdx.x; q < npairs; q += G) {
+        const uint32_t row = listed((uint32_t)(q / maxch)), c = (uint32_t)(q % maxch);
+        if (row == 0xFFFFFFFFu) continue;
+        const RowState st = states[row];
+        const uint32_t R = st.count < cap ? st.count : cap;
+        if ((uint64_t)c * LK_CHUNK >= R) continue;
+        lk_hist_chunk(cbuf + (size_t)row * cap, cbuf + (size_t)row * cap, R, R, c * LK_CHUNK,
+                      lk_digit_of(st, B, bl), lk + (size_t)row * LK_BINS, s_keys);
+      }
     }
   }
-  if (blockIdx.x == 0 && tid == 0) {
-    // every workgroup read nflag before the first grid barrier
-    cs->nflag = 0;
-    cs->nactive = 0;
+
+  // ---- exit ticket.  Every workgroup takes one after its last write; the
+  // last one sees every other workgroup's writes.  If any barrier wait gave
+  // up, it selects every listed row again on its own.
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t t =
+        __hip_atomic_fetch_add(&cs->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = t == G - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_flag = last && (__hip_atomic_load(&cs->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u);
   }
-  // Large k: the exact route's rows into their bucket histograms (their
-  // count, threshold and largest key were final at the last grid barrier)
-  if (!small_k && (lk_flags & LK_HIST_EXACT)) {
-    const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
-    const uint64_t npairs = (uint64_t)nf * maxch;
-    for (uint64_t q = blockIdx.x; q < npairs; q += G) {
-      const uint32_t row = flagged[q / maxch], c = (uint32_t)(q % maxch);
-      const RowState st = states[row];
-      const uint32_t R = st.count < cap ? st.count : cap;
-      if ((uint64_t)c * LK_CHUNK >= R) continue;
-      lk_hist_chunk(cbuf + (size_t)row * cap, cbuf + (size_t)row * cap, R, R, c * LK_CHUNK,
-                    lk_digit_of(st, B, bl), lk + (size_t)row * LK_BINS, s_keys);
-    }
+  __syncthreads();
+  if (!s_flag) return;
+  for (uint32_t f = 0; f < nf; ++f) {
+    const uint32_t row = listed(f);
+    if (row == 0xFFFFFFFFu) continue;
+    reselect_row<DT>(values, n, states + row, row, cbuf, cap, k, B, W, small_k, out_values,
+                     out_idx, (lk_flags & LK_HIST_EXACT) ? lk + (size_t)row * LK_BINS : nullptr,
+                     bl, s_hist, s_misc, s_cand, s_keys);
   }
 }

@@ -145,8 +145,10 @@ __device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t
 }
 
 // Row setup for the sampled route (threshold known).
-__device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint32_t tau) {
+__device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint32_t tau,
+                                                  uint32_t route) {
   st->status = ST_FILTER;
+  st->tau_route = route;
   st->tau_key = tau;
   st->count = 0;
   st->ties = 0;
@@ -160,22 +162,49 @@ __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint
   st->kmax = 0;
 }
 
+// The first kernel of a sampled call also does the call's set-up: the call
+// record to zero, the workspace stamp cleared unless it is this layout's, and
+// (large k) the bucket-sort histograms and fill counters of every row to zero,
+// rows * 2 * LK_BINS words shared out over the grid.
+__device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint64_t sig,
+                                              uint32_t* lk, uint32_t rows) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t nb = gridDim.x * gridDim.y;
+  const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
+  if (b == 0 && tid == 0) {
+    reset_call(cs);
+    stamp_invalidate(hdr, sig);
+  }
+  if (lk) {
+    const size_t words = (size_t)rows * 2 * LK_HIST_BINS;
+    const size_t per = (words + nb - 1) / nb;
+    const size_t w0 = (size_t)b * per, w1 = w0 + per < words ? w0 + per : words;
+    for (size_t i = w0 + tid; i < w1; i += nt) lk[i] = 0u;
+  }
+}
+
 // Writes the keys k_tau selects from: all S sample keys and their 11-bit
 // histogram (lists = 0), or each workgroup's t largest at g * t (lists = 1;
 // k_tau histograms those itself: the largest keys of every workgroup share
-// a few top bins, and global atomics on them would serialise).
+// a few top bins, and global atomics on them would serialise).  The global
+// histogram is used only when the workspace stamp says it starts at zero;
+// otherwise k_tau histograms the keys itself.
 template <int DT>
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
     uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
-    uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr) {
+    uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs,
+    WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows) {
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  const bool gh_ok = !lists && hdr->stamp == sig;   // read before the prologue may clear it
+  call_prologue(cs, hdr, sig, lk, rows);
   // the filter selects tau itself: start the row here (tau set there)
-  if (states && blockIdx.x == 0 && tid == 0) start_sampled_row(states + row, rctr + row, 0u);
+  if (states && blockIdx.x == 0 && tid == 0)
+    start_sampled_row(states + row, rctr + row, 0u, TAU_FILTER_LISTS);
   uint32_t* gh = shist + (size_t)row * SH_BINS;
-  if (!lists) {
+  if (gh_ok) {
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
     __syncthreads();
   }
@@ -189,10 +218,11 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
     if (!lists) {
       skeys[(size_t)row * SP + j] = key;
-      atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
+      if (gh_ok) atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
     }
   }
   if (!lists) {
+    if (!gh_ok) return;
     __syncthreads();
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
       if (h[i]) atomicAdd(&gh[i], h[i]);
@@ -226,9 +256,10 @@ constexpr uint32_t TAU_VEC = 8;
 __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict__ skeys, uint32_t S,
                                                      uint32_t SP, uint32_t t, uint32_t KB,
                                                      uint32_t* __restrict__ shist,
-                                                     uint32_t own_hist,
+                                                     uint32_t lists,
                                                      RowState* __restrict__ states,
-                                                     RowCtr* __restrict__ rctr) {
+                                                     RowCtr* __restrict__ rctr,
+                                                     const WsHeader* hdr, uint64_t sig) {
   static_assert(SH_BINS == 2048, "one wave searches 2048 bins");
   __shared__ __align__(16) uint32_t s_hist[SH_BINS];
   __shared__ uint32_t s_misc[8];
@@ -240,6 +271,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   const u32x4* kv4 = reinterpret_cast<const u32x4*>(keys);
   const uint32_t nv = (S + 3) / 4;
   const bool regs = nv <= TAU_VEC * nt;   // every key fits the registers
+  // the sampler's global histogram, unless it was not usable (stamp)
+  const bool own_hist = lists || hdr->stamp != sig;
+  uint32_t route = lists ? TAU_KTAU_LISTS : (regs ? TAU_KTAU_REGS : TAU_KTAU_STREAM);
   u32x4 kv[TAU_VEC];
 #pragma unroll
   for (uint32_t j = 0; j < TAU_VEC; ++j) {
@@ -248,8 +282,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
   }
   auto valid = [&](uint32_t j, int q) { return (j * nt + tid) * 4u + (uint32_t)q < S; };
   if (tid == 0) s_misc[3] = 0;
-  if (own_hist) {   // few keys: histogram them here
+  if (own_hist) {   // few keys, or no usable global histogram: histogram them here
     for (uint32_t i = tid; i < SH_BINS; i += nt) s_hist[i] = 0;
+    if (!lists) {   // leave the global histogram zero for the stamp
+      uint32_t* gh = shist + (size_t)row * SH_BINS;
+      for (uint32_t i = tid; i < SH_BINS; i += nt) gh[i] = 0;
+    }
     __syncthreads();
     if (regs) {
 #pragma unroll
@@ -318,6 +356,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     st0.in_lds = true;
   }
   uint32_t tau;
+  if (!st0.in_lds) route |= TAU_BIN_STREAMED;
+  else if (st0.m > nt / 4) route |= TAU_BIN_RADIX;
   if (st0.in_lds && st0.m <= nt / 4) {
     // a small bin: the wanted key is the one whose rank inside it (larger
     // keys, then equal keys earlier in the list) is need - 1; four lanes
@@ -338,5 +378,18 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
     __syncthreads();   // every thread has read the bin
     tau = (uint32_t)block_select_from(src, S, KB, st0, 0u, s_hist, s_misc, s_cand, CAND_CAP).thr;
   }
-  if (tid == 0) start_sampled_row(states + row, rctr + row, tau);
+  if (tid == 0) start_sampled_row(states + row, rctr + row, tau, route);
+}
+
+// The caller's threshold for every row (topk_params.use_force_tau): the
+// call's set-up and the row starts that the sampler and k_tau would do.
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_force_tau(RowState* __restrict__ states,
+                                                              RowCtr* __restrict__ rctr,
+                                                              CallState* cs, WsHeader* hdr,
+                                                              uint64_t sig, uint32_t tau,
+                                                              uint32_t* __restrict__ lk,
+                                                              uint32_t rows) {
+  call_prologue(cs, hdr, sig, lk, rows);
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    start_sampled_row(states + blockIdx.y, rctr + blockIdx.y, tau, TAU_FORCED);
 }

@@ -245,14 +245,6 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
   __shared__ uint32_t s_sm[8];
   const uint32_t row = blockIdx.y, tid = threadIdx.x, nt = LK_THREADS;
   const uint32_t lane = tid & 63u, w = tid >> 6;
-  if (blockIdx.x == 0) {   // histogram and fill counters: clean for the next call
-    uint32_t* gh = lk + (size_t)row * LK_BINS;
-    uint32_t* gf = lk + (size_t)(rows + row) * LK_BINS;
-    for (uint32_t i = tid; i < LK_BINS; i += nt) {
-      gh[i] = 0;
-      gf[i] = 0;
-    }
-  }
   const RowState st = states[row];
   if (st.status != ST_SORT) return;
   const uint32_t R = st.count < cap ? st.count : cap;

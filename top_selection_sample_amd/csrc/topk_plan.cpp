@@ -339,7 +339,8 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
     small_cheaper = t_small <= t_sampled;
   }
   bool sampled;
-  if (in.force_path == 1) sampled = true;
+  p.force_tau = in.force_tau;
+  if (in.force_path == 1 || in.force_tau) sampled = true;
   else if (in.force_path == 2) sampled = false;
   else sampled = (n >= 8 * p.S) && (p.M < n / 2) && !small_cheaper;
   if (sampled) {
@@ -368,7 +369,7 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   p.filter_bpr = (uint32_t)fb;
   p.hist_bpr = 1;
 
-  size_t off = 0;
+  size_t off = 256;   // the workspace header (WsHeader)
   p.off_states = off;
   off = align256(off + (size_t)rows * 64);
   p.off_call = off;
@@ -392,6 +393,13 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   p.off_rctr = off;   // sampled route: four 128-byte counter lines per row
   if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 512);
   p.total = off;
+  // layout signature: every offset, the row count and the route
+  uint64_t h = 0x9E3779B97F4A7C15ull;
+  const uint64_t parts[] = {p.total,    p.off_states, p.off_call, p.off_flag, p.off_ghist,
+                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux,  p.off_lk,
+                            p.off_rctr,  (uint64_t)p.rows, (uint64_t)p.path, (uint64_t)p.SP};
+  for (uint64_t v : parts) h ^= v + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+  p.sig = h | 1ull;   // never 0
   *out = p;
   return 0;
 }

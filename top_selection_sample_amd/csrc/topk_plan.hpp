@@ -33,6 +33,7 @@ struct ParamIn {
   // recall target (relaxed-recall mode below 1): parameters for
   // ceil(recall * k), and rows with at least that many survivors keep them
   double recall = 1.0;
+  bool force_tau = false;   // the caller gives the threshold key (sampled route, no sampler)
 };
 
 double normal_quantile(double p);
