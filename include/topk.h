@@ -73,7 +73,8 @@ typedef enum {
   TOPK_EDTYPE = -2,     /* unknown dtype */
   TOPK_EWORKSPACE = -3, /* workspace too small */
   TOPK_EHIP = -4,       /* a HIP call failed */
-  TOPK_ENOTIMPL = -5
+  TOPK_ENOTIMPL = -5,
+  TOPK_ETOOBIG = -6     /* topk_noalloc: the call needs more than its scratch array */
 } topk_status;
 
 /* Parameter policy for (S, t, M).
@@ -221,6 +222,23 @@ int topk(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void
 int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
             int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
             const topk_params* params);
+
+/* topk_ex for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace is a device array built into the
+ * library, TOPK_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on
+ * a GPU until the process ends; every call on a GPU uses that GPU's array.
+ * Calls needing more (topk_workspace_size) return TOPK_ETOOBIG before
+ * anything is enqueued.  No device allocation, free or memset: the array
+ * needs no clearing, since every call writes what it reads (see the
+ * workspace convention above).  Calls that may overlap on one GPU (other
+ * streams, other threads) race on the array: run them one after another.
+ * topk_read_stats is not available for these calls.  Same arguments,
+ * results and errors as topk_ex otherwise. */
+#define TOPK_NOALLOC_SCRATCH_BYTES (32u << 20)
+int topk_noalloc(const void* values, int64_t n, int64_t rows, int64_t k, int dtype,
+                 void* out_values, int64_t* out_indices, void* stream,
+                 const topk_params* params);
 
 /* Copy the per-row records of the last call on `workspace` into out[0..rows)
  * (host memory).  Synchronises `stream`.  Errors: TOPK_EINVAL, TOPK_EHIP. */

@@ -205,8 +205,8 @@ def test_workspace_size_is_plan_size(lib):
 
 def test_status_strings(lib):
     seen = set()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         s = lib.lib.topk_status_string(st)
         assert s
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7

@@ -13,6 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtopk_mi355x.so")
 
 TOPK_OK, TOPK_EINVAL, TOPK_EDTYPE, TOPK_EWORKSPACE, TOPK_EHIP, TOPK_ENOTIMPL = 0, -1, -2, -3, -4, -5
+TOPK_ETOOBIG = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20   # topk_noalloc's built-in scratch per GPU
 DTYPE_CODES = {"int32": 0, "float32": 1, "bf16": 2}
 POLICY_EXACT_TAIL, POLICY_ALG1, POLICY_TUNED = 0, 1, 2
 PATH_AUTO, PATH_FILTER, PATH_EXACT = 0, 1, 2
@@ -29,7 +31,7 @@ TEST_BARRIER_GIVEUP = 1
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
            "topk", "topk_ex", "topk_read_stats", "topk_profile_enable", "topk_profile_read",
-           "topk_scatter", "topk_stream_read", "topk_status_string")
+           "topk_scatter", "topk_stream_read", "topk_status_string", "topk_noalloc")
 STAGES = ("sample", "tau", "filter", "refine", "exact", "sort")
 
 
@@ -78,6 +80,7 @@ def _load():
     L.topk_workspace_init.argtypes = [vp, sz, vp]
     L.topk.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]
     L.topk_ex.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp, P(Params)]
+    L.topk_noalloc.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, P(Params)]
     L.topk_read_stats.argtypes = [vp, i64, P(RowStats), vp]
     L.topk_profile_enable.argtypes = [i32]
     L.topk_profile_read.argtypes = [P(StageTimes)]

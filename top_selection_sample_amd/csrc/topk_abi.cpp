@@ -200,9 +200,15 @@ int topk_workspace_init(void* workspace, size_t bytes, void* stream) {
   return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
 }
 
-int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
-            int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
-            const topk_params* params) {
+}  // extern "C"
+
+namespace {
+
+// The body of topk_ex.  allow_marks = false: no stage-timing events (they
+// are created on demand), for topk_noalloc.
+int topk_run(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+             int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
+             const topk_params* params, bool allow_marks) {
   if (!values || !out_values || !out_indices || !workspace) return TOPK_EINVAL;
   try {
     tk::Plan p;
@@ -236,7 +242,7 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
     a.seed = (params && params->use_seed) ? params->seed
                                           : (0x243F6A8885A308D3ull ^ (ctr * 0x9E3779B97F4A7C15ull));
     a.stream = static_cast<hipStream_t>(stream);
-    if (g_prof.load(std::memory_order_relaxed)) a.mark = mark_stage;
+    if (allow_marks && g_prof.load(std::memory_order_relaxed)) a.mark = mark_stage;
     hipError_t e = tk::launch_pipeline(a);
     return e == hipSuccess ? TOPK_OK : TOPK_EHIP;
   } catch (const std::bad_alloc&) {
@@ -244,6 +250,37 @@ int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, v
   } catch (...) {
     return TOPK_EINVAL;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_ex(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
+            int64_t* out_indices, void* workspace, size_t workspace_bytes, void* stream,
+            const topk_params* params) {
+  return topk_run(values, n, rows, k, dtype, out_values, out_indices, workspace, workspace_bytes,
+                  stream, params, true);
+}
+
+int topk_noalloc(const void* values, int64_t n, int64_t rows, int64_t k, int dtype,
+                 void* out_values, int64_t* out_indices, void* stream,
+                 const topk_params* params) {
+  static_assert(tk::NOALLOC_SCRATCH_BYTES == (size_t)TOPK_NOALLOC_SCRATCH_BYTES,
+                "the header states the scratch size");
+  if (!values || !out_values || !out_indices) return TOPK_EINVAL;
+  try {
+    tk::Plan p;
+    const int rc = plan_of(n, rows, k, dtype, params, &p, true);
+    if (rc) return rc;
+    if (p.total > tk::NOALLOC_SCRATCH_BYTES) return TOPK_ETOOBIG;
+  } catch (...) {
+    return TOPK_EINVAL;
+  }
+  void* ws = nullptr;
+  if (tk::noalloc_scratch(&ws) != hipSuccess) return TOPK_EHIP;
+  return topk_run(values, n, rows, k, dtype, out_values, out_indices, ws,
+                  tk::NOALLOC_SCRATCH_BYTES, stream, params, false);
 }
 
 int topk(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, void* out_values,
@@ -338,6 +375,7 @@ const char* topk_status_string(int status) {
     case TOPK_EWORKSPACE: return "workspace too small";
     case TOPK_EHIP: return "HIP error";
     case TOPK_ENOTIMPL: return "not implemented";
+    case TOPK_ETOOBIG: return "call needs more scratch than topk_noalloc's built-in array";
     default: return "unknown status";
   }
 }

@@ -23,6 +23,8 @@
 // The kernels live in parts included below in order (sampler and threshold,
 // filter and detection, refinement and the one-workgroup route, the finish
 // kernel, the large-k sorts); this file holds the rest and the launchers.
+#include <mutex>
+
 #include "topk_device.hpp"
 #include "topk_launch.hpp"
 #include "topk_select.hpp"
@@ -371,6 +373,34 @@ hipError_t launch_scatter(const void* values, const int64_t* idx, uint64_t rows,
   TK_DISPATCH(dtype, k_scatter_winners, grid, dim3(256), 0, s, values, idx, rows, k, n, out_dense,
               out_mask);
   return hipGetLastError();
+}
+
+// ======================================================================
+// Built-in scratch for callers that cannot allocate (topk_noalloc): a
+// file-scope device array, one per GPU the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: its
+// device address is looked up once per device (with that device current)
+// and kept.
+// ======================================================================
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 uint32_t filter_threads() { return FILTER_THREADS; }

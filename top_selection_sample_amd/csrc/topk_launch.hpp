@@ -72,6 +72,12 @@ struct LaunchArgs {
   hipStream_t stream;
 };
 
+// Bytes of the built-in scratch array of topk_noalloc (per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(32) << 20;
+// Its device address on the current device (looked up on the first call per
+// device, then kept).
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_pipeline(const LaunchArgs& a);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
