@@ -189,7 +189,8 @@ typedef struct {
                          route), 1 per-workgroup top-t lists in the filter's prologue,
                          2 top-t lists in the threshold kernel, 3 every sample key in
                          registers, 4 every sample key streamed, 5 given by the caller
-                         (use_force_tau).  Bit 3: the sample bin holding rank t had more
+                         (use_force_tau), 6 top-t lists radix-selected in the filter's
+                         prologue.  Bit 3: the sample bin holding rank t had more
                          keys than LDS holds (streamed radix select); bit 4: that bin was
                          radix-selected in LDS. */
 } topk_row_stats;

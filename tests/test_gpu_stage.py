@@ -81,12 +81,17 @@ def _routes():
     """name: (data kind, S, t, expected source of tau, expected bin flags or
     None).  With spread data the boundary bin's size depends on the dtype's
     key range (the int32 scores' top-t keys share one bin, for instance), so
-    only the source is asserted there; the one-bin rows force the flags."""
+    only the source is asserted there; the one-bin rows force the flags.
+    Top-t lists (t <= 16) of at most 4096 keys in all are selected in the
+    filter's prologue: by wave max extraction for t <= 8 and at most 2048
+    keys, else by a radix select over [largest list tail, largest head]."""
     tss = _tss()
     return {
         "filter_lists": ("spread", 16384, 3, tss.TAU_FILTER_LISTS, 0),
-        "ktau_lists_t12": ("spread", 16384, 12, tss.TAU_KTAU_LISTS, None),
-        "ktau_lists_many": ("spread", 131072, 8, tss.TAU_KTAU_LISTS, None),
+        "filter_radix_t12": ("spread", 16384, 12, tss.TAU_FILTER_RADIX, 0),
+        "filter_radix_t16": ("spread", 32768, 16, tss.TAU_FILTER_RADIX, 0),
+        "filter_radix_onebin": ("onebin", 16384, 14, tss.TAU_FILTER_RADIX, 0),
+        "ktau_lists_many": ("spread", 131072, 16, tss.TAU_KTAU_LISTS, None),
         "ktau_regs": ("spread", 32768, 32, tss.TAU_KTAU_REGS, None),
         "ktau_stream": ("spread", 40000, 20, tss.TAU_KTAU_STREAM, None),
         "bin_streamed": ("onebin", 16384, 20, tss.TAU_KTAU_REGS, tss.TAU_BIN_STREAMED),
@@ -96,8 +101,9 @@ def _routes():
     }
 
 
-ROUTE_NAMES = ["filter_lists", "ktau_lists_t12", "ktau_lists_many", "ktau_regs", "ktau_stream",
-               "bin_streamed", "bin_radix", "bin_streamed_keys_streamed"]
+ROUTE_NAMES = ["filter_lists", "filter_radix_t12", "filter_radix_t16", "filter_radix_onebin",
+               "ktau_lists_many", "ktau_regs", "ktau_stream", "bin_streamed", "bin_radix",
+               "bin_streamed_keys_streamed"]
 
 
 @pytest.mark.parametrize("dt", ["float32", "int32", "bf16"])

@@ -81,6 +81,7 @@ enum : uint32_t {
   TAU_KTAU_REGS = 3,     // every sample key, held in k_tau's registers
   TAU_KTAU_STREAM = 4,   // every sample key, streamed by k_tau
   TAU_FORCED = 5,        // given by the caller
+  TAU_FILTER_RADIX = 6,  // per-workgroup top-t lists, radix-selected in the filter's prologue
   TAU_BIN_STREAMED = 8,  // flag: the boundary bin exceeded LDS
   TAU_BIN_RADIX = 16,    // flag: the boundary bin was radix-selected in LDS
 };
@@ -235,7 +236,11 @@ __device__ __forceinline__ uint32_t wave_bcast(uint32_t v, uint32_t lane) {
 // its row (or whose row is masked off) takes the identity 0.  Every lane of
 // the wave must be active: the moves read the other lanes' registers, so
 // each one is taken into a temporary before it is combined (a combine that
-// re-reads it could be turned into a branch with lanes switched off).
+// re-reads it could be turned into a branch with lanes switched off).  The
+// result leaves through an empty asm: without it the compiler may fold the
+// caller's arithmetic into the last move (a row-broadcast subtract,
+// v_subrev_u32_dpp row_bcast:31, which gave wrong sums on gfx950 where the
+// move-then-add form is right).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_take(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
@@ -249,6 +254,7 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
   t = dpp_take<0x118, 0xf>(v); v += t;
   t = dpp_take<0x142, 0xa>(v); v += t;
   t = dpp_take<0x143, 0xc>(v); v += t;
+  asm volatile("" : "+v"(v));
   return v;
 }
 
@@ -260,6 +266,7 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
   t = dpp_take<0x118, 0xf>(v); v = __builtin_elementwise_max(v, t);
   t = dpp_take<0x142, 0xa>(v); v = __builtin_elementwise_max(v, t);
   t = dpp_take<0x143, 0xc>(v); v = __builtin_elementwise_max(v, t);
+  asm volatile("" : "+v"(v));
   return v;
 }
 

@@ -115,10 +115,18 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
     cached[dev] = cus > 0 ? cus : 1;
   }
   const Plan& p = a.plan;
+  // the candidates the sample predicts for a row (t n / S for distinct
+  // values), with room for the spread: the refine's prefetch bound
+  uint32_t r_guess = 0;
+  if (p.path == PLAN_SAMPLED && p.S > 0) {
+    const double g = 1.3 * (double)p.t * (double)p.n / (double)p.S + 512.0;
+    r_guess = g >= (double)p.cap ? (uint32_t)p.cap : (uint32_t)g;
+  }
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
-                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit);
+                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit,
+                     r_guess);
   return hipGetLastError();
 }
 
@@ -161,16 +169,18 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     } else if (p.path == PLAN_SAMPLED) {
       const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
       const dim3 sg(sgx, rows);
-      // small threshold ranks: select from per-workgroup top-t lists; for
-      // t <= 8 and few lists every filter workgroup does that itself
+      // small threshold ranks: select from per-workgroup top-t lists; with
+      // few list keys every filter workgroup does that itself
       const bool lists = p.t <= (int64_t)TOPT && (int64_t)sgx * p.t <= p.S;
       const uint32_t ns = lists ? sgx * (uint32_t)p.t : (uint32_t)p.S;   // keys to select from
-      const bool in_filter = lists && p.t <= 8 && ns <= 4 * FILTER_THREADS;
+      const bool in_filter = lists && ns <= TL_PER * FILTER_THREADS;
       mark(STAGE_SAMPLE, 1);
       TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
                   (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
                   (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr, a.call, a.hdr, p.sig,
-                  lk_zero, rows);
+                  lk_zero, rows,
+                  (uint32_t)((p.t <= 8 && ns <= 4 * FILTER_THREADS) ? TAU_FILTER_LISTS
+                                                                    : TAU_FILTER_RADIX));
       mark(STAGE_SAMPLE, 0);
       if (!in_filter) {
         mark(STAGE_TAU, 1);

@@ -237,6 +237,74 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
   else return __uint_as_float(raw << 16) == t.f;
 }
 
+// tau from the sampler's per-workgroup top-t lists (ns keys, list g at
+// [g t, g t + t), largest first), by one filter workgroup, for ns up to
+// FILTER_THREADS * TL_PER keys and any t <= TOPT (inlined, so that it runs
+// while the first loads of the stream are in flight).  tau is at least lo, the
+// largest list tail (the t-th largest of one workgroup's sample), and at
+// most hi, the largest head; the keys >= lo share the bits above the top
+// differing bit of lo and hi, so a radix select with 11-bit digits below
+// that prefix, over the keys held in registers, resolves it in one level
+// when lo and hi differ only in their low 11 bits (else two or three).
+// s_hist: 2048 words; s_red: 2 * FILTER_WAVES + 4 words.  Every thread calls it.
+constexpr uint32_t TL_PER = 8;   // list keys per thread
+__device__ __forceinline__ uint32_t tau_from_lists(const uint32_t* __restrict__ kl, uint32_t ns, uint32_t t,
+                                   uint32_t* s_hist, uint32_t* s_red) {
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  uint32_t v[TL_PER];
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < TL_PER; ++q) {
+    const uint32_t i = q * FILTER_THREADS + tid;
+    const bool ok = i < ns;
+    v[q] = ok ? kl[i] : 0u;
+    const uint32_t r = i % t;
+    if (ok && r == 0) hi = v[q] > hi ? v[q] : hi;
+    if (ok && r == t - 1) lo = v[q] > lo ? v[q] : lo;
+  }
+  lo = wave_max_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    s_red[w] = lo;
+    s_red[FILTER_WAVES + w] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t j = 0; j < FILTER_WAVES; ++j) {   // independent reads
+    const uint32_t a = s_red[j], b = s_red[FILTER_WAVES + j];
+    lo = a > lo ? a : lo;
+    hi = b > hi ? b : hi;
+  }
+  uint32_t diff = lo ^ hi;
+  if (diff == 0) return lo;   // every key >= lo equals lo: the t-th largest is lo
+  // resolved: the bits above `pos`, equal to those of pfx (the prefix of lo
+  // and hi to start with); need: the rank wanted among the keys matching it
+  uint32_t pos = 32u - (uint32_t)__builtin_clz(diff);   // bits below the common prefix
+  uint32_t pfx = lo & ~((pos >= 32u) ? 0xFFFFFFFFu : ((1u << pos) - 1u));
+  uint32_t need = t;
+  while (pos > 0) {
+    const uint32_t width = pos < 11u ? pos : 11u;
+    const uint32_t shift = pos - width;
+    const uint32_t hmask = (pos >= 32u) ? 0u : ~((1u << pos) - 1u);   // the resolved bits
+    for (uint32_t i = tid; i < 2048; i += FILTER_THREADS) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (uint32_t q = 0; q < TL_PER; ++q) {
+      const bool act = q * FILTER_THREADS + tid < ns && v[q] >= lo && (v[q] & hmask) == pfx;
+      hist_add(s_hist, (v[q] >> shift) & ((1u << width) - 1u), act);
+    }
+    __syncthreads();
+    if (tid < 64) wave_find_bucket_2048(s_hist, need, s_red + 2 * FILTER_WAVES);
+    __syncthreads();
+    const uint32_t b = s_red[2 * FILTER_WAVES], acc = s_red[2 * FILTER_WAVES + 1];
+    __syncthreads();
+    need -= acc;
+    pfx |= b << shift;
+    pos = shift;
+  }
+  return pfx;
+}
+
 template <int DT>
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
@@ -251,7 +319,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   if (st->status != ST_FILTER) return;
   Thr thr;   // set below, once tau is known
 
-  __shared__ uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];
+  __shared__ __align__(16) uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];   // (16: the prologue bins)
   __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
   __shared__ uint32_t s_fill[FILTER_WAVES], s_tfill[FILTER_WAVES], s_ties[FILTER_WAVES],
       s_flushed[FILTER_WAVES];
@@ -364,17 +432,23 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // per-workgroup top-t lists, selected here by every workgroup
   uint32_t tau;
   if (tlist_n) {
-    __shared__ uint32_t s_tl[FILTER_WAVES * 8], s_tc[FILTER_WAVES + 1], s_to[8];
+    __shared__ uint32_t s_tl[FILTER_WAVES * 8], s_tc[2 * FILTER_WAVES + 4], s_to[8];
     const uint32_t* kl = tlist + (size_t)row * tlist_stride;
-    uint32_t v[4], cnt = 0;
+    if (t <= 8 && tlist_n <= 4 * FILTER_THREADS) {
+      // few small lists: the t largest by wave max extraction
+      uint32_t v[4], cnt = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-      const uint32_t i = q * FILTER_THREADS + tid;
-      v[q] = i < tlist_n ? kl[i] : 0u;
-      cnt += i < tlist_n ? 1u : 0u;
+      for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t i = q * FILTER_THREADS + tid;
+        v[q] = i < tlist_n ? kl[i] : 0u;
+        cnt += i < tlist_n ? 1u : 0u;
+      }
+      block_top_t4<FILTER_WAVES, 8>(v, cnt, t, s_tl, s_tc, s_to);
+      tau = s_to[t - 1];   // the lists hold at least t keys
+    } else {
+      // (the staging area is free until the loop: its first 8 KB hold the bins)
+      tau = tau_from_lists(kl, tlist_n, t, reinterpret_cast<uint32_t*>(&s_stage[0][0]), s_tc);
     }
-    block_top_t4<FILTER_WAVES, 8>(v, cnt, t, s_tl, s_tc, s_to);
-    tau = s_to[t - 1];   // the lists hold at least t keys
     if (blockIdx.x == 0 && tid == 0) st->tau_key = tau;
   } else {
     tau = st->tau_key;

@@ -51,15 +51,19 @@ constexpr uint32_t SH_BITS = 11;
 constexpr uint32_t SH_BINS = 1u << SH_BITS;
 
 // Small threshold ranks (t <= TOPT): every sampler workgroup keeps only its
-// own t largest keys (zero-padded to t), and k_tau selects from those G * t
-// keys instead of all S.  Their union holds the t largest sampled keys, and
-// padding keys of 0 cannot raise the t-th largest, so tau is unchanged.
-// (Letting the last sampler workgroup select saves the launch but needs an
-// agent-scope release fence in every workgroup: measured slower, much
-// slower with many rows.)
+// own t largest keys, largest first and zero-padded to t, and tau is
+// selected from those G * t keys instead of all S (by every filter
+// workgroup in its prologue when there are few, else by k_tau).  Their
+// union holds the t largest sampled keys, and padding keys of 0 cannot
+// raise the t-th largest, so tau is unchanged.  (Letting the last sampler
+// workgroup select saves the launch but needs an agent-scope release fence
+// in every workgroup: measured slower, much slower with many rows.  Lists
+// of up to 32 keys measured slower too: on 2^28 bf16 with t = 32 the
+// sampler took 17.8 us instead of 7.8 and the filter's prologue select
+// added 6.5 us, against 7 us for k_tau over every key.)
 constexpr uint32_t TOPT = 16;
 constexpr uint32_t SAMPLE_THREADS = 256;
-static_assert((SAMPLE_THREADS / 64) * TOPT <= 64, "one wave merges the wave lists");
+static_assert((SAMPLE_THREADS / 64) * TOPT <= 2 * 64, "one wave merges the wave lists, two per lane");
 
 // The t largest alive values of the wave (with multiplicity), largest first,
 // written by lane 0 to out[0..); returns how many (wave-uniform).
@@ -125,8 +129,11 @@ __device__ __forceinline__ uint32_t block_top_t4(uint32_t (&v)[4], uint32_t cnt,
   return s_wc[NW];
 }
 
-// The same over the whole workgroup (SAMPLE_THREADS); the result in out
-// (TOPT words), its length returned.  s_wl: 4 * TOPT words, s_wc: 5 words.
+// The same over the whole workgroup (SAMPLE_THREADS = four waves); the
+// result in out (TOPT words, largest first), its length returned.  Each
+// wave extracts its own t largest; then one wave merges the four lists, lane
+// l holding entry l % 32 of lists l / 32 and l / 32 + 2 as a sorted pair.
+// s_wl: 4 * TOPT words, s_wc: 5 words.
 __device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
                                                 uint32_t* s_wc, uint32_t* out) {
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
@@ -134,10 +141,11 @@ __device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t
   if (lane == 0) s_wc[w] = c;
   __syncthreads();
   if (w == 0) {
-    const uint32_t q = lane / TOPT, i = lane % TOPT;
-    const bool al = q < SAMPLE_THREADS / 64 && i < s_wc[q];
-    const uint32_t x = al ? s_wl[q * TOPT + i] : 0u;
-    const uint32_t cnt = wave_top_t(x, al, t, out);
+    const uint32_t q = lane >> 5, i = lane & 31u;
+    const bool a0 = i < s_wc[q], a1 = i < s_wc[q + 2];
+    const uint32_t x0 = a0 ? s_wl[q * TOPT + i] : 0u, x1 = a1 ? s_wl[(q + 2) * TOPT + i] : 0u;
+    uint32_t pv[4] = {x0 > x1 ? x0 : x1, x0 > x1 ? x1 : x0, 0u, 0u};
+    const uint32_t cnt = wave_top_t4(pv, (a0 ? 1u : 0u) + (a1 ? 1u : 0u), t, out);
     if (lane == 0) s_wc[4] = cnt;
   }
   __syncthreads();
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
     uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
     uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs,
-    WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows) {
+    WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows, uint32_t route) {
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
   call_prologue(cs, hdr, sig, lk, rows);
   // the filter selects tau itself: start the row here (tau set there)
   if (states && blockIdx.x == 0 && tid == 0)
-    start_sampled_row(states + row, rctr + row, 0u, TAU_FILTER_LISTS);
+    start_sampled_row(states + row, rctr + row, 0u, route);
   uint32_t* gh = shist + (size_t)row * SH_BINS;
   if (gh_ok) {
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
