@@ -115,18 +115,10 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
     cached[dev] = cus > 0 ? cus : 1;
   }
   const Plan& p = a.plan;
-  // the candidates the sample predicts for a row (t n / S for distinct
-  // values), with room for the spread: the refine's prefetch bound
-  uint32_t r_guess = 0;
-  if (p.path == PLAN_SAMPLED && p.S > 0) {
-    const double g = 1.3 * (double)p.t * (double)p.n / (double)p.S + 512.0;
-    r_guess = g >= (double)p.cap ? (uint32_t)p.cap : (uint32_t)g;
-  }
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
-                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit,
-                     r_guess);
+                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit);
   return hipGetLastError();
 }
 

@@ -28,8 +28,11 @@
 // beat a grid-stride sweep by about 20%.
 constexpr uint32_t FILTER_THREADS = 512;
 constexpr uint32_t FILTER_WAVES = FILTER_THREADS / 64;
-constexpr uint32_t STAGE_SLOTS = 256;
+constexpr uint32_t STAGE_SLOTS = 128;
 constexpr uint32_t FILTER_UNROLL = 4;
+// hit-queue entries per wave: fewer than 64 wait between steps, and one
+// step adds at most FILTER_UNROLL * 64
+constexpr uint32_t HITQ = 64 * (FILTER_UNROLL + 1);
 
 struct Stager {
   uint64_t* stage;   // this wave's LDS slots
@@ -374,12 +377,13 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // of ties.  Per vector rather than per unrolled step: with many survivors
   // (bf16 at large k: most 2048-element steps hold one) the masks and drains
   // then cover 8 elements instead of 32.
-  auto vec_survivors = [&](const u32x4& v0, size_t vi_lane) {
+  auto vec_survivors = [&](const u32x4& v0, size_t vi_lane, bool ok) __attribute__((always_inline)) {
     const u32x4 v[1] = {v0};
     auto idx_of = [&](uint32_t b) { return head + (uint32_t)vi_lane * D::VEC + b; };
     uint32_t ge = 0;
 #pragma unroll
     for (uint32_t b = 0; b < D::VEC; ++b) ge |= (uint32_t)pass_of(elemvc<DT, 1>(v, b)) << b;
+    if (!ok) ge = 0u;
     if (ballot(__builtin_popcount(ge) > D::VEC / 2) == 0) {
       // sparse survivors: test each one for a tie as it is drained
       const SplitOut o = drain_split<DT, 1>(sg, tg, tfull, v, ge, idx_of, comp_of, eq_of);
@@ -401,6 +405,37 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     ties += (uint32_t)__builtin_popcount(eq);
     full = drain_bits<DT, 1>(sg, v, ge & ~eq, idx_of, comp_of) || full;
     if (!tfull && ballot(eq != 0u)) tfull = drain_bits<DT, 1>(tg, v, eq, idx_of, comp_of);
+  };
+
+  // The hit queue of the plain-threshold loop: a lane whose vector holds a
+  // survivor appends the vector and its index to its wave's LDS ring; after
+  // a step, while 64 or more are queued, the wave examines 64 of them
+  // together, one per lane.  With sparse survivors (a lane in a few hundred)
+  // the drains then run with every lane busy instead of one, at the cost of
+  // one LDS write per hit.  (One place drains, so the drain code is inlined
+  // once: as a call, the loop's state would live in scratch memory, whose
+  // loads wait for every load in flight.)
+  __shared__ u32x4 s_qv[FILTER_WAVES][HITQ];
+  __shared__ uint32_t s_qi[FILTER_WAVES][HITQ];
+  uint32_t q_head = 0, q_cnt = 0;   // wave-uniform; q_cnt < 64 between steps
+  auto wrapq = [](uint32_t e) { return e >= HITQ ? e - HITQ : e; };   // e < 2 HITQ
+  auto drain_queue = [&](uint32_t cnt) __attribute__((always_inline)) {
+    wave_lds_sync();
+    const bool ok = lane < cnt;
+    const uint32_t e = wrapq(q_head + lane);
+    const u32x4 x = ok ? s_qv[w][e] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t xi = ok ? s_qi[w][e] : 0u;
+    q_head = wrapq(q_head + cnt);
+    q_cnt -= cnt;
+    vec_survivors(x, xi, ok);
+  };
+  auto enqueue = [&](bool hit, uint64_t hm, const u32x4& x, uint32_t xi) {
+    if (hit) {
+      const uint32_t e = wrapq(q_head + q_cnt + rank_below(hm));
+      s_qv[w][e] = x;
+      s_qi[w][e] = xi;
+    }
+    q_cnt += (uint32_t)__builtin_popcountll(hm);
   };
 
   // This workgroup's slice of the row's vectors: [vi0, vend), in steps of
@@ -479,8 +514,11 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
             any |= (uint32_t)native_pass<DT>(v[u][q], thr);
           }
         }
-        if (ballot(any != 0u) != 0) vec_survivors(v[u], vc + u * stride);
+        const uint64_t hm = ballot(any != 0u);
+        if (hm) enqueue(any != 0u, hm, v[u], (uint32_t)(vc + u * stride));
       }
+      // the last pass (more false) drains what is left
+      while (q_cnt >= 64u || (!more && q_cnt)) drain_queue(q_cnt < 64u ? q_cnt : 64u);
       if (full) break;
     }
   } else {
@@ -489,7 +527,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = vp[vi + u * stride];
 #pragma unroll
-      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) vec_survivors(v[u], vi + u * stride);
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) vec_survivors(v[u], vi + u * stride, true);
       if (full) break;
     }
   }

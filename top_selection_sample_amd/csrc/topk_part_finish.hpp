@@ -303,7 +303,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
     uint32_t k_eff, uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode,
     void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk,
-    uint32_t bl, uint32_t lk_flags, uint32_t spin_limit, uint32_t r_guess) {
+    uint32_t bl, uint32_t lk_flags, uint32_t spin_limit) {
   using D = Dt<DT>;
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
@@ -314,29 +314,17 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   __shared__ uint32_t s_flag;
   const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
 
-  // FIN_SCAN (a sampled call): every load this workgroup needs before its
-  // first refine goes out at once, so that they share one round trip: the
-  // check's two counts of row tid (one row per thread), the record of the
-  // workgroup's first row, and (small k) that row's first candidates, up to
-  // the count the sample predicts (r_guess).  Within the sampled call the
-  // indices are clamped rather than branched on.  (The per-row counters
-  // exist only on the sampled route.)
+  // FIN_SCAN (a sampled call): this workgroup's first row's state is read
+  // here, in the same round trip as the check's reads below.
   const uint32_t r_first = blockIdx.x;
   const bool pre = mode == FIN_SCAN && r_first < rows;
-  static_assert(FIN_SCAN_ROWS <= EX_THREADS, "the check reads one row per thread");
-  const uint32_t rf = r_first < rows ? r_first : rows - 1;
-  RsPrefetch pf;   // issued first: nothing below waits on it
-  pf.load(cbuf + (size_t)rf * cap, (pre && small_k) ? (r_guess < cap ? r_guess : cap) : 0u);
-  uint32_t c_above = 0, c_ties = 0, f_status = 0, f_tau = 0, f_count = 0, f_ties = 0, f_kmax = 0;
-  if (mode == FIN_SCAN) {
-    const uint32_t rq = tid < rows ? tid : rows - 1;
-    c_above = rctr[rq].above;
-    c_ties = rctr[rq].ties;
-    f_status = states[rf].status;
-    f_tau = states[rf].tau_key;
-    f_count = rctr[rf].above;
-    f_ties = rctr[rf].ties;
-    f_kmax = rctr[rf].kmax;
+  uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
+  if (pre) {
+    f_status = states[r_first].status;
+    f_count = rctr[r_first].above;
+    f_tau = states[r_first].tau_key;
+    f_ties = rctr[r_first].ties;
+    f_kmax = rctr[r_first].kmax;
   }
   static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
 
@@ -350,8 +338,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const uint32_t words = (rows + 31) / 32;
     for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
     __syncthreads();
-    if (tid < rows && sampled_verdict(c_above, c_ties, k, k_eff, cap) == V_FAIL)
-      atomicOr(&s_bad[tid >> 5], 1u << (tid & 31));
+    for (uint32_t r = tid; r < rows; r += blockDim.x) {
+      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
+      if (sampled_verdict(Ga, E, k, k_eff, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
+    }
     __syncthreads();
     nf = 0;
     for (uint32_t i = 0; i < words; ++i) nf += __builtin_popcount(s_bad[i]);
@@ -360,11 +350,8 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     if (nf > rows) nf = rows;   // (at most one entry per row was listed)
   }
 
-  // ---- this workgroup's rows: list the failed ones, refine the others.
-  // fr: the workgroup's first row of a small-k sampled call, whose record
-  // and first candidates were loaded above into pf; every other row loads
-  // its own.  (Two call sites keep pf's registers free outside this row.)
-  auto do_row = [&](uint32_t r, bool fr, RsPrefetch& rp) {
+  // ---- this workgroup's rows: list the failed ones, refine the others
+  for (uint32_t r = blockIdx.x; r < rows; r += G) {
     RowState* st = states + r;
     if (mode == FIN_SCAN && nf && (s_bad[r >> 5] >> (r & 31)) & 1u) {
       if (tid == 0) {
@@ -378,9 +365,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       }
       // large k: this row's bucket-sort counters start at zero (the sampler
       // zeroed them; LK_HIST_SAMPLED below skips failed rows)
-      return;
+      continue;
     }
-    if ((fr ? f_status : st->status) != ST_FILTER) return;
+    const bool fr = pre && r == r_first;
+    if ((fr ? f_status : st->status) != ST_FILTER) continue;
     // an accepted row; when it needs the ties, they join its candidates
     const uint32_t G = fr ? f_count : rctr[r].above, E = fr ? f_ties : rctr[r].ties;
     const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
@@ -409,23 +397,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       if (R > cap) R = cap;
       // a partial row (fewer than k reach tau) keeps all R and pads the rest
       const uint32_t kk = R < k ? R : k;
-      if (!fr) rp.load(cbuf + (size_t)r * cap, R);
-      // the prefetched registers predate the copied ties: only the first G
-      // of them are candidates then
-      const uint32_t Rv = (fr && ties_in) ? G : R;
       refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, kk, k, B, W,
                          out_values, out_idx, r, s_hist, s_misc, s_tmp, s_cand,
-                         reinterpret_cast<uint64_t*>(s_keys), rp, Rv);
+                         reinterpret_cast<uint64_t*>(s_keys));
     }
-  };
-  uint32_t r_next = blockIdx.x;
-  if (pre && small_k) {
-    do_row(r_next, true, pf);
-    r_next += G;
-  }
-  for (uint32_t r = r_next; r < rows; r += G) {
-    RsPrefetch own;
-    do_row(r, false, own);
   }
   // Large k: the bucket histograms of the accepted sampled rows (the first
   // step of the bucket sort), LK_CHUNK candidates per workgroup and step.

@@ -287,48 +287,13 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
 // winners fill the row's first k slots of ks; a row that keeps fewer than ks
 // (k = R) gets the rest padded.
 constexpr uint32_t RS_VEC = 11;
-
-// The first composites of a row's candidate buffer in registers, loaded
-// before the row's count is known so that the loads share a round trip with
-// the reads of the counts.  The buffer starts 8-byte aligned: an odd start
-// leaves composite 0 to thread 0 (x1); then come 16-byte pairs, pair p =
-// j * nt + tid holding composites nh + 2p and nh + 2p + 1, up to `bound`
-// composites (RS_VEC pairs per thread at most).  The refine masks every
-// composite at or beyond the row's count and streams those beyond the pairs.
-struct RsPrefetch {
-  u64x2 x[RS_VEC];
-  uint64_t x1;
-  uint32_t nh, nvr;
-  __device__ __forceinline__ void load(const uint64_t* __restrict__ cb, uint32_t bound) {
-    const uint32_t tid = threadIdx.x, nt = blockDim.x;
-    nh = (bound && ((reinterpret_cast<uintptr_t>(cb) >> 3) & 1u)) ? 1u : 0u;
-    const uint32_t pairs = bound > nh ? (bound - nh) / 2 : 0u;
-    nvr = pairs < RS_VEC * nt ? pairs : RS_VEC * nt;
-    const u64x2* vp = reinterpret_cast<const u64x2*>(cb + nh);
-    // Every lane loads every slot, the ones past nvr at a clamped index
-    // (the refine masks them): no load sits behind a lane branch, so all of
-    // them are in flight together.
-    if (nvr) {
-#pragma unroll
-      for (uint32_t j = 0; j < RS_VEC; ++j) {
-        const uint32_t v = j * nt + tid;
-        x[j] = __builtin_nontemporal_load(vp + (v < nvr ? v : nvr - 1));
-      }
-    } else {
-#pragma unroll
-      for (uint32_t j = 0; j < RS_VEC; ++j) x[j] = u64x2{0ull, 0ull};
-    }
-    x1 = (tid == 0 && nh) ? cb[0] : 0ull;
-  }
-};
-
 template <int DT>
-__device__ __forceinline__ void refine_sampled(
-    const void* __restrict__ values, uint32_t n, RowState* st, const uint64_t* __restrict__ cb,
-    uint32_t R, uint32_t lo, uint32_t kmax, uint32_t k, uint32_t ks, uint32_t B, uint32_t W,
-    void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t row, uint32_t* s_hist,
-    uint32_t* s_misc, uint32_t* s_tmp, uint64_t* s_cand, uint64_t* s_scratch, const RsPrefetch& pf,
-    uint32_t Rv) {
+__device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowState* st,
+                               const uint64_t* __restrict__ cb, uint32_t R, uint32_t lo,
+                               uint32_t kmax, uint32_t k, uint32_t ks, uint32_t B, uint32_t W,
+                               void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+                               uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
+                               uint64_t* s_cand, uint64_t* s_scratch) {
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   const uint32_t KB = W - B;
   const uint32_t hi = kmax > lo ? kmax : lo;
@@ -337,26 +302,37 @@ __device__ __forceinline__ void refine_sampled(
   const uint32_t kshift = top >= RF_BITS - 1 ? top - (RF_BITS - 1) : 0u;
   auto digit = [&](uint64_t c) { return ((uint32_t)(c >> B) >> kshift) & (RF_BINS - 1); };
 
-  // The registers hold composites [0, nh + 2 nvr) of the buffer as it was
-  // when they were loaded; the first Rv (<= R) of them are still this row's
-  // candidates.  Those below r0 come from the registers, [r0, R) is streamed.
-  const uint32_t rr = pf.nh + 2 * pf.nvr, rv = Rv < R ? Rv : R;
-  const uint32_t r0 = rr < rv ? rr : rv;
-  const bool has1 = tid == 0 && pf.nh && r0 > 0;
-  auto ok0 = [&](uint32_t j) { return pf.nh + 2 * (j * nt + tid) < r0; };
-  auto ok1 = [&](uint32_t j) { return pf.nh + 2 * (j * nt + tid) + 1 < r0; };
+  // Issue every load first.  The row's buffer starts 8-byte aligned: an odd
+  // start leaves one leading composite to thread 0, then come 16-byte pairs,
+  // and an odd last one goes to thread 1.  Candidates beyond the registers
+  // are streamed.
+  const uint32_t nh = (R && ((reinterpret_cast<uintptr_t>(cb) >> 3) & 1u)) ? 1u : 0u;
+  const uint32_t pairs = (R - nh) / 2;
+  const uint32_t nvr = pairs < RS_VEC * nt ? pairs : RS_VEC * nt;
+  const uint32_t tl = (nvr == pairs && ((R - nh) & 1u)) ? 1u : 0u;
+  const uint32_t r0 = nh + 2 * nvr, re = R - tl;   // the streamed range [r0, re)
+  const u64x2* vp = reinterpret_cast<const u64x2*>(cb + nh);
+  u64x2 x[RS_VEC];
+#pragma unroll
+  for (uint32_t j = 0; j < RS_VEC; ++j) {
+    const uint32_t v = j * nt + tid;
+    x[j] = v < nvr ? __builtin_nontemporal_load(vp + v) : u64x2{0ull, 0ull};
+  }
+  const bool has1 = (tid == 0 && nh) || (tid == 1 && tl);
+  const uint64_t x1 = has1 ? cb[tid == 0 ? 0u : R - 1] : 0ull;
   for (uint32_t i = tid; i < RF_BINS; i += nt) s_hist[i] = 0;
   if (tid == 0) s_misc[4] = 0;
   __syncthreads();
-  hist_add(s_hist, digit(pf.x1), has1);
+  hist_add(s_hist, digit(x1), has1);
 #pragma unroll
   for (uint32_t j = 0; j < RS_VEC; ++j) {
-    hist_add(s_hist, digit(pf.x[j].x), ok0(j));
-    hist_add(s_hist, digit(pf.x[j].y), ok1(j));
+    const bool ok = j * nt + tid < nvr;
+    hist_add(s_hist, digit(x[j].x), ok);
+    hist_add(s_hist, digit(x[j].y), ok);
   }
-  if (r0 < R)
+  if (r0 < re)
     for_batched<LOADS_IN_FLIGHT, uint64_t>(
-        R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+        re - r0, [&](uint32_t i) { return cb[r0 + i]; },
         [&](uint64_t c, bool ok) { hist_add(s_hist, digit(c), ok); });
   __syncthreads();
   if (tid < 64) wave_find_bucket_2048(s_hist, k, s_misc);
@@ -366,10 +342,12 @@ __device__ __forceinline__ void refine_sampled(
   if (acc + hb <= RF_SORT_CAP) {
     // the register-held ones: one slot reservation per wave
     auto keep = [&](uint64_t c, bool ok) { return ok && digit(c) >= b; };
-    uint32_t mine = keep(pf.x1, has1) ? 1u : 0u;
+    uint32_t mine = keep(x1, has1) ? 1u : 0u;
 #pragma unroll
-    for (uint32_t j = 0; j < RS_VEC; ++j)
-      mine += (keep(pf.x[j].x, ok0(j)) ? 1u : 0u) + (keep(pf.x[j].y, ok1(j)) ? 1u : 0u);
+    for (uint32_t j = 0; j < RS_VEC; ++j) {
+      const bool ok = j * nt + tid < nvr;
+      mine += (keep(x[j].x, ok) ? 1u : 0u) + (keep(x[j].y, ok) ? 1u : 0u);
+    }
     const uint32_t incl = wave_incl_sum(mine);
     const uint32_t wtot = wave_bcast(incl, 63u);
     uint32_t wbase = 0;
@@ -381,15 +359,16 @@ __device__ __forceinline__ void refine_sampled(
         ++pos;
       }
     };
-    put(pf.x1, keep(pf.x1, has1));
+    put(x1, keep(x1, has1));
 #pragma unroll
     for (uint32_t j = 0; j < RS_VEC; ++j) {
-      put(pf.x[j].x, keep(pf.x[j].x, ok0(j)));
-      put(pf.x[j].y, keep(pf.x[j].y, ok1(j)));
+      const bool ok = j * nt + tid < nvr;
+      put(x[j].x, keep(x[j].x, ok));
+      put(x[j].y, keep(x[j].y, ok));
     }
-    if (r0 < R)
+    if (r0 < re)
       for_batched<LOADS_IN_FLIGHT, uint64_t>(
-          R - r0, [&](uint32_t i) { return cb[r0 + i]; },
+          re - r0, [&](uint32_t i) { return cb[r0 + i]; },
           [&](uint64_t c, bool ok) {
             lds_append(s_cand, &s_misc[4], RF_SORT_CAP, c, ok && digit(c) >= b);
           });
