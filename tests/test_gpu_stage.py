@@ -82,27 +82,33 @@ def _routes():
     None).  With spread data the boundary bin's size depends on the dtype's
     key range (the int32 scores' top-t keys share one bin, for instance), so
     only the source is asserted there; the one-bin rows force the flags.
-    Top-t lists (t <= 16) of at most 4096 keys in all are selected in the
+    Top-t lists (t <= 32) of at most 4096 keys in all are selected in the
     filter's prologue: by wave max extraction for t <= 8 and at most 2048
-    keys, else by a radix select over [largest list tail, largest head]."""
+    keys, else by a radix select over [largest list tail, largest head].  The
+    sampler builds lists of t <= 8 by extraction and longer ones by sorting;
+    beyond 32 every sample key goes to the threshold kernel."""
     tss = _tss()
     return {
         "filter_lists": ("spread", 16384, 3, tss.TAU_FILTER_LISTS, 0),
         "filter_radix_t12": ("spread", 16384, 12, tss.TAU_FILTER_RADIX, 0),
         "filter_radix_t16": ("spread", 32768, 16, tss.TAU_FILTER_RADIX, 0),
+        "filter_radix_t32": ("spread", 32768, 32, tss.TAU_FILTER_RADIX, 0),
         "filter_radix_onebin": ("onebin", 16384, 14, tss.TAU_FILTER_RADIX, 0),
+        "filter_radix_onebin_t30": ("onebin", 4096, 30, tss.TAU_FILTER_RADIX, 0),
         "ktau_lists_many": ("spread", 131072, 16, tss.TAU_KTAU_LISTS, None),
-        "ktau_regs": ("spread", 32768, 32, tss.TAU_KTAU_REGS, None),
-        "ktau_stream": ("spread", 40000, 20, tss.TAU_KTAU_STREAM, None),
-        "bin_streamed": ("onebin", 16384, 20, tss.TAU_KTAU_REGS, tss.TAU_BIN_STREAMED),
-        "bin_radix": ("onebin", 4096, 20, tss.TAU_KTAU_REGS, tss.TAU_BIN_RADIX),
-        "bin_streamed_keys_streamed": ("onebin", 40000, 20, tss.TAU_KTAU_STREAM,
+        "ktau_lists_t32": ("spread", 131072, 32, tss.TAU_KTAU_LISTS, None),
+        "ktau_regs": ("spread", 32768, 40, tss.TAU_KTAU_REGS, None),
+        "ktau_stream": ("spread", 40000, 40, tss.TAU_KTAU_STREAM, None),
+        "bin_streamed": ("onebin", 16384, 40, tss.TAU_KTAU_REGS, tss.TAU_BIN_STREAMED),
+        "bin_radix": ("onebin", 4096, 40, tss.TAU_KTAU_REGS, tss.TAU_BIN_RADIX),
+        "bin_streamed_keys_streamed": ("onebin", 40000, 40, tss.TAU_KTAU_STREAM,
                                        tss.TAU_BIN_STREAMED),
     }
 
 
-ROUTE_NAMES = ["filter_lists", "filter_radix_t12", "filter_radix_t16", "filter_radix_onebin",
-               "ktau_lists_many", "ktau_regs", "ktau_stream", "bin_streamed", "bin_radix",
+ROUTE_NAMES = ["filter_lists", "filter_radix_t12", "filter_radix_t16", "filter_radix_t32",
+               "filter_radix_onebin", "filter_radix_onebin_t30", "ktau_lists_many",
+               "ktau_lists_t32", "ktau_regs", "ktau_stream", "bin_streamed", "bin_radix",
                "bin_streamed_keys_streamed"]
 
 
@@ -293,11 +299,11 @@ def test_workspace_with_arbitrary_bytes(case):
         x = workloads.normal_f32(1, 2 ** 22 + 1, 960)
     rows, n = x.shape
     k = {"large_k": 9000}.get(case, 64)
-    kw = {"all_keys": dict(S=32768, t=32, M=n // 8, force_path=tss.PATH_FILTER),
+    kw = {"all_keys": dict(S=32768, t=40, M=n // 8, force_path=tss.PATH_FILTER),
           "lists": dict(),
           "exact": dict(force_path=tss.PATH_EXACT),
           "large_k": dict(),
-          "batched": dict(S=8192, t=24, M=n // 8, force_path=tss.PATH_FILTER)}[case]
+          "batched": dict(S=8192, t=40, M=n // 8, force_path=tss.PATH_FILTER)}[case]
     xt = to_dev(x, dt)
     need = tss.workspace_size(n, rows, k, dt, tss.default_params(**kw))
     ws = torch.empty(need + 4096, dtype=torch.uint8, device="cuda")

@@ -96,10 +96,10 @@ def test_noalloc_batched_then_large_k_then_tiny():
 
 def test_noalloc_all_keys_threshold_and_exact_route():
     # the sample histogram kept in the array between calls (all sample keys,
-    # t > 16), twice in a row, then the exact route on a smaller row
+    # t > 32), twice in a row, then the exact route on a smaller row
     tss = _tss()
     x = workloads.normal_f32(1, 2 ** 22 + 3, 1205)
-    p = tss.default_params(S=32768, t=32, M=2 ** 19, force_path=tss.PATH_FILTER)
+    p = tss.default_params(S=32768, t=40, M=2 ** 19, force_path=tss.PATH_FILTER)
     _check(x, 100, "float32", "all sample keys", p)
     _check(x, 100, "float32", "all sample keys again", p)
     _check(x[:, : 2 ** 20], 100, "float32", "exact route", tss.default_params(force_path=tss.PATH_EXACT))

@@ -242,8 +242,10 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
 
 // tau from the sampler's per-workgroup top-t lists (ns keys, list g at
 // [g t, g t + t), largest first), by one filter workgroup, for ns up to
-// FILTER_THREADS * TL_PER keys and any t <= TOPT (inlined, so that it runs
-// while the first loads of the stream are in flight).  tau is at least lo, the
+// FILTER_THREADS * TL_PER keys and any t <= TOPT; thread tid holds key
+// q * FILTER_THREADS + tid in v[q] (values at or past ns are ignored).
+// (Inlined, so that it runs while the first loads of the stream are in
+// flight.)  tau is at least lo, the
 // largest list tail (the t-th largest of one workgroup's sample), and at
 // most hi, the largest head; the keys >= lo share the bits above the top
 // differing bit of lo and hi, so a radix select with 11-bit digits below
@@ -251,16 +253,14 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
 // when lo and hi differ only in their low 11 bits (else two or three).
 // s_hist: 2048 words; s_red: 2 * FILTER_WAVES + 4 words.  Every thread calls it.
 constexpr uint32_t TL_PER = 8;   // list keys per thread
-__device__ __forceinline__ uint32_t tau_from_lists(const uint32_t* __restrict__ kl, uint32_t ns, uint32_t t,
-                                   uint32_t* s_hist, uint32_t* s_red) {
+__device__ __forceinline__ uint32_t tau_from_lists(const uint32_t (&v)[TL_PER], uint32_t ns, uint32_t t,
+                                                   uint32_t* s_hist, uint32_t* s_red) {
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  uint32_t v[TL_PER];
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (uint32_t q = 0; q < TL_PER; ++q) {
     const uint32_t i = q * FILTER_THREADS + tid;
     const bool ok = i < ns;
-    v[q] = ok ? kl[i] : 0u;
     const uint32_t r = i % t;
     if (ok && r == 0) hi = v[q] > hi ? v[q] : hi;
     if (ok && r == t - 1) lo = v[q] > lo ? v[q] : lo;
@@ -454,54 +454,78 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // vectors of a wave that has no survivor.
   // The loads of the next step are issued before the current step is
   // examined, so a wave that is draining survivors still has a step's worth
-  // of loads in flight.  The first step's loads go out before tau is known.
-  auto step_ok = [&](size_t at) { return (at - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; };
-  u32x4 nxt[FILTER_UNROLL];
-  bool more = step_ok(vi);
-  if (more) {
+  // of loads in flight.  The first two steps' loads go out before tau is
+  // known, so that selecting it overlaps more of the stream.
+  // (the same for every lane of the wave; said so with readfirstlane, so that
+  // the loads below sit behind scalar branches: behind lane-masked ones the
+  // loaded registers are merged with their old values, and the merge copy
+  // waits for the loads)
+  auto step_ok = [&](size_t at) {
+    const bool ok = (at - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend;
+    return __builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0;
+  };
+  // tau's inputs are read first: loads complete in order, so a wait for
+  // them must not come after the stream's first loads
+  uint32_t tlv[TL_PER];
+  {
+    const uint32_t* kl = tlist_n ? tlist + (size_t)row * tlist_stride
+                                 : reinterpret_cast<const uint32_t*>(st);
+    const uint32_t klast = tlist_n ? tlist_n - 1 : 0u;
 #pragma unroll
-    for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
-      nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+    for (uint32_t q = 0; q < TL_PER; ++q) {
+      const uint32_t i = q * FILTER_THREADS + tid;
+      tlv[q] = kl[i < klast ? i : klast];   // (clamped: masked where used)
+    }
+  }
+  const uint32_t tau_given = tlist_n ? 0u : st->tau_key;
+  constexpr size_t sstep = FILTER_UNROLL * stride;
+  u32x4 nxt[FILTER_UNROLL], nx2[FILTER_UNROLL];
+  const bool more2_ = step_ok(vi + sstep);
+  bool more = step_ok(vi);
+  bool more2 = more && more2_;
+  {
+    // unconditional, at clamped indices (a step that is not taken loads
+    // vectors it never reads; with no vectors at all, the row state): no
+    // branch, so nothing merges these registers and waits for the loads
+    const u32x4* vq = nvec ? vp : reinterpret_cast<const u32x4*>(st);
+    const size_t vlast = nvec ? (size_t)nvec - 1 : 0;
+#pragma unroll
+    for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
+      const size_t i0 = vi + u * stride, i1 = i0 + sstep;
+      nxt[u] = __builtin_nontemporal_load(vq + (i0 < vlast ? i0 : vlast));
+      nx2[u] = __builtin_nontemporal_load(vq + (i1 < vlast ? i1 : vlast));
+    }
   }
   // tau: given by k_tau, or (tlist_n > 0) the t-th largest of the sampler's
   // per-workgroup top-t lists, selected here by every workgroup
   uint32_t tau;
   if (tlist_n) {
     __shared__ uint32_t s_tl[FILTER_WAVES * 8], s_tc[2 * FILTER_WAVES + 4], s_to[8];
-    const uint32_t* kl = tlist + (size_t)row * tlist_stride;
     if (t <= 8 && tlist_n <= 4 * FILTER_THREADS) {
       // few small lists: the t largest by wave max extraction
       uint32_t v[4], cnt = 0;
 #pragma unroll
       for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t i = q * FILTER_THREADS + tid;
-        v[q] = i < tlist_n ? kl[i] : 0u;
-        cnt += i < tlist_n ? 1u : 0u;
+        const bool ok = q * FILTER_THREADS + tid < tlist_n;
+        v[q] = ok ? tlv[q] : 0u;
+        cnt += ok ? 1u : 0u;
       }
       block_top_t4<FILTER_WAVES, 8>(v, cnt, t, s_tl, s_tc, s_to);
       tau = s_to[t - 1];   // the lists hold at least t keys
     } else {
       // (the staging area is free until the loop: its first 8 KB hold the bins)
-      tau = tau_from_lists(kl, tlist_n, t, reinterpret_cast<uint32_t*>(&s_stage[0][0]), s_tc);
+      tau = tau_from_lists(tlv, tlist_n, t, reinterpret_cast<uint32_t*>(&s_stage[0][0]), s_tc);
     }
     if (blockIdx.x == 0 && tid == 0) st->tau_key = tau;
   } else {
-    tau = st->tau_key;
+    tau = tau_given;
   }
   thr = make_thr<DT>(tau, 0xFFFFFFFFu);
   if (thr.kind == 0) {
-    while (more) {
-      u32x4 v[FILTER_UNROLL];
-#pragma unroll
-      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = nxt[u];
-      const size_t vc = vi;
-      vi += FILTER_UNROLL * stride;
-      more = step_ok(vi);
-      if (more) {
-#pragma unroll
-        for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
-          nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
-      }
+    // one step: the compares, the hits queued, then the drains the queue
+    // calls for (all that is left after the last step)
+    auto scan_step = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vc, bool last)
+                         __attribute__((always_inline)) {
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
         uint32_t any = 0;
@@ -517,8 +541,33 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
         const uint64_t hm = ballot(any != 0u);
         if (hm) enqueue(any != 0u, hm, v[u], (uint32_t)(vc + u * stride));
       }
-      // the last pass (more false) drains what is left
-      while (q_cnt >= 64u || (!more && q_cnt)) drain_queue(q_cnt < 64u ? q_cnt : 64u);
+      while (q_cnt >= 64u || (last && q_cnt)) drain_queue(q_cnt < 64u ? q_cnt : 64u);
+    };
+    // The first step straight from its registers, the second one's loads
+    // still in flight; from then on one step ahead (the registers of the
+    // next step are copied into those of the current one, and a copy waits
+    // for its loads).
+    if (more) {
+      const size_t vc = vi;
+      vi += sstep;
+      scan_step(nxt, vc, !more2);
+      more = more2 && !full;
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) nxt[u] = nx2[u];
+    }
+    while (more) {
+      u32x4 v[FILTER_UNROLL];
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = nxt[u];
+      const size_t vc = vi;
+      vi += sstep;
+      more = step_ok(vi);
+      if (more) {
+#pragma unroll
+        for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+          nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+      }
+      scan_step(v, vc, !more);
       if (full) break;
     }
   } else {

@@ -55,15 +55,72 @@ constexpr uint32_t SH_BINS = 1u << SH_BITS;
 // selected from those G * t keys instead of all S (by every filter
 // workgroup in its prologue when there are few, else by k_tau).  Their
 // union holds the t largest sampled keys, and padding keys of 0 cannot
-// raise the t-th largest, so tau is unchanged.  (Letting the last sampler
-// workgroup select saves the launch but needs an agent-scope release fence
-// in every workgroup: measured slower, much slower with many rows.  Lists
-// of up to 32 keys measured slower too: on 2^28 bf16 with t = 32 the
-// sampler took 17.8 us instead of 7.8 and the filter's prologue select
-// added 6.5 us, against 7 us for k_tau over every key.)
-constexpr uint32_t TOPT = 16;
+// raise the t-th largest, so tau is unchanged.  Up to TOPT_EXTRACT the
+// workgroup extracts its t largest one at a time; above, it sorts its keys
+// (a bitonic network over each wave's lanes, then two bitonic merges of the
+// wave lists).  (Letting the last sampler workgroup select saves the launch
+// but needs an agent-scope release fence in every workgroup: measured
+// slower, much slower with many rows.  Extraction up to 32 measured slower
+// too: on 2^28 bf16 with t = 32 the sampler took 17.8 us instead of 7.8.)
+constexpr uint32_t TOPT = 32;
+constexpr uint32_t TOPT_EXTRACT = 8;
 constexpr uint32_t SAMPLE_THREADS = 256;
-static_assert((SAMPLE_THREADS / 64) * TOPT <= 2 * 64, "one wave merges the wave lists, two per lane");
+static_assert((SAMPLE_THREADS / 64) * TOPT_EXTRACT <= 2 * 64, "one wave merges the wave lists, two per lane");
+static_assert(SAMPLE_THREADS == 256 && TOPT == 32, "the sorted path merges four wave lists of 32");
+
+// One wave's 64 values sorted largest first (lane 0 the largest): Batcher's
+// bitonic sorting network, partners exchanged across lanes.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
+  const uint32_t l = lane_id();
+#pragma unroll
+  for (uint32_t k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t p = (uint32_t)__shfl_xor((int)v, (int)j, 64);
+      // runs of k alternate descending / ascending, so that each pair of
+      // runs is a bitonic sequence for the next k; the last run descends
+      const bool desc = (l & k) == 0u, low = (l & j) == 0u;
+      const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
+      v = (low == desc) ? mx : mn;
+    }
+  }
+  return v;
+}
+
+// A bitonic sequence over the wave's 64 lanes sorted largest first.
+__device__ __forceinline__ uint32_t wave_merge_desc(uint32_t v) {
+  const uint32_t l = lane_id();
+#pragma unroll
+  for (uint32_t j = 32; j > 0; j >>= 1) {
+    const uint32_t p = (uint32_t)__shfl_xor((int)v, (int)j, 64);
+    const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
+    v = (l & j) == 0u ? mx : mn;
+  }
+  return v;
+}
+
+// The 32 largest of the workgroup's values (one per thread, 0 for none),
+// largest first, into out[0..32).  s_l: 128 words, s_m: 64 words.  Every
+// thread calls it.
+__device__ __forceinline__ void block_top32_sorted(uint32_t v, uint32_t* s_l, uint32_t* s_m,
+                                                   uint32_t* out) {
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  v = wave_sort_desc(v);
+  if (lane < 32) s_l[w * 32 + lane] = v;
+  __syncthreads();
+  if (w < 2) {   // lists 2w and 2w + 1: the second one reversed makes a bitonic sequence
+    uint32_t x = lane < 32 ? s_l[2 * w * 32 + lane] : s_l[(2 * w + 1) * 32 + (63 - lane)];
+    x = wave_merge_desc(x);
+    if (lane < 32) s_m[w * 32 + lane] = x;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint32_t x = lane < 32 ? s_m[lane] : s_m[32 + (63 - lane)];
+    x = wave_merge_desc(x);
+    if (lane < 32) out[lane] = x;
+  }
+  __syncthreads();
+}
 
 // The t largest alive values of the wave (with multiplicity), largest first,
 // written by lane 0 to out[0..); returns how many (wave-uniform).
@@ -129,21 +186,23 @@ __device__ __forceinline__ uint32_t block_top_t4(uint32_t (&v)[4], uint32_t cnt,
   return s_wc[NW];
 }
 
-// The same over the whole workgroup (SAMPLE_THREADS = four waves); the
-// result in out (TOPT words, largest first), its length returned.  Each
+// The same over the whole workgroup (SAMPLE_THREADS = four waves) for t <=
+// TOPT_EXTRACT; the result in out (t words, largest first), its length
+// returned.  Each
 // wave extracts its own t largest; then one wave merges the four lists, lane
 // l holding entry l % 32 of lists l / 32 and l / 32 + 2 as a sorted pair.
 // s_wl: 4 * TOPT words, s_wc: 5 words.
 __device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
                                                 uint32_t* s_wc, uint32_t* out) {
   const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  const uint32_t c = wave_top_t(v, alive, t, s_wl + w * TOPT);
+  const uint32_t c = wave_top_t(v, alive, t, s_wl + w * TOPT_EXTRACT);
   if (lane == 0) s_wc[w] = c;
   __syncthreads();
   if (w == 0) {
     const uint32_t q = lane >> 5, i = lane & 31u;
     const bool a0 = i < s_wc[q], a1 = i < s_wc[q + 2];
-    const uint32_t x0 = a0 ? s_wl[q * TOPT + i] : 0u, x1 = a1 ? s_wl[(q + 2) * TOPT + i] : 0u;
+    const uint32_t x0 = a0 ? s_wl[q * TOPT_EXTRACT + i] : 0u;
+    const uint32_t x1 = a1 ? s_wl[(q + 2) * TOPT_EXTRACT + i] : 0u;
     uint32_t pv[4] = {x0 > x1 ? x0 : x1, x0 > x1 ? x1 : x0, 0u, 0u};
     const uint32_t cnt = wave_top_t4(pv, (a0 ? 1u : 0u) + (a1 ? 1u : 0u), t, out);
     if (lane == 0) s_wc[4] = cnt;
@@ -204,7 +263,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs,
     WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows, uint32_t route) {
   __shared__ uint32_t h[SH_BINS];
-  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT];
+  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT], s_m[2 * TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
   const bool gh_ok = !lists && hdr->stamp == sig;   // read before the prologue may clear it
   call_prologue(cs, hdr, sig, lk, rows);
@@ -237,7 +296,9 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     return;
   }
   // this workgroup's t largest keys, zero-padded
-  const uint32_t c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
+  uint32_t c = TOPT;
+  if (t <= TOPT_EXTRACT) c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
+  else block_top32_sorted(j < S ? key : 0u, s_wl, s_m, s_out);
   if (tid < t) skeys[(size_t)row * SP + blockIdx.x * t + tid] = tid < c ? s_out[tid] : 0u;
 }
 
