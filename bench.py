@@ -11,9 +11,10 @@ in the 256 MB last-level cache.  Prints one JSON line.
 Extra modes (measurement plumbing, not part of the timed line):
     --pmc-run                 a short run for rocprofv3 --pmc: two calibration
                               kernels of known traffic, then a few steps
-    --pmc-summary A B         read the rocprofv3 counter CSVs of the FETCH_SIZE
-                              run (A) and the WRITE_SIZE run (B) of --workload
-                              and print the traffic summary for profiles/
+    --pmc-summary A B [C]     read the rocprofv3 counter CSVs of the FETCH_SIZE
+                              run (A), the WRITE_SIZE run (B) and optionally
+                              an instruction-mix run (C, SQ counters) of
+                              --workload and print the summary for profiles/
     --calibrate W1,W2,...     measure the whole call over the tuned policy's
                               grid of sample sizes on each workload and fit
                               the cost ratio tau_B / tau_A of Eq. 13
@@ -503,7 +504,10 @@ def pmc_summary(args):
     the WRITE_SIZE run (B): each counter (KiB per dispatch) scaled by what
     it reads for its calibration kernel, per kernel of the pipeline (median
     over its dispatches)."""
-    fetch_dir, write_dir = args.pmc_summary
+    if len(args.pmc_summary) not in (2, 3):
+        raise SystemExit("--pmc-summary takes FETCH_DIR WRITE_DIR [SQ_DIR]")
+    fetch_dir, write_dir = args.pmc_summary[:2]
+    sq_dir = args.pmc_summary[2] if len(args.pmc_summary) == 3 else None
     fe = _rows_of(os.path.join(fetch_dir, "**", "*counter_collection.csv"), "FETCH_SIZE")
     wr = _rows_of(os.path.join(write_dir, "**", "*counter_collection.csv"), "WRITE_SIZE")
     kib = 1024.0
@@ -568,7 +572,50 @@ def pmc_summary(args):
         lines.append(f"k_filter_fetch_bytes_scaled: {filt[0]:.0f}")
         lines.append(f"k_filter_write_bytes_scaled: {filt[1]:.0f}")
         lines.append(f"hbm_bytes_per_launch: {filt[0] + filt[1]:.0f}")
+    if sq_dir:
+        lines += [""] + sq_table(sq_dir, args.workload)
     print("\n".join(lines))
+
+
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_BRANCH",
+               "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
+
+
+def sq_table(sq_dir, workload):
+    """Instruction mix per pipeline kernel from one rocprofv3 run of the eight
+    SQ counters above (medians over the kernel's dispatches); per wave: the
+    counter divided by SQ_WAVES."""
+    pat = os.path.join(sq_dir, "**", "*counter_collection.csv")
+    med = {}
+    for c in SQ_COUNTERS:
+        per = {}
+        for _, name, v in _rows_of(pat, c):
+            nm = _short(name)
+            if nm.startswith("tk::") and "k_stream_read" not in nm:
+                per.setdefault(nm, []).append(v)
+        for nm, vs in per.items():
+            vs = sorted(vs)
+            med.setdefault(nm, {})[c] = vs[len(vs) // 2]
+    out = [
+        "Instruction mix (one more run, the same program:",
+        f"  rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d OUT_SQ -o run -- "
+        f"python3 REPO/bench.py --pmc-run --workload {workload} --steps 3",
+        f"  python3 REPO/bench.py --pmc-summary OUT_F OUT_W OUT_SQ --workload {workload})",
+        "",
+        "| kernel | waves | VALU / wave | SALU / wave | LDS / wave | branch / wave | ACTIVE_INST_VALU / BUSY_CYCLES |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for nm in sorted(med):
+        m = med[nm]
+        wv = m.get("SQ_WAVES") or 0.0
+
+        def per(c):
+            return f"{m[c] / wv:.1f}" if wv and c in m else ""
+        act = (f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_BUSY_CYCLES']:.3f}"
+               if m.get("SQ_BUSY_CYCLES") and "SQ_ACTIVE_INST_VALU" in m else "")
+        out.append(f"| {nm} | {wv:.0f} | {per('SQ_INSTS_VALU')} | {per('SQ_INSTS_SALU')} | "
+                   f"{per('SQ_INSTS_LDS')} | {per('SQ_INSTS_BRANCH')} | {act} |")
+    return out
 
 
 def calibrate(args):
@@ -664,7 +711,8 @@ def main():
     ap.add_argument("--calibrate", metavar="WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [SQ_DIR]")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)

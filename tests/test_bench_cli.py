@@ -58,3 +58,32 @@ def test_pmc_summary_scales_each_kernel(tmp_path):
     assert int(out["k_filter_write_bytes_scaled"]) == 92 * 1024
     assert int(out["hbm_bytes_per_launch"]) == 524310 * 2048 + 92 * 1024
     assert "| tk::k_sample<1> | 2 |" in r.stdout
+
+
+def test_pmc_summary_instruction_mix(tmp_path):
+    # a third directory of SQ counters adds per-wave instruction counts
+    import csv
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    fixed = [(1, "tk::k_stream_read(uint4 const*)", "FETCH_SIZE", 524288.0),
+             (2, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)]
+    sq = []
+    for did, waves, valu in ((3, 100.0, 26400.0), (5, 100.0, 26600.0), (7, 100.0, 26500.0)):
+        for c, v in (("SQ_WAVES", waves), ("SQ_INSTS_VALU", valu), ("SQ_INSTS_SALU", 500.0),
+                     ("SQ_INSTS_LDS", 300.0), ("SQ_INSTS_BRANCH", 200.0),
+                     ("SQ_WAVE_CYCLES", 9.0e5), ("SQ_BUSY_CYCLES", 1000.0),
+                     ("SQ_ACTIVE_INST_VALU", 250.0)):
+            sq.append((did, "void tk::k_filter<2>(...)", c, v))
+    for name, rows in (("f", fixed[:1]), ("w", fixed[1:]), ("q", sq)):
+        d = tmp_path / name
+        d.mkdir(parents=True)
+        with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+            wr = csv.DictWriter(fh, fieldnames=fields)
+            wr.writeheader()
+            for did, kn, c, v in rows:
+                wr.writerow({"Dispatch_Id": did, "Kernel_Name": kn, "Counter_Name": c,
+                             "Counter_Value": v})
+    r = _run(["--pmc-summary", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "q"),
+              "--workload", "c5"])
+    assert r.returncode == 0, r.stderr
+    # medians: 100 waves, 26500 VALU -> 265.0 per wave; 250 / 1000 busy
+    assert "| tk::k_filter<2> | 100 | 265.0 | 5.0 | 3.0 | 2.0 | 0.250 |" in r.stdout
