@@ -15,6 +15,8 @@ Extra modes (measurement plumbing, not part of the timed line):
                               run (A), the WRITE_SIZE run (B) and optionally
                               an instruction-mix run (C, SQ counters) of
                               --workload and print the summary for profiles/
+    --trace-summary D         per-kernel durations from a rocprofv3 kernel trace
+                              of a bench run (directory D) for profiles/
     --calibrate W1,W2,...     measure the whole call over the tuned policy's
                               grid of sample sizes on each workload and fit
                               the cost ratio tau_B / tau_A of Eq. 13
@@ -577,6 +579,51 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+def trace_summary(args):
+    """Per-kernel durations of the top-k calls of one bench run under
+    rocprofv3 --kernel-trace (the CSV under TRACE_DIR): the warm-up, timed
+    and first graph-replayed calls, all on the default plan.  A call starts
+    at its first kernel (the sampler, a caller-given threshold's set-up, the
+    exact route's set-up or the one-workgroup route)."""
+    files = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {args.trace_summary}")
+    with open(files[0]) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+    ks = [(_short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    ks = [k for k in ks if k[0].startswith("tk::") and "k_stream_read" not in k[0]]
+    firsts = ("tk::k_sample", "tk::k_force_tau", "tk::k_setup_exact", "tk::k_exact_small")
+    starts = [i for i, k in enumerate(ks) if k[0].startswith(firsts)]
+    calls = [ks[s:(starts[j + 1] if j + 1 < len(starts) else len(ks))] for j, s in enumerate(starts)]
+    sel = calls[:args.warmup + 2 * args.steps]
+    per, spans = {}, []
+    for c in sel:
+        spans.append((c[-1][2] - c[0][1]) / 1e3)
+        for name, a, b in c:
+            per.setdefault(name, []).append((b - a) / 1e3)
+    cfg, k, desc = WORKLOADS[args.workload]
+    out = [f"rocprofv3 kernel trace, workload {args.workload}: {desc}", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; REPO = the repository root):",
+           f"  rocprofv3 --kernel-trace --stats --output-format csv -d OUT -o run -- python3 REPO/bench.py "
+           f"--steps {args.steps} --warmup {args.warmup} --workload {args.workload} --no-cpu-baseline "
+           f"--fallback-calls 3",
+           f"  python3 REPO/bench.py --trace-summary OUT --steps {args.steps} --warmup {args.warmup} "
+           f"--workload {args.workload}", "",
+           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
+           f"Statistics over the first {len(sel)} top-k calls of that run (warm-up, timed and "
+           "graph-replayed calls: the default plan); the later calls of the run (stage timing, "
+           "fallback-rate policies, forced exact route) are left out.", "",
+           "| kernel | launches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {name} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+                   f"{min(v):.2f} | {max(v):.2f} |")
+    if spans:
+        out.append(f"| whole call (first kernel start to last kernel end) | {len(spans)} | "
+                   f"{statistics.mean(spans):.2f} | {statistics.median(spans):.2f} | "
+                   f"{min(spans):.2f} | {max(spans):.2f} |")
+    print("\n".join(out))
+
+
 SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_BRANCH",
                "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
 
@@ -713,9 +760,13 @@ def main():
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="FETCH_DIR WRITE_DIR [SQ_DIR]")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.gpus != 1:
         print("bench.py: this engine runs on one GPU; --gpus must be 1", file=sys.stderr)

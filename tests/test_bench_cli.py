@@ -87,3 +87,30 @@ def test_pmc_summary_instruction_mix(tmp_path):
     assert r.returncode == 0, r.stderr
     # medians: 100 waves, 26500 VALU -> 265.0 per wave; 250 / 1000 busy
     assert "| tk::k_filter<2> | 100 | 265.0 | 5.0 | 3.0 | 2.0 | 0.250 |" in r.stdout
+
+
+def test_trace_summary_splits_calls(tmp_path):
+    # two calls of three kernels each (sample, filter, finish), then a
+    # third call beyond warm-up + 2 x steps that must be left out
+    import csv
+    d = tmp_path / "t" / "host"
+    d.mkdir(parents=True)
+    rows, did, t = [], 0, 1000
+    for call in range(3):
+        for kn, dur in (("void tk::k_sample<1>(...)", 5000), ("void tk::k_filter<1>(...)", 150000 + call),
+                        ("void tk::k_finish<1>(...)", 10000)):
+            did += 1
+            rows.append({"Dispatch_Id": did, "Kernel_Name": kn, "Start_Timestamp": t,
+                         "End_Timestamp": t + dur})
+            t += dur + 1000
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        wr.writeheader()
+        wr.writerows(rows)
+    r = _run(["--trace-summary", str(tmp_path / "t"), "--steps", "1", "--warmup", "0",
+              "--workload", "c3k64"])
+    assert r.returncode == 0, r.stderr
+    assert "| tk::k_filter<1> | 2 | 150.00 | 150.00 | 150.00 | 150.00 |" in r.stdout
+    assert "| tk::k_sample<1> | 2 | 5.00 | 5.00 | 5.00 | 5.00 |" in r.stdout
+    # whole call: 5 + 1 + 150 + 1 + 10 us
+    assert "| whole call (first kernel start to last kernel end) | 2 | 167.00" in r.stdout
