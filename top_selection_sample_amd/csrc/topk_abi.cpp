@@ -236,7 +236,8 @@ int topk_run(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, 
     a.shist = reinterpret_cast<uint32_t*>(ws + p.off_shist);
     a.cbuf = reinterpret_cast<uint64_t*>(ws + p.off_cbuf);
     a.aux = reinterpret_cast<uint64_t*>(ws + p.off_aux);
-    a.lk = reinterpret_cast<uint32_t*>(ws + p.off_lk);
+    a.lkc = reinterpret_cast<uint32_t*>(ws + p.off_lkc);
+    a.lks = reinterpret_cast<uint64_t*>(ws + p.off_lks);
     a.rctr = reinterpret_cast<tk::RowCtr*>(ws + p.off_rctr);
     const uint64_t ctr = g_calls.fetch_add(1, std::memory_order_relaxed);
     a.seed = (params && params->use_seed) ? params->seed

@@ -16,7 +16,7 @@
 //                  failed rows, in one persistent launch
 //   k_exact_small  small rows: the whole exact selection in one workgroup
 //   k_tile_sort / k_merge / k_output   large k: sort all candidates
-//   k_lk_hist / k_lk_scatter / k_lk_sort  large k: bucket sort
+//   k_lk_chunk / k_lk_sort  large k: bucket sort (chunk step, window sort)
 //   k_stream_read  measurement aid: the filter's read pattern alone
 //   k_fill_zero / k_scatter_winners   the BatchTopK consumer
 //
@@ -118,7 +118,8 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
                      a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
                      a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
-                     p.W, small_k, mode, a.out_values, a.out_idx, a.lk, bl, lk_flags, a.spin_limit);
+                     p.W, small_k, mode, a.out_values, a.out_idx, a.lkc, bl, lk_flags,
+                     a.spin_limit);
   return hipGetLastError();
 }
 
@@ -138,19 +139,18 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     if (a.mark) a.mark(a.mark_ctx, stage, begin, s);
   };
 
-  uint32_t* lk_zero = bucket_sort ? a.lk : nullptr;   // large k: zeroed by the call's first kernel
   if (p.path == PLAN_EXACT_SMALL) {
     mark(STAGE_EXACT, 1);
     TK_DISPATCH(dt, k_exact_small, row_grid, dim3(SEL_THREADS), 0, s, a.values, n, a.states,
                 a.cbuf, cap, k, B, W, (uint32_t)(p.small_k ? 1 : 0), a.out_values, a.out_idx,
-                a.call, a.hdr, p.sig, lk_zero, rows);
+                a.call, a.hdr, p.sig);
     mark(STAGE_EXACT, 0);
   } else {
     if (p.path == PLAN_SAMPLED && p.force_tau) {
       // the caller's threshold: no sampler, no threshold select
       mark(STAGE_SAMPLE, 1);
-      hipLaunchKernelGGL(k_force_tau, dim3(8, rows), dim3(SAMPLE_THREADS), 0, s, a.states, a.rctr,
-                         a.call, a.hdr, p.sig, a.tau_key, lk_zero, rows);
+      hipLaunchKernelGGL(k_force_tau, dim3(1, rows), dim3(SAMPLE_THREADS), 0, s, a.states, a.rctr,
+                         a.call, a.hdr, p.sig, a.tau_key);
       mark(STAGE_SAMPLE, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
@@ -170,7 +170,6 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
                   (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
                   (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr, a.call, a.hdr, p.sig,
-                  lk_zero, rows,
                   (uint32_t)((p.t <= 8 && ns <= 4 * FILTER_THREADS) ? TAU_FILTER_LISTS
                                                                     : TAU_FILTER_RADIX));
       mark(STAGE_SAMPLE, 0);
@@ -225,12 +224,11 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
     mark(STAGE_SORT, 1);
     const dim3 hg((cap + LK_CHUNK - 1) / LK_CHUNK, rows);
     if (!hist_done)
-      hipLaunchKernelGGL(k_lk_hist, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, cap, B, bl, a.lk);
-    hipLaunchKernelGGL(k_lk_scatter, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, a.aux, cap, k,
-                       B, bl, a.lk, rows);
+      hipLaunchKernelGGL(k_lk_chunk, hg, dim3(LK_THREADS), 0, s, a.states, a.cbuf, cap, B, bl,
+                         a.lkc);
     const dim3 sgr((k + LK_WIN - 1) / LK_WIN, rows);
-    TK_DISPATCH(dt, k_lk_sort, sgr, dim3(LK_THREADS), 0, s, a.values, n, a.states, a.call, a.aux,
-                a.cbuf, cap, k, B, bl, a.lk, rows, a.out_values, a.out_idx);
+    TK_DISPATCH(dt, k_lk_sort, sgr, dim3(LK_THREADS), 0, s, a.values, n, a.states, a.call, a.cbuf,
+                a.aux, a.lks, cap, k, B, bl, a.lkc, a.out_values, a.out_idx);
     mark(STAGE_SORT, 0);
   } else if (!p.small_k) {
     // capacities beyond the bucket sort's: tile sort and pairwise merges

@@ -16,8 +16,9 @@ enum : int { PLAN_SAMPLED = 0, PLAN_EXACT = 1, PLAN_EXACT_SMALL = 2 };
 
 constexpr int64_t KSMALL = 4096;            // largest k sorted inside one workgroup
 constexpr int64_t LK_CAP_MAX = int64_t(1) << 21;  // large k: bucket sort up to this capacity
-constexpr uint32_t LK_HIST_BINS = 4096;     // large k: bucket-sort histogram bins per row
-constexpr size_t LK_WORDS_PER_ROW = 4096 + 4096 + 4100 + 2 * 2048;   // its workspace (u32)
+constexpr uint32_t LK_RANKS = 4096;         // large k: buckets of the bucket sort
+constexpr uint32_t LK_CSTRIDE = 4096 + 64;   // words per chunk: prefix counts, then every 64th
+constexpr int64_t LK_CHUNK_CANDS = 4096;    // candidates per chunk of the bucket sort
 constexpr int64_t EXACT_SMALL_MAX = 1 << 18; // rows this short run in one workgroup
 
 struct Plan {
@@ -33,7 +34,7 @@ struct Plan {
   bool force_tau = false;   // the caller gives the threshold: no sampler
   // workspace layout (byte offsets; the header is at 0)
   uint64_t sig = 0;         // layout signature (never 0)
-  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lk = 0, off_rctr = 0, total = 0;
+  size_t off_states = 0, off_call = 0, off_flag = 0, off_ghist = 0, off_skeys = 0, off_shist = 0, off_cbuf = 0, off_aux = 0, off_lkc = 0, off_lks = 0, off_rctr = 0, total = 0;
 };
 
 // Pipeline stages that can be bracketed by timing events.
@@ -67,7 +68,8 @@ struct LaunchArgs {
   uint32_t* shist;
   uint64_t* cbuf;
   uint64_t* aux;     // large k: merge buffer; sampled route: tie region (rows x cap)
-  uint32_t* lk;      // large-k bucket sort: histograms, fill counters, bucket starts
+  uint32_t* lkc;     // large-k bucket sort: per chunk, its prefix count by rank
+  uint64_t* lks;     // large-k bucket sort: split scratch (rows x cap)
   uint64_t seed;
   hipStream_t stream;
 };

@@ -120,36 +120,47 @@ __device__ __forceinline__ RowGeom row_geom(const void* values, uint32_t n, uint
 //     v = (key - lo) << bl | (low bl bits of the inverted index)
 // (bl = index bits that vary, 2^bl >= n) orders the candidates exactly as
 // their composites do, with no constant bits in between.  Its top 12 bits
-// are the bucket:
-//   k_lk_hist     bucket histogram (one LDS histogram per 4096 candidates)
-//   k_lk_scatter  bucket starts (descending order), then every candidate of
-//                 a bucket that starts below k goes to its bucket in aux
-//   k_lk_sort     one workgroup per LK_WIN output positions sorts the buckets
-//                 starting there in LDS and writes the winners directly; a
-//                 bucket too large for LDS is split further in the
-//                 workgroup (11-bit digits below the common prefix of its
-//                 smallest and largest value, through global scratch).
-// Workspace lk (u32): [rows][4096] histogram, [rows][4096] fill counters
-// (both zero between calls), [rows][LK_STRIDE] bucket starts by rank
-// (rank r = 4095 - bucket, so starts ascend with r; entry 4096 = the total),
-// [rows][2][LK_MAXWIN] per sort window the first and last rank of the
-// non-empty buckets starting in it (first = ~0: none).
+// are the bucket, and its rank r = 4095 - bucket (ranks ascend as buckets
+// descend, so the output is the buckets in rank order):
+//   chunk step    (lk_sort_chunk: in k_finish, in k_lk_chunk for rows that
+//                 never pass through it) per 4096 candidates: the chunk
+//                 rewritten in place grouped by rank, with its prefix count
+//                 per rank (LDS counting sort; no global atomics)
+//   k_lk_sort     one workgroup per LK_WIN output positions: the bucket
+//                 start of rank r is the sum over the chunks of their prefix
+//                 counts at r; a search over r finds the ranks whose buckets
+//                 start in the window, their candidates are gathered from
+//                 every chunk (each chunk holds them as one run), sorted in
+//                 LDS and written as winners; a bucket too large for LDS is
+//                 split further in the workgroup (11-bit digits below the
+//                 common prefix of its smallest and largest value, through
+//                 the split scratch).
+// A global bucket histogram built with atomics measured about 10 us slower
+// to read back in the next kernel (2^28 bf16, k = 131072: 166k atomics on
+// 4096 words) than data written with plain stores, however its words were
+// spread over lines or channels; the sums over the chunks avoid it.
+// Workspace: lkc (u32) [rows][chunks][4096] the chunks' prefix counts by
+// rank; lks (u64) [rows][cap] the split scratch.
 // ======================================================================
 constexpr uint32_t LK_BITS = 12;
 constexpr uint32_t LK_BINS = 1u << LK_BITS;
-static_assert(LK_BINS == LK_HIST_BINS, "the call prologue zeroes LK_HIST_BINS words per row");
-constexpr uint32_t LK_STRIDE = LK_BINS + 4;
+static_assert(LK_BINS == LK_RANKS && LK_CSTRIDE == LK_BINS + 64,
+              "per chunk: LK_BINS prefix counts, then every 64th of them");
 constexpr uint32_t LK_THREADS = 1024;
-constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per histogram / scatter workgroup
+constexpr uint32_t LK_CHUNK = 4 * LK_THREADS;   // candidates per chunk step
 constexpr uint32_t LK_WIN = 1024;               // output positions per sort workgroup
 constexpr uint32_t LK_LCAP = 2048;              // largest range sorted in LDS
 constexpr uint32_t LK_STACK = 1024;             // pending oversized ranges per workgroup
-constexpr uint32_t LK_MAXWIN = (uint32_t)(LK_CAP_MAX / LK_WIN);
-static_assert(LK_WORDS_PER_ROW == 2 * LK_BINS + LK_STRIDE + 2 * LK_MAXWIN, "workspace layout");
+constexpr uint32_t LK_MAXCH = (uint32_t)(LK_CAP_MAX / LK_CHUNK);   // chunks of a row at most
 static_assert((int64_t)LK_STACK * LK_LCAP >= LK_CAP_MAX,
               "oversized ranges are disjoint and larger than LK_LCAP, so at most "
               "LK_CAP_MAX / LK_LCAP of them are ever pending");
 static_assert(LK_LCAP >= 2 * LK_WIN, "a window's small buckets fit one LDS sort");
+
+// Chunks of LK_CHUNK candidates in a row's buffer of capacity cap.
+__device__ __forceinline__ uint32_t lk_maxch(uint32_t cap) { return (cap + LK_CHUNK - 1) / LK_CHUNK; }
+static_assert(LK_BINS == 4 * LK_THREADS && LK_CHUNK == 4 * LK_THREADS && LK_CHUNK == LK_CHUNK_CANDS,
+              "a chunk step: four candidates and four ranks per thread");
 
 struct LkDigit {
   uint32_t B, bl, lo, shift;
@@ -183,28 +194,66 @@ __device__ __forceinline__ LkDigit lk_digit_of(const RowState& st, uint32_t B, u
   return lk_digit(st.thr_key, st.kmax, B, bl);
 }
 
-// One LK_CHUNK of a row's candidates into the row's bucket histogram (lk):
-// an LDS histogram, then one global atomic per non-empty bucket.  Candidate
-// i is cb[i] below G and tb[i - G] from G on (the tie region, for a row
-// whose ties join its candidates before they are copied over).  Every
-// thread of the workgroup calls it; h: LK_BINS words of LDS.
-__device__ void lk_hist_chunk(const uint64_t* __restrict__ cb, const uint64_t* __restrict__ tb,
+// One LK_CHUNK of a row's candidates, [base, base + len) with len =
+// min(LK_CHUNK, R - base): an LDS histogram of its buckets, then the chunk
+// written back to out[base, base + len) grouped by rank (rank r = LK_BINS -
+// 1 - bucket: ranks ascend as buckets descend), with pre[r] = the number of
+// the chunk's candidates of ranks below r (LK_BINS words) and pre[LK_BINS +
+// m] = pre[64 m] (64 words, for the window search).  Candidate i is cb[i] below G and tb[i - G] from G on (the tie
+// region, for a sampled row whose ties were never copied over).  out may be
+// cb: the workgroup reads its chunk before it writes it, and no other
+// workgroup touches [base, base + len).  Every thread of the workgroup
+// (LK_CHUNK / 4 of them) calls it; h: LK_BINS + 16 words of LDS, s_sorted:
+// LK_CHUNK composites of LDS.
+__device__ void lk_sort_chunk(const uint64_t* __restrict__ cb, const uint64_t* __restrict__ tb,
                               uint32_t G, uint32_t R, uint32_t base, const LkDigit& g,
-                              uint32_t* __restrict__ gh, uint32_t* h) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+                              uint64_t* out, uint32_t* __restrict__ pre, uint32_t* h,
+                              uint64_t* s_sorted) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x, lane = tid & 63u, w = tid >> 6;
+  uint32_t* s_wsum = h + LK_BINS;
   for (uint32_t i = tid; i < LK_BINS; i += nt) h[i] = 0;
   uint64_t c[4];
+  uint32_t bk[4];
+  bool ok[4];
 #pragma unroll
   for (uint32_t j = 0; j < 4; ++j) {
     const uint32_t i = base + j * nt + tid;
-    c[j] = i < R ? (i < G ? cb[i] : tb[i - G]) : 0ull;
+    ok[j] = i < R;
+    c[j] = ok[j] ? (i < G ? cb[i] : tb[i - G]) : 0ull;
   }
   __syncthreads();
 #pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) hist_add(h, g(c[j]), base + j * nt + tid < R);
+  for (uint32_t j = 0; j < 4; ++j) {
+    bk[j] = ok[j] ? g(c[j]) : 0u;
+    hist_add(h, bk[j], ok[j]);
+  }
   __syncthreads();
-  for (uint32_t i = tid; i < LK_BINS; i += nt)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  // ranks 4 tid .. 4 tid + 3: their exclusive prefix in rank order
+  uint32_t hv[4], sum = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    hv[j] = h[LK_BINS - 1 - (4 * tid + j)];
+    sum += hv[j];
+  }
+  const uint32_t incl = wave_incl_sum(sum);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();   // (also: every count read before the counts become cursors)
+  uint32_t run = incl - sum;
+  for (uint32_t i = 0; i < nt / 64; ++i) run += i < w ? s_wsum[i] : 0u;
+  if ((tid & 15u) == 0) pre[LK_BINS + (tid >> 4)] = run;   // rank 4 tid = 64 (tid / 16)
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    pre[4 * tid + j] = run;
+    h[LK_BINS - 1 - (4 * tid + j)] = run;
+    run += hv[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j)
+    if (ok[j]) s_sorted[atomicAdd(&h[bk[j]], 1u)] = c[j];
+  __syncthreads();
+  const uint32_t len = R - base < LK_CHUNK ? R - base : LK_CHUNK;
+  for (uint32_t i = tid; i < len; i += nt) out[base + i] = s_sorted[i];
   __syncthreads();
 }
 
@@ -216,8 +265,8 @@ __device__ void lk_hist_chunk(const uint64_t* __restrict__ cb, const uint64_t* _
 //    the row failed.  The common case (no failure) then needs no barrier.
 //  FIN_LISTED: an earlier kernel listed the failed rows (nflag, flagged[]).
 enum : uint32_t { FIN_SCAN = 0, FIN_LISTED = 1 };
-// k_finish builds the large-k bucket histograms of the accepted sampled rows
-// and/or of the exact route's rows (the first step of the bucket sort).
+// k_finish runs the bucket sort's chunk step for the accepted sampled rows
+// and/or for the exact route's rows (large k).
 enum : uint32_t { LK_HIST_SAMPLED = 1, LK_HIST_EXACT = 2 };
 constexpr uint32_t FIN_SCAN_ROWS = 1024;
 
@@ -232,7 +281,7 @@ __device__ __attribute__((noinline)) void reselect_row(const void* __restrict__ 
                              uint32_t row, uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k,
                              uint32_t B, uint32_t W, uint32_t small_k,
                              void* __restrict__ out_values, int64_t* __restrict__ out_idx,
-                             uint32_t* __restrict__ lk_row, uint32_t bl, uint32_t* s_hist,
+                             uint32_t* __restrict__ pre_row, uint32_t bl, uint32_t* s_hist,
                              uint32_t* s_misc, uint64_t* s_cand, uint32_t* s_keys) {
   using D = Dt<DT>;
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
@@ -279,12 +328,11 @@ __device__ __attribute__((noinline)) void reselect_row(const void* __restrict__ 
   __syncthreads();
   const uint32_t R = s_misc[4] < cap ? s_misc[4] : cap;
   const uint32_t thr_key = (uint32_t)(sel.thr >> B), kmax = s_misc[5];
-  if (lk_row) {   // the bucket histogram, rebuilt from zero
-    for (uint32_t i = tid; i < LK_BINS; i += nt) lk_row[i] = 0u;
-    __syncthreads();
+  if (pre_row) {   // the chunks grouped by rank, for the bucket sort
     const LkDigit g = lk_digit(thr_key, kmax, B, bl);
     for (uint32_t base = 0; base < R; base += LK_CHUNK)
-      lk_hist_chunk(out, out, R, R, base, g, lk_row, s_keys);
+      lk_sort_chunk(out, out, R, R, base, g, out, pre_row + (size_t)(base / LK_CHUNK) * LK_CSTRIDE,
+                    s_keys, s_cand);
   }
   if (tid == 0) {
     st->count = R;
@@ -302,7 +350,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     uint32_t* __restrict__ ghist,
     uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
     uint32_t k_eff, uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode,
-    void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lk,
+    void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lkc,
     uint32_t bl, uint32_t lk_flags, uint32_t spin_limit) {
   using D = Dt<DT>;
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
@@ -363,8 +411,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         start_exact(st, k, PATH_FALLBACK);
         flagged[slot] = r;
       }
-      // large k: this row's bucket-sort counters start at zero (the sampler
-      // zeroed them; LK_HIST_SAMPLED below skips failed rows)
+      // (large k: the chunk step below skips failed rows)
       continue;
     }
     const bool fr = pre && r == r_first;
@@ -375,7 +422,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const uint32_t verdict = sampled_verdict(G, E, k, k_eff, cap);
     const bool ties_in = verdict == V_OK_TIES || verdict == V_PARTIAL;
     if (!fr) __syncthreads();   // every thread has read the counts
-    if (ties_in) {
+    // (the bucket sort's chunk step reads them from the tie region instead)
+    const bool copy_ties = ties_in && !(lk_flags & LK_HIST_SAMPLED);
+    if (copy_ties) {
       uint64_t* dst = cbuf + (size_t)r * cap + G;
       const uint64_t* src = tbuf + (size_t)r * cap;
       for (uint32_t i = tid; i < E; i += blockDim.x) dst[i] = src[i];
@@ -391,7 +440,7 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         st->status = ST_SORT;
       }
     }
-    if (ties_in) __syncthreads();   // the copied ties are visible to every thread
+    if (copy_ties) __syncthreads();   // the copied ties are visible to every thread
     if (small_k) {
       uint32_t R = G < k ? G + E : G;
       if (R > cap) R = cap;
@@ -402,14 +451,15 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
                          reinterpret_cast<uint64_t*>(s_keys));
     }
   }
-  // Large k: the bucket histograms of the accepted sampled rows (the first
-  // step of the bucket sort), LK_CHUNK candidates per workgroup and step.
-  // Every count read here is final: the filter's above-tau count and tie
-  // count, tau and the largest key (the row's owner rewrites only the
-  // RowState count, and copies the ties later; they are read from the tie
-  // region).
+  // Large k: the bucket histograms of the accepted sampled rows and their
+  // chunks grouped by rank (the first step of the bucket sort), LK_CHUNK
+  // candidates per workgroup and step.  Every count read here is final: the
+  // filter's above-tau count and tie count, tau and the largest key (the
+  // row's owner rewrites only the RowState count).  A row's ties are read
+  // from the tie region: for large k they are never copied into the
+  // candidate buffer, whose chunks are rewritten here.
   if (lk_flags & LK_HIST_SAMPLED) {
-    const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
+    const uint32_t maxch = lk_maxch(cap);
     const uint64_t npairs = (uint64_t)rows * maxch;
     for (uint64_t q = blockIdx.x; q < npairs; q += G) {
       const uint32_t r = (uint32_t)(q / maxch), c = (uint32_t)(q % maxch);
@@ -420,8 +470,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
       if (R > cap) R = cap;
       if ((uint64_t)c * LK_CHUNK >= R) continue;
       const LkDigit g = lk_digit(states[r].tau_key, rctr[r].kmax, B, bl);
-      lk_hist_chunk(cbuf + (size_t)r * cap, tbuf + (size_t)r * cap, Ga, R, c * LK_CHUNK, g,
-                    lk + (size_t)r * LK_BINS, s_keys);
+      lk_sort_chunk(cbuf + (size_t)r * cap, tbuf + (size_t)r * cap, Ga, R, c * LK_CHUNK, g,
+                    cbuf + (size_t)r * cap, lkc + ((size_t)r * maxch + c) * LK_CSTRIDE, s_keys,
+                    s_cand);
     }
   }
   if (nf == 0) return;                        // the common case: nothing more to do
@@ -440,18 +491,6 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   // per-call scratch: the listed rows' exact-route histograms start at zero
   for (uint32_t f = blockIdx.x; f < nf; f += G)
     if (tid < 256) ghist[(size_t)f * 256 + tid] = 0u;
-  // (FIN_LISTED from the exact route's set-up: the bucket-sort counters of
-  // the rows too; FIN_SCAN rows had theirs zeroed by the sampler)
-  if ((lk_flags & LK_HIST_EXACT) && mode == FIN_LISTED) {
-    for (uint32_t f = blockIdx.x; f < nf; f += G) {
-      const uint32_t row = listed(f);
-      if (row == 0xFFFFFFFFu) continue;
-      for (uint32_t i = tid; i < LK_BINS; i += blockDim.x) {
-        lk[(size_t)row * LK_BINS + i] = 0u;
-        lk[(size_t)(rows + row) * LK_BINS + i] = 0u;
-      }
-    }
-  }
   bool ok = grid_barrier(cs, G, spin_limit, &s_flag);   // the listed rows' states are visible to all
 
   uint32_t ipr = (n / D::VEC + EX_ITEM_VEC - 1) / EX_ITEM_VEC;   // items per row
@@ -681,10 +720,10 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         states[row].status = ST_SORT;
       }
     }
-    // Large k: the exact route's rows into their bucket histograms (their
-    // count, threshold and largest key were final at the last grid barrier)
+    // Large k: the chunk step for the exact route's rows (their count,
+    // threshold and largest key were final at the last grid barrier)
     if (!small_k && (lk_flags & LK_HIST_EXACT)) {
-      const uint32_t maxch = (cap + LK_CHUNK - 1) / LK_CHUNK;
+      const uint32_t maxch = lk_maxch(cap);
       const uint64_t npairs = (uint64_t)nf * maxch;
       for (uint64_t q = blockIdx.x; q < npairs; q += G) {
         const uint32_t row = listed((uint32_t)(q / maxch)), c = (uint32_t)(q % maxch);
@@ -692,8 +731,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
         const RowState st = states[row];
         const uint32_t R = st.count < cap ? st.count : cap;
         if ((uint64_t)c * LK_CHUNK >= R) continue;
-        lk_hist_chunk(cbuf + (size_t)row * cap, cbuf + (size_t)row * cap, R, R, c * LK_CHUNK,
-                      lk_digit_of(st, B, bl), lk + (size_t)row * LK_BINS, s_keys);
+        lk_sort_chunk(cbuf + (size_t)row * cap, cbuf + (size_t)row * cap, R, R, c * LK_CHUNK,
+                      lk_digit_of(st, B, bl), cbuf + (size_t)row * cap,
+                      lkc + ((size_t)row * maxch + c) * LK_CSTRIDE, s_keys, s_cand);
       }
     }
   }
@@ -716,7 +756,9 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
     const uint32_t row = listed(f);
     if (row == 0xFFFFFFFFu) continue;
     reselect_row<DT>(values, n, states + row, row, cbuf, cap, k, B, W, small_k, out_values,
-                     out_idx, (lk_flags & LK_HIST_EXACT) ? lk + (size_t)row * LK_BINS : nullptr,
+                     out_idx,
+                     (lk_flags & LK_HIST_EXACT) ? lkc + (size_t)row * lk_maxch(cap) * LK_CSTRIDE
+                                                : nullptr,
                      bl, s_hist, s_misc, s_cand, s_keys);
   }
 }

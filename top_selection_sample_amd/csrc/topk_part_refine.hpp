@@ -569,7 +569,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
     const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
     uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
     uint32_t small_k, void* __restrict__ out_values, int64_t* __restrict__ out_idx,
-    CallState* cs, WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows) {
+    CallState* cs, WsHeader* hdr, uint64_t sig) {
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_misc[8];
   __shared__ __align__(16) uint64_t s_cand[CAND_CAP];
@@ -577,16 +577,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_exact_small(
   const uint32_t row = blockIdx.x;
   RowState* st = states + row;
   // the call's set-up (this route's only kernel before the large-k sort):
-  // the call record, the stamp, and this row's bucket-sort counters
+  // the call record and the stamp
   if (row == 0 && threadIdx.x == 0) {
     reset_call(cs);
     stamp_invalidate(hdr, sig);
-  }
-  if (lk) {
-    for (uint32_t i = threadIdx.x; i < LK_HIST_BINS; i += blockDim.x) {
-      lk[(size_t)row * LK_HIST_BINS + i] = 0u;
-      lk[(size_t)(rows + row) * LK_HIST_BINS + i] = 0u;
-    }
   }
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
   auto finish_row = [&]() {

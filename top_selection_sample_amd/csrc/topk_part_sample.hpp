@@ -230,23 +230,11 @@ __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint
 }
 
 // The first kernel of a sampled call also does the call's set-up: the call
-// record to zero, the workspace stamp cleared unless it is this layout's, and
-// (large k) the bucket-sort histograms and fill counters of every row to zero,
-// rows * 2 * LK_BINS words shared out over the grid.
-__device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint64_t sig,
-                                              uint32_t* lk, uint32_t rows) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  const uint32_t nb = gridDim.x * gridDim.y;
-  const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
-  if (b == 0 && tid == 0) {
+// record to zero, and the workspace stamp cleared unless it is this layout's.
+__device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint64_t sig) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     reset_call(cs);
     stamp_invalidate(hdr, sig);
-  }
-  if (lk) {
-    const size_t words = (size_t)rows * 2 * LK_HIST_BINS;
-    const size_t per = (words + nb - 1) / nb;
-    const size_t w0 = (size_t)b * per, w1 = w0 + per < words ? w0 + per : words;
-    for (size_t i = w0 + tid; i < w1; i += nt) lk[i] = 0u;
   }
 }
 
@@ -261,12 +249,12 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
     uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
     uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs,
-    WsHeader* hdr, uint64_t sig, uint32_t* __restrict__ lk, uint32_t rows, uint32_t route) {
+    WsHeader* hdr, uint64_t sig, uint32_t route) {
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT], s_m[2 * TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
   const bool gh_ok = !lists && hdr->stamp == sig;   // read before the prologue may clear it
-  call_prologue(cs, hdr, sig, lk, rows);
+  call_prologue(cs, hdr, sig);
   // the filter selects tau itself: start the row here (tau set there)
   if (states && blockIdx.x == 0 && tid == 0)
     start_sampled_row(states + row, rctr + row, 0u, route);
@@ -455,10 +443,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tau(const uint32_t* __restrict_
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_force_tau(RowState* __restrict__ states,
                                                               RowCtr* __restrict__ rctr,
                                                               CallState* cs, WsHeader* hdr,
-                                                              uint64_t sig, uint32_t tau,
-                                                              uint32_t* __restrict__ lk,
-                                                              uint32_t rows) {
-  call_prologue(cs, hdr, sig, lk, rows);
+                                                              uint64_t sig, uint32_t tau) {
+  call_prologue(cs, hdr, sig);
   if (blockIdx.x == 0 && threadIdx.x == 0)
     start_sampled_row(states + blockIdx.y, rctr + blockIdx.y, tau, TAU_FORCED);
 }

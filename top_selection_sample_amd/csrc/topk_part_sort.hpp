@@ -103,138 +103,36 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ values,
     default: hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__); break;         \
   }
 
-__global__ __launch_bounds__(LK_THREADS) void k_lk_hist(const RowState* __restrict__ states,
-                                                        const uint64_t* __restrict__ cbuf,
-                                                        uint32_t cap, uint32_t B, uint32_t bl,
-                                                        uint32_t* __restrict__ lk) {
-  __shared__ uint32_t h[LK_BINS];
-  const uint32_t row = blockIdx.y, tid = threadIdx.x;
+// The chunk step of the bucket sort for rows that never pass through the
+// finish kernel (the one-workgroup route's large-k rows): one chunk per
+// workgroup.
+__global__ __launch_bounds__(LK_THREADS) void k_lk_chunk(const RowState* __restrict__ states,
+                                                         uint64_t* __restrict__ cbuf, uint32_t cap,
+                                                         uint32_t B, uint32_t bl,
+                                                         uint32_t* __restrict__ lkc) {
+  __shared__ uint32_t h[LK_BINS + 16];
+  __shared__ uint64_t s_sorted[LK_CHUNK];
+  const uint32_t row = blockIdx.y;
   const RowState st = states[row];
   const uint32_t R = st.count < cap ? st.count : cap;
   const uint32_t base = blockIdx.x * LK_CHUNK;
   if (st.status != ST_SORT || base >= R) return;
-  const LkDigit g = lk_digit_of(st, B, bl);
-  for (uint32_t i = tid; i < LK_BINS; i += LK_THREADS) h[i] = 0;
-  __syncthreads();
-  const uint64_t* p = cbuf + (size_t)row * cap;
-  uint64_t c[4];
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const uint32_t i = base + j * LK_THREADS + tid;
-    c[j] = i < R ? p[i] : 0ull;
-  }
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j)
-    if (base + j * LK_THREADS + tid < R) atomicAdd(&h[g(c[j])], 1u);
-  __syncthreads();
-  uint32_t* gh = lk + (size_t)row * LK_BINS;
-  for (uint32_t i = tid; i < LK_BINS; i += LK_THREADS)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  uint64_t* cb = cbuf + (size_t)row * cap;
+  lk_sort_chunk(cb, cb, R, R, base, lk_digit_of(st, B, bl), cb,
+                lkc + ((size_t)row * lk_maxch(cap) + blockIdx.x) * LK_CSTRIDE, h, s_sorted);
 }
 
-__global__ __launch_bounds__(LK_THREADS) void k_lk_scatter(const RowState* __restrict__ states,
-                                                           const uint64_t* __restrict__ cbuf,
-                                                           uint64_t* __restrict__ aux, uint32_t cap,
-                                                           uint32_t k, uint32_t B, uint32_t bl,
-                                                           uint32_t* __restrict__ lk,
-                                                           uint32_t rows) {
-  __shared__ uint32_t s_start[LK_BINS];   // by rank
-  __shared__ uint32_t s_cnt[LK_BINS];     // this workgroup's count, then its base, per rank
-  __shared__ uint32_t s_wsum[LK_THREADS / 64];
-  __shared__ uint32_t s_win[2 * LK_MAXWIN];
-  const uint32_t row = blockIdx.y, tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
-  const RowState st = states[row];
-  const uint32_t R = st.count < cap ? st.count : cap;
-  const uint32_t base = blockIdx.x * LK_CHUNK;
-  if (st.status != ST_SORT || base >= R) return;
-  const LkDigit g = lk_digit_of(st, B, bl);
-  const uint32_t* gh = lk + (size_t)row * LK_BINS;
-  uint32_t* gfill = lk + (size_t)(rows + row) * LK_BINS;
-  uint32_t* gstart = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
-  // this workgroup's candidates, loaded first so the histogram read overlaps
-  const uint64_t* p = cbuf + (size_t)row * cap;
-  uint64_t c[4];
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const uint32_t i = base + j * LK_THREADS + tid;
-    c[j] = i < R ? p[i] : 0ull;
-  }
-
-  // bucket starts in descending bucket order: thread t owns ranks 4t..4t+3
-  uint32_t hv[4], sum = 0;
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    hv[j] = gh[LK_BINS - 1 - (4 * tid + j)];
-    sum += hv[j];
-  }
-  const uint32_t incl = wave_incl_sum(sum);
-  if (lane == 63) s_wsum[w] = incl;
-  __syncthreads();
-  uint32_t run = incl - sum;
-#pragma unroll
-  for (uint32_t i = 0; i < LK_THREADS / 64; ++i) run += i < w ? s_wsum[i] : 0u;
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    s_start[4 * tid + j] = run;
-    s_cnt[4 * tid + j] = 0;
-    if (blockIdx.x == 0) gstart[4 * tid + j] = run;
-    run += hv[j];
-  }
-  if (blockIdx.x == 0 && tid == LK_THREADS - 1) gstart[LK_BINS] = run;
-  if (blockIdx.x == 0)
-    for (uint32_t i = tid; i < 2 * LK_MAXWIN; i += LK_THREADS) s_win[i] = i < LK_MAXWIN ? ~0u : 0u;
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    // each sort window: first and last non-empty bucket starting in it
-    const uint32_t nwin = (k + LK_WIN - 1) / LK_WIN;
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) {
-      const uint32_t rr = 4 * tid + j, b0 = s_start[rr];
-      if (hv[j] && b0 < k) {
-        atomicMin(&s_win[b0 / LK_WIN], rr);
-        atomicMax(&s_win[LK_MAXWIN + b0 / LK_WIN], rr);
-      }
-    }
-    __syncthreads();
-    uint32_t* gwin = lk + (size_t)rows * (2 * LK_BINS + LK_STRIDE) + (size_t)row * 2 * LK_MAXWIN;
-    for (uint32_t i = tid; i < nwin; i += LK_THREADS) {
-      gwin[i] = s_win[i];
-      gwin[LK_MAXWIN + i] = s_win[LK_MAXWIN + i];
-    }
-  }
-
-  // this workgroup's candidates: local rank inside its bucket
-  uint32_t r[4], lr[4];
-  bool need[4];
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const uint32_t i = base + j * LK_THREADS + tid;
-    const bool ok = i < R;
-    r[j] = ok ? LK_BINS - 1 - g(c[j]) : 0u;
-    need[j] = ok && s_start[r[j]] < k;
-    lr[j] = need[j] ? atomicAdd(&s_cnt[r[j]], 1u) : 0u;
-  }
-  __syncthreads();
-  // one reservation per bucket and workgroup
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const uint32_t rr = 4 * tid + j;
-    const uint32_t cnt = s_cnt[rr];
-    if (cnt) s_cnt[rr] = atomicAdd(&gfill[rr], cnt);
-  }
-  __syncthreads();
-  uint64_t* a = aux + (size_t)row * cap;   // compacted values, by bucket
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j)
-    if (need[j]) a[s_start[r[j]] + s_cnt[r[j]] + lr[j]] = g.compact(c[j]);
-}
-
+// One workgroup per LK_WIN output positions of a row.  cbuf: the row's
+// candidates grouped by rank within each chunk (the chunk step), lkc their
+// prefix counts; aux: the window's candidates gathered by bucket, as v
+// values; scratch: the split's second buffer.
 template <int DT>
 __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
     const void* __restrict__ values, uint32_t n, const RowState* __restrict__ states,
-    CallState* __restrict__ cs, uint64_t* __restrict__ aux, uint64_t* __restrict__ scratch,
-    uint32_t cap, uint32_t k, uint32_t B, uint32_t bl, uint32_t* __restrict__ lk, uint32_t rows,
-    void* __restrict__ out_values, int64_t* __restrict__ out_idx) {
+    CallState* __restrict__ cs, const uint64_t* __restrict__ cbuf, uint64_t* __restrict__ aux,
+    uint64_t* __restrict__ scratch, uint32_t cap, uint32_t k, uint32_t B, uint32_t bl,
+    const uint32_t* __restrict__ lkc, void* __restrict__ out_values,
+    int64_t* __restrict__ out_idx) {
   __shared__ uint64_t s_a[LK_LCAP];
   __shared__ uint64_t s_b[LK_LCAP];
   __shared__ uint32_t s_hist[2048];
@@ -253,28 +151,204 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
     for (uint32_t i = (w0 > R ? w0 : R) + tid; i < w1; i += nt)
       store_pad<DT>(out_values, out_idx, (size_t)row * k + i);
   }
-  const uint32_t* gs = lk + (size_t)2 * rows * LK_BINS + (size_t)row * LK_STRIDE;
-  const uint32_t* gwin = lk + (size_t)rows * (2 * LK_BINS + LK_STRIDE) + (size_t)row * 2 * LK_MAXWIN;
-  if (blockIdx.x * LK_WIN >= k) return;
-  // the non-empty buckets that start in this window and below k
-  const uint32_t r_lo = gwin[blockIdx.x];
-  if (r_lo == ~0u) return;
-  const uint32_t r_end = gwin[LK_MAXWIN + blockIdx.x] + 1;
-
+  const uint32_t w0 = blockIdx.x * LK_WIN;
+  if (w0 >= k) return;
+  const uint32_t w1 = w0 + LK_WIN < k ? w0 + LK_WIN : k;
   const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
   uint64_t* A = aux + (size_t)row * cap;
   uint64_t* S = scratch + (size_t)row * cap;
   const LkDigit g = lk_digit_of(st, B, bl);
 
-  // sort [lo, lo + len) of src (compacted values, unique, len <= LK_LCAP) in
-  // LDS and write the output positions below k.  nb > 0: the range is the
+  // Bucket starts: start(r) = the sum over the row's chunks of their prefix
+  // counts at rank r (start(LK_BINS) = R).  The window's buckets are the
+  // ranks [rho(w0), rho(x1)), x1 = min(w1, R), with rho(x) = the least rank
+  // whose bucket starts at or after x.  Two rounds of 64 probes find each
+  // rho: every 64th rank (from the chunks' coarse copies), then the 64 ranks
+  // of the step that holds it.  Lane i holds probe i and the waves share out
+  // the chunks, so each load is 64 consecutive words of one chunk.
+  // Invariant per bound x > 0: start(lo) < x <= start(hi).
+  if (w0 >= R) return;   // (a row that keeps fewer than k: nothing starts here)
+  const uint32_t nch = (R + LK_CHUNK - 1) / LK_CHUNK, maxch = lk_maxch(cap);
+  const uint32_t* lkr = lkc + (size_t)row * maxch * LK_CSTRIDE;
+  const uint32_t x1 = w1 < R ? w1 : R;
+  constexpr uint32_t NW = LK_THREADS / 64;
+  __shared__ uint32_t s_bnd[2][4];   // per bound: lo, hi, start(lo), start(hi)
+  __shared__ uint32_t s_part[NW][64];
+  __shared__ uint32_t s_pv[2][64];
+  if (tid < 2) {
+    s_bnd[tid][0] = 0u;
+    s_bnd[tid][1] = LK_BINS;
+    s_bnd[tid][2] = 0u;
+    s_bnd[tid][3] = R;
+  }
+  auto clen = [&](uint32_t c) { return R - c * LK_CHUNK < LK_CHUNK ? R - c * LK_CHUNK : LK_CHUNK; };
+  // for bound bd, by one wave: the first probe at or above it (probes at lo
+  // + step (i + 1), their starts in s_pv[pv][i], non-decreasing in i, so the
+  // probes below the bound are a prefix; the last probe is never below it)
+  auto narrow = [&](uint32_t bd, uint32_t pv, uint32_t step) {
+    const uint32_t x = bd == 0 ? w0 : x1;
+    uint32_t i = (uint32_t)__builtin_popcountll(ballot(s_pv[pv][lane] < x));
+    if (i > 63) i = 63;
+    if (lane == 0) {
+      const uint32_t lo = s_bnd[bd][0];
+      if (i > 0) s_bnd[bd][2] = s_pv[pv][i - 1];
+      s_bnd[bd][0] = lo + step * i;
+      s_bnd[bd][1] = lo + step * (i + 1);
+      s_bnd[bd][3] = s_pv[pv][i];
+    }
+  };
+  // one lane's sum over the chunks c0, c0 + dc, ... of word `word` of each
+  // chunk (LK_BINS + 1 meaning the chunk's length), eight loads in flight at
+  // a time
+  auto chunk_sum = [&](uint32_t c0, uint32_t dc, uint32_t word) {
+    uint32_t part = 0;
+    for (uint32_t cb = c0; cb < nch; cb += 8 * dc) {
+      uint32_t v[8];
+#pragma unroll
+      for (uint32_t q = 0; q < 8; ++q) {
+        const uint32_t c = cb + q * dc;
+        v[q] = (c < nch && word <= LK_CSTRIDE - 1) ? lkr[(size_t)c * LK_CSTRIDE + word] : 0u;
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < 8; ++q) {
+        const uint32_t c = cb + q * dc;
+        if (c < nch) {
+          const uint32_t len = clen(c);
+          const uint32_t x = word <= LK_CSTRIDE - 1 ? v[q] : len;
+          part += x < len ? x : len;
+        }
+      }
+    }
+    return part;
+  };
+  {   // round 1: ranks 64 (i + 1), the same probes for both bounds
+    // (rank 64 m is word LK_BINS + m of a chunk; rank LK_BINS its length)
+    const uint32_t part = chunk_sum(w, NW, lane < 63 ? LK_BINS + lane + 1 : LK_CSTRIDE);
+    s_part[w][lane] = part;
+    __syncthreads();
+    if (w == 0) {
+      uint32_t sm = 0;
+      for (uint32_t q = 0; q < NW; ++q) sm += s_part[q][lane];
+      s_pv[0][lane] = sm;
+    }
+    __syncthreads();
+    if (w < 2) narrow(w, 0, 64);
+    __syncthreads();
+  }
+  {   // round 2: the 64 ranks after each bound's lo; wave w: bound w & 1,
+      // chunks w / 2, w / 2 + NW / 2, ...
+    const uint32_t bd = w & 1u, r = s_bnd[bd][0] + 1 + lane;   // r <= LK_BINS
+    const uint32_t part = chunk_sum(w >> 1, NW / 2, r < LK_BINS ? r : LK_CSTRIDE);
+    s_part[w][lane] = part;
+    __syncthreads();
+    if (w < 2) {
+      uint32_t sm = 0;
+      for (uint32_t q = w; q < NW; q += 2) sm += s_part[q][lane];
+      s_pv[w][lane] = sm;
+    }
+    __syncthreads();
+    if (w < 2) narrow(w, w, 1);
+    __syncthreads();
+  }
+  // rho(0) = 0 (the first window's lower bound; the search assumes x > 0)
+  const uint32_t r_lo = w0 == 0 ? 0u : s_bnd[0][1];
+  const uint32_t a0s = w0 == 0 ? 0u : s_bnd[0][3];
+  const uint32_t r_end = s_bnd[1][1], e0s = s_bnd[1][3], lasts = s_bnd[1][2];
+  if (r_lo >= r_end) return;   // no bucket starts in this window
+  const uint32_t r_last = r_end - 1;
+  // the window's candidates fit one LDS sort (the common case): gathered
+  // straight into LDS; otherwise into aux, for the split
+  const bool in_lds = e0s - a0s <= LK_LCAP;
+  __syncthreads();   // every thread has read the bounds
+
+  // Gather: chunk c holds ranks [r_lo, r_last) as one run and rank r_last
+  // right after it; the runs of the chunks in chunk order go to A[a0, last)
+  // and A[last, e0) as v values (one thread per chunk finds its runs, a
+  // prefix over the chunks places them, then every thread copies).
+  {
+    __shared__ uint32_t s_hp[LK_MAXCH + 1], s_tp[LK_MAXCH + 1], s_lo[LK_MAXCH], s_mid[LK_MAXCH];
+    __shared__ uint32_t s_ws[2 * (LK_THREADS / 64)];
+    static_assert(LK_MAXCH <= LK_THREADS, "one thread per chunk");
+    uint32_t hd = 0, tl = 0, lo = 0, mid = 0;
+    if (tid < nch) {
+      const uint32_t* pc = lkc + ((size_t)row * maxch + tid) * LK_CSTRIDE;
+      const uint32_t len = R - tid * LK_CHUNK < LK_CHUNK ? R - tid * LK_CHUNK : LK_CHUNK;
+      lo = pc[r_lo];
+      mid = pc[r_last];
+      uint32_t hi = r_end < LK_BINS ? pc[r_end] : len;
+      // (prefix counts never exceed the chunk; clamped all the same)
+      hi = hi < len ? hi : len;
+      mid = mid < hi ? mid : hi;
+      lo = lo < mid ? lo : mid;
+      hd = mid - lo;
+      tl = hi - mid;
+    }
+    const uint32_t ih = wave_incl_sum(hd), it = wave_incl_sum(tl);
+    if (lane == 63) {
+      s_ws[w] = ih;
+      s_ws[LK_THREADS / 64 + w] = it;
+    }
+    __syncthreads();
+    uint32_t ph = ih - hd, pt = it - tl;
+    for (uint32_t i = 0; i < nt / 64; ++i) {
+      ph += i < w ? s_ws[i] : 0u;
+      pt += i < w ? s_ws[LK_THREADS / 64 + i] : 0u;
+    }
+    if (tid < nch) {
+      s_hp[tid] = ph;
+      s_tp[tid] = pt;
+      s_lo[tid] = tid * LK_CHUNK + lo;
+      s_mid[tid] = tid * LK_CHUNK + mid;
+    }
+    if (tid == nch - 1) {
+      s_hp[nch] = ph + hd;
+      s_tp[nch] = pt + tl;
+    }
+    __syncthreads();
+    const uint32_t a0 = a0s, last = lasts;
+    const uint64_t* cb = cbuf + (size_t)row * cap;
+    // the chunk holding gathered element i: the last c with s_p[c] <= i
+    auto chunk_of = [&](const uint32_t* s_p, uint32_t i) {
+      uint32_t lo_c = 0, hi_c = nch;   // s_p[lo_c] <= i < s_p[hi_c]
+      while (hi_c - lo_c > 1) {
+        const uint32_t m = (lo_c + hi_c) >> 1;
+        if (s_p[m] <= i) lo_c = m;
+        else hi_c = m;
+      }
+      return lo_c;
+    };
+    // (equal to last - a0 and e0 - last when the chunks and the histogram
+    // agree, as they always do; bounded by them all the same)
+    const uint32_t e0c = e0s < cap ? e0s : cap;
+    const uint32_t H = s_hp[nch] < last - a0 ? s_hp[nch] : last - a0;
+    const uint32_t T = last < e0c ? (s_tp[nch] < e0c - last ? s_tp[nch] : e0c - last) : 0u;
+    for (uint32_t i = tid; i < H; i += nt) {
+      const uint32_t c = chunk_of(s_hp, i);
+      const uint64_t v = g.compact(cb[s_lo[c] + (i - s_hp[c])]);
+      if (in_lds) s_a[i] = v;
+      else A[a0 + i] = v;
+    }
+    for (uint32_t i = tid; i < T; i += nt) {
+      const uint32_t c = chunk_of(s_tp, i);
+      const uint64_t v = g.compact(cb[s_mid[c] + (i - s_tp[c])]);
+      if (in_lds) s_a[(last - a0) + i] = v;
+      else A[last + i] = v;
+    }
+    __syncthreads();   // the gathered values are visible to the workgroup
+  }
+
+  // sort [lo, lo + len) of src (compacted values, unique, len <= LK_LCAP; src
+  // null: they are in s_a already) in LDS and write the output positions
+  // below k.  nb > 0: the range is the
   // buckets of ranks r_last - nb + 1 .. r_last, and the sort's bins are the
   // bucket and the bits just below the bucket digit; nb = 0: bins from the
   // range's extremes.
   auto sort_out = [&](const uint64_t* src, uint32_t lo, uint32_t len, uint32_t nb,
                       uint32_t r_last) {
-    for (uint32_t i = tid; i < len; i += nt) s_a[i] = src[lo + i];
-    __syncthreads();
+    if (src) {   // (null: the range is in s_a already)
+      for (uint32_t i = tid; i < len; i += nt) s_a[i] = src[lo + i];
+      __syncthreads();
+    }
     bool ok;
     if (nb > 0 && nb <= 2048) {
       uint32_t sb = 31u - (uint32_t)__builtin_clz(2048u / nb);   // nb << sb <= 2048
@@ -320,9 +394,9 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
     }
   };
 
-  const uint32_t a0 = gs[r_lo], e0 = gs[r_end], last = gs[r_end - 1];
-  if (e0 - a0 <= LK_LCAP) {
-    sort_out(A, a0, e0 - a0, r_end - r_lo, r_end - 1);
+  const uint32_t a0 = a0s, e0 = e0s, last = lasts;
+  if (in_lds) {
+    sort_out(nullptr, a0, e0 - a0, r_end - r_lo, r_end - 1);
   } else {
     // every bucket but the last starts and ends inside the window
     if (last > a0) sort_out(A, a0, last - a0, r_end - 1 - r_lo, r_end - 2);

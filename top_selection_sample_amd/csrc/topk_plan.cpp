@@ -388,16 +388,23 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.off_aux = off;   // large k: the merge buffer; sampled route: the tie region first
   if (!p.small_k || p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * (size_t)p.cap * 8);
-  p.off_lk = off;   // large k: bucket histogram, fill counters, starts, sort windows
-  if (!p.small_k && p.cap <= LK_CAP_MAX) off = align256(off + (size_t)rows * LK_WORDS_PER_ROW * 4);
+  const bool lk = !p.small_k && p.cap <= LK_CAP_MAX;   // the bucket sort
+  p.off_lkc = off;  // large k: per chunk, its prefix count by bucket rank
+  if (lk) {
+    const size_t chunks = (size_t)((p.cap + LK_CHUNK_CANDS - 1) / LK_CHUNK_CANDS);
+    off = align256(off + (size_t)rows * chunks * LK_CSTRIDE * 4);
+  }
+  p.off_lks = off;  // large k: the split scratch
+  if (lk) off = align256(off + (size_t)rows * (size_t)p.cap * 8);
   p.off_rctr = off;   // sampled route: four 128-byte counter lines per row
   if (p.path == PLAN_SAMPLED) off = align256(off + (size_t)rows * 512);
   p.total = off;
   // layout signature: every offset, the row count and the route
   uint64_t h = 0x9E3779B97F4A7C15ull;
   const uint64_t parts[] = {p.total,    p.off_states, p.off_call, p.off_flag, p.off_ghist,
-                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux,  p.off_lk,
-                            p.off_rctr,  (uint64_t)p.rows, (uint64_t)p.path, (uint64_t)p.SP};
+                            p.off_skeys, p.off_shist, p.off_cbuf, p.off_aux,  p.off_lkc,
+                            p.off_lks,   p.off_rctr,  (uint64_t)p.rows,
+                            (uint64_t)p.path, (uint64_t)p.SP};
   for (uint64_t v : parts) h ^= v + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
   p.sig = h | 1ull;   // never 0
   *out = p;
