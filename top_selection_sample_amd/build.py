@@ -9,8 +9,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtopk_mi355x.so")
 SOURCES = ["topk_kernels.hip", "topk_plan.cpp", "topk_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -amdgpu-kernarg-preload-count: the first 14 argument words of every kernel
+# arrive in scalar registers with the launch instead of being loaded from the
+# argument block (the kernels order their arguments for it).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-Wall", "-Wno-unused-function"]
 
 

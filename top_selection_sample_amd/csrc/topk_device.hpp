@@ -127,6 +127,15 @@ static_assert(sizeof(WsHeader) == 256, "one 256-byte header");
 // and every call that does not build the sample histogram) clears it unless
 // it is already its own: the call may overwrite the region.  Racing readers
 // in the same kernel see either value, and neither equals `sig`.
+// The workgroup size a kernel is always launched with, told to the compiler:
+// blockDim.x is otherwise read from the dispatch's hidden arguments, a memory
+// round trip at the start of the kernel.
+#define assume_block_threads(N)                   \
+  do {                                            \
+    const uint32_t bd_ = blockDim.x;              \
+    __builtin_assume(bd_ == (uint32_t)(N));       \
+  } while (0)
+
 __device__ __forceinline__ void stamp_invalidate(WsHeader* h, uint64_t sig) {
   if (h->stamp != sig) h->stamp = 0;
 }

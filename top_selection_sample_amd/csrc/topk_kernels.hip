@@ -115,11 +115,12 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
     cached[dev] = cus > 0 ? cus : 1;
   }
   const Plan& p = a.plan;
-  hipLaunchKernelGGL(k_finish<DT>, dim3((uint32_t)cached[dev]), dim3(EX_THREADS), 0, a.stream,
-                     a.values, (uint32_t)p.n, (uint32_t)p.rows, a.states, a.rctr, a.call, a.flagged,
-                     a.ghist, a.cbuf, a.aux, (uint32_t)p.cap, (uint32_t)p.k, (uint32_t)p.k_eff, p.B,
-                     p.W, small_k, mode, a.out_values, a.out_idx, a.lkc, bl, lk_flags,
-                     a.spin_limit);
+  const uint32_t G = (uint32_t)cached[dev];
+  hipLaunchKernelGGL(k_finish<DT>, dim3(G), dim3(EX_THREADS), 0, a.stream, a.states, a.rctr,
+                     a.cbuf, (uint32_t)p.rows, mode, (uint32_t)p.k, (uint32_t)p.k_eff,
+                     (uint32_t)p.cap, lk_flags | (small_k ? FIN_SMALL_K : 0u), p.B, p.W, G,
+                     a.values, (uint32_t)p.n, a.call, a.flagged, a.ghist, a.aux, a.out_values,
+                     a.out_idx, a.lkc, bl, a.spin_limit);
   return hipGetLastError();
 }
 
@@ -154,8 +155,8 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_SAMPLE, 0);
       const dim3 fg(p.filter_bpr, rows);
       mark(STAGE_FILTER, 1);
-      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
-                  a.cbuf, a.aux, cap, B, 1u, a.skeys, 0u, (uint32_t)p.SP, (uint32_t)p.t,
+      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
+                  0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr, a.cbuf, a.aux,
                   (WsHeader*)nullptr, p.sig);
       mark(STAGE_FILTER, 0);
     } else if (p.path == PLAN_SAMPLED) {
@@ -167,11 +168,12 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       const uint32_t ns = lists ? sgx * (uint32_t)p.t : (uint32_t)p.S;   // keys to select from
       const bool in_filter = lists && ns <= TL_PER * FILTER_THREADS;
       mark(STAGE_SAMPLE, 1);
-      TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, n, (uint32_t)p.S,
-                  (uint32_t)p.SP, a.seed, p.half_bits, a.skeys, a.shist, (uint32_t)(lists ? 1 : 0),
-                  (uint32_t)p.t, in_filter ? a.states : nullptr, a.rctr, a.call, a.hdr, p.sig,
+      TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, a.seed, a.skeys, n,
+                  (uint32_t)p.S, (uint32_t)p.SP, p.half_bits, (uint32_t)(lists ? 1 : 0),
+                  (uint32_t)p.t,
                   (uint32_t)((p.t <= 8 && ns <= 4 * FILTER_THREADS) ? TAU_FILTER_LISTS
-                                                                    : TAU_FILTER_RADIX));
+                                                                    : TAU_FILTER_RADIX),
+                  in_filter ? a.states : nullptr, a.rctr, a.call, a.hdr, a.shist, p.sig);
       mark(STAGE_SAMPLE, 0);
       if (!in_filter) {
         mark(STAGE_TAU, 1);
@@ -184,9 +186,9 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_FILTER, 1);
       // after k_tau (all keys) every row's sample histogram is zero again
       WsHeader* validate = lists ? nullptr : a.hdr;
-      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, n, a.states, a.rctr,
-                  a.cbuf, a.aux, cap, B, 1u, a.skeys,
-                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, validate, p.sig);
+      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
+                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr,
+                  a.cbuf, a.aux, validate, p.sig);
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,

@@ -309,17 +309,20 @@ __device__ __forceinline__ uint32_t tau_from_lists(const uint32_t (&v)[TL_PER], 
 }
 
 template <int DT>
+// The arguments the prologue needs come first: the first 14 words of the
+// argument block arrive in scalar registers with the launch, the rest takes a
+// memory round trip.  bpr = the grid's x size (workgroups per row), passed
+// rather than read from the dispatch's hidden arguments for the same reason.
 __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
-    const void* __restrict__ values, uint32_t n, RowState* __restrict__ states,
+    const void* __restrict__ values, const uint32_t* __restrict__ tlist,
+    RowState* __restrict__ states, uint32_t n, uint32_t tlist_n, uint32_t tlist_stride,
+    uint32_t t, uint32_t bpr, uint32_t cap, uint32_t B, uint32_t track_kmax,
     RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf,
-    uint32_t cap, uint32_t B, uint32_t track_kmax, const uint32_t* __restrict__ tlist,
-    uint32_t tlist_n, uint32_t tlist_stride, uint32_t t, WsHeader* validate, uint64_t sig) {
+    WsHeader* validate, uint64_t sig) {
   using D = Dt<DT>;
+  assume_block_threads(FILTER_THREADS);
   const uint32_t row = blockIdx.y;
-  // k_tau has left every row's sample histogram zero: stamp the workspace
-  if (validate && row == 0 && blockIdx.x == 0 && threadIdx.x == 0) validate->stamp = sig;
   RowState* st = states + row;
-  if (st->status != ST_FILTER) return;
   Thr thr;   // set below, once tau is known
 
   __shared__ __align__(16) uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];   // (16: the prologue bins)
@@ -440,7 +443,6 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 
   // This workgroup's slice of the row's vectors: [vi0, vend), in steps of
   // FILTER_THREADS * FILTER_UNROLL vectors.
-  const uint32_t bpr = gridDim.x;
   constexpr size_t step = (size_t)FILTER_THREADS * FILTER_UNROLL;
   const size_t per = (((size_t)nvec + bpr - 1) / bpr + step - 1) / step * step;
   const size_t vi0 = (size_t)blockIdx.x * per;
@@ -477,7 +479,6 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       tlv[q] = kl[i < klast ? i : klast];   // (clamped: masked where used)
     }
   }
-  const uint32_t tau_given = tlist_n ? 0u : st->tau_key;
   constexpr size_t sstep = FILTER_UNROLL * stride;
   u32x4 nxt[FILTER_UNROLL], nx2[FILTER_UNROLL];
   const bool more2_ = step_ok(vi + sstep);
@@ -496,6 +497,14 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       nx2[u] = __builtin_nontemporal_load(vq + (i1 < vlast ? i1 : vlast));
     }
   }
+  // (after the loads above: a row left to another route reads and discards
+  // them, and stores nothing; the empty asm keeps the compiler from moving
+  // this check, and its wait for the row state, in front of them)
+  asm volatile("" ::: "memory");
+  if (st->status != ST_FILTER) return;
+  // k_tau has left every row's sample histogram zero: stamp the workspace
+  if (validate && row == 0 && blockIdx.x == 0 && tid == 0) validate->stamp = sig;
+  const uint32_t tau_given = tlist_n ? 0u : st->tau_key;
   // tau: given by k_tau, or (tlist_n > 0) the t-th largest of the sampler's
   // per-workgroup top-t lists, selected here by every workgroup
   uint32_t tau;

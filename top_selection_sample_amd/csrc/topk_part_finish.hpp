@@ -267,7 +267,7 @@ __device__ void lk_sort_chunk(const uint64_t* __restrict__ cb, const uint64_t* _
 enum : uint32_t { FIN_SCAN = 0, FIN_LISTED = 1 };
 // k_finish runs the bucket sort's chunk step for the accepted sampled rows
 // and/or for the exact route's rows (large k).
-enum : uint32_t { LK_HIST_SAMPLED = 1, LK_HIST_EXACT = 2 };
+enum : uint32_t { LK_HIST_SAMPLED = 1, LK_HIST_EXACT = 2, FIN_SMALL_K = 4 };
 constexpr uint32_t FIN_SCAN_ROWS = 1024;
 
 // One listed row selected again by one workgroup (every thread calls it):
@@ -344,15 +344,22 @@ __device__ __attribute__((noinline)) void reselect_row(const void* __restrict__ 
 }
 
 template <int DT>
+// flags: FIN_SMALL_K | LK_HIST_SAMPLED | LK_HIST_EXACT.  The arguments the
+// check and the refine need come first (the first 14 words of the argument
+// block arrive in scalar registers with the launch); G = the grid size,
+// passed rather than read from the dispatch's hidden arguments.
 __global__ __launch_bounds__(EX_THREADS) void k_finish(
-    const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
-    const RowCtr* __restrict__ rctr, CallState* __restrict__ cs, uint32_t* __restrict__ flagged,
-    uint32_t* __restrict__ ghist,
-    uint64_t* __restrict__ cbuf, const uint64_t* __restrict__ tbuf, uint32_t cap, uint32_t k,
-    uint32_t k_eff, uint32_t B, uint32_t W, uint32_t small_k, uint32_t mode,
-    void* __restrict__ out_values, int64_t* __restrict__ out_idx, uint32_t* __restrict__ lkc,
-    uint32_t bl, uint32_t lk_flags, uint32_t spin_limit) {
+    RowState* __restrict__ states, const RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf,
+    uint32_t rows, uint32_t mode, uint32_t k, uint32_t k_eff, uint32_t cap, uint32_t flags,
+    uint32_t B, uint32_t W, uint32_t G, const void* __restrict__ values, uint32_t n,
+    CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
+    const uint64_t* __restrict__ tbuf, void* __restrict__ out_values,
+    int64_t* __restrict__ out_idx, uint32_t* __restrict__ lkc, uint32_t bl,
+    uint32_t spin_limit) {
   using D = Dt<DT>;
+  assume_block_threads(EX_THREADS);
+  const uint32_t small_k = (flags & FIN_SMALL_K) ? 1u : 0u;
+  const uint32_t lk_flags = flags & (LK_HIST_SAMPLED | LK_HIST_EXACT);
   __shared__ __align__(16) uint32_t s_hist[RF_BINS];
   __shared__ uint32_t s_misc[8];
   __shared__ uint32_t s_tmp[16];
@@ -360,19 +367,24 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
   __shared__ uint32_t s_keys[RF_KCAP];
   __shared__ uint32_t s_idx[RF_SORT_CAP];
   __shared__ uint32_t s_flag;
-  const uint32_t G = gridDim.x, tid = threadIdx.x, w = tid >> 6;
+  const uint32_t tid = threadIdx.x, w = tid >> 6;
 
   // FIN_SCAN (a sampled call): this workgroup's first row's state is read
-  // here, in the same round trip as the check's reads below.
+  // here, in the same round trip as the check's reads below (as vector
+  // loads, which go out together: the compiler serialises scalar loads here
+  // to save scalar registers)
   const uint32_t r_first = blockIdx.x;
   const bool pre = mode == FIN_SCAN && r_first < rows;
   uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
   if (pre) {
-    f_status = states[r_first].status;
-    f_count = rctr[r_first].above;
-    f_tau = states[r_first].tau_key;
-    f_ties = rctr[r_first].ties;
-    f_kmax = rctr[r_first].kmax;
+    auto ld = [](const uint32_t* q) {
+      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    f_status = ld(&states[r_first].status);
+    f_count = ld(&rctr[r_first].above);
+    f_tau = ld(&states[r_first].tau_key);
+    f_ties = ld(&rctr[r_first].ties);
+    f_kmax = ld(&rctr[r_first].kmax);
   }
   static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
 

@@ -246,13 +246,30 @@ __device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint
 // otherwise k_tau histograms the keys itself.
 template <int DT>
 __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
-    const void* __restrict__ values, uint32_t n, uint32_t S, uint32_t SP, uint64_t seed,
-    uint32_t half_bits, uint32_t* __restrict__ skeys, uint32_t* __restrict__ shist, uint32_t lists,
-    uint32_t t, RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs,
-    WsHeader* hdr, uint64_t sig, uint32_t route) {
+    const void* __restrict__ values, uint64_t seed, uint32_t* __restrict__ skeys, uint32_t n,
+    uint32_t S, uint32_t SP, uint32_t half_bits, uint32_t lists, uint32_t t, uint32_t route,
+    RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs, WsHeader* hdr,
+    uint32_t* __restrict__ shist, uint64_t sig) {
+  // (the arguments the gather needs come first: the first 14 words of the
+  // argument block arrive in scalar registers with the launch)
   __shared__ uint32_t h[SH_BINS];
   __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT], s_m[2 * TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
+  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
+  const bool in = j < S;
+  // The gather goes out first, unconditionally (a lane past S reads element
+  // 0 and drops it): the rest of the set-up overlaps its latency, and the
+  // empty asm keeps the compiler from moving that set-up's stores, and the
+  // waits for their addresses, in front of it.
+  uint64_t x = 0;
+  if (in) {
+    const Feistel f(seed, row, half_bits);
+    x = f.apply(j);
+    while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
+  }
+  const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
+  const uint32_t raw = load_raw<DT>(rowp, (uint32_t)x);
+  asm volatile("" ::: "memory");
   const bool gh_ok = !lists && hdr->stamp == sig;   // read before the prologue may clear it
   call_prologue(cs, hdr, sig);
   // the filter selects tau itself: start the row here (tau set there)
@@ -263,14 +280,9 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
     __syncthreads();
   }
-  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
   uint32_t key = 0;
-  if (j < S) {
-    const Feistel f(seed, row, half_bits);
-    uint64_t x = f.apply(j);
-    while (x >= n) x = f.apply(x);   // ends: the cycle through j < n returns below n
-    const char* rowp = static_cast<const char*>(values) + (size_t)row * n * Dt<DT>::ES;
-    key = Dt<DT>::key(load_raw<DT>(rowp, (uint32_t)x));
+  if (in) {
+    key = Dt<DT>::key(raw);
     if (!lists) {
       skeys[(size_t)row * SP + j] = key;
       if (gh_ok) atomicAdd(&h[key >> (Dt<DT>::KB - SH_BITS)], 1u);
