@@ -127,6 +127,26 @@ static_assert(sizeof(WsHeader) == 256, "one 256-byte header");
 // and every call that does not build the sample histogram) clears it unless
 // it is already its own: the call may overwrite the region.  Racing readers
 // in the same kernel see either value, and neither equals `sig`.
+// The workspace's first regions follow from the row count alone (the header,
+// the row states, the call record, the flagged-row list and the exact-route
+// histograms, each 256-byte aligned), so a kernel that has the row states
+// finds the rest without arguments that would have to be loaded.
+__host__ __device__ __forceinline__ size_t ws_align256(size_t v) { return (v + 255) & ~(size_t)255; }
+__host__ __device__ __forceinline__ size_t ws_off_call(uint32_t rows) {
+  return ws_align256(256 + (size_t)rows * 64);
+}
+__host__ __device__ __forceinline__ size_t ws_off_flag(uint32_t rows) {
+  return ws_align256(ws_off_call(rows) + 64);
+}
+__host__ __device__ __forceinline__ size_t ws_off_ghist(uint32_t rows) {
+  return ws_align256(ws_off_flag(rows) + (size_t)rows * 4);
+}
+// (the row states start at byte 256)
+template <class T>
+__device__ __forceinline__ T* ws_region(const void* states, size_t off) {
+  return reinterpret_cast<T*>(const_cast<char*>(static_cast<const char*>(states)) - 256 + off);
+}
+
 // The workgroup size a kernel is always launched with, told to the compiler:
 // blockDim.x is otherwise read from the dispatch's hidden arguments, a memory
 // round trip at the start of the kernel.

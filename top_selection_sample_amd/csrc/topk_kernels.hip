@@ -116,10 +116,16 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   }
   const Plan& p = a.plan;
   const uint32_t G = (uint32_t)cached[dev];
-  hipLaunchKernelGGL(k_finish<DT>, dim3(G), dim3(EX_THREADS), 0, a.stream, a.states, a.rctr,
-                     a.cbuf, (uint32_t)p.rows, mode, (uint32_t)p.k, (uint32_t)p.k_eff,
-                     (uint32_t)p.cap, lk_flags | (small_k ? FIN_SMALL_K : 0u), p.B, p.W, G,
-                     a.values, (uint32_t)p.n, a.call, a.flagged, a.ghist, a.aux, a.out_values,
+  // (k_finish derives W and the regions below from B and rows)
+  if (p.W != p.B + Dt<DT>::KB) return hipErrorInvalidValue;
+  const char* st0 = reinterpret_cast<const char*>(a.states);
+  if (reinterpret_cast<const char*>(a.call) != st0 - 256 + ws_off_call((uint32_t)p.rows) ||
+      reinterpret_cast<const char*>(a.flagged) != st0 - 256 + ws_off_flag((uint32_t)p.rows) ||
+      reinterpret_cast<const char*>(a.ghist) != st0 - 256 + ws_off_ghist((uint32_t)p.rows))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_finish<DT>, dim3(G), dim3(EX_THREADS), 0, a.stream, a.states, a.rctr, a.cbuf, (uint32_t)p.rows, mode, (uint32_t)p.k, (uint32_t)p.k_eff,
+                     (uint32_t)p.cap, lk_flags | (small_k ? FIN_SMALL_K : 0u), p.B, G,
+                     a.values, (uint32_t)p.n, a.aux, a.out_values,
                      a.out_idx, a.lkc, bl, a.spin_limit);
   return hipGetLastError();
 }

@@ -343,152 +343,22 @@ __device__ __attribute__((noinline)) void reselect_row(const void* __restrict__ 
   __syncthreads();
 }
 
+// The exact route of k_finish (every row that failed the check, nf > 0 in
+// every workgroup): a function of its own, called only then, so that its
+// registers do not crowd those of the common path (check and refine).  The
+// LDS arrays are k_finish's.
 template <int DT>
-// flags: FIN_SMALL_K | LK_HIST_SAMPLED | LK_HIST_EXACT.  The arguments the
-// check and the refine need come first (the first 14 words of the argument
-// block arrive in scalar registers with the launch); G = the grid size,
-// passed rather than read from the dispatch's hidden arguments.
-__global__ __launch_bounds__(EX_THREADS) void k_finish(
-    RowState* __restrict__ states, const RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf,
-    uint32_t rows, uint32_t mode, uint32_t k, uint32_t k_eff, uint32_t cap, uint32_t flags,
-    uint32_t B, uint32_t W, uint32_t G, const void* __restrict__ values, uint32_t n,
+__device__ __attribute__((noinline)) void finish_exact(
+    const void* __restrict__ values, uint32_t n, uint32_t rows, RowState* __restrict__ states,
     CallState* __restrict__ cs, uint32_t* __restrict__ flagged, uint32_t* __restrict__ ghist,
-    const uint64_t* __restrict__ tbuf, void* __restrict__ out_values,
-    int64_t* __restrict__ out_idx, uint32_t* __restrict__ lkc, uint32_t bl,
-    uint32_t spin_limit) {
+    uint64_t* __restrict__ cbuf, uint32_t cap, uint32_t k, uint32_t B, uint32_t W,
+    uint32_t small_k, uint32_t mode, void* __restrict__ out_values, int64_t* __restrict__ out_idx,
+    uint32_t* __restrict__ lkc, uint32_t bl, uint32_t lk_flags, uint32_t spin_limit, uint32_t G,
+    uint32_t nf, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp, uint64_t* s_cand,
+    uint32_t* s_keys, uint32_t* s_idx, uint32_t* s_flag_p) {
   using D = Dt<DT>;
-  assume_block_threads(EX_THREADS);
-  const uint32_t small_k = (flags & FIN_SMALL_K) ? 1u : 0u;
-  const uint32_t lk_flags = flags & (LK_HIST_SAMPLED | LK_HIST_EXACT);
-  __shared__ __align__(16) uint32_t s_hist[RF_BINS];
-  __shared__ uint32_t s_misc[8];
-  __shared__ uint32_t s_tmp[16];
-  __shared__ uint64_t s_cand[RF_SORT_CAP];
-  __shared__ uint32_t s_keys[RF_KCAP];
-  __shared__ uint32_t s_idx[RF_SORT_CAP];
-  __shared__ uint32_t s_flag;
   const uint32_t tid = threadIdx.x, w = tid >> 6;
-
-  // FIN_SCAN (a sampled call): this workgroup's first row's state is read
-  // here, in the same round trip as the check's reads below (as vector
-  // loads, which go out together: the compiler serialises scalar loads here
-  // to save scalar registers)
-  const uint32_t r_first = blockIdx.x;
-  const bool pre = mode == FIN_SCAN && r_first < rows;
-  uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
-  if (pre) {
-    auto ld = [](const uint32_t* q) {
-      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    f_status = ld(&states[r_first].status);
-    f_count = ld(&rctr[r_first].above);
-    f_tau = ld(&states[r_first].tau_key);
-    f_ties = ld(&rctr[r_first].ties);
-    f_kmax = ld(&rctr[r_first].kmax);
-  }
-  static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
-
-  // ---- which rows failed the check (Prof-K section 3, stage 4).  Every
-  // count read here is final and never rewritten in this kernel (the
-  // filter's above-tau count and tie count), so every workgroup reaches the
-  // same verdict for every row.
-  __shared__ uint32_t s_bad[FIN_SCAN_ROWS / 32];   // FIN_SCAN: one bit per row
-  uint32_t nf;
-  if (mode == FIN_SCAN) {
-    const uint32_t words = (rows + 31) / 32;
-    for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
-    __syncthreads();
-    for (uint32_t r = tid; r < rows; r += blockDim.x) {
-      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
-      if (sampled_verdict(Ga, E, k, k_eff, cap) == V_FAIL) atomicOr(&s_bad[r >> 5], 1u << (r & 31));
-    }
-    __syncthreads();
-    nf = 0;
-    for (uint32_t i = 0; i < words; ++i) nf += __builtin_popcount(s_bad[i]);
-  } else {
-    nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (nf > rows) nf = rows;   // (at most one entry per row was listed)
-  }
-
-  // ---- this workgroup's rows: list the failed ones, refine the others
-  for (uint32_t r = blockIdx.x; r < rows; r += G) {
-    RowState* st = states + r;
-    if (mode == FIN_SCAN && nf && (s_bad[r >> 5] >> (r & 31)) & 1u) {
-      if (tid == 0) {
-        uint32_t slot = 0;   // failed rows below r
-        for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
-        slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
-        st->ties = rctr[r].ties;
-        st->r_sampled = rctr[r].above + st->ties;
-        start_exact(st, k, PATH_FALLBACK);
-        flagged[slot] = r;
-      }
-      // (large k: the chunk step below skips failed rows)
-      continue;
-    }
-    const bool fr = pre && r == r_first;
-    if ((fr ? f_status : st->status) != ST_FILTER) continue;
-    // an accepted row; when it needs the ties, they join its candidates
-    const uint32_t G = fr ? f_count : rctr[r].above, E = fr ? f_ties : rctr[r].ties;
-    const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
-    const uint32_t verdict = sampled_verdict(G, E, k, k_eff, cap);
-    const bool ties_in = verdict == V_OK_TIES || verdict == V_PARTIAL;
-    if (!fr) __syncthreads();   // every thread has read the counts
-    // (the bucket sort's chunk step reads them from the tie region instead)
-    const bool copy_ties = ties_in && !(lk_flags & LK_HIST_SAMPLED);
-    if (copy_ties) {
-      uint64_t* dst = cbuf + (size_t)r * cap + G;
-      const uint64_t* src = tbuf + (size_t)r * cap;
-      for (uint32_t i = tid; i < E; i += blockDim.x) dst[i] = src[i];
-    }
-    if (tid == 0) {
-      st->r_sampled = G + E;
-      st->ties = E;
-      if (G < k) st->count = G + E;
-      if (verdict == V_PARTIAL) st->path = PATH_PARTIAL;
-      if (!small_k) {
-        st->thr_key = st->tau_key;   // every candidate key is >= this
-        st->kmax = rctr[r].kmax;
-        st->status = ST_SORT;
-      }
-    }
-    if (copy_ties) __syncthreads();   // the copied ties are visible to every thread
-    if (small_k) {
-      uint32_t R = G < k ? G + E : G;
-      if (R > cap) R = cap;
-      // a partial row (fewer than k reach tau) keeps all R and pads the rest
-      const uint32_t kk = R < k ? R : k;
-      refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, kk, k, B, W,
-                         out_values, out_idx, r, s_hist, s_misc, s_tmp, s_cand,
-                         reinterpret_cast<uint64_t*>(s_keys));
-    }
-  }
-  // Large k: the bucket histograms of the accepted sampled rows and their
-  // chunks grouped by rank (the first step of the bucket sort), LK_CHUNK
-  // candidates per workgroup and step.  Every count read here is final: the
-  // filter's above-tau count and tie count, tau and the largest key (the
-  // row's owner rewrites only the RowState count).  A row's ties are read
-  // from the tie region: for large k they are never copied into the
-  // candidate buffer, whose chunks are rewritten here.
-  if (lk_flags & LK_HIST_SAMPLED) {
-    const uint32_t maxch = lk_maxch(cap);
-    const uint64_t npairs = (uint64_t)rows * maxch;
-    for (uint64_t q = blockIdx.x; q < npairs; q += G) {
-      const uint32_t r = (uint32_t)(q / maxch), c = (uint32_t)(q % maxch);
-      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
-      const uint32_t v = sampled_verdict(Ga, E, k, k_eff, cap);
-      if (v == V_FAIL) continue;   // the exact route's rows: below
-      uint32_t R = (v == V_OK_TIES || v == V_PARTIAL) ? Ga + E : Ga;
-      if (R > cap) R = cap;
-      if ((uint64_t)c * LK_CHUNK >= R) continue;
-      const LkDigit g = lk_digit(states[r].tau_key, rctr[r].kmax, B, bl);
-      lk_sort_chunk(cbuf + (size_t)r * cap, tbuf + (size_t)r * cap, Ga, R, c * LK_CHUNK, g,
-                    cbuf + (size_t)r * cap, lkc + ((size_t)r * maxch + c) * LK_CSTRIDE, s_keys,
-                    s_cand);
-    }
-  }
-  if (nf == 0) return;                        // the common case: nothing more to do
-
+  uint32_t& s_flag = *s_flag_p;
   // ======================= exact route (nf > 0 in every workgroup) =======
   // A listed entry always names a row of this call once the barrier after
   // the listing has passed; the bound is kept anyway for every read.
@@ -773,4 +643,164 @@ __global__ __launch_bounds__(EX_THREADS) void k_finish(
                                                 : nullptr,
                      bl, s_hist, s_misc, s_cand, s_keys);
   }
+}
+
+template <int DT>
+// flags: FIN_SMALL_K | LK_HIST_SAMPLED | LK_HIST_EXACT.  The arguments the
+// check and the refine need come first (the first 14 words of the argument
+// block arrive in scalar registers with the launch); G = the grid size,
+// passed rather than read from the dispatch's hidden arguments; the
+// composite width W = B + the key bits; the call record, the flagged-row
+// list and the exact-route histograms sit at offsets that follow from rows.
+__global__ __launch_bounds__(EX_THREADS) void k_finish(
+    RowState* __restrict__ states, const RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf,
+    uint32_t rows, uint32_t mode, uint32_t k, uint32_t k_eff, uint32_t cap, uint32_t flags,
+    uint32_t B, uint32_t G, const void* __restrict__ values, uint32_t n,
+    const uint64_t* __restrict__ tbuf, void* __restrict__ out_values,
+    int64_t* __restrict__ out_idx, uint32_t* __restrict__ lkc, uint32_t bl,
+    uint32_t spin_limit) {
+  using D = Dt<DT>;
+  assume_block_threads(EX_THREADS);
+  const uint32_t W = B + D::KB;
+  CallState* __restrict__ cs = ws_region<CallState>(states, ws_off_call(rows));
+  uint32_t* __restrict__ flagged = ws_region<uint32_t>(states, ws_off_flag(rows));
+  uint32_t* __restrict__ ghist = ws_region<uint32_t>(states, ws_off_ghist(rows));
+  const uint32_t small_k = (flags & FIN_SMALL_K) ? 1u : 0u;
+  const uint32_t lk_flags = flags & (LK_HIST_SAMPLED | LK_HIST_EXACT);
+  __shared__ __align__(16) uint32_t s_hist[RF_BINS];
+  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint64_t s_cand[RF_SORT_CAP];
+  __shared__ uint32_t s_keys[RF_KCAP];
+  __shared__ uint32_t s_idx[RF_SORT_CAP];
+  __shared__ uint32_t s_flag;
+  const uint32_t tid = threadIdx.x, w = tid >> 6;
+
+  // FIN_SCAN (a sampled call): this workgroup's first row's state is read
+  // here, in the same round trip as the check's reads below (as vector
+  // loads, which go out together: the compiler serialises scalar loads here
+  // to save scalar registers)
+  const uint32_t r_first = blockIdx.x;
+  const bool pre = mode == FIN_SCAN && r_first < rows;
+  uint32_t f_status = 0, f_count = 0, f_ties = 0, f_kmax = 0, f_tau = 0;
+  if (pre) {
+    auto ld = [](const uint32_t* q) {
+      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    f_status = ld(&states[r_first].status);
+    f_count = ld(&rctr[r_first].above);
+    f_tau = ld(&states[r_first].tau_key);
+    f_ties = ld(&rctr[r_first].ties);
+    f_kmax = ld(&rctr[r_first].kmax);
+  }
+  static_assert(FIN_SCAN_ROWS % 32 == 0, "whole words of row bits");
+
+  // ---- which rows failed the check (Prof-K section 3, stage 4).  Every
+  // count read here is final and never rewritten in this kernel (the
+  // filter's above-tau count and tie count), so every workgroup reaches the
+  // same verdict for every row.
+  __shared__ uint32_t s_bad[FIN_SCAN_ROWS / 32];   // FIN_SCAN: one bit per row
+  uint32_t nf;
+  if (mode == FIN_SCAN) {
+    // (rows <= FIN_SCAN_ROWS = the workgroup: one row per thread; both
+    // counts are read before the LDS set-up, unconditionally at a clamped
+    // row, so the two loads go out together)
+    static_assert(FIN_SCAN_ROWS <= EX_THREADS, "one row per thread");
+    const uint32_t words = (rows + 31) / 32;
+    const uint32_t rr = tid < rows ? tid : rows - 1;
+    const uint32_t Ga = __hip_atomic_load(&rctr[rr].above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t Ea = __hip_atomic_load(&rctr[rr].ties, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t i = tid; i < words; i += blockDim.x) s_bad[i] = 0u;
+    __syncthreads();
+    if (tid < rows && sampled_verdict(Ga, Ea, k, k_eff, cap) == V_FAIL)
+      atomicOr(&s_bad[tid >> 5], 1u << (tid & 31));
+    __syncthreads();
+    nf = 0;
+    for (uint32_t i = 0; i < words; ++i) nf += __builtin_popcount(s_bad[i]);
+  } else {
+    nf = __hip_atomic_load(&cs->nflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nf > rows) nf = rows;   // (at most one entry per row was listed)
+  }
+
+  // ---- this workgroup's rows: list the failed ones, refine the others
+  for (uint32_t r = blockIdx.x; r < rows; r += G) {
+    RowState* st = states + r;
+    if (mode == FIN_SCAN && nf && (s_bad[r >> 5] >> (r & 31)) & 1u) {
+      if (tid == 0) {
+        uint32_t slot = 0;   // failed rows below r
+        for (uint32_t i = 0; i < (r >> 5); ++i) slot += __builtin_popcount(s_bad[i]);
+        slot += __builtin_popcount(s_bad[r >> 5] & ((1u << (r & 31)) - 1u));
+        st->ties = rctr[r].ties;
+        st->r_sampled = rctr[r].above + st->ties;
+        start_exact(st, k, PATH_FALLBACK);
+        flagged[slot] = r;
+      }
+      // (large k: the chunk step below skips failed rows)
+      continue;
+    }
+    const bool fr = pre && r == r_first;
+    if ((fr ? f_status : st->status) != ST_FILTER) continue;
+    // an accepted row; when it needs the ties, they join its candidates
+    const uint32_t G = fr ? f_count : rctr[r].above, E = fr ? f_ties : rctr[r].ties;
+    const uint32_t kmx = fr ? f_kmax : rctr[r].kmax, tau = fr ? f_tau : st->tau_key;
+    const uint32_t verdict = sampled_verdict(G, E, k, k_eff, cap);
+    const bool ties_in = verdict == V_OK_TIES || verdict == V_PARTIAL;
+    if (!fr) __syncthreads();   // every thread has read the counts
+    // (the bucket sort's chunk step reads them from the tie region instead)
+    const bool copy_ties = ties_in && !(lk_flags & LK_HIST_SAMPLED);
+    if (copy_ties) {
+      uint64_t* dst = cbuf + (size_t)r * cap + G;
+      const uint64_t* src = tbuf + (size_t)r * cap;
+      for (uint32_t i = tid; i < E; i += blockDim.x) dst[i] = src[i];
+    }
+    if (tid == 0) {
+      st->r_sampled = G + E;
+      st->ties = E;
+      if (G < k) st->count = G + E;
+      if (verdict == V_PARTIAL) st->path = PATH_PARTIAL;
+      if (!small_k) {
+        st->thr_key = st->tau_key;   // every candidate key is >= this
+        st->kmax = rctr[r].kmax;
+        st->status = ST_SORT;
+      }
+    }
+    if (copy_ties) __syncthreads();   // the copied ties are visible to every thread
+    if (small_k) {
+      uint32_t R = G < k ? G + E : G;
+      if (R > cap) R = cap;
+      // a partial row (fewer than k reach tau) keeps all R and pads the rest
+      const uint32_t kk = R < k ? R : k;
+      refine_sampled<DT>(values, n, st, cbuf + (size_t)r * cap, R, tau, kmx, kk, k, B, W,
+                         out_values, out_idx, r, s_hist, s_misc, s_tmp, s_cand,
+                         reinterpret_cast<uint64_t*>(s_keys));
+    }
+  }
+  // Large k: the bucket histograms of the accepted sampled rows and their
+  // chunks grouped by rank (the first step of the bucket sort), LK_CHUNK
+  // candidates per workgroup and step.  Every count read here is final: the
+  // filter's above-tau count and tie count, tau and the largest key (the
+  // row's owner rewrites only the RowState count).  A row's ties are read
+  // from the tie region: for large k they are never copied into the
+  // candidate buffer, whose chunks are rewritten here.
+  if (lk_flags & LK_HIST_SAMPLED) {
+    const uint32_t maxch = lk_maxch(cap);
+    const uint64_t npairs = (uint64_t)rows * maxch;
+    for (uint64_t q = blockIdx.x; q < npairs; q += G) {
+      const uint32_t r = (uint32_t)(q / maxch), c = (uint32_t)(q % maxch);
+      const uint32_t Ga = rctr[r].above, E = rctr[r].ties;
+      const uint32_t v = sampled_verdict(Ga, E, k, k_eff, cap);
+      if (v == V_FAIL) continue;   // the exact route's rows: below
+      uint32_t R = (v == V_OK_TIES || v == V_PARTIAL) ? Ga + E : Ga;
+      if (R > cap) R = cap;
+      if ((uint64_t)c * LK_CHUNK >= R) continue;
+      const LkDigit g = lk_digit(states[r].tau_key, rctr[r].kmax, B, bl);
+      lk_sort_chunk(cbuf + (size_t)r * cap, tbuf + (size_t)r * cap, Ga, R, c * LK_CHUNK, g,
+                    cbuf + (size_t)r * cap, lkc + ((size_t)r * maxch + c) * LK_CSTRIDE, s_keys,
+                    s_cand);
+    }
+  }
+  if (nf == 0) return;                        // the common case: nothing more to do
+  finish_exact<DT>(values, n, rows, states, cs, flagged, ghist, cbuf, cap, k, B, W, small_k, mode,
+                   out_values, out_idx, lkc, bl, lk_flags, spin_limit, G, nf, s_hist, s_misc,
+                   s_tmp, s_cand, s_keys, s_idx, &s_flag);
 }
