@@ -374,6 +374,60 @@ __device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, uint32_t 
   }
 }
 
+// The same over a 2048-bin histogram by a whole workgroup of NT threads
+// (every thread calls it; the result is in out[] after the caller's next
+// barrier): thread i holds bins [2048 i / NT, 2048 (i + 1) / NT), each wave
+// posts its total to s_wt (NT / 64 words), and the one thread whose bins
+// hold the rank resolves it.  Four dependent LDS and DPP steps per thread
+// instead of one wave walking all 2048 bins.  Needs 1 <= need <= the total.
+template <uint32_t NT>
+__device__ __forceinline__ void block_find_bucket_2048(const uint32_t* hist, uint32_t need,
+                                                       uint32_t* out, uint32_t* s_wt) {
+  constexpr uint32_t BPT = 2048 / NT, NW = NT / 64;
+  static_assert(BPT * NT == 2048 && (BPT == 2 || BPT == 4), "2 or 4 bins per thread");
+  const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
+  uint32_t h[BPT];
+  if constexpr (BPT == 2) {
+    const uint2 v = reinterpret_cast<const uint2*>(hist)[tid];
+    h[0] = v.x;
+    h[1] = v.y;
+  } else {
+    const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
+    h[0] = v.x;
+    h[1] = v.y;
+    h[2] = v.z;
+    h[3] = v.w;
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < BPT; ++q) mine += h[q];
+  const uint32_t incl = wave_incl_sum(mine);
+  const uint32_t wtot = wave_bcast(incl, 63u);
+  if (l == 0) s_wt[w] = wtot;
+  __syncthreads();
+  uint32_t above = 0;   // elements in the waves holding higher bins
+#pragma unroll
+  for (uint32_t q = 0; q < NW; ++q) above += q > w ? s_wt[q] : 0u;
+  above += wtot - incl;   // ... and in this wave's higher lanes
+  if (above < need && above + mine >= need) {
+    uint32_t a = above, b = BPT * tid, hb = h[0];
+    bool found = false;
+#pragma unroll
+    for (int q = (int)BPT - 1; q >= 0; --q) {
+      if (!found && a + h[q] >= need) {
+        found = true;
+        b = BPT * tid + (uint32_t)q;
+        hb = h[q];
+      } else if (!found) {
+        a += h[q];
+      }
+    }
+    out[0] = b;
+    out[1] = a;
+    out[2] = hb;
+  }
+}
+
 // The same over a 2048-bin histogram.  Read step j gives lane l the four
 // bins 256j + 4l .. 256j + 4l + 3 (consecutive lanes read consecutive 16-byte
 // words: no bank conflicts).  The group of 256 bins holding the rank is

@@ -69,6 +69,7 @@ __device__ bool grid_barrier(CallState* cs, uint32_t G, uint32_t spin_limit, uin
 }
 
 constexpr uint32_t EX_THREADS = 1024;
+static_assert(EX_THREADS == RS_THREADS, "k_finish runs refine_sampled with its workgroup");
 static_assert(RF_RANK_MAX * 4 <= EX_THREADS, "rank counting: four lanes per element");
 constexpr uint32_t EX_VPT = 4;                            // vectors per thread per item
 constexpr uint32_t EX_ITEM_VEC = EX_THREADS * EX_VPT;     // vectors per item

@@ -56,6 +56,7 @@ __device__ void rank_and_write(const uint64_t* s, uint32_t cnt, uint32_t k, uint
                                uint32_t B, const char* rowp, uint32_t n, void* out_values,
                                int64_t* out_idx, uint32_t row) {
   const uint32_t i = threadIdx.x >> 2, q = threadIdx.x & 3u;
+  if (((threadIdx.x & ~63u) >> 2) >= cnt) return;   // a wave with no element (uniform)
   const uint64_t c = i < cnt ? s[i] : ~0ull;
   uint32_t r0 = 0, r1 = 0;
   uint32_t j = q;
@@ -287,6 +288,7 @@ __device__ void refine_row(const void* __restrict__ values, uint32_t n, RowState
 // winners fill the row's first k slots of ks; a row that keeps fewer than ks
 // (k = R) gets the rest padded.
 constexpr uint32_t RS_VEC = 11;
+constexpr uint32_t RS_THREADS = 1024;
 template <int DT>
 __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowState* st,
                                const uint64_t* __restrict__ cb, uint32_t R, uint32_t lo,
@@ -294,7 +296,7 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
                                void* __restrict__ out_values, int64_t* __restrict__ out_idx,
                                uint32_t row, uint32_t* s_hist, uint32_t* s_misc, uint32_t* s_tmp,
                                uint64_t* s_cand, uint64_t* s_scratch) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t tid = threadIdx.x, nt = RS_THREADS;
   const uint32_t KB = W - B;
   const uint32_t hi = kmax > lo ? kmax : lo;
   const uint32_t diff = (lo ^ hi) & (KB == 32 ? 0xFFFFFFFFu : 0xFFFFu);
@@ -335,7 +337,7 @@ __device__ void refine_sampled(const void* __restrict__ values, uint32_t n, RowS
         re - r0, [&](uint32_t i) { return cb[r0 + i]; },
         [&](uint64_t c, bool ok) { hist_add(s_hist, digit(c), ok); });
   __syncthreads();
-  if (tid < 64) wave_find_bucket_2048(s_hist, k, s_misc);
+  block_find_bucket_2048<RS_THREADS>(s_hist, k, s_misc, s_tmp);
   __syncthreads();
   const uint32_t b = s_misc[0], acc = s_misc[1], hb = s_misc[2];
   uint32_t got;
