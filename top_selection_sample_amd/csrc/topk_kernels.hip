@@ -24,6 +24,7 @@
 // filter and detection, refinement and the one-workgroup route, the finish
 // kernel, the large-k sorts); this file holds the rest and the launchers.
 #include <mutex>
+#include <type_traits>
 
 #include "topk_device.hpp"
 #include "topk_launch.hpp"

@@ -422,7 +422,9 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   __shared__ uint32_t s_qi[FILTER_WAVES][HITQ];
   uint32_t q_head = 0, q_cnt = 0;   // wave-uniform; q_cnt < 64 between steps
   auto wrapq = [](uint32_t e) { return e >= HITQ ? e - HITQ : e; };   // e < 2 HITQ
-  auto drain_queue = [&](uint32_t cnt) __attribute__((always_inline)) {
+  // (DENSE: the counting mode, whose ties were counted in the compare loop:
+  // only the elements above tau are stored)
+  auto drain_queue_t = [&](uint32_t cnt, auto dense_tag) __attribute__((always_inline)) {
     wave_lds_sync();
     const bool ok = lane < cnt;
     const uint32_t e = wrapq(q_head + lane);
@@ -430,7 +432,27 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     const uint32_t xi = ok ? s_qi[w][e] : 0u;
     q_head = wrapq(q_head + cnt);
     q_cnt -= cnt;
-    vec_survivors(x, xi, ok);
+    if constexpr (decltype(dense_tag)::value) {
+      const u32x4 v[1] = {x};
+      uint32_t gt = 0;
+#pragma unroll
+      for (uint32_t b = 0; b < D::VEC; ++b) {
+        const uint32_t y = elemvc<DT, 1>(v, b);
+        gt |= (uint32_t)(pass_of(y) && !eq_of(y)) << b;
+      }
+      if (!ok) gt = 0u;
+      full = drain_bits<DT, 1>(
+                 sg, v, gt, [&](uint32_t b) { return head + xi * D::VEC + b; }, comp_of) ||
+             full;
+    } else {
+      vec_survivors(x, xi, ok);
+    }
+  };
+  auto drain_queue = [&](uint32_t cnt) __attribute__((always_inline)) {
+    drain_queue_t(cnt, std::false_type{});
+  };
+  auto drain_queue_dense = [&](uint32_t cnt) __attribute__((always_inline)) {
+    drain_queue_t(cnt, std::true_type{});
   };
   auto enqueue = [&](bool hit, uint64_t hm, const u32x4& x, uint32_t xi) {
     if (hit) {
@@ -552,6 +574,33 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       }
       while (q_cnt >= 64u || (last && q_cnt)) drain_queue(q_cnt < 64u ? q_cnt : 64u);
     };
+    // the same in the counting mode: ties counted as they are compared, and
+    // only vectors with an element above tau queued
+    auto scan_step_dense = [&](const u32x4 (&v)[FILTER_UNROLL], size_t vc, bool last)
+                               __attribute__((always_inline)) {
+#pragma unroll
+      for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
+        uint32_t gt = 0, eqn = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          auto one = [&](uint32_t x) {
+            const bool eq = native_eq<DT>(x, thr);
+            gt |= (uint32_t)(native_pass<DT>(x, thr) && !eq);
+            eqn += eq ? 1u : 0u;
+          };
+          if constexpr (DT == DT_BF16) {
+            one(v[u][q] & 0xFFFFu);
+            one(v[u][q] >> 16);
+          } else {
+            one(v[u][q]);
+          }
+        }
+        ties += eqn;
+        const uint64_t hm = ballot(gt != 0u);
+        if (hm) enqueue(gt != 0u, hm, v[u], (uint32_t)(vc + u * stride));
+      }
+      while (q_cnt >= 64u || (last && q_cnt)) drain_queue_dense(q_cnt < 64u ? q_cnt : 64u);
+    };
     // The first step straight from its registers, the second one's loads
     // still in flight; from then on one step ahead (the registers of the
     // next step are copied into those of the current one, and a copy waits
@@ -564,7 +613,7 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) nxt[u] = nx2[u];
     }
-    while (more) {
+    while (more && !tfull) {   // (the tie region full: on to the counting loop)
       u32x4 v[FILTER_UNROLL];
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = nxt[u];
@@ -578,6 +627,28 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       }
       scan_step(v, vc, !more);
       if (full) break;
+    }
+    // the tie region is full (and the queue empty): the rest of the slice
+    // counts ties as it compares
+    // (a row of ties, such as all zeros with tau = 0, otherwise sends every
+    // vector through the survivor code)
+    if (more && !full) {
+      while (q_cnt) drain_queue(q_cnt < 64u ? q_cnt : 64u);   // (queued in this mode)
+      while (more) {
+        u32x4 v[FILTER_UNROLL];
+#pragma unroll
+        for (uint32_t u = 0; u < FILTER_UNROLL; ++u) v[u] = nxt[u];
+        const size_t vc = vi;
+        vi += sstep;
+        more = step_ok(vi);
+        if (more) {
+#pragma unroll
+          for (uint32_t u = 0; u < FILTER_UNROLL; ++u)
+            nxt[u] = __builtin_nontemporal_load(vp + vi + u * stride);
+        }
+        scan_step_dense(v, vc, !more);
+        if (full) break;
+      }
     }
   } else {
     for (; (vi - lane) + 63 + (FILTER_UNROLL - 1) * stride < vend; vi += FILTER_UNROLL * stride) {
