@@ -721,10 +721,20 @@ def calibrate(args):
         del bufs, x0, ov, oi
         torch.cuda.empty_cache()
     # the two refines (k <= 4096 in one workgroup, larger k by the bucket
-    # sort) have their own ratio: fit each on its own workloads
+    # sort) have their own ratio, and so do batches of small-k rows, whose
+    # samples are gathered together: fit each on its own workloads
     ratios = [10 ** (e / 8.0) for e in range(-24, 9)]
-    for group, field in (("k <= 4096", "tuned_ratio"), ("k > 4096", "tuned_ratio_large")):
-        names_g = [nm for nm, v in meas.items() if (v[2] <= 4096) == (field == "tuned_ratio")]
+
+    def group_of(v):
+        n, rows, k = v[0], v[1], v[2]
+        if k > 4096:
+            return "tuned_ratio_large"
+        return "tuned_ratio_batched" if rows >= d0.tuned_batch_rows else "tuned_ratio"
+
+    for group, field in (("k <= 4096, fewer rows", "tuned_ratio"),
+                         (f"k <= 4096, {d0.tuned_batch_rows} rows or more", "tuned_ratio_batched"),
+                         ("k > 4096", "tuned_ratio_large")):
+        names_g = [nm for nm, v in meas.items() if group_of(v) == field]
         if not names_g:
             continue
         table = []

@@ -87,8 +87,10 @@ typedef enum {
  *  TOPK_POLICY_TUNED (default): t and M as in EXACT_TAIL; S minimises the
  *    overhead of Eq. 13, tau_A*S + tau_B*M(S)*log2(k), with the exact-tail
  *    M(S) and tau_B/tau_A = tuned_ratio (k <= 4096, candidates refined in
- *    one workgroup) or tuned_ratio_large (k > 4096, the multi-workgroup
- *    bucket sort), over the sample sizes
+ *    one workgroup), tuned_ratio_batched (k <= 4096 in calls of at least
+ *    tuned_batch_rows rows: their samples are gathered together and cost
+ *    bandwidth, while the rows refine side by side) or tuned_ratio_large
+ *    (k > 4096, the multi-workgroup bucket sort), over the sample sizes
  *    tuned_s_min * 2^(j/4) (j = 0, 1, ...) up to min(s_max, n/8).  Sets S
  *    the way section 4 ("Optimal Sample Size") suggests, with the cost ratio
  *    measured on this engine instead of the default 1. */
@@ -148,7 +150,10 @@ typedef struct {
   uint32_t test_flags;  /* test aid, 0 in normal use: TOPK_TEST_BARRIER_GIVEUP makes
                          every grid-barrier wait of the exact route give up at once,
                          as when workgroups are not co-resident.  Other bits: EINVAL. */
-  int32_t reserved2;
+  int32_t tuned_batch_rows;   /* TUNED policy: least row count priced with
+                         tuned_ratio_batched (default 32) */
+  double tuned_ratio_batched; /* TUNED policy, k <= 4096 and rows >= tuned_batch_rows:
+                         tau_B / tau_A (default 0.03) */
 } topk_params;
 
 enum { TOPK_TEST_BARRIER_GIVEUP = 1 };

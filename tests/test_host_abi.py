@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_params_layout(lib):
-    assert ctypes.sizeof(lib.Params) == 128
+    assert ctypes.sizeof(lib.Params) == 136
     assert ctypes.sizeof(lib.RowStats) == 28
     p = lib.default_params()
     assert (p.use_force_tau, p.force_tau_key, p.test_flags) == (0, 0, 0)
@@ -45,6 +45,7 @@ def test_params_layout(lib):
     assert (p.eps, p.s_min, p.s_max, p.cost_ratio) == (1e-3, 32768, 131072, 1.0)
     assert p.policy == lib.POLICY_TUNED and p.force_path == 0
     assert (p.tuned_ratio, p.tuned_s_min, p.tuned_ratio_large) == (0.13, 1024, 0.01)
+    assert (p.tuned_ratio_batched, p.tuned_batch_rows) == (0.03, 32)
     assert (p.S, p.t, p.M, p.use_seed) == (0, 0, 0, 0)
 
 
@@ -82,6 +83,28 @@ def test_tuned_policy_matches_oracle(lib, n, k, s_max):
     ratio = p.tuned_ratio if k <= 4096 else p.tuned_ratio_large   # the engine's two refines
     e = P.tuned(n, k, eps=1e-3 / 3, s_hi=min(s_max, n // 8), ratio=ratio)   # eps per call, 3 rows
     assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
+
+
+@pytest.mark.parametrize("n,k,rows", [(2 ** 20, 64, 128), (2 ** 20, 64, 32), (2 ** 20, 64, 31),
+                                      (2 ** 22, 1000, 64), (2 ** 20, 5000, 128)])
+def test_tuned_policy_prices_batches(lib, n, k, rows):
+    # calls of tuned_batch_rows rows or more price small k with the batched
+    # ratio (their rows' samples are gathered together); large k keeps the
+    # bucket sort's ratio whatever the row count
+    rc, info = _plan(lib, n, rows, k, 1)
+    assert rc == 0
+    p = lib.default_params()
+    if k > 4096:
+        ratio = p.tuned_ratio_large
+    else:
+        ratio = p.tuned_ratio_batched if rows >= p.tuned_batch_rows else p.tuned_ratio
+    e = P.tuned(n, k, eps=1e-3 / rows, s_hi=min(131072, n // 8), ratio=ratio)
+    assert (info.S, info.t, info.M) == (e["S"], e["t"], e["M"])
+    # the threshold is a parameter: a row count below it uses the one-row ratio
+    rc, info2 = _plan(lib, n, rows, k, 1, tuned_batch_rows=rows + 1)
+    e2 = P.tuned(n, k, eps=1e-3 / rows, s_hi=min(131072, n // 8),
+                 ratio=p.tuned_ratio_large if k > 4096 else p.tuned_ratio)
+    assert (info2.S, info2.t, info2.M) == (e2["S"], e2["t"], e2["M"])
 
 
 def test_eps_is_spent_per_call(lib):
@@ -150,7 +173,8 @@ def test_shape_errors(lib, args, status):
                                 dict(cost_ratio=0.0), dict(policy=3), dict(policy=-1),
                                 dict(force_path=3), dict(S=-1), dict(tuned_ratio=0.0),
                                 dict(tuned_s_min=0), dict(recall=0.0), dict(recall=1.5),
-                                dict(recall=-0.5), dict(recall=float("nan"))])
+                                dict(recall=-0.5), dict(recall=float("nan")),
+                                dict(tuned_ratio_batched=0.0), dict(tuned_batch_rows=0)])
 def test_param_errors(lib, kw):
     assert _plan(lib, 2 ** 20, 1, 64, 1, **kw)[0] == -1
 

@@ -45,7 +45,8 @@ class Params(ctypes.Structure):
                 ("tuned_ratio", ctypes.c_double), ("tuned_s_min", ctypes.c_int64),
                 ("tuned_ratio_large", ctypes.c_double), ("recall", ctypes.c_double),
                 ("force_tau_key", ctypes.c_uint32), ("use_force_tau", ctypes.c_int32),
-                ("test_flags", ctypes.c_uint32), ("reserved2", ctypes.c_int32)]
+                ("test_flags", ctypes.c_uint32), ("tuned_batch_rows", ctypes.c_int32),
+                ("tuned_ratio_batched", ctypes.c_double)]
 
 
 class PlanInfo(ctypes.Structure):

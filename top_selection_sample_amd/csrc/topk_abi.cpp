@@ -74,6 +74,8 @@ tk::ParamIn to_in(const topk_params* p) {
   in.tuned_ratio = p->tuned_ratio;
   in.tuned_s_min = p->tuned_s_min;
   in.tuned_ratio_large = p->tuned_ratio_large;
+  in.tuned_ratio_batched = p->tuned_ratio_batched;
+  in.tuned_batch_rows = p->tuned_batch_rows;
   in.recall = p->recall;
   in.force_tau = p->use_force_tau != 0;
   return in;
@@ -87,6 +89,7 @@ int check_params(const topk_params* p) {
   if (p->policy < 0 || p->policy > 2) return TOPK_EINVAL;
   if (!(p->tuned_ratio > 0.0) || p->tuned_s_min < 1) return TOPK_EINVAL;
   if (!(p->tuned_ratio_large > 0.0)) return TOPK_EINVAL;
+  if (!(p->tuned_ratio_batched > 0.0) || p->tuned_batch_rows < 1) return TOPK_EINVAL;
   if (!(p->recall > 0.0 && p->recall <= 1.0)) return TOPK_EINVAL;
   if (p->force_path < 0 || p->force_path > 2) return TOPK_EINVAL;
   if (p->S < 0 || p->t < 0 || p->M < 0) return TOPK_EINVAL;
@@ -138,7 +141,7 @@ int plan_of(int64_t n, int64_t rows, int64_t k, int dtype, const topk_params* pa
 
 extern "C" {
 
-static_assert(sizeof(topk_params) == 128, "topk_params layout is part of the ABI");
+static_assert(sizeof(topk_params) == 136, "topk_params layout is part of the ABI");
 static_assert(sizeof(topk_row_stats) == 28, "topk_row_stats layout is part of the ABI");
 static_assert(sizeof(tk::WsHeader) == 256 && sizeof(tk::RowState) == 64, "workspace header and rows");
 
@@ -154,6 +157,8 @@ int topk_default_params(topk_params* p) {
   p->tuned_ratio = 0.13;
   p->tuned_s_min = 1024;
   p->tuned_ratio_large = 0.01;
+  p->tuned_ratio_batched = 0.03;
+  p->tuned_batch_rows = 32;
   p->recall = 1.0;
   return TOPK_OK;
 }

@@ -322,6 +322,7 @@ int make_plan(int64_t n, int64_t rows, int64_t k, int dtype, const ParamIn& in, 
   }
   // the refine that runs is the one for k: its cost ratio prices the buffer
   if (k > KSMALL) row_in.tuned_ratio = in.tuned_ratio_large;
+  else if (rows >= in.tuned_batch_rows) row_in.tuned_ratio = in.tuned_ratio_batched;
   sample_params(n, p.k_eff, row_in, &p.S, &p.t, &p.M, &p.p_recall, &p.p_overflow);
   const int es = (dtype == 2) ? 2 : 4;
   const int64_t cus = in.cus > 0 ? in.cus : 256;

@@ -30,6 +30,11 @@ struct ParamIn {
   double tuned_ratio = 0.13;
   int64_t tuned_s_min = 1024;  // least sample size the tuned policy considers
   double tuned_ratio_large = 0.01;
+  // k <= KSMALL in calls of at least tuned_batch_rows rows: the rows'
+  // samples are gathered together, so sampling costs bandwidth, while the
+  // rows are refined side by side (about one workgroup each)
+  double tuned_ratio_batched = 0.03;
+  int64_t tuned_batch_rows = 32;
   // recall target (relaxed-recall mode below 1): parameters for
   // ceil(recall * k), and rows with at least that many survivors keep them
   double recall = 1.0;
