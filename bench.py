@@ -20,6 +20,8 @@ Extra modes (measurement plumbing, not part of the timed line):
     --calibrate W1,W2,...     measure the whole call over the tuned policy's
                               grid of sample sizes on each workload and fit
                               the cost ratio tau_B / tau_A of Eq. 13
+    --balance                 the filter's per-workgroup end times by XCD and
+                              slot (workgroup trace), for profiles/
 """
 from __future__ import annotations
 
@@ -757,6 +759,82 @@ def calibrate(args):
         print(f"{name}: best measured S={sb} ({times[sb] * 1e3:.1f} us)")
 
 
+def balance(args):
+    """Filter workgroup balance (the table for profiles/): per-workgroup
+    realtime stamps (topk_filter_trace) of the workload's filter over
+    rotating inputs.  Per XCD (workgroup l runs on XCD l mod 8) and slot
+    (first or second workgroup on its compute unit): the mean end of the scan
+    relative to the call's median end, and the group's rate (the inverse of
+    its mean time to the end of its scan) relative to the mean rate; then the
+    spread of end times and the filter's span (first start to last end)."""
+    import numpy as np
+    import torch
+    import top_selection_sample_amd as tss
+
+    x, dt, k, desc, meta = load_inputs(args.workload)
+    rows, n = x.shape
+    es = 2 if dt == "bf16" else 4
+    x0 = to_device(x, dt)
+    bufs = [x0] + [torch.roll(x0, shifts=sh, dims=1).contiguous()
+                   for sh in (n // 3 + 1, (2 * n) // 3 + 7)]
+    ov = torch.empty((rows, k), dtype=x0.dtype, device="cuda")
+    oi = torch.empty((rows, k), dtype=torch.int64, device="cuda")
+    plan = tss.plan(n, rows, k, dt)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    trace = torch.zeros(2 * 8192, dtype=torch.int64, device="cuda")
+    for i in range(3):
+        tss.topk(bufs[i % 3], k, out=(ov, oi))
+    tss.filter_trace(trace)
+    ends, durs, spans, nwg = [], [], [], None
+    for i in range(args.steps):
+        trace.zero_()
+        tss.topk(bufs[i % 3], k, out=(ov, oi))
+        torch.cuda.synchronize()
+        t = trace.cpu().numpy().reshape(-1, 2)
+        if nwg is None:
+            nwg = int(np.count_nonzero(t[:, 0]))
+        t = t[:nwg].astype(np.int64)
+        t0 = t[:, 0].min()
+        ends.append((t[:, 1] - t0) / 100.0)
+        durs.append((t[:, 1] - t[:, 0]) / 100.0)
+        spans.append((t[:, 1].max() - t0) / 100.0)
+    tss.filter_trace(None)
+    E, D = np.array(ends), np.array(durs)
+    l = np.arange(nwg)
+    two = nwg > cus
+    groups = [(g, s) for s in ((0, 1) if two else (0,)) for g in range(8)]
+    gbytes = rows * n * es
+    print(f"# Filter workgroup balance: {desc}")
+    print()
+    print("Command (REPO = the repository root):")
+    print(f"  python3 REPO/bench.py --balance --workload {args.workload} --steps {args.steps}")
+    print()
+    print(f"Plan: S={plan['S']} t={plan['t']} M={plan['M']}; {nwg} filter workgroups "
+          f"({'two' if two else 'one'} per compute unit, {cus} units), equal slices; "
+          f"{args.steps} calls on three rotating inputs.  Stamps: the device's 100 MHz realtime "
+          f"counter at each workgroup's start and at the end of its scan.")
+    print()
+    span = float(np.mean(spans))
+    print("| filter span (first start to last end) | end spread (max - min) | last end - median end | input / span |")
+    print("|---|---|---|---|")
+    print(f"| {span:.1f} us | {np.mean(E.max(1) - E.min(1)):.1f} us | "
+          f"{np.mean(E.max(1) - np.median(E, axis=1)):.1f} us | {gbytes / span / 1e3:.0f} GB/s |")
+    print()
+    print("Per group (XCD = workgroup index mod 8; slot b = the second workgroup on its unit): "
+          "mean end relative to the call's median end, and the group's rate (1 / mean time to "
+          "the end of its scan) relative to the mean rate, parts per 1024.")
+    print()
+    print("| group | end - median us | rate (/1024) |")
+    print("|---|---|---|")
+    rates = {}
+    for g in groups:
+        mk = (l % 8 == g[0]) & ((l >= cus) == bool(g[1]))
+        rates[g] = (float(np.mean(E[:, mk].mean(1) - np.median(E, axis=1))), 1.0 / D[:, mk].mean())
+    mr = np.mean([r for _, r in rates.values()])
+    for g in groups:
+        print(f"| {g[0]}{'b' if g[1] else 'a'} | {rates[g][0]:+.1f} | {rates[g][1] / mr * 1024:.0f} |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -771,6 +849,8 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="FETCH_DIR WRITE_DIR [SQ_DIR]")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
+    ap.add_argument("--balance", action="store_true",
+                    help="filter workgroup balance table (per-workgroup trace), for profiles/")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
@@ -789,6 +869,9 @@ def main():
         return
     if args.calibrate:
         calibrate(args)
+        return
+    if args.balance:
+        balance(args)
         return
     run_bench(args)
 

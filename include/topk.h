@@ -263,6 +263,19 @@ typedef struct {
 int topk_profile_enable(int on);
 int topk_profile_read(topk_stage_times* out);
 
+/* Filter workgroup trace (measurement aid: how evenly the filter's
+ * workgroups finish; Appendix D, "Efficient GPU Implementation", asks for a
+ * pass at memory speed, which the slowest workgroup bounds).  While set,
+ * every call's filter launch writes, for each of its workgroups l < words / 2
+ * (l = row * workgroups per row + the workgroup's index in its row; workgroup
+ * l runs on XCD l mod 8), the device's 100 MHz realtime counter at the
+ * workgroup's start into buf[2 l] and at the end of its scan into
+ * buf[2 l + 1].  buf: caller-owned device memory of `words` 64-bit words,
+ * 8-byte aligned, written by later calls until replaced; NULL stops the
+ * trace.  Process-wide; not synchronised with calls in flight.  Errors:
+ * TOPK_EINVAL (misaligned buf). */
+int topk_filter_trace(uint64_t* buf, size_t words);
+
 /* BatchTopK consumer (Prof-K section 5, "Application: BatchTopK Sparse
  * Autoencoders": the batch-global top-k keeps the K largest of the flattened
  * B x d_dict activations).  Turns a selection into the sparse activation:

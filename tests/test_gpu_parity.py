@@ -442,6 +442,36 @@ def test_out_tensors_checked_and_empty_batch():
         tss.topk(e, 1001)
 
 
+def test_filter_trace_stamps_every_workgroup():
+    # the workgroup trace (a measurement aid) stamps every filter workgroup's
+    # start and end, leaves the answer exact, and stops when cleared
+    tss = _tss()
+    x = workloads.normal_f32(3, 2 ** 20 + 9, 431)
+    xt = to_dev(x, "float32")
+    trace = torch.zeros(2 * 4096, dtype=torch.int64, device="cuda")
+    tss.filter_trace(trace)
+    try:
+        say("filter trace: 3 rows")
+        v, i = tss.topk(xt, 64)
+        torch.cuda.synchronize()
+    finally:
+        tss.filter_trace(None)
+    assert np.array_equal(i.cpu().numpy(), oracle.topk(x, 64)[1])
+    t = trace.cpu().numpy().reshape(-1, 2)
+    used = np.nonzero(t[:, 0])[0]
+    assert len(used) >= 3 and np.array_equal(used, np.arange(len(used)))   # rows x workgroups
+    assert len(used) % 3 == 0
+    assert (t[used, 1] > t[used, 0]).all()
+    assert (t[used, 1] - t[used, 0]).max() < 100 * 100_000   # under 100 ms at 100 MHz
+    assert not t[len(used):].any()
+    trace.zero_()
+    tss.topk(xt, 64)
+    torch.cuda.synchronize()
+    assert not trace.cpu().numpy().any()   # stopped
+    with pytest.raises(ValueError):
+        tss.filter_trace(torch.zeros(4, dtype=torch.int32, device="cuda"))
+
+
 def test_stream_read_reads_and_writes_nothing():
     # the read-ceiling aid: valid sizes run, a ragged or misaligned buffer
     # is refused, and the data and the sink are left as they were

@@ -31,7 +31,7 @@ __all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "sca
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code",
            "TAU_NONE", "TAU_FILTER_LISTS", "TAU_KTAU_LISTS", "TAU_KTAU_REGS", "TAU_KTAU_STREAM",
            "TAU_FORCED", "TAU_FILTER_RADIX", "TAU_BIN_STREAMED", "TAU_BIN_RADIX",
-           "TEST_BARRIER_GIVEUP"]
+           "TEST_BARRIER_GIVEUP", "filter_trace"]
 
 _TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}
 _NAME_CODES = _lib.DTYPE_CODES
@@ -180,6 +180,19 @@ def read_stats(rows: int, workspace: Workspace | None = None, device=None) -> li
         _lib.check(_lib.lib.topk_read_stats(ws.buf.data_ptr(), rows, arr, stream), "topk_read_stats")
     return [{"tau_key": a.tau_key, "r_sampled": a.r_sampled, "path": a.path, "passes": a.passes,
              "flags": a.flags, "ties": a.ties, "tau_route": a.tau_route} for a in arr]
+
+
+def filter_trace(buf) -> None:
+    """Measurement aid: while set, every call's filter launch writes, per
+    workgroup l (row * workgroups per row + index), the device's 100 MHz
+    realtime counter at its start and at the end of its scan into buf[2l] and
+    buf[2l + 1] (buf: an int64 CUDA tensor; None stops the trace)."""
+    if buf is None:
+        _lib.check(_lib.lib.topk_filter_trace(None, 0), "topk_filter_trace")
+        return
+    if not (buf.is_cuda and buf.dtype == torch.int64 and buf.is_contiguous()):
+        raise ValueError("filter_trace: a contiguous int64 CUDA tensor")
+    _lib.check(_lib.lib.topk_filter_trace(buf.data_ptr(), buf.numel()), "topk_filter_trace")
 
 
 def profile_enable(on: bool = True) -> None:

@@ -32,7 +32,8 @@ TEST_BARRIER_GIVEUP = 1
 # Names of every function include/topk.h declares.
 EXPORTS = ("topk_default_params", "topk_plan", "topk_workspace_size", "topk_workspace_init",
            "topk", "topk_ex", "topk_read_stats", "topk_profile_enable", "topk_profile_read",
-           "topk_scatter", "topk_stream_read", "topk_status_string", "topk_noalloc")
+           "topk_scatter", "topk_stream_read", "topk_status_string", "topk_noalloc",
+           "topk_filter_trace")
 STAGES = ("sample", "tau", "filter", "refine", "exact", "sort")
 
 
@@ -86,6 +87,7 @@ def _load():
     L.topk_read_stats.argtypes = [vp, i64, P(RowStats), vp]
     L.topk_profile_enable.argtypes = [i32]
     L.topk_profile_read.argtypes = [P(StageTimes)]
+    L.topk_filter_trace.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     L.topk_stream_read.argtypes = [vp, sz, vp, vp]
     L.topk_scatter.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
     L.topk_status_string.argtypes = [i32]

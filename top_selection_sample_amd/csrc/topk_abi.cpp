@@ -18,6 +18,10 @@ namespace {
 
 std::atomic<uint64_t> g_calls{0};
 
+// ---- filter workgroup trace (measurement aid)
+std::atomic<uint64_t*> g_trace_buf{nullptr};
+std::atomic<uint64_t> g_trace_words{0};
+
 // ---- stage timing
 std::atomic<int> g_prof{0};
 std::mutex g_prof_mu;
@@ -230,6 +234,11 @@ int topk_run(const void* values, int64_t n, int64_t rows, int64_t k, int dtype, 
     a.hdr = reinterpret_cast<tk::WsHeader*>(ws);
     a.tau_key = (params && params->use_force_tau) ? params->force_tau_key : 0u;
     if (params && (params->test_flags & TOPK_TEST_BARRIER_GIVEUP)) a.spin_limit = 0;
+    a.filter_trace = g_trace_buf.load();
+    {
+      const uint64_t wgs = g_trace_words.load() / 2;
+      a.trace_wgs = a.filter_trace ? (uint32_t)(wgs < 0xFFFFFFFFull ? wgs : 0xFFFFFFFFull) : 0u;
+    }
     a.values = values;
     a.out_values = out_values;
     a.out_idx = out_indices;
@@ -324,6 +333,13 @@ int topk_read_stats(const void* workspace, int64_t rows, topk_row_stats* out, vo
   } catch (...) {
     return TOPK_EINVAL;
   }
+}
+
+int topk_filter_trace(uint64_t* buf, size_t words) {
+  if (buf && reinterpret_cast<uintptr_t>(buf) % 8) return TOPK_EINVAL;
+  g_trace_words.store(buf ? (uint64_t)words : 0);
+  g_trace_buf.store(buf && words >= 2 ? buf : nullptr);
+  return TOPK_OK;
 }
 
 int topk_profile_enable(int on) {

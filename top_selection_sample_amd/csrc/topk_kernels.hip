@@ -164,7 +164,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_FILTER, 1);
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
                   0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr, a.cbuf, a.aux,
-                  (WsHeader*)nullptr, p.sig);
+                  (WsHeader*)nullptr, p.sig, a.filter_trace, a.trace_wgs);
       mark(STAGE_FILTER, 0);
     } else if (p.path == PLAN_SAMPLED) {
       const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
@@ -195,7 +195,7 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       WsHeader* validate = lists ? nullptr : a.hdr;
       TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
                   in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr,
-                  a.cbuf, a.aux, validate, p.sig);
+                  a.cbuf, a.aux, validate, p.sig, a.filter_trace, a.trace_wgs);
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,

@@ -56,6 +56,8 @@ struct LaunchArgs {
   WsHeader* hdr;
   uint32_t tau_key = 0;          // plan.force_tau: the threshold key of every row
   uint32_t spin_limit = SPIN_LIMIT_DEFAULT;
+  uint64_t* filter_trace = nullptr;   // measurement aid: per-workgroup stamps of the filter
+  uint32_t trace_wgs = 0;             //   (for workgroups below this count)
   const void* values;
   void* out_values;
   int64_t* out_idx;

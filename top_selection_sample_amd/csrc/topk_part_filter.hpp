@@ -318,12 +318,17 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     RowState* __restrict__ states, uint32_t n, uint32_t tlist_n, uint32_t tlist_stride,
     uint32_t t, uint32_t bpr, uint32_t cap, uint32_t B, uint32_t track_kmax,
     RowCtr* __restrict__ rctr, uint64_t* __restrict__ cbuf, uint64_t* __restrict__ tbuf,
-    WsHeader* validate, uint64_t sig) {
+    WsHeader* validate, uint64_t sig, uint64_t* __restrict__ wg_trace, uint32_t trace_wgs) {
   using D = Dt<DT>;
   assume_block_threads(FILTER_THREADS);
   const uint32_t row = blockIdx.y;
   RowState* st = states + row;
   Thr thr;   // set below, once tau is known
+  // (measurement aid: realtime stamps of this workgroup's start and the end
+  // of its scan)
+  const uint32_t lwg = row * bpr + blockIdx.x;
+  const bool traced = wg_trace && lwg < trace_wgs;
+  if (traced && threadIdx.x == 0) wg_trace[2 * (size_t)lwg] = __builtin_amdgcn_s_memrealtime();
 
   __shared__ __align__(16) uint64_t s_stage[FILTER_WAVES][STAGE_SLOTS];   // (16: the prologue bins)
   __shared__ uint64_t s_tstage[FILTER_WAVES][STAGE_SLOTS];
@@ -702,6 +707,8 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       push_one(ok && pass_of(raw), raw, idx);
     }
   }
+
+  if (traced && threadIdx.x == 0) wg_trace[2 * (size_t)lwg + 1] = __builtin_amdgcn_s_memrealtime();
 
   // Workgroup flush: one atomic per buffer, one for the tie count, and one
   // for the above-tau total (the staged entries plus those the waves
