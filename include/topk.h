@@ -195,6 +195,7 @@ typedef struct {
                          2 top-t lists in the threshold kernel, 3 every sample key in
                          registers, 4 every sample key streamed, 5 given by the caller
                          (use_force_tau), 6 top-t lists radix-selected in the filter's
+                         prologue, 7 sorted lists of 32 (t > 8) merged in the filter's
                          prologue.  Bit 3: the sample bin holding rank t had more
                          keys than LDS holds (streamed radix select); bit 4: that bin was
                          radix-selected in LDS. */

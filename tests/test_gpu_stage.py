@@ -82,21 +82,28 @@ def _routes():
     None).  With spread data the boundary bin's size depends on the dtype's
     key range (the int32 scores' top-t keys share one bin, for instance), so
     only the source is asserted there; the one-bin rows force the flags.
-    Top-t lists (t <= 32) of at most 4096 keys in all are selected in the
-    filter's prologue: by wave max extraction for t <= 8 and at most 2048
-    keys, else by a radix select over [largest list tail, largest head].  The
-    sampler builds lists of t <= 8 by extraction and longer ones by sorting;
-    beyond 32 every sample key goes to the threshold kernel."""
+    The sampler keeps per-workgroup lists of its t largest keys for t <= 8
+    (256 samples per workgroup, by extraction) and of its 32 largest, sorted,
+    for 8 < t <= 32 (1024 samples per workgroup); lists of at most 4096 keys
+    in all are selected in the filter's prologue: by wave max extraction for
+    t <= 8 and at most 2048 keys, by a radix select over [largest list tail,
+    largest head] for t <= 8 and more keys, and by bitonic merges of the
+    sorted lists for t > 8.  More list keys, or t beyond 32 (every sample
+    key), go to the threshold kernel."""
     tss = _tss()
     return {
         "filter_lists": ("spread", 16384, 3, tss.TAU_FILTER_LISTS, 0),
-        "filter_radix_t12": ("spread", 16384, 12, tss.TAU_FILTER_RADIX, 0),
-        "filter_radix_t16": ("spread", 32768, 16, tss.TAU_FILTER_RADIX, 0),
-        "filter_radix_t32": ("spread", 32768, 32, tss.TAU_FILTER_RADIX, 0),
-        "filter_radix_onebin": ("onebin", 16384, 14, tss.TAU_FILTER_RADIX, 0),
-        "filter_radix_onebin_t30": ("onebin", 4096, 30, tss.TAU_FILTER_RADIX, 0),
-        "ktau_lists_many": ("spread", 131072, 16, tss.TAU_KTAU_LISTS, None),
-        "ktau_lists_t32": ("spread", 131072, 32, tss.TAU_KTAU_LISTS, None),
+        "filter_radix_t8": ("spread", 131072, 8, tss.TAU_FILTER_RADIX, 0),
+        "filter_radix_onebin_t6": ("onebin", 100000, 6, tss.TAU_FILTER_RADIX, 0),
+        "filter_merge_t12": ("spread", 16384, 12, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_t16": ("spread", 32768, 16, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_t16_many": ("spread", 131072, 16, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_t32": ("spread", 32768, 32, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_t9_short": ("spread", 2048, 9, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_onebin": ("onebin", 16384, 14, tss.TAU_FILTER_MERGE, 0),
+        "filter_merge_onebin_t30": ("onebin", 4096, 30, tss.TAU_FILTER_MERGE, 0),
+        "ktau_lists_many": ("spread", 200000, 8, tss.TAU_KTAU_LISTS, None),
+        "ktau_lists_t32": ("spread", 262144, 32, tss.TAU_KTAU_LISTS, None),
         "ktau_regs": ("spread", 32768, 40, tss.TAU_KTAU_REGS, None),
         "ktau_stream": ("spread", 40000, 40, tss.TAU_KTAU_STREAM, None),
         "bin_streamed": ("onebin", 16384, 40, tss.TAU_KTAU_REGS, tss.TAU_BIN_STREAMED),
@@ -106,8 +113,10 @@ def _routes():
     }
 
 
-ROUTE_NAMES = ["filter_lists", "filter_radix_t12", "filter_radix_t16", "filter_radix_t32",
-               "filter_radix_onebin", "filter_radix_onebin_t30", "ktau_lists_many",
+ROUTE_NAMES = ["filter_lists", "filter_radix_t8", "filter_radix_onebin_t6", "filter_merge_t12",
+               "filter_merge_t16", "filter_merge_t16_many", "filter_merge_t32",
+               "filter_merge_t9_short",
+               "filter_merge_onebin", "filter_merge_onebin_t30", "ktau_lists_many",
                "ktau_lists_t32", "ktau_regs", "ktau_stream", "bin_streamed", "bin_radix",
                "bin_streamed_keys_streamed"]
 

@@ -18,7 +18,8 @@ import torch
 from . import _lib
 from ._lib import (PATH_AUTO, PATH_EXACT, PATH_FILTER, POLICY_ALG1, POLICY_EXACT_TAIL, POLICY_TUNED,
                    ROUTE_EXACT, ROUTE_FALLBACK, ROUTE_PARTIAL, ROUTE_SAMPLED, TAU_BIN_RADIX,
-                   TAU_BIN_STREAMED, TAU_FILTER_LISTS, TAU_FILTER_RADIX, TAU_FORCED,
+                   TAU_BIN_STREAMED, TAU_FILTER_LISTS, TAU_FILTER_MERGE, TAU_FILTER_RADIX,
+                   TAU_FORCED,
                    TAU_KTAU_LISTS, TAU_KTAU_REGS,
                    TAU_KTAU_STREAM, TAU_NONE, TEST_BARRIER_GIVEUP, Params, TopkError,
                    default_params)
@@ -30,7 +31,7 @@ __all__ = ["topk", "plan", "profile_enable", "profile_read", "stream_read", "sca
            "ROUTE_SAMPLED", "ROUTE_FALLBACK", "ROUTE_EXACT", "ROUTE_PARTIAL",
            "POLICY_EXACT_TAIL", "POLICY_ALG1", "POLICY_TUNED", "dtype_code",
            "TAU_NONE", "TAU_FILTER_LISTS", "TAU_KTAU_LISTS", "TAU_KTAU_REGS", "TAU_KTAU_STREAM",
-           "TAU_FORCED", "TAU_FILTER_RADIX", "TAU_BIN_STREAMED", "TAU_BIN_RADIX",
+           "TAU_FORCED", "TAU_FILTER_RADIX", "TAU_FILTER_MERGE", "TAU_BIN_STREAMED", "TAU_BIN_RADIX",
            "TEST_BARRIER_GIVEUP", "filter_trace"]
 
 _TORCH_CODES = {torch.int32: 0, torch.float32: 1, torch.bfloat16: 2}

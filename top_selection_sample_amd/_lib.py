@@ -24,7 +24,7 @@ ROUTE_SAMPLED, ROUTE_FALLBACK, ROUTE_EXACT, ROUTE_PARTIAL = 0, 1, 2, 3
 # how the threshold was selected (read_stats "tau_route"): the source in the
 # low 3 bits, plus flags for a boundary bin beyond LDS / radix-selected in LDS
 (TAU_NONE, TAU_FILTER_LISTS, TAU_KTAU_LISTS, TAU_KTAU_REGS, TAU_KTAU_STREAM, TAU_FORCED,
- TAU_FILTER_RADIX) = range(7)
+ TAU_FILTER_RADIX, TAU_FILTER_MERGE) = range(8)
 TAU_BIN_STREAMED, TAU_BIN_RADIX = 8, 16
 # topk_params.test_flags: every exact-route grid-barrier wait gives up at once
 TEST_BARRIER_GIVEUP = 1

@@ -82,6 +82,7 @@ enum : uint32_t {
   TAU_KTAU_STREAM = 4,   // every sample key, streamed by k_tau
   TAU_FORCED = 5,        // given by the caller
   TAU_FILTER_RADIX = 6,  // per-workgroup top-t lists, radix-selected in the filter's prologue
+  TAU_FILTER_MERGE = 7,  // per-workgroup sorted lists of 32, merged in the filter's prologue
   TAU_BIN_STREAMED = 8,  // flag: the boundary bin exceeded LDS
   TAU_BIN_RADIX = 16,    // flag: the boundary bin was radix-selected in LDS
 };

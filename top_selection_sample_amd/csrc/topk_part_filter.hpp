@@ -240,6 +240,26 @@ __device__ __forceinline__ bool native_eq(uint32_t raw, const Thr& t) {
   else return __uint_as_float(raw << 16) == t.f;
 }
 
+// bf16 screen of a 16-byte vector (eight elements) for the plain-threshold
+// loop: whether some element's magnitude bits reach tau's bits, with packed
+// 16-bit operations (a mask of the sign bits, three maxima, one saturating
+// subtraction), where the exact test takes two instructions per element and
+// a scalar OR per pair.  With tau > 0 (tb1x2 = tau's bits - 1 in both halves)
+// every passing element is caught: a positive one at or above tau, and NaN
+// of either sign, whose magnitude bits exceed every finite value's.  The
+// screen also flags negative elements of magnitude >= tau; the survivor code
+// tests each flagged element exactly, so that only costs a queue entry.  With
+// tau <= 0 (all = true) every vector is flagged: most elements pass then.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bool bf16_screen(const u32x4& v, uint32_t tb1x2, bool all) {
+  auto mag = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
+  const u16x2 a = __builtin_elementwise_max(mag(v[0]), mag(v[1]));
+  const u16x2 b = __builtin_elementwise_max(mag(v[2]), mag(v[3]));
+  const u16x2 d = __builtin_elementwise_sub_sat(__builtin_elementwise_max(a, b),
+                                                __builtin_bit_cast(u16x2, tb1x2));
+  return all || __builtin_bit_cast(uint32_t, d) != 0u;
+}
+
 // tau from the sampler's per-workgroup top-t lists (ns keys, list g at
 // [g t, g t + t), largest first), by one filter workgroup, for ns up to
 // FILTER_THREADS * TL_PER keys and any t <= TOPT; thread tid holds key
@@ -306,6 +326,60 @@ __device__ __forceinline__ uint32_t tau_from_lists(const uint32_t (&v)[TL_PER], 
     pos = shift;
   }
   return pfx;
+}
+
+// tau from the sampler's sorted per-workgroup lists of TOPT = 32 keys (list
+// g at keys [32 g, 32 g + 32), largest first), for 8 < t <= 32 and ns <=
+// FILTER_THREADS * TL_PER keys: the t-th largest of their union, by bitonic
+// merges that keep the 32 largest.  Thread tid holds key q * FILTER_THREADS
+// + tid in v[q] (keys at or past ns count as 0, which cannot raise the t-th
+// largest), so each register of a wave holds two whole lists, one per half:
+// the second reversed makes the 64 lanes bitonic and one merge leaves the
+// pair's 32 largest, sorted, in lanes 0-31.  The eight registers are merged
+// pairwise in three more rounds, then one wave merges the eight waves'
+// lists.  s_m: FILTER_WAVES * 32 + 1 words.  Every thread calls it.
+__device__ __forceinline__ uint32_t tau_from_sorted32(const uint32_t (&v0)[TL_PER], uint32_t ns,
+                                                      uint32_t t, uint32_t* s_m) {
+  static_assert(TOPT == 32 && FILTER_THREADS % 64 == 0, "two lists of 32 per wave register");
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  // (only the registers that hold keys: the merges are VALU-bound, and with
+  // two workgroups per compute unit sixteen waves share its four SIMDs)
+  const uint32_t nq = (ns + FILTER_THREADS - 1) / FILTER_THREADS;   // 1 .. TL_PER, uniform
+  uint32_t v[TL_PER];
+#pragma unroll
+  for (uint32_t q = 0; q < TL_PER; ++q) {
+    v[q] = 0u;
+    if (q < nq) {
+      const uint32_t x = q * FILTER_THREADS + tid < ns ? v0[q] : 0u;
+      const uint32_t y = (uint32_t)__shfl((int)x, (int)(lane < 32 ? lane : 95u - lane), 64);
+      v[q] = wave_merge_desc(y);
+    }
+  }
+  auto pair = [&](uint32_t a, uint32_t b) {   // lanes 0-31 of a, then lanes 31..0 of b
+    const uint32_t rb = (uint32_t)__shfl((int)b, (int)(63u - lane), 64);
+    return wave_merge_desc(lane < 32 ? a : rb);
+  };
+#pragma unroll
+  for (uint32_t step = 1; step < TL_PER; step <<= 1) {
+#pragma unroll
+    for (uint32_t q = 0; q + step < TL_PER; q += 2 * step)
+      if (q + step < nq) v[q] = pair(v[q], v[q + step]);
+  }
+  if (lane < 32) s_m[w * 32 + lane] = v[0];
+  __syncthreads();
+  if (w == 0) {
+    uint32_t x[FILTER_WAVES];
+#pragma unroll
+    for (uint32_t j = 0; j < FILTER_WAVES; ++j) x[j] = s_m[j * 32 + (lane & 31u)];
+#pragma unroll
+    for (uint32_t step = 1; step < FILTER_WAVES; step <<= 1) {
+#pragma unroll
+      for (uint32_t j = 0; j + step < FILTER_WAVES; j += 2 * step) x[j] = pair(x[j], x[j + step]);
+    }
+    if (lane == t - 1) s_m[FILTER_WAVES * 32] = x[0];
+  }
+  __syncthreads();
+  return s_m[FILTER_WAVES * 32];
 }
 
 template <int DT>
@@ -506,6 +580,11 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       tlv[q] = kl[i < klast ? i : klast];   // (clamped: masked where used)
     }
   }
+  // so are the row's state and, when k_tau or the caller set it, tau: read
+  // after the stream's first loads, they came back only after them (about
+  // 2 us with one workgroup per unit, 4 with two)
+  const uint32_t row_status = st->status;
+  const uint32_t tau_given = tlist_n ? 0u : st->tau_key;
   constexpr size_t sstep = FILTER_UNROLL * stride;
   u32x4 nxt[FILTER_UNROLL], nx2[FILTER_UNROLL];
   const bool more2_ = step_ok(vi + sstep);
@@ -528,10 +607,9 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
   // them, and stores nothing; the empty asm keeps the compiler from moving
   // this check, and its wait for the row state, in front of them)
   asm volatile("" ::: "memory");
-  if (st->status != ST_FILTER) return;
+  if (row_status != ST_FILTER) return;
   // k_tau has left every row's sample histogram zero: stamp the workspace
   if (validate && row == 0 && blockIdx.x == 0 && tid == 0) validate->stamp = sig;
-  const uint32_t tau_given = tlist_n ? 0u : st->tau_key;
   // tau: given by k_tau, or (tlist_n > 0) the t-th largest of the sampler's
   // per-workgroup top-t lists, selected here by every workgroup
   uint32_t tau;
@@ -548,6 +626,9 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
       }
       block_top_t4<FILTER_WAVES, 8>(v, cnt, t, s_tl, s_tc, s_to);
       tau = s_to[t - 1];   // the lists hold at least t keys
+    } else if (t > TOPT_EXTRACT) {
+      // (sorted lists of 32; the staging area is free until the loop)
+      tau = tau_from_sorted32(tlv, tlist_n, t, reinterpret_cast<uint32_t*>(&s_stage[0][0]));
     } else {
       // (the staging area is free until the loop: its first 8 KB hold the bins)
       tau = tau_from_lists(tlv, tlist_n, t, reinterpret_cast<uint32_t*>(&s_stage[0][0]), s_tc);
@@ -557,6 +638,9 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
     tau = tau_given;
   }
   thr = make_thr<DT>(tau, 0xFFFFFFFFu);
+  // (bf16: the screen's constant, and whether it flags every vector)
+  const bool scr_all = !(thr.f > 0.f);
+  const uint32_t scr_tb1 = scr_all ? 0u : ((__float_as_uint(thr.f) >> 16) - 1u) * 0x10001u;
   if (thr.kind == 0) {
     // one step: the compares, the hits queued, then the drains the queue
     // calls for (all that is left after the last step)
@@ -565,14 +649,11 @@ __global__ __launch_bounds__(FILTER_THREADS) void k_filter(
 #pragma unroll
       for (uint32_t u = 0; u < FILTER_UNROLL; ++u) {
         uint32_t any = 0;
+        if constexpr (DT == DT_BF16) {
+          any = bf16_screen(v[u], scr_tb1, scr_all) ? 1u : 0u;
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (DT == DT_BF16) {
-            any |= (uint32_t)native_pass<DT>(v[u][q] & 0xFFFFu, thr);
-            any |= (uint32_t)native_pass<DT>(v[u][q] >> 16, thr);
-          } else {
-            any |= (uint32_t)native_pass<DT>(v[u][q], thr);
-          }
+          for (int q = 0; q < 4; ++q) any |= (uint32_t)native_pass<DT>(v[u][q], thr);
         }
         const uint64_t hm = ballot(any != 0u);
         if (hm) enqueue(any != 0u, hm, v[u], (uint32_t)(vc + u * stride));

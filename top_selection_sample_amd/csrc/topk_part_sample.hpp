@@ -65,39 +65,72 @@ constexpr uint32_t SH_BINS = 1u << SH_BITS;
 constexpr uint32_t TOPT = 32;
 constexpr uint32_t TOPT_EXTRACT = 8;
 constexpr uint32_t SAMPLE_THREADS = 256;
+constexpr uint32_t SAMPLE_THREADS_SORTED = 1024;
 static_assert((SAMPLE_THREADS / 64) * TOPT_EXTRACT <= 2 * 64, "one wave merges the wave lists, two per lane");
 static_assert(SAMPLE_THREADS == 256 && TOPT == 32, "the sorted path merges four wave lists of 32");
 
-// One wave's 64 values sorted largest first (lane 0 the largest): Batcher's
-// bitonic sorting network, partners exchanged across lanes.
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
-  const uint32_t l = lane_id();
-#pragma unroll
-  for (uint32_t k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t p = (uint32_t)__shfl_xor((int)v, (int)j, 64);
-      // runs of k alternate descending / ascending, so that each pair of
-      // runs is a bitonic sequence for the next k; the last run descends
-      const bool desc = (l & k) == 0u, low = (l & j) == 0u;
-      const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
-      v = (low == desc) ? mx : mn;
-    }
+// The value of lane (this lane ^ J) for J = 1, 2, ..., 32, without the LDS
+// crossbar for J <= 8: DPP moves (quad permutations for 1 and 2, row shifts
+// for 4, a row rotation for 8), a swizzle for 16 and a half-wave swap for 32
+// (each checked against a shuffle on the GPU, all 64 lanes).  Each DPP move
+// is taken into a temporary (the empty asm, not volatile, so independent
+// networks still interleave) before it is combined, so that no DPP-modified
+// arithmetic is formed from it.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+  asm("" : "+v"(r));
+  return r;
+}
+template <uint32_t J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) {
+    return dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  } else if constexpr (J == 2) {
+    return dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  } else if constexpr (J == 4) {
+    const uint32_t a = dpp_mov<0x104>(v), b = dpp_mov<0x114>(v);   // row_shl:4, row_shr:4
+    return (lane_id() & 4u) ? b : a;
+  } else if constexpr (J == 8) {
+    return dpp_mov<0x128>(v);   // row_ror:8
+  } else if constexpr (J == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);   // swap 16-lane halves
+  } else {
+    static_assert(J == 32, "lane strides 1 to 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // swap 32-lane halves
+    return lane_id() < 32 ? r[1] : r[0];
   }
-  return v;
 }
 
-// A bitonic sequence over the wave's 64 lanes sorted largest first.
-__device__ __forceinline__ uint32_t wave_merge_desc(uint32_t v) {
+// Batcher's bitonic network over a wave's 64 lanes, one compare-exchange
+// stage per template step (partner lane ^ J; runs of K alternate descending
+// and ascending so that each pair of runs is bitonic for the next K; the last
+// run, K = 64, descends).
+template <uint32_t K, uint32_t J>
+__device__ __forceinline__ uint32_t bitonic_sort_steps(uint32_t v) {
   const uint32_t l = lane_id();
-#pragma unroll
-  for (uint32_t j = 32; j > 0; j >>= 1) {
-    const uint32_t p = (uint32_t)__shfl_xor((int)v, (int)j, 64);
-    const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
-    v = (l & j) == 0u ? mx : mn;
-  }
-  return v;
+  const uint32_t p = xor_lane<J>(v);
+  const bool desc = (l & K) == 0u, low = (l & J) == 0u;
+  const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
+  v = (low == desc) ? mx : mn;
+  if constexpr (J > 1) return bitonic_sort_steps<K, J / 2>(v);
+  else if constexpr (K < 64) return bitonic_sort_steps<2 * K, K>(v);
+  else return v;
 }
+template <uint32_t J>
+__device__ __forceinline__ uint32_t bitonic_merge_steps(uint32_t v) {
+  const uint32_t p = xor_lane<J>(v);
+  const uint32_t mx = v > p ? v : p, mn = v > p ? p : v;
+  v = (lane_id() & J) == 0u ? mx : mn;
+  if constexpr (J > 1) return bitonic_merge_steps<J / 2>(v);
+  else return v;
+}
+
+// One wave's 64 values sorted largest first (lane 0 the largest).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) { return bitonic_sort_steps<2, 1>(v); }
+
+// A bitonic sequence over the wave's 64 lanes sorted largest first.
+__device__ __forceinline__ uint32_t wave_merge_desc(uint32_t v) { return bitonic_merge_steps<32>(v); }
 
 // The 32 largest of the workgroup's values (one per thread, 0 for none),
 // largest first, into out[0..32).  s_l: 128 words, s_m: 64 words.  Every
@@ -120,6 +153,33 @@ __device__ __forceinline__ void block_top32_sorted(uint32_t v, uint32_t* s_l, ui
     if (lane < 32) out[lane] = x;
   }
   __syncthreads();
+}
+
+// The same for a workgroup of NW waves (a power of two): each wave sorts its
+// 64, then rounds of bitonic merges halve the wave lists (the second list of
+// each pair reversed).  s_a: NW * 32 words, s_b: NW / 2 * 32 words.
+template <uint32_t NW>
+__device__ __forceinline__ void block_top32_sorted_n(uint32_t v, uint32_t* s_a, uint32_t* s_b,
+                                                     uint32_t* out) {
+  static_assert(NW >= 2 && (NW & (NW - 1)) == 0, "a power of two of waves");
+  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
+  v = wave_sort_desc(v);
+  if (lane < 32) s_a[w * 32 + lane] = v;
+  __syncthreads();
+  uint32_t* src = s_a;
+  uint32_t* dst = s_b;
+#pragma unroll
+  for (uint32_t m = NW / 2; m >= 1; m >>= 1) {
+    if (w < m) {
+      uint32_t x = lane < 32 ? src[2 * w * 32 + lane] : src[(2 * w + 1) * 32 + (63 - lane)];
+      x = wave_merge_desc(x);
+      if (lane < 32) (m == 1 ? out : dst)[w * 32 + lane] = x;
+    }
+    __syncthreads();
+    uint32_t* tmp = src;
+    src = dst;
+    dst = tmp;
+  }
 }
 
 // The t largest alive values of the wave (with multiplicity), largest first,
@@ -239,23 +299,28 @@ __device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint
 }
 
 // Writes the keys k_tau selects from: all S sample keys and their 11-bit
-// histogram (lists = 0), or each workgroup's t largest at g * t (lists = 1;
+// histogram (lists = 0), or each workgroup's t largest at g * t, for t above
+// TOPT_EXTRACT its TOPT largest at g * TOPT, sorted (lists = 1;
 // k_tau histograms those itself: the largest keys of every workgroup share
 // a few top bins, and global atomics on them would serialise).  The global
 // histogram is used only when the workspace stamp says it starts at zero;
 // otherwise k_tau histograms the keys itself.
-template <int DT>
-__global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
+// NT threads per workgroup: SAMPLE_THREADS, or SAMPLE_THREADS_SORTED for the
+// sorted lists of 32 (t > TOPT_EXTRACT), whose fewer, longer lists make the
+// filter's merge of them cheaper.
+template <int DT, uint32_t NT>
+__global__ __launch_bounds__(NT) void k_sample(
     const void* __restrict__ values, uint64_t seed, uint32_t* __restrict__ skeys, uint32_t n,
     uint32_t S, uint32_t SP, uint32_t half_bits, uint32_t lists, uint32_t t, uint32_t route,
     RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs, WsHeader* hdr,
     uint32_t* __restrict__ shist, uint64_t sig) {
   // (the arguments the gather needs come first: the first 14 words of the
   // argument block arrive in scalar registers with the launch)
+  static_assert(NT == SAMPLE_THREADS || NT == SAMPLE_THREADS_SORTED, "two workgroup sizes");
   __shared__ uint32_t h[SH_BINS];
-  __shared__ uint32_t s_wl[4 * TOPT], s_wc[8], s_out[TOPT], s_m[2 * TOPT];
+  __shared__ uint32_t s_wl[NT / 64 * TOPT], s_wc[8], s_out[TOPT], s_m[NT / 128 * TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
-  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
+  const uint32_t j = blockIdx.x * NT + tid;
   const bool in = j < S;
   // The gather goes out first, unconditionally (a lane past S reads element
   // 0 and drops it): the rest of the set-up overlaps its latency, and the
@@ -277,7 +342,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     start_sampled_row(states + row, rctr + row, 0u, route);
   uint32_t* gh = shist + (size_t)row * SH_BINS;
   if (gh_ok) {
-    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
+    for (uint32_t i = tid; i < SH_BINS; i += NT) h[i] = 0;
     __syncthreads();
   }
   uint32_t key = 0;
@@ -291,15 +356,22 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
   if (!lists) {
     if (!gh_ok) return;
     __syncthreads();
-    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
+    for (uint32_t i = tid; i < SH_BINS; i += NT)
       if (h[i]) atomicAdd(&gh[i], h[i]);
     return;
   }
   // this workgroup's t largest keys, zero-padded
   uint32_t c = TOPT;
-  if (t <= TOPT_EXTRACT) c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
-  else block_top32_sorted(j < S ? key : 0u, s_wl, s_m, s_out);
-  if (tid < t) skeys[(size_t)row * SP + blockIdx.x * t + tid] = tid < c ? s_out[tid] : 0u;
+  if constexpr (NT == SAMPLE_THREADS) {
+    if (t <= TOPT_EXTRACT) c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
+    else block_top32_sorted(j < S ? key : 0u, s_wl, s_m, s_out);
+  } else {
+    block_top32_sorted_n<NT / 64>(j < S ? key : 0u, s_wl, s_m, s_out);
+  }
+  // (t > TOPT_EXTRACT: all TOPT sorted keys; the union of these longer lists
+  // still holds the t largest sampled keys, each list its own largest first)
+  const uint32_t len = t <= TOPT_EXTRACT ? t : TOPT;
+  if (tid < len) skeys[(size_t)row * SP + blockIdx.x * len + tid] = tid < c ? s_out[tid] : 0u;
 }
 
 // ======================================================================
