@@ -82,9 +82,9 @@ def _routes():
     None).  With spread data the boundary bin's size depends on the dtype's
     key range (the int32 scores' top-t keys share one bin, for instance), so
     only the source is asserted there; the one-bin rows force the flags.
-    The sampler keeps per-workgroup lists of its t largest keys for t <= 8
-    (256 samples per workgroup, by extraction) and of its 32 largest, sorted,
-    for 8 < t <= 32 (1024 samples per workgroup); lists of at most 4096 keys
+    The sampler keeps per-workgroup lists (256 samples each) of its t
+    largest keys for t <= 8 (by extraction) and of its 32 largest, sorted,
+    for 8 < t <= 32; lists of at most 4096 keys
     in all are selected in the filter's prologue: by wave max extraction for
     t <= 8 and at most 2048 keys, by a radix select over [largest list tail,
     largest head] for t <= 8 and more keys, and by bitonic merges of the
@@ -97,7 +97,7 @@ def _routes():
         "filter_radix_onebin_t6": ("onebin", 100000, 6, tss.TAU_FILTER_RADIX, 0),
         "filter_merge_t12": ("spread", 16384, 12, tss.TAU_FILTER_MERGE, 0),
         "filter_merge_t16": ("spread", 32768, 16, tss.TAU_FILTER_MERGE, 0),
-        "filter_merge_t16_many": ("spread", 131072, 16, tss.TAU_FILTER_MERGE, 0),
+        "ktau_sorted_lists": ("spread", 131072, 16, tss.TAU_KTAU_LISTS, None),
         "filter_merge_t32": ("spread", 32768, 32, tss.TAU_FILTER_MERGE, 0),
         "filter_merge_t9_short": ("spread", 2048, 9, tss.TAU_FILTER_MERGE, 0),
         "filter_merge_onebin": ("onebin", 16384, 14, tss.TAU_FILTER_MERGE, 0),
@@ -114,7 +114,7 @@ def _routes():
 
 
 ROUTE_NAMES = ["filter_lists", "filter_radix_t8", "filter_radix_onebin_t6", "filter_merge_t12",
-               "filter_merge_t16", "filter_merge_t16_many", "filter_merge_t32",
+               "filter_merge_t16", "ktau_sorted_lists", "filter_merge_t32",
                "filter_merge_t9_short",
                "filter_merge_onebin", "filter_merge_onebin_t30", "ktau_lists_many",
                "ktau_lists_t32", "ktau_regs", "ktau_stream", "bin_streamed", "bin_radix",

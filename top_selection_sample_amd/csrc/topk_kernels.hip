@@ -131,24 +131,6 @@ static hipError_t launch_finish(const LaunchArgs& a, uint32_t small_k, uint32_t 
   return hipGetLastError();
 }
 
-// k_sample for a dtype and a workgroup size (SAMPLE_THREADS or SAMPLE_THREADS_SORTED).
-#define SAMPLE_DISPATCH(dt, nt, grid, stream, ...)                                           \
-  do {                                                                                       \
-    if ((nt) == SAMPLE_THREADS_SORTED) {                                                     \
-      switch (dt) {                                                                          \
-        case DT_I32: hipLaunchKernelGGL((k_sample<DT_I32, SAMPLE_THREADS_SORTED>), grid, dim3(SAMPLE_THREADS_SORTED), 0, stream, __VA_ARGS__); break; \
-        case DT_F32: hipLaunchKernelGGL((k_sample<DT_F32, SAMPLE_THREADS_SORTED>), grid, dim3(SAMPLE_THREADS_SORTED), 0, stream, __VA_ARGS__); break; \
-        default: hipLaunchKernelGGL((k_sample<DT_BF16, SAMPLE_THREADS_SORTED>), grid, dim3(SAMPLE_THREADS_SORTED), 0, stream, __VA_ARGS__); break; \
-      }                                                                                      \
-    } else {                                                                                 \
-      switch (dt) {                                                                          \
-        case DT_I32: hipLaunchKernelGGL((k_sample<DT_I32, SAMPLE_THREADS>), grid, dim3(SAMPLE_THREADS), 0, stream, __VA_ARGS__); break; \
-        case DT_F32: hipLaunchKernelGGL((k_sample<DT_F32, SAMPLE_THREADS>), grid, dim3(SAMPLE_THREADS), 0, stream, __VA_ARGS__); break; \
-        default: hipLaunchKernelGGL((k_sample<DT_BF16, SAMPLE_THREADS>), grid, dim3(SAMPLE_THREADS), 0, stream, __VA_ARGS__); break; \
-      }                                                                                      \
-    }                                                                                        \
-  } while (0)
-
 hipError_t launch_pipeline(const LaunchArgs& a) {
   const Plan& p = a.plan;
   const uint32_t rows = (uint32_t)p.rows, n = (uint32_t)p.n, k = (uint32_t)p.k;
@@ -185,23 +167,18 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
                   (WsHeader*)nullptr, p.sig, a.filter_trace, a.trace_wgs);
       mark(STAGE_FILTER, 0);
     } else if (p.path == PLAN_SAMPLED) {
-      // small threshold ranks: select from per-workgroup top-t lists; with
-      // few list keys every filter workgroup does that itself.  Lists of t
-      // keys from SAMPLE_THREADS samples each for t <= TOPT_EXTRACT, else
-      // sorted lists of TOPT keys from SAMPLE_THREADS_SORTED samples each;
-      // all of them within the row's S key slots
-      const bool sorted32 = p.t > (int64_t)TOPT_EXTRACT && p.t <= (int64_t)TOPT;
-      const uint32_t snt = sorted32 ? SAMPLE_THREADS_SORTED : SAMPLE_THREADS;
-      uint32_t sgx = (uint32_t)((p.S + snt - 1) / snt);
-      const uint32_t len = sorted32 ? TOPT : (uint32_t)p.t;
-      const bool lists = p.t <= (int64_t)TOPT && (int64_t)sgx * len <= p.S;
-      const uint32_t nt = lists ? snt : SAMPLE_THREADS;   // (all keys: SAMPLE_THREADS)
-      if (!lists) sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
+      const uint32_t sgx = (uint32_t)((p.S + SAMPLE_THREADS - 1) / SAMPLE_THREADS);
       const dim3 sg(sgx, rows);
+      // small threshold ranks: select from per-workgroup lists, of the t
+      // largest keys for t <= TOPT_EXTRACT, else of the TOPT largest, sorted;
+      // all of them within the row's S key slots.  With few list keys every
+      // filter workgroup selects tau itself.
+      const uint32_t len = p.t <= (int64_t)TOPT_EXTRACT ? (uint32_t)p.t : TOPT;
+      const bool lists = p.t <= (int64_t)TOPT && (int64_t)sgx * len <= p.S;
       const uint32_t ns = lists ? sgx * len : (uint32_t)p.S;   // keys to select from
       const bool in_filter = lists && ns <= TL_PER * FILTER_THREADS;
       mark(STAGE_SAMPLE, 1);
-      SAMPLE_DISPATCH(dt, nt, sg, s, a.values, a.seed, a.skeys, n,
+      TK_DISPATCH(dt, k_sample, sg, dim3(SAMPLE_THREADS), 0, s, a.values, a.seed, a.skeys, n,
                   (uint32_t)p.S, (uint32_t)p.SP, p.half_bits, (uint32_t)(lists ? 1 : 0),
                   (uint32_t)p.t,
                   (uint32_t)((p.t <= 8 && ns <= 4 * FILTER_THREADS)

@@ -51,22 +51,20 @@ constexpr uint32_t SH_BITS = 11;
 constexpr uint32_t SH_BINS = 1u << SH_BITS;
 
 // Small threshold ranks (t <= TOPT): every sampler workgroup keeps only its
-// own t largest keys, largest first and zero-padded to t, and tau is
-// selected from those G * t keys instead of all S (by every filter
-// workgroup in its prologue when there are few, else by k_tau).  Their
-// union holds the t largest sampled keys, and padding keys of 0 cannot
-// raise the t-th largest, so tau is unchanged.  Up to TOPT_EXTRACT the
-// workgroup extracts its t largest one at a time; above, it sorts its keys
-// (a bitonic network over each wave's lanes, then two bitonic merges of the
-// wave lists).  (Letting the last sampler workgroup select saves the launch
-// but needs an agent-scope release fence in every workgroup: measured
-// slower, much slower with many rows.  Extraction up to 32 measured slower
-// too: on 2^28 bf16 with t = 32 the sampler took 17.8 us instead of 7.8.)
+// own largest keys, sorted largest first and zero-padded (a bitonic network
+// over each wave's lanes, then two bitonic merges of the wave lists): its t
+// largest for t <= TOPT_EXTRACT, its TOPT largest above, and tau is selected
+// from those lists instead of all S keys (by every filter workgroup in its
+// prologue when there are few, else by k_tau).  Their union holds the t
+// largest sampled keys, and longer lists or padding keys of 0 cannot change
+// the t-th largest, so tau is unchanged.  (Letting the last sampler
+// workgroup select saves the launch but needs an agent-scope release fence
+// in every workgroup: measured slower, much slower with many rows.
+// Extracting the t largest one at a time measured as fast up to t = 2 and
+// slower above: 17.8 us instead of 7.8 on 2^28 bf16 with t = 32.)
 constexpr uint32_t TOPT = 32;
-constexpr uint32_t TOPT_EXTRACT = 8;
+constexpr uint32_t TOPT_EXTRACT = 8;   // up to here the lists hold t keys, above TOPT
 constexpr uint32_t SAMPLE_THREADS = 256;
-constexpr uint32_t SAMPLE_THREADS_SORTED = 1024;
-static_assert((SAMPLE_THREADS / 64) * TOPT_EXTRACT <= 2 * 64, "one wave merges the wave lists, two per lane");
 static_assert(SAMPLE_THREADS == 256 && TOPT == 32, "the sorted path merges four wave lists of 32");
 
 // The value of lane (this lane ^ J) for J = 1, 2, ..., 32, without the LDS
@@ -155,33 +153,6 @@ __device__ __forceinline__ void block_top32_sorted(uint32_t v, uint32_t* s_l, ui
   __syncthreads();
 }
 
-// The same for a workgroup of NW waves (a power of two): each wave sorts its
-// 64, then rounds of bitonic merges halve the wave lists (the second list of
-// each pair reversed).  s_a: NW * 32 words, s_b: NW / 2 * 32 words.
-template <uint32_t NW>
-__device__ __forceinline__ void block_top32_sorted_n(uint32_t v, uint32_t* s_a, uint32_t* s_b,
-                                                     uint32_t* out) {
-  static_assert(NW >= 2 && (NW & (NW - 1)) == 0, "a power of two of waves");
-  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  v = wave_sort_desc(v);
-  if (lane < 32) s_a[w * 32 + lane] = v;
-  __syncthreads();
-  uint32_t* src = s_a;
-  uint32_t* dst = s_b;
-#pragma unroll
-  for (uint32_t m = NW / 2; m >= 1; m >>= 1) {
-    if (w < m) {
-      uint32_t x = lane < 32 ? src[2 * w * 32 + lane] : src[(2 * w + 1) * 32 + (63 - lane)];
-      x = wave_merge_desc(x);
-      if (lane < 32) (m == 1 ? out : dst)[w * 32 + lane] = x;
-    }
-    __syncthreads();
-    uint32_t* tmp = src;
-    src = dst;
-    dst = tmp;
-  }
-}
-
 // The t largest alive values of the wave (with multiplicity), largest first,
 // written by lane 0 to out[0..); returns how many (wave-uniform).
 __device__ __forceinline__ uint32_t wave_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* out) {
@@ -246,31 +217,6 @@ __device__ __forceinline__ uint32_t block_top_t4(uint32_t (&v)[4], uint32_t cnt,
   return s_wc[NW];
 }
 
-// The same over the whole workgroup (SAMPLE_THREADS = four waves) for t <=
-// TOPT_EXTRACT; the result in out (t words, largest first), its length
-// returned.  Each
-// wave extracts its own t largest; then one wave merges the four lists, lane
-// l holding entry l % 32 of lists l / 32 and l / 32 + 2 as a sorted pair.
-// s_wl: 4 * TOPT words, s_wc: 5 words.
-__device__ __forceinline__ uint32_t block_top_t(uint32_t v, bool alive, uint32_t t, uint32_t* s_wl,
-                                                uint32_t* s_wc, uint32_t* out) {
-  const uint32_t tid = threadIdx.x, w = tid >> 6, lane = tid & 63u;
-  const uint32_t c = wave_top_t(v, alive, t, s_wl + w * TOPT_EXTRACT);
-  if (lane == 0) s_wc[w] = c;
-  __syncthreads();
-  if (w == 0) {
-    const uint32_t q = lane >> 5, i = lane & 31u;
-    const bool a0 = i < s_wc[q], a1 = i < s_wc[q + 2];
-    const uint32_t x0 = a0 ? s_wl[q * TOPT_EXTRACT + i] : 0u;
-    const uint32_t x1 = a1 ? s_wl[(q + 2) * TOPT_EXTRACT + i] : 0u;
-    uint32_t pv[4] = {x0 > x1 ? x0 : x1, x0 > x1 ? x1 : x0, 0u, 0u};
-    const uint32_t cnt = wave_top_t4(pv, (a0 ? 1u : 0u) + (a1 ? 1u : 0u), t, out);
-    if (lane == 0) s_wc[4] = cnt;
-  }
-  __syncthreads();
-  return s_wc[4];
-}
-
 // Row setup for the sampled route (threshold known).
 __device__ __forceinline__ void start_sampled_row(RowState* st, RowCtr* rc, uint32_t tau,
                                                   uint32_t route) {
@@ -305,22 +251,18 @@ __device__ __forceinline__ void call_prologue(CallState* cs, WsHeader* hdr, uint
 // a few top bins, and global atomics on them would serialise).  The global
 // histogram is used only when the workspace stamp says it starts at zero;
 // otherwise k_tau histograms the keys itself.
-// NT threads per workgroup: SAMPLE_THREADS, or SAMPLE_THREADS_SORTED for the
-// sorted lists of 32 (t > TOPT_EXTRACT), whose fewer, longer lists make the
-// filter's merge of them cheaper.
-template <int DT, uint32_t NT>
-__global__ __launch_bounds__(NT) void k_sample(
+template <int DT>
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(
     const void* __restrict__ values, uint64_t seed, uint32_t* __restrict__ skeys, uint32_t n,
     uint32_t S, uint32_t SP, uint32_t half_bits, uint32_t lists, uint32_t t, uint32_t route,
     RowState* __restrict__ states, RowCtr* __restrict__ rctr, CallState* cs, WsHeader* hdr,
     uint32_t* __restrict__ shist, uint64_t sig) {
   // (the arguments the gather needs come first: the first 14 words of the
   // argument block arrive in scalar registers with the launch)
-  static_assert(NT == SAMPLE_THREADS || NT == SAMPLE_THREADS_SORTED, "two workgroup sizes");
   __shared__ uint32_t h[SH_BINS];
-  __shared__ uint32_t s_wl[NT / 64 * TOPT], s_wc[8], s_out[TOPT], s_m[NT / 128 * TOPT];
+  __shared__ uint32_t s_wl[4 * TOPT], s_out[TOPT], s_m[2 * TOPT];
   const uint32_t row = blockIdx.y, tid = threadIdx.x;
-  const uint32_t j = blockIdx.x * NT + tid;
+  const uint32_t j = blockIdx.x * SAMPLE_THREADS + tid;
   const bool in = j < S;
   // The gather goes out first, unconditionally (a lane past S reads element
   // 0 and drops it): the rest of the set-up overlaps its latency, and the
@@ -342,7 +284,7 @@ __global__ __launch_bounds__(NT) void k_sample(
     start_sampled_row(states + row, rctr + row, 0u, route);
   uint32_t* gh = shist + (size_t)row * SH_BINS;
   if (gh_ok) {
-    for (uint32_t i = tid; i < SH_BINS; i += NT) h[i] = 0;
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS) h[i] = 0;
     __syncthreads();
   }
   uint32_t key = 0;
@@ -356,22 +298,18 @@ __global__ __launch_bounds__(NT) void k_sample(
   if (!lists) {
     if (!gh_ok) return;
     __syncthreads();
-    for (uint32_t i = tid; i < SH_BINS; i += NT)
+    for (uint32_t i = tid; i < SH_BINS; i += SAMPLE_THREADS)
       if (h[i]) atomicAdd(&gh[i], h[i]);
     return;
   }
   // this workgroup's t largest keys, zero-padded
-  uint32_t c = TOPT;
-  if constexpr (NT == SAMPLE_THREADS) {
-    if (t <= TOPT_EXTRACT) c = block_top_t(key, j < S, t, s_wl, s_wc, s_out);
-    else block_top32_sorted(j < S ? key : 0u, s_wl, s_m, s_out);
-  } else {
-    block_top32_sorted_n<NT / 64>(j < S ? key : 0u, s_wl, s_m, s_out);
-  }
-  // (t > TOPT_EXTRACT: all TOPT sorted keys; the union of these longer lists
-  // still holds the t largest sampled keys, each list its own largest first)
+  // (sorted by Batcher's network even for t <= TOPT_EXTRACT: as fast as
+  // extracting t keys one at a time up to t = 2, faster above; t > TOPT_EXTRACT
+  // keeps all TOPT sorted keys: the union of these longer lists still holds
+  // the t largest sampled keys, each list its own largest first)
+  block_top32_sorted(j < S ? key : 0u, s_wl, s_m, s_out);
   const uint32_t len = t <= TOPT_EXTRACT ? t : TOPT;
-  if (tid < len) skeys[(size_t)row * SP + blockIdx.x * len + tid] = tid < c ? s_out[tid] : 0u;
+  if (tid < len) skeys[(size_t)row * SP + blockIdx.x * len + tid] = s_out[tid];
 }
 
 // ======================================================================
