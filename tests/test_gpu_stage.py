@@ -193,6 +193,46 @@ def test_forced_threshold_drives_detection(dt):
             assert st["path"] == 1
 
 
+def _bf16_special_row(n, seed):
+    """bf16 bits of every kind: spread normals of both signs, +-0, +-inf, NaN
+    of both signs with several payloads, denormals of both signs, and the
+    largest finite values; shuffled."""
+    g = workloads.rng(seed)
+    x = workloads.f32_to_bf16_bits(g.standard_normal(size=n).astype(np.float32) * 3.0)
+    picks = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0x7FFF, 0xFFC0, 0xFF81,
+                      0xFFFF, 0x0001, 0x8001, 0x007F, 0x807F, 0x7F7F, 0xFF7F, 0x3F80, 0xBF80],
+                     dtype=np.uint16)
+    m = n // 20
+    x[:m] = g.choice(picks, size=m)
+    g.shuffle(x)
+    return x.reshape(1, n)
+
+
+def test_bf16_screen_every_threshold_kind():
+    """The bf16 filter screens each 16-byte vector on the magnitude bits of
+    its eight elements and tests flagged vectors exactly.  Thresholds given
+    from the host across every kind of bf16 value (negative, -0/+0, a
+    denormal, +1, the largest finite, +inf, NaN): the survivor count R must
+    equal the number of elements whose order-preserving key reaches tau (the
+    definition, counted on the CPU), and the output the exact top-k."""
+    tss = _tss()
+    n, k = 2 ** 20 + 3, 100
+    x = _bf16_special_row(n, 1201)
+    xt = to_dev(x, "bf16")
+    kk = oracle.keys(x[0], "bf16").astype(np.int64)
+    for bits in (0xBF80, 0x8001, 0x8000, 0x0000, 0x0001, 0x3F80, 0x7F7F, 0x7F80):
+        key = int(oracle.keys(np.array([bits], dtype=np.uint16), "bf16")[0])
+        for tk in (key, 0xFFFF if bits == 0x7F80 else key):
+            p = _seeded(7, use_force_tau=1, force_tau_key=tk, M=n)
+            say(f"bf16 screen: tau bits {bits:#06x} key {tk:#06x}")
+            v, i = tss.topk(xt, k, params=p)
+            torch.cuda.synchronize()
+            assert_same(vals_to_host(v, "bf16"), i.cpu().numpy(), x, k, "bf16", f"tau key {tk:#x}")
+            st = tss.read_stats(1)[0]
+            assert st["r_sampled"] == int((kk >= tk).sum()), (hex(tk), st)
+            assert st["ties"] == int((kk == tk).sum()), (hex(tk), st)
+
+
 # ------------------------------------------------------------ relaxed recall, ties at tau
 @pytest.mark.parametrize("dt", ["float32", "bf16"])
 def test_relaxed_recall_heavy_ties_every_workgroup_agrees(dt):

@@ -357,6 +357,16 @@ __global__ __launch_bounds__(LK_THREADS) void k_lk_sort(
       const uint64_t dbase = (uint64_t)(LK_BINS - 1 - r_last) << sb;
       ok = block_sort_binned_desc(s_a, len, s_b, s_hist, s_sm, reinterpret_cast<uint32_t*>(s_red),
                                   [&](uint64_t v) { return (uint32_t)((v >> dsh) - dbase); }, 64u);
+    } else if (nb > 2048) {
+      // more buckets than bins (the first windows, where the largest keys are
+      // sparse): 2^sm neighbouring buckets per bin
+      uint32_t sm = 1;
+      while (((nb - 1) >> sm) >= 2048u) ++sm;
+      const uint64_t dbase = (uint64_t)(LK_BINS - 1 - r_last);
+      ok = block_sort_binned_desc(s_a, len, s_b, s_hist, s_sm, reinterpret_cast<uint32_t*>(s_red),
+                                  [&](uint64_t v) { return (uint32_t)(((v >> g.shift) - dbase) >> sm); },
+                                  64u);
+      if (!ok) ok = block_sort_unique_desc(s_a, len, s_b, s_hist, s_sm, s_red, 64u);
     } else {
       ok = block_sort_unique_desc(s_a, len, s_b, s_hist, s_sm, s_red, 64u);
     }
