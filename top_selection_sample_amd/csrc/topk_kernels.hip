@@ -198,9 +198,17 @@ hipError_t launch_pipeline(const LaunchArgs& a) {
       mark(STAGE_FILTER, 1);
       // after k_tau (all keys) every row's sample histogram is zero again
       WsHeader* validate = lists ? nullptr : a.hdr;
-      TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
-                  in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr,
-                  a.cbuf, a.aux, validate, p.sig, a.filter_trace, a.trace_wgs);
+      // (the merge of sorted lists selects tau last: a third step of the
+      // stream is loaded before it)
+      if (in_filter && p.t > (int64_t)TOPT_EXTRACT) {
+        TK_DISPATCH(dt, k_filter_ahead3, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys,
+                    a.states, n, ns, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u, a.rctr,
+                    a.cbuf, a.aux, validate, p.sig, a.filter_trace, a.trace_wgs);
+      } else {
+        TK_DISPATCH(dt, k_filter, fg, dim3(FILTER_THREADS), 0, s, a.values, a.skeys, a.states, n,
+                    in_filter ? ns : 0u, (uint32_t)p.SP, (uint32_t)p.t, fg.x, cap, B, 1u,
+                    a.rctr, a.cbuf, a.aux, validate, p.sig, a.filter_trace, a.trace_wgs);
+      }
       mark(STAGE_FILTER, 0);
     } else {
       hipLaunchKernelGGL(k_setup_exact, tiny, dim3(64), 0, s, a.states, a.call, a.flagged, rows,
