@@ -9,6 +9,8 @@
 //   k_sample       S sample keys per row through a keyed permutation
 //   k_tau          workgroup radix select of the t-th largest sample key
 //   k_filter       the streaming pass: keep composites with key >= tau
+//                  (k_filter_ahead3: the same with three steps loaded before
+//                  tau, for the merge of sorted lists)
 //   k_check        many rows: list the rows whose candidate count fails
 //   k_setup_exact  rows that start on the exact path
 //   k_finish       the check, the refine of every accepted row (small k: select,
